@@ -1,0 +1,110 @@
+"""Seeded synthetic inputs for the attention forward pass.
+
+This module only draws numbers and names workloads; it holds none of the
+attention arithmetic.  Both the GPU path's tests and the oracle consume what it
+returns, so neither side generates its own inputs.
+
+Recipe (the same on every machine, CPU generator only):
+  * ``torch.Generator('cpu').manual_seed(seed)``;
+  * q, k, v drawn in that order with ``torch.randn`` in float32, multiplied by
+    ``std``, then cast to bfloat16 (round to nearest even);
+  * ``hot_row_frac > 0``: a Bernoulli(hot_row_frac) mask over the (b, i, hq)
+    query rows, drawn after v from the same generator with ``torch.rand``;
+    selected rows are multiplied by ``hot_row_mult`` in float32 before the cast
+    (8 is a power of two, so the bf16 values are exactly 8x the plain draw).
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import torch
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Sq: int
+    Sk: int
+    D: int
+    causal: bool
+    o_dtype: str = "bf16"          # "bf16" or "f32"
+    std: float = 1.0
+    hot_row_frac: float = 0.0
+    hot_row_mult: float = 1.0
+    seed: int = 0
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+    def allowed_pairs(self) -> int:
+        """Allowed (query, key) pairs over all (b, hq)."""
+        if not self.causal:
+            per_head = self.Sq * self.Sk
+        else:
+            per_head = 0
+            off = self.Sk - self.Sq
+            # rows i with i + off + 1 keys (clamped to [0, Sk])
+            for i in range(self.Sq):
+                per_head += min(max(i + off + 1, 0), self.Sk)
+        return per_head * self.B * self.Hq
+
+    def flops(self) -> int:
+        """Algorithmic FLOPs: 4*D per allowed pair (2*D for QK^T, 2*D for PV)."""
+        return 4 * self.D * self.allowed_pairs()
+
+    def hbm_bytes(self) -> int:
+        """Algorithmic bytes: Q, K, V read once, O and LSE written once."""
+        q = self.B * self.Sq * self.Hq * self.D * 2
+        kv = 2 * self.B * self.Sk * self.Hkv * self.D * 2
+        o = self.B * self.Sq * self.Hq * self.D * (4 if self.o_dtype == "f32" else 2)
+        lse = self.B * self.Hq * self.Sq * 4
+        return q + kv + o + lse
+
+
+# The five workloads of the benchmark suite, named by what they are.
+WORKLOADS = {
+    w.name: w for w in [
+        Workload("single_head_s128_d64", B=1, Hq=1, Hkv=1, Sq=128, Sk=128, D=64,
+                 causal=False, o_dtype="f32", seed=0),
+        Workload("causal_b2_h8_s1024_d64", B=2, Hq=8, Hkv=8, Sq=1024, Sk=1024, D=64,
+                 causal=True, seed=1),
+        Workload("causal_b4_h16_s4096_d128", B=4, Hq=16, Hkv=16, Sq=4096, Sk=4096, D=128,
+                 causal=True, hot_row_frac=0.01, hot_row_mult=8.0, seed=2),
+        Workload("decode_b32_hq32_hkv8_sk8192_d128", B=32, Hq=32, Hkv=8, Sq=1, Sk=8192,
+                 D=128, causal=False, seed=3),
+        Workload("gqa_b1_hq32_hkv8_s16384_d128", B=1, Hq=32, Hkv=8, Sq=16384, Sk=16384,
+                 D=128, causal=False, std=0.5, seed=4),
+    ]
+}
+
+
+def make_inputs(w: Workload, seed: int | None = None, device: str = "cpu"):
+    """Return (q, k, v) bf16 tensors: q [B,Sq,Hq,D], k/v [B,Sk,Hkv,D]."""
+    g = torch.Generator("cpu")
+    g.manual_seed(w.seed if seed is None else seed)
+    q = torch.randn((w.B, w.Sq, w.Hq, w.D), generator=g, dtype=torch.float32)
+    k = torch.randn((w.B, w.Sk, w.Hkv, w.D), generator=g, dtype=torch.float32)
+    v = torch.randn((w.B, w.Sk, w.Hkv, w.D), generator=g, dtype=torch.float32)
+    if w.std != 1.0:
+        q.mul_(w.std)
+        k.mul_(w.std)
+        v.mul_(w.std)
+    if w.hot_row_frac > 0.0:
+        hot = torch.rand((w.B, w.Sq, w.Hq), generator=g) < w.hot_row_frac
+        q = torch.where(hot.unsqueeze(-1), q * w.hot_row_mult, q)
+    q, k, v = (t.to(torch.bfloat16) for t in (q, k, v))
+    if device != "cpu":
+        q, k, v = (t.to(device) for t in (q, k, v))
+    return q, k, v
+
+
+def random_qkv(B, Hq, Hkv, Sq, Sk, D, seed, std=1.0, device="cpu"):
+    """Ad-hoc shapes for tests: same recipe, no hot rows."""
+    w = Workload("adhoc", B=B, Hq=Hq, Hkv=Hkv, Sq=Sq, Sk=Sk, D=D, causal=False,
+                 std=std, seed=seed)
+    return make_inputs(w, device=device)

@@ -1,0 +1,125 @@
+"""Double-precision CPU oracle for the attention forward pass.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package; the library under
+``attention_fwd_02_amd`` never does, and the two share no code.
+
+The arithmetic lives in ``oracle.c`` (plain C, fp64, libm ``exp``/``log``,
+pthreads over rows); this module only loads it with ctypes and marshals numpy
+arrays.  ``oracle.c`` documents which passage of the pages each step follows
+and every reading taken where the pages are silent.
+
+Parity status: pinned.  ``tests/test_oracle.py`` checks it against a 40-digit
+``decimal`` brute force, a torch fp64 library evaluation of the same
+definition, closed forms worked out by hand, invariants and layout probes;
+``tests/test_oracle_mutants.py`` shows that planted slips fail those pins.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so with gcc (-O2, no fast-math)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(
+            ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread", "-Wall",
+             "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB):
+        build(force=False)
+    _lib = _bind(ctypes.CDLL(_LIB))
+    return _lib
+
+
+def _bind(lib):
+    lib.oracle_attn_fwd.restype = ctypes.c_int
+    lib.oracle_attn_fwd.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_int,
+        ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+    lib.oracle_allowed_pairs.restype = ctypes.c_int64
+    lib.oracle_allowed_pairs.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    return lib
+
+
+def _bits(x) -> np.ndarray:
+    """bf16 data as a contiguous uint16 numpy array (accepts torch or numpy)."""
+    if hasattr(x, "detach"):  # torch tensor
+        import torch
+        t = x.detach()
+        if t.device.type != "cpu":
+            t = t.cpu()
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"oracle expects bfloat16 inputs, got {t.dtype}")
+        return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+    a = np.ascontiguousarray(x)
+    if a.dtype != np.uint16:
+        raise TypeError("numpy inputs must be raw bf16 bits (uint16)")
+    return a
+
+
+def default_threads() -> int:
+    n = os.cpu_count() or 1
+    return max(1, n)
+
+
+def attn_fwd(q, k, v, causal: bool, scale: float, *, rows=None,
+             key_range=None, nthreads: int | None = None, _lib_override=None):
+    """Run the oracle.
+
+    q: [B, Sq, Hq, D] bf16; k, v: [B, Sk, Hkv, D] bf16.
+    rows: None for every row, else an int64 array [n, 3] of (b, hq, i).
+    key_range: None for all keys, else (begin, end).
+    Returns (o, lse) as float64 numpy arrays: o [B,Sq,Hq,D] / lse [B,Hq,Sq],
+    or o [n, D] / lse [n] when rows is given.
+    """
+    lib = _lib_override if _lib_override is not None else _load()
+    qb, kb, vb = _bits(q), _bits(k), _bits(v)
+    if qb.ndim != 4 or kb.ndim != 4 or vb.ndim != 4:
+        raise ValueError("q, k, v must be 4-D [B, S, H, D]")
+    B, Sq, Hq, D = qb.shape
+    Bk, Sk, Hkv, Dk = kb.shape
+    if (Bk, Dk) != (B, D) or vb.shape != kb.shape:
+        raise ValueError("shape mismatch between q, k, v")
+    kr = (0, Sk) if key_range is None else (int(key_range[0]), int(key_range[1]))
+    if rows is None:
+        o = np.empty((B, Sq, Hq, D), dtype=np.float64)
+        lse = np.empty((B, Hq, Sq), dtype=np.float64)
+        rows_p, n_rows = None, 0
+    else:
+        r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1, 3))
+        n_rows = r.shape[0]
+        o = np.empty((n_rows, D), dtype=np.float64)
+        lse = np.empty((n_rows,), dtype=np.float64)
+        rows_p = r.ctypes.data
+    nt = default_threads() if nthreads is None else int(nthreads)
+    rc = lib.oracle_attn_fwd(qb.ctypes.data, kb.ctypes.data, vb.ctypes.data,
+                             B, Hq, Hkv, Sq, Sk, D, int(bool(causal)), float(scale),
+                             kr[0], kr[1], rows_p, n_rows, o.ctypes.data, lse.ctypes.data, nt)
+    if rc != 0:
+        raise RuntimeError(f"oracle_attn_fwd failed with code {rc}")
+    return o, lse
+
+
+def allowed_pairs(Sq: int, Sk: int, causal: bool) -> int:
+    """Allowed (query, key) pairs of one head: the unit of algorithmic work."""
+    return int(_load().oracle_allowed_pairs(Sq, Sk, int(bool(causal))))

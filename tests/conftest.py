@@ -1,0 +1,24 @@
+"""Shared pytest configuration.
+
+Tests marked ``gpu`` need an MI355X (gfx950) and the built HIP library; every
+other test runs on the CPU alone.
+"""
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X GPU and the built HIP library")
+
+
+@pytest.fixture(scope="session")
+def oracle_mod():
+    import oracle
+    oracle._load()  # builds liboracle.so if nothing is built yet
+    return oracle

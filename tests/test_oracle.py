@@ -1,0 +1,349 @@
+"""Pins for the fp64 oracle (CPU only).
+
+The oracle is the plain definition softmax(scale * Q K^T [+ causal mask]) V plus
+the row log-sum-exp.  Nothing here re-calls the oracle's own code to check it:
+each test compares it with something else that fixes the answer --
+
+  * a 40-digit ``decimal`` brute force on tiny inputs;
+  * torch's float64 ``softmax`` / ``logsumexp`` (a library evaluation of the
+    same definition) on medium shapes;
+  * closed forms worked out by hand: one key, two keys, uniform scores,
+    causal first row, constant V;
+  * invariants: key permutation, GQA == MHA with repeated KV heads, key
+    partition + log-sum-exp merge, sign of the scale;
+  * layout probes whose answer is known from where each value was placed.
+
+Each is chosen so that a plausible slip (a dropped term, the causal offset on
+the wrong side, the GQA head map hq % Hkv instead of hq // group, q and k
+swapped, a transposed layout) fails at least one of them.
+"""
+from __future__ import annotations
+
+import decimal
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from attention_fwd_02_amd.inputs import random_qkv
+
+pytestmark = []
+
+
+def bf16(x) -> torch.Tensor:
+    return torch.as_tensor(x, dtype=torch.float32).to(torch.bfloat16)
+
+
+# ----------------------------------------------------------------------------
+# brute force in 40-digit decimal arithmetic
+# ----------------------------------------------------------------------------
+def decimal_reference(q, k, v, causal, scale, key_range=None):
+    ctx = decimal.Context(prec=40)
+    qf = q.float().numpy().astype(np.float64)
+    kf = k.float().numpy().astype(np.float64)
+    vf = v.float().numpy().astype(np.float64)
+    B, Sq, Hq, D = qf.shape
+    _, Sk, Hkv, _ = kf.shape
+    group = Hq // Hkv
+    sc = decimal.Decimal(float(np.float32(scale)))
+    lo, hi = (0, Sk) if key_range is None else key_range
+    o = np.zeros((B, Sq, Hq, D))
+    lse = np.zeros((B, Hq, Sq))
+    for b in range(B):
+        for h in range(Hq):
+            g = h // group
+            for i in range(Sq):
+                keys = [j for j in range(lo, hi) if (not causal) or j <= i + Sk - Sq]
+                if not keys:
+                    lse[b, h, i] = -math.inf
+                    continue
+                s = {}
+                for j in keys:
+                    acc = decimal.Decimal(0)
+                    for d in range(D):
+                        acc = ctx.add(acc, ctx.multiply(decimal.Decimal(qf[b, i, h, d]),
+                                                        decimal.Decimal(kf[b, j, g, d])))
+                    s[j] = ctx.multiply(sc, acc)
+                m = max(s.values())
+                w = {j: ctx.exp(ctx.subtract(s[j], m)) for j in keys}
+                l_sum = decimal.Decimal(0)
+                for j in keys:
+                    l_sum = ctx.add(l_sum, w[j])
+                for d in range(D):
+                    acc = decimal.Decimal(0)
+                    for j in keys:
+                        acc = ctx.add(acc, ctx.multiply(w[j], decimal.Decimal(vf[b, j, g, d])))
+                    o[b, i, h, d] = float(ctx.divide(acc, l_sum))
+                lse[b, h, i] = float(ctx.add(m, ctx.ln(l_sum)))
+    return o, lse
+
+
+BRUTE_CASES = [
+    # B, Hq, Hkv, Sq, Sk, D, causal, scale, key_range
+    (1, 1, 1, 4, 4, 4, False, 0.5, None),
+    (1, 1, 1, 5, 5, 8, True, 0.35355339, None),
+    (2, 4, 2, 3, 7, 4, True, 0.5, None),        # GQA, Sq < Sk causal
+    (1, 2, 1, 7, 3, 4, True, 0.5, None),        # Sq > Sk causal: empty rows
+    (1, 2, 2, 4, 6, 8, False, -0.7, None),      # negative scale
+    (1, 3, 1, 4, 8, 4, False, 0.25, (2, 6)),    # key sub-range, MQA
+    (1, 2, 1, 6, 6, 4, True, 0.5, (1, 5)),      # key sub-range with causal
+]
+
+
+@pytest.mark.parametrize("case", BRUTE_CASES)
+def test_oracle_matches_decimal_bruteforce(oracle_mod, case):
+    B, Hq, Hkv, Sq, Sk, D, causal, scale, kr = case
+    q, k, v = random_qkv(B, Hq, Hkv, Sq, Sk, D, seed=11 + Sq * 7 + D)
+    o, lse = oracle_mod.attn_fwd(q, k, v, causal, scale, key_range=kr)
+    o_ref, lse_ref = decimal_reference(q, k, v, causal, scale, key_range=kr)
+    fin = np.isfinite(lse_ref)
+    assert np.array_equal(np.isfinite(lse), fin)
+    assert np.all(lse[~fin] == -np.inf)
+    np.testing.assert_allclose(lse[fin], lse_ref[fin], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(o, o_ref, rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# library evaluation of the same definition (torch, float64, CPU)
+# ----------------------------------------------------------------------------
+def torch_reference(q, k, v, causal, scale):
+    qd, kd, vd = (t.double() for t in (q, k, v))
+    B, Sq, Hq, D = qd.shape
+    Sk, Hkv = kd.shape[1], kd.shape[2]
+    kd = kd.repeat_interleave(Hq // Hkv, dim=2)
+    vd = vd.repeat_interleave(Hq // Hkv, dim=2)
+    s = torch.einsum("bihd,bjhd->bhij", qd, kd) * float(np.float32(scale))
+    if causal:
+        i = torch.arange(Sq).view(-1, 1)
+        j = torch.arange(Sk).view(1, -1)
+        s = s.masked_fill(j > i + (Sk - Sq), -math.inf)
+    lse = torch.logsumexp(s, dim=-1)
+    p = torch.softmax(s, dim=-1)
+    o = torch.einsum("bhij,bjhd->bihd", p, vd)
+    return o.numpy(), lse.numpy()
+
+
+@pytest.mark.parametrize("shape", [
+    (1, 2, 2, 128, 128, 64, False),
+    (2, 4, 2, 96, 160, 64, True),
+    (1, 8, 2, 200, 200, 128, True),
+    (1, 4, 1, 1, 300, 128, False),
+    (1, 2, 2, 257, 129, 64, False),
+])
+def test_oracle_matches_torch_float64(oracle_mod, shape):
+    B, Hq, Hkv, Sq, Sk, D, causal = shape
+    q, k, v = random_qkv(B, Hq, Hkv, Sq, Sk, D, seed=Sq + Sk)
+    scale = 1.0 / math.sqrt(D)
+    o, lse = oracle_mod.attn_fwd(q, k, v, causal, scale)
+    o_ref, lse_ref = torch_reference(q, k, v, causal, scale)
+    np.testing.assert_allclose(lse, lse_ref, rtol=0, atol=1e-10)
+    np.testing.assert_allclose(o, o_ref, rtol=0, atol=1e-10)
+
+
+# ----------------------------------------------------------------------------
+# closed forms
+# ----------------------------------------------------------------------------
+def test_single_key_gives_that_value_row(oracle_mod):
+    # one key: the softmax weight is exactly 1, O = v0, LSE = s0
+    q = bf16([[[[1.0, 2.0, 0.0, -1.0]]]])
+    k = bf16([[[[0.5, 0.25, 3.0, 2.0]]]])
+    v = bf16([[[[7.0, -3.0, 0.125, 1.5]]]])
+    o, lse = oracle_mod.attn_fwd(q, k, v, False, 0.5)
+    s0 = 0.5 * (0.5 + 0.5 + 0.0 - 2.0)
+    assert lse[0, 0, 0] == pytest.approx(s0, abs=1e-15)
+    np.testing.assert_array_equal(o[0, 0, 0], [7.0, -3.0, 0.125, 1.5])
+
+
+def test_two_keys_closed_form(oracle_mod):
+    # q = e0, k0 = 2 e0, k1 = -e0, scale 0.5: scores s0 = 1, s1 = -0.5
+    q = bf16([[[[1.0, 0.0]]]])
+    k = bf16([[[[2.0, 0.0]], [[-1.0, 0.0]]]])
+    v = bf16([[[[1.0, 2.0]], [[3.0, -1.0]]]])
+    o, lse = oracle_mod.attn_fwd(q, k, v, False, 0.5)
+    s0, s1 = 1.0, -0.5
+    want_lse = math.log(math.exp(s0) + math.exp(s1))
+    p0 = 1.0 / (1.0 + math.exp(s1 - s0))  # logistic of the score gap
+    p1 = 1.0 - p0
+    assert lse[0, 0, 0] == pytest.approx(want_lse, abs=1e-14)
+    np.testing.assert_allclose(o[0, 0, 0], [p0 * 1 + p1 * 3, p0 * 2 - p1 * 1], atol=1e-14)
+
+
+@pytest.mark.parametrize("Sq,Sk", [(3, 5), (5, 3), (6, 6), (1, 9)])
+def test_uniform_scores_lse_is_log_count_and_o_is_prefix_mean(oracle_mod, Sq, Sk):
+    # scale = 0 makes every allowed score 0: LSE = ln(#allowed), O = mean of allowed V
+    q, k, v = random_qkv(1, 2, 1, Sq, Sk, 8, seed=5)
+    o, lse = oracle_mod.attn_fwd(q, k, v, True, 0.0)
+    vf = v.double().numpy()
+    for h in range(2):
+        for i in range(Sq):
+            n = min(max(i + Sk - Sq + 1, 0), Sk)
+            if n == 0:
+                assert lse[0, h, i] == -math.inf
+                assert np.all(o[0, i, h] == 0.0)
+            else:
+                assert lse[0, h, i] == pytest.approx(math.log(n), abs=1e-14)
+                np.testing.assert_allclose(o[0, i, h], vf[0, :n, 0].mean(axis=0), atol=1e-14)
+
+
+def test_zero_q_is_uniform_too(oracle_mod):
+    q, k, v = random_qkv(1, 1, 1, 4, 10, 8, seed=9)
+    q = torch.zeros_like(q)
+    o, lse = oracle_mod.attn_fwd(q, k, v, False, 0.125)
+    assert np.allclose(lse, math.log(10), atol=1e-14)
+    np.testing.assert_allclose(o[0, :, 0], np.broadcast_to(v.double().numpy()[0, :, 0].mean(0), (4, 8)),
+                               atol=1e-14)
+
+
+def test_causal_first_row_is_v0(oracle_mod):
+    q, k, v = random_qkv(2, 4, 2, 16, 16, 64, seed=3)
+    scale = 0.125
+    o, lse = oracle_mod.attn_fwd(q, k, v, True, scale)
+    qd, kd, vd = (t.double().numpy() for t in (q, k, v))
+    for b in range(2):
+        for h in range(4):
+            g = h // 2
+            np.testing.assert_array_equal(o[b, 0, h], vd[b, 0, g])
+            s00 = float(np.float32(scale)) * float(qd[b, 0, h] @ kd[b, 0, g])
+            assert lse[b, h, 0] == pytest.approx(s00, abs=1e-12)
+
+
+def test_causal_last_row_sees_every_key(oracle_mod):
+    q, k, v = random_qkv(1, 2, 2, 24, 24, 64, seed=4)
+    oc, lc = oracle_mod.attn_fwd(q, k, v, True, 0.125)
+    on, ln_ = oracle_mod.attn_fwd(q, k, v, False, 0.125)
+    np.testing.assert_allclose(oc[:, -1], on[:, -1], atol=1e-14)
+    np.testing.assert_allclose(lc[:, :, -1], ln_[:, :, -1], atol=1e-14)
+    # and an interior row differs (the mask is not a no-op)
+    assert not np.allclose(oc[:, 5], on[:, 5])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_constant_v_gives_constant_o(oracle_mod, causal):
+    q, k, _ = random_qkv(1, 2, 1, 12, 12, 64, seed=6)
+    v = torch.full((1, 12, 1, 64), 1.75, dtype=torch.bfloat16)
+    o, _ = oracle_mod.attn_fwd(q, k, v, causal, 0.3)
+    np.testing.assert_allclose(o, 1.75, atol=1e-14)
+
+
+# ----------------------------------------------------------------------------
+# invariants
+# ----------------------------------------------------------------------------
+def test_key_permutation_invariance(oracle_mod):
+    q, k, v = random_qkv(2, 2, 2, 20, 33, 64, seed=7)
+    perm = torch.randperm(33, generator=torch.Generator().manual_seed(1))
+    o1, l1 = oracle_mod.attn_fwd(q, k, v, False, 0.125)
+    o2, l2 = oracle_mod.attn_fwd(q, k[:, perm].contiguous(), v[:, perm].contiguous(), False, 0.125)
+    np.testing.assert_allclose(o1, o2, atol=1e-13)
+    np.testing.assert_allclose(l1, l2, atol=1e-13)
+
+
+def test_gqa_equals_mha_with_repeated_kv_heads(oracle_mod):
+    q, k, v = random_qkv(2, 8, 2, 10, 14, 64, seed=8)
+    o1, l1 = oracle_mod.attn_fwd(q, k, v, True, 0.125)
+    k4 = k.repeat_interleave(4, dim=2).contiguous()
+    v4 = v.repeat_interleave(4, dim=2).contiguous()
+    o2, l2 = oracle_mod.attn_fwd(q, k4, v4, True, 0.125)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+
+
+def test_negative_scale_equals_negated_query(oracle_mod):
+    q, k, v = random_qkv(1, 2, 2, 9, 9, 64, seed=10)
+    o1, l1 = oracle_mod.attn_fwd(q, k, v, True, -0.2)
+    o2, l2 = oracle_mod.attn_fwd(-q, k, v, True, 0.2)
+    np.testing.assert_allclose(o1, o2, atol=1e-14)
+    np.testing.assert_allclose(l1, l2, atol=1e-14)
+
+
+def lse_merge(parts):
+    """Combine per-partition (O_s, LSE_s) into the whole: the merge the split
+    decode path performs, written out in float64."""
+    lses = np.stack([p[1] for p in parts])            # [S, ...]
+    M = np.max(lses, axis=0)
+    Msafe = np.where(np.isfinite(M), M, 0.0)
+    w = np.where(np.isfinite(lses), np.exp(lses - Msafe), 0.0)
+    wsum = w.sum(axis=0)
+    lse = np.where(wsum > 0, Msafe + np.log(np.where(wsum > 0, wsum, 1.0)), -np.inf)
+    o = sum(wi[..., None] * p[0] for wi, p in zip(w, parts))
+    o = np.where(wsum[..., None] > 0, o / np.where(wsum > 0, wsum, 1.0)[..., None], 0.0)
+    return o, lse
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_key_partition_merge_equals_whole(oracle_mod, causal):
+    B, Hq, Hkv, Sq, Sk, D = 1, 4, 2, 6, 50, 64
+    q, k, v = random_qkv(B, Hq, Hkv, Sq, Sk, D, seed=12)
+    o, lse = oracle_mod.attn_fwd(q, k, v, causal, 0.125)
+    rng = np.random.default_rng(0)
+    cuts = sorted(rng.choice(np.arange(1, Sk), size=4, replace=False).tolist())
+    bounds = [0] + cuts + [Sk]
+    parts = []
+    for a, b in zip(bounds[:-1], bounds[1:]):
+        po, pl = oracle_mod.attn_fwd(q, k, v, causal, 0.125, key_range=(a, b))
+        # rows are (b, i, h, d) for o and (b, h, i) for lse: bring o to (b, h, i, d)
+        parts.append((po.transpose(0, 2, 1, 3), pl))
+    mo, ml = lse_merge(parts)
+    np.testing.assert_allclose(mo.transpose(0, 2, 1, 3), o, atol=1e-13)
+    np.testing.assert_allclose(ml, lse, atol=1e-13)
+
+
+# ----------------------------------------------------------------------------
+# layout probes
+# ----------------------------------------------------------------------------
+def test_layout_of_v_o_and_lse(oracle_mod):
+    # scale 0 and non-causal: O[b,i,hq,:] = mean_j V[b,j,g,:]; V encodes its own position
+    B, Hq, Hkv, Sq, Sk, D = 2, 4, 2, 3, 5, 4
+    v = torch.zeros((B, Sk, Hkv, D))
+    for b in range(B):
+        for j in range(Sk):
+            for g in range(Hkv):
+                for d in range(D):
+                    v[b, j, g, d] = 64 * b + 16 * g + d + (j - 2)   # mean over j adds 0
+    v = v.to(torch.bfloat16)
+    q = torch.zeros((B, Sq, Hq, D), dtype=torch.bfloat16)
+    k = torch.zeros((B, Sk, Hkv, D), dtype=torch.bfloat16)
+    o, lse = oracle_mod.attn_fwd(q, k, v, False, 0.0)
+    for b in range(B):
+        for i in range(Sq):
+            for h in range(Hq):
+                g = h // 2
+                np.testing.assert_allclose(o[b, i, h], [64 * b + 16 * g + d for d in range(D)],
+                                           atol=1e-12)
+    assert np.allclose(lse, math.log(Sk))
+
+
+def test_layout_of_q_and_k(oracle_mod):
+    # one query row (b=1, i=2, hq=3) aligned with one key (b=1, j=4, g=1); all
+    # other scores are 0.  With a large scale that row picks V[1,4,1] exactly.
+    B, Hq, Hkv, Sq, Sk, D = 2, 4, 2, 3, 6, 8
+    q = torch.zeros((B, Sq, Hq, D))
+    k = torch.zeros((B, Sk, Hkv, D))
+    q[1, 2, 3, 5] = 1.0
+    k[1, 4, 1, 5] = 1.0
+    v = torch.arange(B * Sk * Hkv * D, dtype=torch.float32).reshape(B, Sk, Hkv, D)
+    q, k, v = (t.to(torch.bfloat16) for t in (q, k, v))
+    o, lse = oracle_mod.attn_fwd(q, k, v, False, 200.0)
+    vd = v.double().numpy()
+    np.testing.assert_allclose(o[1, 2, 3], vd[1, 4, 1], rtol=1e-12)
+    assert lse[1, 3, 2] == pytest.approx(200.0, abs=1e-9)
+    # the same query slot in other heads / batches sees only zero scores
+    assert lse[0, 3, 2] == pytest.approx(math.log(Sk), abs=1e-14)
+    assert lse[1, 2, 2] == pytest.approx(math.log(Sk), abs=1e-14)
+
+
+def test_row_subset_matches_full(oracle_mod):
+    q, k, v = random_qkv(2, 4, 2, 33, 40, 64, seed=13)
+    o, lse = oracle_mod.attn_fwd(q, k, v, True, 0.125)
+    rows = np.array([[0, 0, 0], [1, 3, 32], [0, 2, 17], [1, 1, 5]], dtype=np.int64)
+    ro, rl = oracle_mod.attn_fwd(q, k, v, True, 0.125, rows=rows)
+    for n, (b, h, i) in enumerate(rows):
+        np.testing.assert_array_equal(ro[n], o[b, i, h])
+        assert rl[n] == lse[b, h, i]
+
+
+def test_allowed_pairs_count(oracle_mod):
+    assert oracle_mod.allowed_pairs(4096, 4096, True) == 4096 * 4097 // 2
+    assert oracle_mod.allowed_pairs(3, 5, True) == 3 + 4 + 5
+    assert oracle_mod.allowed_pairs(5, 3, True) == 0 + 0 + 1 + 2 + 3
+    assert oracle_mod.allowed_pairs(7, 9, False) == 63

@@ -1,0 +1,79 @@
+"""The oracle's pins must reject plausible slips.
+
+Each case copies oracle.c, plants one mistake in the copy (on the CPU, in a
+temporary directory), builds it, and runs the pin tests of test_oracle.py
+against the mutant; at least one pin has to fail.  The real oracle is never
+modified.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+import oracle as oracle_pkg
+from tests import test_oracle as pins
+
+MUTANTS = {
+    "gqa_head_map_modulo": ("const int g = hq / (J->Hq / J->Hkv);", "const int g = hq % J->Hkv;"),
+    "causal_offset_top_left": ("int64_t lim = (int64_t)i + J->Sk - J->Sq + 1;",
+                               "int64_t lim = (int64_t)i + 1;"),
+    "causal_off_by_one": ("int64_t lim = (int64_t)i + J->Sk - J->Sq + 1;",
+                          "int64_t lim = (int64_t)i + J->Sk - J->Sq;"),
+    "scale_dropped": ("double s = J->scale * dot;", "double s = dot;"),
+    "lse_base_two": ("*lse_out = m + log(l);", "*lse_out = m + log2(l);"),
+    "lse_without_max": ("*lse_out = m + log(l);", "*lse_out = log(l);"),
+    "v_indexed_by_query_head": (
+        "const uint16_t *vrow = J->v + (((int64_t)b * J->Sk + j) * J->Hkv + g) * D;",
+        "const uint16_t *vrow = J->v + (((int64_t)b * J->Sk + j) * J->Hkv + (hq % J->Hkv)) * D;"),
+    "key_row_uses_query_index": (
+        "const uint16_t *krow = J->k + (((int64_t)b * J->Sk + j) * J->Hkv + g) * D;",
+        "const uint16_t *krow = J->k + (((int64_t)b * J->Sk + (j + i) % J->Sk) * J->Hkv + g) * D;"),
+    "no_normalisation": ("        o_row[d] /= l;\n", "        o_row[d] /= 1.0;\n"),
+    "empty_row_lse_zero": ("        *lse_out = -INFINITY;\n        return 0;", "        *lse_out = 0.0;\n        return 0;"),
+}
+
+PIN_TESTS = [
+    lambda m: pins.test_oracle_matches_decimal_bruteforce(m, pins.BRUTE_CASES[2]),
+    lambda m: pins.test_oracle_matches_decimal_bruteforce(m, pins.BRUTE_CASES[3]),
+    lambda m: pins.test_two_keys_closed_form(m),
+    lambda m: pins.test_uniform_scores_lse_is_log_count_and_o_is_prefix_mean(m, 3, 5),
+    lambda m: pins.test_uniform_scores_lse_is_log_count_and_o_is_prefix_mean(m, 5, 3),
+    lambda m: pins.test_causal_first_row_is_v0(m),
+    lambda m: pins.test_gqa_equals_mha_with_repeated_kv_heads(m),
+    lambda m: pins.test_layout_of_v_o_and_lse(m),
+    lambda m: pins.test_layout_of_q_and_k(m),
+    lambda m: pins.test_single_key_gives_that_value_row(m),
+]
+
+
+class _Mutant:
+    """Quacks like the oracle package but calls the mutant library."""
+
+    def __init__(self, lib):
+        self._lib = lib
+
+    def attn_fwd(self, *a, **kw):
+        return oracle_pkg.attn_fwd(*a, _lib_override=self._lib, **kw)
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_reject_mutant(tmp_path, name):
+    before, after = MUTANTS[name]
+    src = open(os.path.join(os.path.dirname(oracle_pkg.__file__), "oracle.c")).read()
+    assert src.count(before) == 1, f"mutation anchor for {name} not found exactly once"
+    path_c = tmp_path / "mutant.c"
+    path_c.write_text(src.replace(before, after))
+    path_so = tmp_path / "libmutant.so"
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
+                           "-o", str(path_so), str(path_c), "-lm"])
+    mutant = _Mutant(oracle_pkg._bind(ctypes.CDLL(str(path_so))))
+    caught = 0
+    for pin in PIN_TESTS:
+        try:
+            pin(mutant)
+        except (AssertionError, RuntimeError):
+            caught += 1
+    assert caught > 0, f"no pin detects mutant {name}"
