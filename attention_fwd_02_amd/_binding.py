@@ -1,0 +1,155 @@
+"""ctypes binding of libfa.so: argument marshalling only.
+
+Every function here has the name of the C entry point it calls (include/fa.h)
+and does no arithmetic of its own: it checks that torch tensors have the
+layout the library expects, passes their device pointers and sizes, and turns
+a non-OK status into an exception.  If libfa.so is missing the import of this
+module fails loudly: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libfa.so")
+
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_NOMEM, FA_ERR_HIP = range(5)
+FA_DTYPE_BF16, FA_DTYPE_F32 = 0, 1
+STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_INVALID_ARG", 2: "FA_ERR_UNSUPPORTED",
+                3: "FA_ERR_NOMEM", 4: "FA_ERR_HIP"}
+
+# every symbol include/fa.h declares
+EXPORTS = ["fa_fwd", "fa_fwd_ex", "fa_workspace_size", "fa_plan", "fa_last_error",
+           "fa_release_workspace", "fa_version"]
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+class FaPlanInfo(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int), ("num_splits", ctypes.c_int),
+                ("block_m", ctypes.c_int), ("block_n", ctypes.c_int),
+                ("grid", ctypes.c_int), ("work_items", ctypes.c_int),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -m attention_fwd_02_amd.build` "
+            "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(LIB_PATH)
+    c_int, c_float, c_void_p, c_size_t = ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+    fwd_args = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_float, c_void_p]
+    lib.fa_fwd.argtypes = fwd_args
+    lib.fa_fwd.restype = c_int
+    lib.fa_fwd_ex.argtypes = fwd_args + [c_int, c_int, c_void_p, c_size_t]
+    lib.fa_fwd_ex.restype = c_int
+    lib.fa_workspace_size.argtypes = [c_int] * 7
+    lib.fa_workspace_size.restype = c_size_t
+    lib.fa_plan.argtypes = [c_int] * 8 + [ctypes.POINTER(FaPlanInfo)]
+    lib.fa_plan.restype = c_int
+    lib.fa_last_error.argtypes = []
+    lib.fa_last_error.restype = ctypes.c_char_p
+    lib.fa_release_workspace.argtypes = []
+    lib.fa_release_workspace.restype = c_int
+    lib.fa_version.argtypes = []
+    lib.fa_version.restype = c_int
+    return lib
+
+
+lib = _load()
+
+
+def _check(status: int):
+    if status != FA_OK:
+        raise FaError(status, (lib.fa_last_error() or b"").decode())
+
+
+def fa_last_error() -> str:
+    return (lib.fa_last_error() or b"").decode()
+
+
+def fa_version() -> int:
+    return lib.fa_version()
+
+
+def fa_release_workspace() -> None:
+    _check(lib.fa_release_workspace())
+
+
+def fa_workspace_size(B, Hq, Hkv, Sq, Sk, D, num_splits=0) -> int:
+    return int(lib.fa_workspace_size(B, Hq, Hkv, Sq, Sk, D, num_splits))
+
+
+def fa_plan(B, Hq, Hkv, Sq, Sk, D, causal=False, num_splits=0) -> dict:
+    info = FaPlanInfo()
+    _check(lib.fa_plan(B, Hq, Hkv, Sq, Sk, D, int(bool(causal)), num_splits, ctypes.byref(info)))
+    return {f: getattr(info, f) for f, _ in FaPlanInfo._fields_}
+
+
+def _stream_handle(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def _shapes(q, k, v, o, lse):
+    import torch
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or o.dim() != 4:
+        raise ValueError("q, k, v, o must be 4-D: [B, S, H, D]")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be bfloat16")
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    B, Sq, Hq, D = q.shape
+    _, Sk, Hkv, _ = k.shape
+    if tuple(k.shape) != (B, Sk, Hkv, D) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v must both be [B, Sk, Hkv, D]")
+    if tuple(o.shape) != (B, Sq, Hq, D):
+        raise ValueError("o must be [B, Sq, Hq, D]")
+    if lse is not None:
+        if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Sq) or not lse.is_contiguous():
+            raise ValueError("lse must be a contiguous float32 [B, Hq, Sq] tensor")
+    return B, Hq, Hkv, Sq, Sk, D
+
+
+def fa_fwd(q, k, v, o, lse, causal: bool, scale: float, stream=None) -> None:
+    """O (bf16) and LSE of q, k, v on the current (or given) HIP stream."""
+    import torch
+    if o.dtype != torch.bfloat16:
+        raise TypeError("fa_fwd writes a bfloat16 o; use fa_fwd_ex for float32")
+    B, Hq, Hkv, Sq, Sk, D = _shapes(q, k, v, o, lse)
+    _check(lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                      lse.data_ptr() if lse is not None else None,
+                      B, Hq, Hkv, Sq, Sk, D, int(bool(causal)), float(scale),
+                      _stream_handle(stream)))
+
+
+def fa_fwd_ex(q, k, v, o, lse, causal: bool, scale: float, stream=None, num_splits: int = 0,
+              workspace=None) -> None:
+    """As fa_fwd; o may be bfloat16 or float32, num_splits forces the split path."""
+    import torch
+    if o.dtype == torch.bfloat16:
+        odt = FA_DTYPE_BF16
+    elif o.dtype == torch.float32:
+        odt = FA_DTYPE_F32
+    else:
+        raise TypeError("o must be bfloat16 or float32")
+    B, Hq, Hkv, Sq, Sk, D = _shapes(q, k, v, o, lse)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    _check(lib.fa_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                         lse.data_ptr() if lse is not None else None,
+                         B, Hq, Hkv, Sq, Sk, D, int(bool(causal)), float(scale),
+                         _stream_handle(stream), odt, int(num_splits), ws_ptr, ws_bytes))

@@ -1,0 +1,349 @@
+// fa_api.cpp -- the C ABI declared in include/fa.h: argument checks, planning,
+// split workspace, launches.  All device work is in fa_kernels.hip.
+//
+// The interface itself is this library's own: the pages name no API (the
+// FlashAttention page of the Inference Cookbook lists a Python API page only
+// by title).  Planning follows the waves-and-tail and persistent-scheduling
+// discussion of "理解 H100：从硬件数据路径到 Nsight Compute 瓶颈分析" (occupancy
+// and wave sections): the prefill grid is sized to the number of workgroups
+// the CUs hold at once, and the decode path splits the key axis until the
+// (batch, KV head, split) items fill the machine.
+
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/fa.h"
+#include "fa_launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+fa_status fail(fa_status st, const std::string &msg)
+{
+    g_last_error = msg;
+    return st;
+}
+
+// ---- device facts, queried once per device ---------------------------------
+struct DeviceInfo {
+    bool probed = false;
+    bool supported = false;
+    int cus = 0;
+    std::string arch;
+    // library-owned split workspace
+    void *ws = nullptr;
+    size_t ws_bytes = 0;
+};
+
+std::mutex g_mu;
+std::vector<DeviceInfo> g_dev;
+
+fa_status device_info(int *dev_out, DeviceInfo **info_out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(FA_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+    std::lock_guard<std::mutex> lk(g_mu);
+    if ((int)g_dev.size() <= dev) g_dev.resize(dev + 1);
+    DeviceInfo &d = g_dev[dev];
+    if (!d.probed) {
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess)
+            return fail(FA_ERR_HIP, std::string("hipGetDeviceProperties: ") + hipGetErrorString(e));
+        d.arch = prop.gcnArchName;
+        d.cus = prop.multiProcessorCount;
+        d.supported = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+        d.probed = true;
+    }
+    if (!d.supported) return fail(FA_ERR_UNSUPPORTED, "device architecture " + d.arch + " is not gfx950");
+    *dev_out = dev;
+    *info_out = &d;
+    return FA_OK;
+}
+
+bool log_enabled()
+{
+    const char *s = getenv("FA_LOG");
+    return s && s[0] == '1';
+}
+
+int env_int(const char *name, int dflt)
+{
+    const char *s = getenv(name);
+    return (s && *s) ? atoi(s) : dflt;
+}
+
+// ---- argument checks (no HIP calls) ------------------------------------------
+fa_status check_sizes(int B, int Hq, int Hkv, int Sq, int Sk, int D)
+{
+    if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Sk < 1 || D < 1)
+        return fail(FA_ERR_INVALID_ARG, "every dimension must be >= 1");
+    if (Hq % Hkv != 0) return fail(FA_ERR_INVALID_ARG, "Hq must be a multiple of Hkv");
+    if (D != 64 && D != 128) return fail(FA_ERR_UNSUPPORTED, "head dim must be 64 or 128");
+    const int64_t q_elems = (int64_t)B * Sq * Hq * D;
+    const int64_t k_elems = (int64_t)B * Sk * Hkv * D;
+    if (q_elems >= (int64_t(1) << 40) || k_elems >= (int64_t(1) << 40))
+        return fail(FA_ERR_UNSUPPORTED, "tensor too large");
+    // K/V rows of one batch are addressed through 32-bit buffer byte offsets
+    if ((int64_t)Sk * Hkv * D * 2 >= (int64_t(1) << 31))
+        return fail(FA_ERR_UNSUPPORTED, "one batch of K or V exceeds 2 GiB");
+    if ((int64_t)Sk + Sq >= (int64_t(1) << 30) || (int64_t)B * Hq >= (int64_t(1) << 30))
+        return fail(FA_ERR_UNSUPPORTED, "sizes beyond 32-bit indexing");
+    return FA_OK;
+}
+
+// ---- planning ------------------------------------------------------------------
+struct Plan {
+    int path = 0;        // 0 prefill, 1 split decode
+    int num_splits = 1;
+    int split_len = 0;
+    int block_m = 0, block_n = 0;
+    int grid = 0, items = 0;
+    size_t ws_bytes = 0;
+};
+
+size_t split_ws_bytes(int B, int Hq, int Sq, int D, int ns)
+{
+    if (ns <= 1) return 0;
+    return (size_t)ns * B * Hq * Sq * (size_t)(D + 1) * sizeof(float);
+}
+
+// cus = 0 when unknown (pure host query): use the MI355X count
+fa_status make_plan(int B, int Hq, int Hkv, int Sq, int Sk, int D, int num_splits, int cus,
+                    Plan *out)
+{
+    if (num_splits < 0) return fail(FA_ERR_INVALID_ARG, "num_splits must be >= 0");
+    if (cus <= 0) cus = 256;
+    Plan pl;
+    const int group = Hq / Hkv;
+    const int64_t rows_per_kv = (int64_t)Sq * group;
+    const bool decode_ok = rows_per_kv <= fa::kDecodeRows;
+    const int max_splits = (Sk + fa::kDecodeBN - 1) / fa::kDecodeBN;
+    if (num_splits >= 1 && !decode_ok)
+        return fail(FA_ERR_UNSUPPORTED,
+                    "the split-key path serves at most 32 query rows per KV head (Sq * Hq / Hkv)");
+    if (num_splits >= 1 || decode_ok) {
+        pl.path = 1;
+        int ns = num_splits;
+        if (ns == 0) {
+            ns = env_int("FA_NUM_SPLITS", 0);
+            if (ns <= 0) {
+                // enough (b, g, split) waves for ~8 per CU, each split >= 4 tiles
+                const int64_t bg = (int64_t)B * Hkv;
+                const int64_t want = ((int64_t)cus * 8 + bg - 1) / bg;
+                const int64_t by_len = std::max<int64_t>(1, Sk / (4 * fa::kDecodeBN));
+                ns = (int)std::max<int64_t>(1, std::min<int64_t>(want, by_len));
+            }
+        }
+        if (ns > max_splits) ns = max_splits;
+        int len = (Sk + ns - 1) / ns;
+        len = (len + fa::kDecodeBN - 1) / fa::kDecodeBN * fa::kDecodeBN;
+        ns = (Sk + len - 1) / len;
+        pl.num_splits = ns;
+        pl.split_len = len;
+        pl.block_m = fa::kDecodeRows;
+        pl.block_n = fa::kDecodeBN;
+        pl.items = B * Hkv * ns;
+        pl.grid = pl.items;
+        pl.ws_bytes = split_ws_bytes(B, Hq, Sq, D, ns);
+    } else {
+        pl.path = 0;
+        pl.block_m = fa::kPrefillBM;
+        pl.block_n = fa::prefill_block_n(D);
+        const int64_t items = (int64_t)B * Hq * ((Sq + fa::kPrefillBM - 1) / fa::kPrefillBM);
+        if (items >= (int64_t(1) << 31)) return fail(FA_ERR_UNSUPPORTED, "too many work items");
+        const int wg_per_cu = std::max(1, env_int("FA_WG_PER_CU", 2));
+        int64_t grid = std::min<int64_t>(items, (int64_t)cus * wg_per_cu);
+        if (env_int("FA_PERSISTENT", 1) == 0) grid = items;
+        pl.items = (int)items;
+        pl.grid = (int)grid;
+    }
+    *out = pl;
+    return FA_OK;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse, int B,
+                    int Hq, int Hkv, int Sq, int Sk, int D, int causal, float scale,
+                    hipStream_t stream, fa_dtype o_dtype, int num_splits, void *workspace,
+                    size_t workspace_bytes)
+{
+    g_last_error.clear();
+    if (!q || !k || !v || !o) return fail(FA_ERR_INVALID_ARG, "q, k, v and o must not be NULL");
+    fa_status st = check_sizes(B, Hq, Hkv, Sq, Sk, D);
+    if (st != FA_OK) return st;
+    if (!isfinite(scale)) return fail(FA_ERR_INVALID_ARG, "scale must be finite");
+    if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "causal must be 0 or 1");
+    if (o_dtype != FA_DTYPE_BF16 && o_dtype != FA_DTYPE_F32)
+        return fail(FA_ERR_INVALID_ARG, "o_dtype must be FA_DTYPE_BF16 or FA_DTYPE_F32");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+        (lse && !aligned16(lse)))
+        return fail(FA_ERR_UNSUPPORTED, "q, k, v, o and lse must be 16-byte aligned");
+    if (workspace && !aligned16(workspace))
+        return fail(FA_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
+    if (num_splits < 0) return fail(FA_ERR_INVALID_ARG, "num_splits must be >= 0");
+    {
+        // size-only plan check before touching the device
+        Plan pre;
+        st = make_plan(B, Hq, Hkv, Sq, Sk, D, num_splits, 0, &pre);
+        if (st != FA_OK) return st;
+    }
+
+    int dev = 0;
+    DeviceInfo *info = nullptr;
+    st = device_info(&dev, &info);
+    if (st != FA_OK) return st;
+
+    Plan pl;
+    st = make_plan(B, Hq, Hkv, Sq, Sk, D, num_splits, info->cus, &pl);
+    if (st != FA_OK) return st;
+
+    fa::Launch L;
+    L.q = q; L.k = k; L.v = v; L.o = o; L.lse = lse;
+    L.part_o = nullptr; L.part_lse = nullptr;
+    L.B = B; L.Hq = Hq; L.Hkv = Hkv; L.Sq = Sq; L.Sk = Sk; L.D = D;
+    L.causal = causal;
+    L.o_f32 = (o_dtype == FA_DTYPE_F32);
+    L.scale = scale;
+    L.num_splits = pl.num_splits;
+    L.split_len = pl.split_len;
+    L.grid = pl.grid;
+    L.stream = stream;
+
+    if (log_enabled())
+        fprintf(stderr,
+                "[fa] path=%s B=%d Hq=%d Hkv=%d Sq=%d Sk=%d D=%d causal=%d splits=%d "
+                "split_len=%d block=%dx%d grid=%d items=%d ws=%zu\n",
+                pl.path ? "split-decode" : "prefill", B, Hq, Hkv, Sq, Sk, D, causal,
+                pl.num_splits, pl.split_len, pl.block_m, pl.block_n, pl.grid, pl.items,
+                pl.ws_bytes);
+
+    hipError_t e;
+    if (pl.path == 0) {
+        e = fa::launch_prefill(L);
+    } else {
+        std::unique_lock<std::mutex> lk(g_mu, std::defer_lock);
+        if (pl.ws_bytes > 0) {
+            void *ws = workspace;
+            if (ws) {
+                if (workspace_bytes < pl.ws_bytes)
+                    return fail(FA_ERR_INVALID_ARG, "workspace_bytes is smaller than fa_workspace_size()");
+            } else {
+                lk.lock();
+                const char *force_fail = getenv("FA_TEST_FAIL_ALLOC");
+                if (force_fail && force_fail[0] == '1')
+                    return fail(FA_ERR_NOMEM, "workspace allocation failed (forced by FA_TEST_FAIL_ALLOC)");
+                if (info->ws_bytes < pl.ws_bytes) {
+                    if (info->ws) {
+                        // hipFree waits for the device, so work still queued on
+                        // any stream with the old buffer finishes first
+                        (void)hipFree(info->ws);
+                        info->ws = nullptr;
+                        info->ws_bytes = 0;
+                    }
+                    void *p = nullptr;
+                    e = hipMalloc(&p, pl.ws_bytes);
+                    if (e != hipSuccess || !p)
+                        return fail(FA_ERR_NOMEM, std::string("workspace hipMalloc: ") + hipGetErrorString(e));
+                    info->ws = p;
+                    info->ws_bytes = pl.ws_bytes;
+                }
+                ws = info->ws;
+            }
+            const size_t n_rows = (size_t)B * Hq * Sq;
+            L.part_o = static_cast<float *>(ws);
+            L.part_lse = L.part_o + (size_t)pl.num_splits * n_rows * D;
+        }
+        e = fa::launch_decode(L);
+    }
+    if (e != hipSuccess) return fail(FA_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
+    return FA_OK;
+}
+
+fa_status fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int Hq,
+                 int Hkv, int Sq, int Sk, int D, int causal, float scale, hipStream_t stream)
+{
+    return fa_fwd_ex(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, causal, scale, stream,
+                     FA_DTYPE_BF16, 0, nullptr, 0);
+}
+
+size_t fa_workspace_size(int B, int Hq, int Hkv, int Sq, int Sk, int D, int num_splits)
+{
+    if (check_sizes(B, Hq, Hkv, Sq, Sk, D) != FA_OK) return 0;
+    int cus = 0;
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        int dev = 0;
+        if (hipGetDevice(&dev) == hipSuccess && dev < (int)g_dev.size() && g_dev[dev].probed)
+            cus = g_dev[dev].cus;
+    }
+    Plan pl;
+    if (make_plan(B, Hq, Hkv, Sq, Sk, D, num_splits, cus, &pl) != FA_OK) return 0;
+    return pl.ws_bytes;
+}
+
+fa_status fa_plan(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal, int num_splits,
+                  fa_plan_info *out)
+{
+    (void)causal;
+    g_last_error.clear();
+    if (!out) return fail(FA_ERR_INVALID_ARG, "out must not be NULL");
+    fa_status st = check_sizes(B, Hq, Hkv, Sq, Sk, D);
+    if (st != FA_OK) return st;
+    int cus = 0;
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        int dev = 0;
+        if (hipGetDevice(&dev) == hipSuccess && dev < (int)g_dev.size() && g_dev[dev].probed)
+            cus = g_dev[dev].cus;
+    }
+    Plan pl;
+    st = make_plan(B, Hq, Hkv, Sq, Sk, D, num_splits, cus, &pl);
+    if (st != FA_OK) return st;
+    out->path = pl.path;
+    out->num_splits = pl.num_splits;
+    out->block_m = pl.block_m;
+    out->block_n = pl.block_n;
+    out->grid = pl.grid;
+    out->work_items = pl.items;
+    out->workspace_bytes = pl.ws_bytes;
+    return FA_OK;
+}
+
+const char *fa_last_error(void) { return g_last_error.c_str(); }
+
+fa_status fa_release_workspace(void)
+{
+    std::lock_guard<std::mutex> lk(g_mu);
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess) cur = -1;
+    for (size_t d = 0; d < g_dev.size(); ++d) {
+        if (!g_dev[d].ws) continue;
+        if (hipSetDevice((int)d) == hipSuccess) (void)hipFree(g_dev[d].ws);
+        g_dev[d].ws = nullptr;
+        g_dev[d].ws_bytes = 0;
+    }
+    if (cur >= 0) (void)hipSetDevice(cur);
+    return FA_OK;
+}
+
+int fa_version(void) { return 100; }
+
+}  // extern "C"

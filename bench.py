@@ -1,0 +1,233 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused attention forward on one MI355X.
+
+One step is one pass of the whole path over synthetic inputs already resident
+in HBM:
+  * the compute-bound causal prefill, B=4, Hq=Hkv=16, Sq=Sk=4096, D=128, bf16
+    (one fa_fwd call: the persistent prefill kernel), and
+  * the memory-bound decode, B=32, Hq=32, Hkv=8, Sq=1, Sk=8192, D=128, bf16
+    (one fa_fwd call: the split-key kernel and the log-sum-exp merge).
+Both go to the same stream; HIP events recorded on that stream around each
+call give the per-call durations.
+
+Printed: one JSON line.  `value` is the prefill's algorithmic TFLOP/s (4*D
+flops per allowed query-key pair); `decode` holds the decode's algorithmic
+GB/s (Q, K, V read once, O and LSE written once).  `roofline` is the prefill
+kernel against the dense bf16 MFMA peak; `decode.roofline` the decode call
+against HBM.  `cpu_baseline` times the fp64 oracle on a bounded sample of the
+prefill workload's rows and also compares those rows with the timed output.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("attention fwd TFLOP/s + % bf16 MFMA peak (causal S=4096 D=128); "
+          "decode HBM GB/s")
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA (datasheet)
+PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E (datasheet)
+PREFILL = "causal_b4_h16_s4096_d128"
+DECODE = "decode_b32_hq32_hkv8_sk8192_d128"
+COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
+KERNEL_SRC = os.path.join(ROOT, "attention_fwd_02_amd", "csrc", "fa_kernels.hip")
+
+
+def roofline(achieved, peak, unit, bound, traffic=None):
+    return {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": traffic}
+
+
+def kernel_source_hash():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(key):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, or None
+    when the kernel source changed since they were taken."""
+    try:
+        with open(COUNTERS) as f:
+            c = json.load(f)[key]
+    except (OSError, KeyError, ValueError):
+        return None
+    if c.get("source_sha256") != kernel_source_hash():
+        return None
+    return int(c["hbm_bytes_per_launch"])
+
+
+def cpu_baseline_leg(w, q, k, v, o_gpu, lse_gpu, seconds):
+    """The oracle as it stands, on a bounded sample of the workload's rows,
+    timed on this host's cores; the sampled rows of the timed GPU output are
+    compared with it on the way."""
+    import numpy as np
+    import oracle
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from tests.helpers import check
+
+    threads = max(1, min(os.cpu_count() or 1, 16))
+    rng = np.random.default_rng(1234)
+
+    def rows_of(n):
+        idx = rng.choice(w.B * w.Hq * w.Sq, size=n, replace=False)
+        b = idx // (w.Hq * w.Sq)
+        h = (idx // w.Sq) % w.Hq
+        i = idx % w.Sq
+        return np.stack([b, h, i], axis=1).astype(np.int64)
+
+    def flops_of(rows):
+        off = w.Sk - w.Sq
+        keys = np.clip(rows[:, 2] + off + 1, 0, w.Sk) if w.causal else np.full(len(rows), w.Sk)
+        return int(4 * w.D * keys.sum())
+
+    cal = rows_of(4 * threads)
+    t0 = time.perf_counter()
+    oracle.attn_fwd(q, k, v, w.causal, w.scale, rows=cal, nthreads=threads)
+    t_cal = max(time.perf_counter() - t0, 1e-3)
+    n = int(min(w.B * w.Hq * w.Sq, max(len(cal), len(cal) * seconds / t_cal)))
+    rows = rows_of(n)
+    t0 = time.perf_counter()
+    o_ref, lse_ref = oracle.attn_fwd(q, k, v, w.causal, w.scale, rows=rows, nthreads=threads)
+    dt = time.perf_counter() - t0
+    fl = flops_of(rows)
+
+    og = o_gpu.float().cpu().numpy().astype(np.float64)
+    lg = lse_gpu.float().cpu().numpy().astype(np.float64)
+    o_s = np.stack([og[b, i, h] for b, h, i in rows])
+    l_s = np.array([lg[b, h, i] for b, h, i in rows])
+    eo, el = check(o_s, l_s, o_ref, lse_ref, w.o_dtype, "timed output")
+    return {
+        "value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+        "kind": "oracle",
+        "sample": (f"{n} random query rows of the {PREFILL} workload "
+                   f"({fl / 1e9:.1f} GFLOP algorithmic, {dt:.1f} s, fp64, "
+                   f"{threads} threads)"),
+        "parity_on_timed_output": {"rows": n, "max_abs_dO": eo, "max_abs_dLSE": el},
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+              "(the multi-GPU sharding is a design note only).", file=sys.stderr)
+        return 2
+
+    import torch
+    from attention_fwd_02_amd import _binding as fa
+    from attention_fwd_02_amd.inputs import WORKLOADS, make_inputs
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    wp, wd = WORKLOADS[PREFILL], WORKLOADS[DECODE]
+    qp_h, kp_h, vp_h = make_inputs(wp)
+    qp, kp, vp = (t.to(dev) for t in (qp_h, kp_h, vp_h))
+    op = torch.empty_like(qp)
+    lp = torch.empty((wp.B, wp.Hq, wp.Sq), dtype=torch.float32, device=dev)
+    qd, kd, vd = (t.to(dev) for t in make_inputs(wd))
+    od = torch.empty_like(qd)
+    ld = torch.empty((wd.B, wd.Hq, wd.Sq), dtype=torch.float32, device=dev)
+
+    stream = torch.cuda.current_stream()
+
+    def prefill():
+        fa.fa_fwd(qp, kp, vp, op, lp, wp.causal, wp.scale, stream=stream)
+
+    def decode():
+        fa.fa_fwd(qd, kd, vd, od, ld, wd.causal, wd.scale, stream=stream)
+
+    for _ in range(args.warmup):
+        prefill()
+        decode()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for s in range(K):
+        evs[s][0].record(stream)
+        prefill()
+        evs[s][1].record(stream)
+        decode()
+        evs[s][2].record(stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+
+    total_ms = start.elapsed_time(stop)
+    p_ms = sorted(e[0].elapsed_time(e[1]) for e in evs)
+    d_ms = sorted(e[1].elapsed_time(e[2]) for e in evs)
+    p_avg = sum(p_ms) / K
+    d_avg = sum(d_ms) / K
+
+    flops = wp.flops()
+    tflops = flops / (p_avg * 1e-3) / 1e12
+    dbytes = wd.hbm_bytes()
+    gbps = dbytes / (d_avg * 1e-3) / 1e9
+
+    plan_p = fa.fa_plan(wp.B, wp.Hq, wp.Hkv, wp.Sq, wp.Sk, wp.D, wp.causal, 0)
+    plan_d = fa.fa_plan(wd.B, wd.Hq, wd.Hkv, wd.Sq, wd.Sk, wd.D, wd.causal, 0)
+    props = torch.cuda.get_device_properties(0)
+
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / K, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{PREFILL} (causal prefill B=4 Hq=Hkv=16 Sq=Sk=4096 D=128) + "
+                         f"{DECODE} (decode B=32 Hq=32 Hkv=8 Sq=1 Sk=8192 D=128)"),
+            "prefill": {"B": wp.B, "Hq": wp.Hq, "Hkv": wp.Hkv, "Sq": wp.Sq, "Sk": wp.Sk,
+                        "D": wp.D, "causal": wp.causal, "algorithmic_flops": flops,
+                        "plan": plan_p},
+            "decode": {"B": wd.B, "Hq": wd.Hq, "Hkv": wd.Hkv, "Sq": wd.Sq, "Sk": wd.Sk,
+                       "D": wd.D, "causal": wd.causal, "algorithmic_bytes": dbytes,
+                       "plan": plan_d},
+            "device": props.name, "cus": props.multi_processor_count,
+        },
+        "pct_bf16_mfma_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "prefill_ms": {"avg": round(p_avg, 4), "median": round(p_ms[K // 2], 4),
+                       "min": round(p_ms[0], 4)},
+        "decode": {
+            "value": round(gbps, 1), "unit": "GB/s",
+            "ms": {"avg": round(d_avg, 4), "median": round(d_ms[K // 2], 4),
+                   "min": round(d_ms[0], 4)},
+            "roofline": roofline(gbps, PEAK_HBM_GBPS, "GB/s", "hbm",
+                                 measured_traffic("decode")),
+        },
+        "roofline": roofline(tflops, PEAK_BF16_TFLOPS, "TFLOP/s", "mfma",
+                             measured_traffic("prefill")),
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_leg(wp, qp_h, kp_h, vp_h, op, lp, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

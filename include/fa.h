@@ -1,0 +1,146 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) fused attention forward library.
+ *
+ * Operation.  For every batch b, query head hq, query row i:
+ *
+ *   O[b,i,hq,:] = softmax_j( scale * q[b,i,hq,:] . k[b,j,g,:] )  V[b,j,g,:]
+ *   LSE[b,hq,i] = ln sum_j exp( scale * q[b,i,hq,:] . k[b,j,g,:] )
+ *
+ * over the allowed keys j, with g = hq / (Hq / Hkv).  This is the fused
+ * attention forward whose tiled SM80 and SM90 main loops are laid out in
+ * "SM80 内核实现对比" (Inference Cookbook, FlashAttention), sections 4.1 and
+ * 5.2: Q K^T, online softmax, then P V, with S and P kept on chip.  The
+ * softmax components (row max, exp, row sum, rescale, causal mask) are the ones
+ * listed in "从 Volta/Turing、Ampere、Ada 到 Hopper：硬件、PTX 与 Kernel 编程范式
+ * 演进", section "Attention 的瓶颈会在 Tensor Core 与 CUDA Core 之间迁移".  The
+ * pages give no interface, no layout and no LSE; those are this library's
+ * choices:
+ *
+ *   layout   q, o : [B][Sq][Hq][D]   k, v : [B][Sk][Hkv][D]   (D innermost,
+ *            fully contiguous, row-major)      lse : [B][Hq][Sq] float32
+ *   causal   key j is allowed for query i iff j <= i + (Sk - Sq); a row with
+ *            no allowed key gets O = 0 and LSE = -inf
+ *   dtypes   q, k, v bfloat16; o bfloat16 (round to nearest even) or float32;
+ *            all arithmetic accumulates in float32
+ *
+ * Conventions shared by every call:
+ *   - All pointers except `workspace` of fa_fwd_ex are device pointers owned
+ *     by the caller; the library neither frees nor retains them.  Each must be
+ *     16-byte aligned.  `lse` may be NULL (then no LSE is written).
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *     stream).  Nothing inside synchronises the host.  All launches of one call
+ *     go to that one stream, in order.
+ *   - Results are deterministic: repeated calls with the same arguments give
+ *     bit-identical outputs (no floating-point atomics).
+ *   - Argument checks run before any HIP call and return synchronously.
+ *   - Every non-OK status leaves a message for fa_last_error() in the calling
+ *     thread.  No call throws, aborts or prints (unless FA_LOG=1 is set, which
+ *     prints the chosen plan to stderr).
+ *   - Thread-safe: calls may come from several host threads.  The
+ *     library-owned split workspace (see fa_fwd_ex) is one buffer per device,
+ *     shared by every call on that device: split-path calls whose kernels may
+ *     overlap in time (different streams) must each pass their own workspace.
+ *     Growing that buffer frees the old one with hipFree, which waits for the
+ *     device; this is the only point where a call can block the host.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_INVALID_ARG = 1, /* NULL q/k/v/o, a dimension < 1, Hq % Hkv != 0,
+                               non-finite scale, bad workspace size          */
+    FA_ERR_UNSUPPORTED = 2, /* D not in {64, 128}, pointer not 16-B aligned,
+                               device not gfx950, split request the split
+                               path cannot serve, sizes beyond 32-bit indexing */
+    FA_ERR_NOMEM = 3,       /* the library-owned workspace could not be
+                               allocated                                     */
+    FA_ERR_HIP = 4          /* a HIP call failed; fa_last_error() has its text */
+} fa_status;
+
+typedef enum { FA_DTYPE_BF16 = 0, FA_DTYPE_F32 = 1 } fa_dtype;
+
+/*
+ * fa_fwd -- attention forward, bf16 O.  Same as
+ * fa_fwd_ex(..., FA_DTYPE_BF16, 0, NULL, 0).
+ *
+ * q   [B][Sq][Hq][D]  bf16, device     k, v  [B][Sk][Hkv][D]  bf16, device
+ * o   [B][Sq][Hq][D]  bf16, device     lse   [B][Hq][Sq] float32, device or NULL
+ * causal: 0 or 1.  scale: any finite float applied to the raw dot products
+ * (negative and zero included).
+ */
+fa_status fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B,
+                 int Hq, int Hkv, int Sq, int Sk, int D, int causal, float scale,
+                 hipStream_t stream);
+
+/*
+ * fa_fwd_ex -- as fa_fwd, plus:
+ *   o_dtype      FA_DTYPE_BF16 or FA_DTYPE_F32 (o then holds float32).
+ *   num_splits   0 = let the library choose.  >= 1 forces the split-key path:
+ *                the key range is cut into num_splits contiguous pieces, each
+ *                piece produces a partial (O_s, LSE_s), and a merge pass
+ *                combines them by log-sum-exp weights.  The split path serves
+ *                problems whose Sq * (Hq / Hkv) query rows per KV head fit one
+ *                64-lane wave's tile (<= 32); otherwise FA_ERR_UNSUPPORTED.
+ *                num_splits is clamped to ceil(Sk / 32).  The split-key
+ *                decomposition and merge are not on the pages; they follow
+ *                from the log-sum-exp definition above.
+ *   workspace    device memory for the split partials, or NULL for a
+ *                library-owned buffer (allocated on first need per device,
+ *                grown on demand, kept until fa_release_workspace).
+ *   workspace_bytes  size of `workspace`; must be >= fa_workspace_size(...)
+ *                of the same problem when `workspace` is not NULL.
+ */
+fa_status fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse, int B,
+                    int Hq, int Hkv, int Sq, int Sk, int D, int causal, float scale,
+                    hipStream_t stream, fa_dtype o_dtype, int num_splits, void *workspace,
+                    size_t workspace_bytes);
+
+/*
+ * fa_workspace_size -- bytes of split workspace the call with these sizes and
+ * this num_splits (0 = automatic) needs; 0 when it takes the single-pass path.
+ * Pure host arithmetic, no device access.  Returns 0 for invalid sizes.
+ */
+size_t fa_workspace_size(int B, int Hq, int Hkv, int Sq, int Sk, int D, int num_splits);
+
+/*
+ * fa_plan -- which kernels a call with these sizes would launch.  Pure host
+ * arithmetic except the one-time device query (CU count, architecture).
+ * Fills *out; returns FA_ERR_INVALID_ARG / FA_ERR_UNSUPPORTED as fa_fwd_ex would.
+ */
+typedef struct {
+    int path;            /* 0 = prefill (single pass), 1 = split-key decode + merge */
+    int num_splits;      /* 1 for the prefill path                                */
+    int block_m;         /* query rows per workgroup tile                          */
+    int block_n;         /* keys per K/V tile                                      */
+    int grid;            /* workgroups of the main kernel                          */
+    int work_items;      /* tiles of work the grid walks                           */
+    size_t workspace_bytes;
+} fa_plan_info;
+
+fa_status fa_plan(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal, int num_splits,
+                  fa_plan_info *out);
+
+/* fa_last_error -- message for the last non-OK status of this host thread
+ * ("" if none).  The pointer stays valid until the next call on this thread. */
+const char *fa_last_error(void);
+
+/* fa_release_workspace -- frees every library-owned workspace (all devices).
+ * The caller must make sure no kernel still uses it (synchronise first). */
+fa_status fa_release_workspace(void);
+
+/* fa_version -- major * 10000 + minor * 100 + patch. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

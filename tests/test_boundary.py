@@ -1,0 +1,117 @@
+"""C-ABI boundary on the CPU: the library loads, exports every symbol its
+header declares, and rejects each class of bad argument before any HIP call.
+No test here launches a kernel."""
+from __future__ import annotations
+
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+@pytest.fixture(scope="module")
+def b():
+    from attention_fwd_02_amd import _binding
+    return _binding
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports(b):
+    assert declared_functions() == sorted(b.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(b):
+    out = subprocess.run(["nm", "-D", "--defined-only", b.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s(\w+)", out))
+    for name in declared_functions():
+        assert name in exported, f"{name} declared in fa.h but not exported"
+        assert hasattr(b.lib, name)
+
+
+def test_version(b):
+    assert b.fa_version() == 100
+
+
+P = 0x10000  # a 16-byte aligned fake device address; never dereferenced
+
+
+def call(b, q=P, k=P, v=P, o=P, lse=None, B=1, Hq=1, Hkv=1, Sq=128, Sk=128, D=64,
+         causal=0, scale=0.125, o_dtype=0, num_splits=0, ws=None, ws_bytes=0):
+    st = b.lib.fa_fwd_ex(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, causal, scale, None, o_dtype,
+                         num_splits, ws, ws_bytes)
+    return st, b.fa_last_error()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(o=None), 1),
+    (dict(B=0), 1), (dict(Hq=0), 1), (dict(Hkv=0), 1), (dict(Sq=0), 1), (dict(Sk=0), 1),
+    (dict(B=-3), 1), (dict(D=0), 1),
+    (dict(Hq=6, Hkv=4), 1),
+    (dict(scale=math.inf), 1), (dict(scale=-math.inf), 1), (dict(scale=math.nan), 1),
+    (dict(causal=2), 1), (dict(o_dtype=7), 1), (dict(num_splits=-1), 1),
+    (dict(D=96), 2), (dict(D=256), 2), (dict(D=32), 2),
+    (dict(q=P + 2), 2), (dict(k=P + 8), 2), (dict(v=P + 4), 2), (dict(o=P + 2), 2),
+    (dict(lse=P + 4), 2), (dict(ws=P + 8, ws_bytes=1 << 20, num_splits=2, Sq=1), 2),
+    # split path limited to 32 query rows per KV head
+    (dict(num_splits=4, Sq=33), 2), (dict(num_splits=2, Sq=9, Hq=4, Hkv=1), 2),
+])
+def test_bad_arguments_rejected_before_any_hip_call(b, kw, status):
+    st, msg = call(b, **kw)
+    assert st == status, (st, msg)
+    assert msg, "a non-OK status must leave a message"
+
+
+def test_fa_fwd_checks_too(b):
+    st = b.lib.fa_fwd(P, P, None, P, None, 1, 1, 1, 4, 4, 64, 0, 0.1, None)
+    assert st == 1 and "NULL" in b.fa_last_error()
+
+
+def test_valid_call_without_device_reports_hip_error(b):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a device is present: this test never launches on fake pointers")
+    st, msg = call(b)
+    assert st == 4 and msg
+
+
+def test_workspace_size_and_plan_host_arithmetic(b):
+    # decode shape: 8 splits on a 256-CU part, partials [splits][B][Hq][Sq][D+1] fp32
+    assert b.fa_workspace_size(32, 32, 8, 1, 8192, 128, 0) == 8 * 32 * 32 * 1 * 129 * 4
+    assert b.fa_workspace_size(32, 32, 8, 1, 8192, 128, 16) == 16 * 32 * 32 * 129 * 4
+    assert b.fa_workspace_size(32, 32, 8, 1, 8192, 128, 1) == 0
+    assert b.fa_workspace_size(4, 16, 16, 4096, 4096, 128, 0) == 0   # prefill path
+    assert b.fa_workspace_size(0, 16, 16, 4096, 4096, 128, 0) == 0   # invalid sizes
+    p = b.fa_plan(4, 16, 16, 4096, 4096, 128, True, 0)
+    assert p["path"] == 0 and p["block_m"] == 128 and p["block_n"] == 64
+    assert p["work_items"] == 4 * 16 * 32 and p["grid"] == min(p["work_items"], 2 * 256)
+    p = b.fa_plan(2, 8, 8, 1024, 1024, 64, True, 0)
+    assert p["block_n"] == 128 and p["work_items"] == 2 * 8 * 8
+    p = b.fa_plan(32, 32, 8, 1, 8192, 128, False, 0)
+    assert p["path"] == 1 and p["num_splits"] == 8 and p["grid"] == 32 * 8 * 8
+    # splits clamp to one per 32-key tile, and forced splits are honoured
+    assert b.fa_plan(1, 4, 1, 1, 100, 64, False, 64)["num_splits"] == 4
+    assert b.fa_plan(1, 4, 1, 1, 1000, 64, False, 3)["num_splits"] == 3
+    with pytest.raises(b.FaError) as e:
+        b.fa_plan(1, 64, 1, 1, 100, 64, False, 2)
+    assert e.value.status == 2
+
+
+def test_product_path_never_touches_the_oracle():
+    pkg = os.path.join(ROOT, "attention_fwd_02_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle", text, re.M), f
+                assert "oracle.c" not in text and "liboracle" not in text, f

@@ -1,0 +1,238 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Small and ragged shapes are compared element by element on every output;
+the five full-size workloads run in the launch configuration the benchmark
+times and are compared on sampled rows, which the oracle computes one by one.
+Tolerances and the -inf rule are in tests/helpers.py.
+"""
+from __future__ import annotations
+
+import math
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from attention_fwd_02_amd.inputs import WORKLOADS, make_inputs, random_qkv
+from tests.helpers import check, to64
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def ops():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from attention_fwd_02_amd import _binding
+    return _binding
+
+
+@pytest.fixture(scope="module")
+def oracle():
+    import oracle as o
+    o._load()
+    return o
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_gpu(ops, q, k, v, causal, scale, out="bf16", num_splits=0, with_lse=True, stream=None,
+            workspace=None):
+    qd, kd, vd = (t.to(DEV) for t in (q, k, v))
+    B, Sq, Hq, D = q.shape
+    o = torch.empty((B, Sq, Hq, D), dtype=torch.float32 if out == "f32" else torch.bfloat16,
+                    device=DEV)
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=DEV) if with_lse else None
+    ops.fa_fwd_ex(qd, kd, vd, o, lse, causal, scale, stream=stream, num_splits=num_splits,
+                  workspace=workspace)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def full_check(ops, oracle, q, k, v, causal, scale, out="bf16", num_splits=0, label=""):
+    o, lse = run_gpu(ops, q, k, v, causal, scale, out=out, num_splits=num_splits)
+    o_ref, lse_ref = oracle.attn_fwd(q, k, v, causal, scale)
+    return check(to64(o), to64(lse), o_ref, lse_ref, out, label)
+
+
+# ---------------------------------------------------------------------------
+# element-by-element on small, ragged and edge shapes
+# ---------------------------------------------------------------------------
+SHAPES = [
+    # B, Hq, Hkv, Sq, Sk, D, causal, out
+    (1, 1, 1, 128, 128, 64, False, "f32"),
+    (1, 1, 1, 128, 128, 64, True, "bf16"),
+    (2, 3, 3, 77, 77, 64, True, "bf16"),          # one ragged block
+    (1, 2, 1, 200, 333, 128, False, "bf16"),      # ragged Sq and Sk, MQA
+    (1, 2, 1, 200, 333, 128, True, "f32"),        # causal with Sk > Sq
+    (1, 2, 2, 300, 100, 64, True, "bf16"),        # Sq > Sk: leading rows see no key
+    (1, 8, 2, 129, 257, 128, False, "bf16"),      # GQA, one row past a block
+    (2, 4, 4, 513, 513, 128, True, "bf16"),       # several blocks + tail
+    (1, 2, 2, 640, 640, 64, True, "f32"),         # several tiles of 128 keys
+    (1, 64, 1, 1, 300, 128, False, "bf16"),       # Sq = 1 but 64 rows per KV head: prefill path
+    (1, 1, 1, 1, 1, 64, False, "bf16"),           # one query, one key
+    (1, 1, 1, 5, 1, 128, True, "f32"),            # one key, causal: only the last row sees it
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_prefill_shapes_elementwise(ops, oracle, shape):
+    B, Hq, Hkv, Sq, Sk, D, causal, out = shape
+    say(f"[parity] shape {shape}")
+    q, k, v = random_qkv(B, Hq, Hkv, Sq, Sk, D, seed=Sq * 31 + Sk + D)
+    full_check(ops, oracle, q, k, v, causal, 1.0 / math.sqrt(D), out=out, label=str(shape))
+
+
+DECODE_SHAPES = [
+    # B, Hq, Hkv, Sq, Sk, D, causal, num_splits
+    (2, 8, 2, 1, 1000, 128, False, 0),
+    (2, 8, 2, 1, 1000, 128, False, 1),
+    (2, 8, 2, 1, 1000, 128, False, 7),
+    (1, 4, 1, 1, 8192, 64, False, 0),
+    (3, 8, 2, 3, 517, 128, True, 0),      # 12 (row, head) columns, causal decode
+    (1, 32, 4, 4, 300, 128, True, 5),     # 32 columns: the largest the split path serves
+    (2, 1, 1, 1, 33, 64, False, 2),       # last split holds one key
+    (1, 2, 2, 7, 5, 64, True, 2),         # Sq > Sk on the split path: empty rows
+]
+
+
+@pytest.mark.parametrize("shape", DECODE_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_decode_shapes_elementwise(ops, oracle, shape):
+    B, Hq, Hkv, Sq, Sk, D, causal, ns = shape
+    say(f"[parity] decode shape {shape}")
+    q, k, v = random_qkv(B, Hq, Hkv, Sq, Sk, D, seed=Sk + 7 * Sq)
+    plan = ops.fa_plan(B, Hq, Hkv, Sq, Sk, D, causal, ns)
+    assert plan["path"] == 1
+    full_check(ops, oracle, q, k, v, causal, 1.0 / math.sqrt(D), num_splits=ns, label=str(shape))
+
+
+@pytest.mark.parametrize("scale", [-0.125, 0.0, 2.5])
+@pytest.mark.parametrize("causal", [False, True])
+def test_scale_sign_and_zero(ops, oracle, scale, causal):
+    say(f"[parity] scale {scale} causal {causal}")
+    q, k, v = random_qkv(1, 2, 2, 150, 150, 64, seed=21)
+    full_check(ops, oracle, q, k, v, causal, scale, out="f32", label=f"scale={scale}")
+    qd, kd, vd = random_qkv(2, 8, 2, 1, 700, 128, seed=22)
+    full_check(ops, oracle, qd, kd, vd, causal, scale, out="f32", label=f"decode scale={scale}")
+
+
+def test_lse_optional(ops, oracle):
+    q, k, v = random_qkv(1, 2, 2, 100, 100, 128, seed=23)
+    o, lse = run_gpu(ops, q, k, v, True, 0.088, with_lse=False)
+    o_ref, _ = oracle.attn_fwd(q, k, v, True, 0.088)
+    check(to64(o), None, o_ref, None, "bf16", "no lse")
+    o, lse = run_gpu(ops, *random_qkv(2, 4, 1, 1, 900, 64, seed=24), False, 0.125,
+                     with_lse=False, num_splits=3)
+    assert lse is None
+
+
+def test_split_invariance(ops):
+    q, k, v = random_qkv(4, 16, 4, 1, 4096, 128, seed=25)
+    outs = []
+    for ns in (1, 2, 4, 8, 16, 32):
+        o, lse = run_gpu(ops, q, k, v, False, 0.088, out="f32", num_splits=ns)
+        outs.append((ns, to64(o), to64(lse)))
+    for ns, o, lse in outs[1:]:
+        assert np.abs(o - outs[0][1]).max() <= 1e-5, ns
+        assert np.abs(lse - outs[0][2]).max() <= 1e-5, ns
+
+
+def test_repeat_launches_bitwise_equal(ops):
+    for shape, ns in (((2, 8, 8, 300, 300, 128), 0), ((8, 32, 8, 1, 2048, 128), 0)):
+        q, k, v = random_qkv(*shape, seed=26)
+        causal = shape[3] > 1
+        o1, l1 = run_gpu(ops, q, k, v, causal, 0.1, num_splits=ns)
+        o2, l2 = run_gpu(ops, q, k, v, causal, 0.1, num_splits=ns)
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_caller_workspace_and_stream(ops):
+    q, k, v = random_qkv(2, 8, 2, 1, 3000, 128, seed=27)
+    ref_o, ref_l = run_gpu(ops, q, k, v, False, 0.088, num_splits=6)
+    nbytes = ops.fa_workspace_size(2, 8, 2, 1, 3000, 128, 6)
+    assert nbytes > 0
+    ws = torch.empty(nbytes // 4 + 4, dtype=torch.float32, device=DEV)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o, l = run_gpu(ops, q, k, v, False, 0.088, num_splits=6, stream=s, workspace=ws)
+    assert torch.equal(o, ref_o) and torch.equal(l, ref_l)
+    # a too-small caller workspace is rejected
+    small = torch.empty(16, dtype=torch.float32, device=DEV)
+    with pytest.raises(ops.FaError) as e:
+        run_gpu(ops, q, k, v, False, 0.088, num_splits=6, workspace=small)
+    assert e.value.status == ops.FA_ERR_INVALID_ARG
+
+
+def test_forced_allocation_failure_reports_nomem(ops):
+    q, k, v = random_qkv(1, 4, 1, 1, 500, 64, seed=28)
+    os.environ["FA_TEST_FAIL_ALLOC"] = "1"
+    try:
+        with pytest.raises(ops.FaError) as e:
+            run_gpu(ops, q, k, v, False, 0.125, num_splits=4)
+        assert e.value.status == ops.FA_ERR_NOMEM
+    finally:
+        del os.environ["FA_TEST_FAIL_ALLOC"]
+    run_gpu(ops, q, k, v, False, 0.125, num_splits=4)   # works again
+
+
+# ---------------------------------------------------------------------------
+# the five full-size workloads, in the benchmark's launch configuration
+# ---------------------------------------------------------------------------
+def sample_rows(w, q, n_random, seed):
+    rng = np.random.default_rng(seed)
+    rows = set()
+    edge_i = sorted({0, 1, 31, 32, 63, 64, 127, 128, w.Sq // 2, w.Sq - 2, w.Sq - 1} &
+                    set(range(w.Sq)))
+    for b in {0, w.B - 1}:
+        for h in {0, w.Hq - 1, w.Hq // 2}:
+            for i in edge_i:
+                rows.add((b, h, i))
+    for _ in range(n_random):
+        rows.add((int(rng.integers(w.B)), int(rng.integers(w.Hq)), int(rng.integers(w.Sq))))
+    if w.hot_row_frac > 0:
+        hot = (q.float().abs().amax(dim=-1) > 6.0).nonzero().tolist()   # [b, i, h]
+        for b, i, h in hot[:: max(1, len(hot) // 64)][:64]:
+            rows.add((b, h, i))
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_full_size_workloads_sampled(ops, oracle, name):
+    w = WORKLOADS[name]
+    say(f"[parity] full-size workload {name}")
+    q, k, v = make_inputs(w)
+    o, lse = run_gpu(ops, q, k, v, w.causal, w.scale, out=w.o_dtype)
+    if w.Sq * w.Hq * w.B <= 2048:      # small enough: every row
+        rows = np.array([(b, h, i) for b in range(w.B) for h in range(w.Hq)
+                         for i in range(w.Sq)], dtype=np.int64)
+    else:
+        rows = sample_rows(w, q, 160, seed=w.seed)
+    o_ref, lse_ref = oracle.attn_fwd(q, k, v, w.causal, w.scale, rows=rows)
+    og = to64(o)
+    lg = to64(lse)
+    o_s = np.stack([og[b, i, h] for b, h, i in rows])
+    l_s = np.array([lg[b, h, i] for b, h, i in rows])
+    eo, el = check(o_s, l_s, o_ref, lse_ref, w.o_dtype, name)
+    say(f"[parity] {name}: {len(rows)} rows, max|dO|={eo:.2e} max|dLSE|={el:.2e}")
+    assert np.isfinite(lg).all() or w.causal  # no -inf rows in these workloads
+    assert not torch.isnan(o).any()
+
+
+def test_compute_bound_workload_float32_output_strict(ops, oracle):
+    # float32 O at full size on the causal S=4096 workload: the plain 1e-2 bound
+    w = WORKLOADS["causal_b4_h16_s4096_d128"]
+    q, k, v = make_inputs(w)
+    o, lse = run_gpu(ops, q, k, v, w.causal, w.scale, out="f32")
+    rows = sample_rows(w, q, 96, seed=5)
+    o_ref, lse_ref = oracle.attn_fwd(q, k, v, w.causal, w.scale, rows=rows)
+    og, lg = to64(o), to64(lse)
+    o_s = np.stack([og[b, i, h] for b, h, i in rows])
+    l_s = np.array([lg[b, h, i] for b, h, i in rows])
+    check(o_s, l_s, o_ref, lse_ref, "f32", "f32 output")
