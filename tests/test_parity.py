@@ -134,13 +134,17 @@ def test_lse_optional(ops, oracle):
 
 
 def test_split_invariance(ops):
+    # Splitting the keys changes only rounding: P is rounded to bf16 relative
+    # to each split's own running max, which moves O by about
+    # 2^-8 * max|v| * ||w||_2 (~2e-4 for near-uniform weights over 4096 keys
+    # with |v| <= 5), while the LSE sums the unrounded weights in fp32.
     q, k, v = random_qkv(4, 16, 4, 1, 4096, 128, seed=25)
     outs = []
     for ns in (1, 2, 4, 8, 16, 32):
         o, lse = run_gpu(ops, q, k, v, False, 0.088, out="f32", num_splits=ns)
         outs.append((ns, to64(o), to64(lse)))
     for ns, o, lse in outs[1:]:
-        assert np.abs(o - outs[0][1]).max() <= 1e-5, ns
+        assert np.abs(o - outs[0][1]).max() <= 1e-3, ns
         assert np.abs(lse - outs[0][2]).max() <= 1e-5, ns
 
 
