@@ -4,10 +4,11 @@
 // row, never writing S or P to HBM.  The structure follows the FlashAttention
 // forward main loop laid out in "SM80 内核实现对比" (Inference Cookbook): Q kept
 // in registers for the whole key loop (section 5.3, Q_in_regs), K/V tiles
-// staged through on-chip memory with a software pipeline (section 4.1), the
-// S = Q K^T product, the online softmax, then P V with P taken from registers
-// (section 5.2), and 16-byte global copies (section 2.1).  The online-softmax
-// pieces -- row max, exp, row sum, rescale, causal mask -- are those named in
+// staged through on-chip memory by asynchronous 16-byte copies with zero fill
+// at the edges, two stages deep (sections 2.1 and 4.1), the S = Q K^T product,
+// the online softmax, then P V with P taken from registers (section 5.2), and
+// an XOR-swizzled on-chip layout (section 6.3).  The online-softmax pieces --
+// row max, exp, row sum, rescale, causal mask -- are those named in
 // "从 Volta/Turing、Ampere、Ada 到 Hopper：硬件、PTX 与 Kernel 编程范式演进",
 // section "Attention 的瓶颈会在 Tensor Core 与 CUDA Core 之间迁移".
 //
@@ -16,14 +17,22 @@
 //    S^T = K Q^T and O^T = V^T P^T.  In the 32x32 accumulator layout a lane owns
 //    one output column (here: one query) and 16 rows (keys, or head dims), so
 //    the row max and row sum need a single cross-lane step (v_permlane32_swap)
-//    instead of a shuffle tree, and the per-query rescale factor is lane-local.
-//  * P never leaves registers: the S^T accumulator registers are reused as the
-//    B operand of the PV MFMA.  The keys a lane holds there are not
-//    contiguous, so the V tile is written to LDS transposed (V^T[d][key]) and
-//    with the key index permuted inside each 16-key group (bits 2 and 3
-//    swapped); summing over keys in a permuted order is exact.
-//  * LDS rows are XOR-swizzled in 16-byte chunks so that the 32 rows read by
-//    one ds_read_b128 fall on distinct banks.
+//    and the per-query rescale factor is lane-local.
+//  * P never leaves registers: the S^T accumulator registers, converted to
+//    bf16, are the B operand of the PV MFMA.  The A operand V^T is read from
+//    the natural [key][d] V tile with the transposing LDS read
+//    ds_read_b64_tr_b16 (each lane gets 4 consecutive keys of one head dim),
+//    so V needs no transposed copy anywhere.
+//  * K and V tiles go from HBM to LDS with buffer_load_dwordx4 ... lds (no
+//    staging registers); the buffer descriptor's byte range makes rows past
+//    the last key read as zero.
+//  * The LDS swizzle (chunk ^ swz(row)) is chosen so that both the 32-row
+//    ds_read_b128 of K and the 4-row x 64-byte transposing read of V hit
+//    distinct banks, for a 32- and a 64-bank LDS alike.
+//  * The running max is a lazy reference: it only moves when a row's max
+//    grows by more than 2^8 in exp2 units, so the O rescale is skipped on
+//    almost every tile.  P values then stay below 2^8, which bf16 and the fp32
+//    accumulators hold without loss; the result is the same function.
 //  * Prefill runs a persistent grid (two 256-thread workgroups per CU) that
 //    walks (batch, head, query block) items in a snake order, longest causal
 //    blocks first, and keeps all blocks of a head on one XCD so that their K/V
@@ -38,18 +47,24 @@
 #include "fa_launch.h"
 
 namespace fa {
-namespace {
+namespace kern {
 
 typedef __bf16 bf16x8_t __attribute__((__vector_size__(16)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((__vector_size__(64)));
 typedef uint32_t u32x4_t __attribute__((__vector_size__(16)));
 typedef uint32_t u32x2_t __attribute__((__vector_size__(8)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kNegInf = -__builtin_inff();
 // Word 3 of a gfx9-family buffer descriptor: 32-bit data format, so that
 // untyped dword loads are valid; out-of-range offsets return zero.
 constexpr int kBufferFlags = 0x00020000;
+// The lazy running max moves when a row max exceeds it by more than this
+// (exp2 units): P stays below 2^8.
+constexpr float kRescaleThreshold = 8.0f;
 
 struct Params {
     const uint16_t *q, *k, *v;
@@ -88,19 +103,6 @@ __device__ __forceinline__ float add_halves(float x)
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Position of key `key` (0..) inside a transposed V tile: bits 2 and 3 of the
-// key index swap inside each 16-key group, so that the 8 keys lane-half h of
-// the PV MFMA needs (keys 4h..4h+3 and 8+4h..8+4h+3 of the group) are adjacent.
-__device__ __forceinline__ int vt_pos(int key)
-{
-    return (key & ~15) | ((key & 4) << 1) | ((key & 8) >> 1) | (key & 3);
-}
-
-__device__ __forceinline__ u32x4_t ld16(const uint16_t *p)
-{
-    return *reinterpret_cast<const u32x4_t *>(p);
-}
-
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b)
 {
     __bf16 x = (__bf16)a, y = (__bf16)b;  // round to nearest even (v_cvt_pk_bf16_f32)
@@ -108,31 +110,131 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b)
            ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
 }
 
+__device__ __forceinline__ u32x4_t ld16(const uint16_t *p)
+{
+    return *reinterpret_cast<const u32x4_t *>(p);
+}
+
+// Wait until this wave's outstanding vector-memory operations (including the
+// HBM -> LDS copies) are done.  gfx9 s_waitcnt: vmcnt(0), expcnt(7), lgkmcnt(15).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// ---------------------------------------------------------------------------
+// LDS tile layout, K and V alike: [rows][D] bf16, rows of 2*D bytes; the
+// 16-byte chunk c of row r sits at chunk c ^ swz(r).  Bits ri of the row:
+//   D = 128 (16 chunks): swz = r0<<3 | r1<<2 | (r0^r2)<<1 | (r2^r3)
+//   D =  64 ( 8 chunks): swz = r1<<2 | (r0^r2)<<1 | (r0^r3)
+// Any 16 consecutive rows at one chunk (the K read) and any 4 rows starting at
+// a multiple of 4 over an aligned block of 4 chunks (the V transposing read)
+// land on distinct banks.
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ int swz(int r)
+{
+    const int r0 = r & 1, r1 = (r >> 1) & 1, r2 = (r >> 2) & 1, r3 = (r >> 3) & 1;
+    if (D == 128) return (r0 << 3) | (r1 << 2) | ((r0 ^ r2) << 1) | (r2 ^ r3);
+    return (r1 << 2) | ((r0 ^ r2) << 1) | (r0 ^ r3);
+}
+
+// HBM -> LDS copy of one K and one V tile of BN keys by NW waves.  One
+// buffer_load_dwordx4 ... lds instruction writes 1 KiB: 64 lanes x 16 bytes at
+// consecutive LDS addresses.  Lane l of instruction q fills tile row
+// q * RPI + l / CPR at physical chunk l % CPR, i.e. it loads the logical chunk
+// (l % CPR) ^ swz(row) of that key's row.
+template <int D, int BN, int NW>
+struct TileLoader {
+    static constexpr int CPR = D / 8;                 // 16-byte chunks per row
+    static constexpr int RPI = 64 / CPR;              // rows per instruction
+    static constexpr int NQ = BN / RPI;               // instructions per tensor
+    static constexpr int PER_WAVE = NQ / NW;
+    static constexpr int TILE_BYTES = BN * D * 2;
+    static_assert(NQ % NW == 0, "instructions must split evenly over the waves");
+
+    const uint16_t *kbase, *vbase;
+    int kstride_bytes;   // bytes between consecutive keys in HBM
+    int key_end;         // keys >= key_end read as zero
+
+    // Descriptor over the rows from `row0` on: rows at or beyond key_end fall
+    // outside its byte range.  Uniform values only (scalar registers).
+    __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const uint16_t *base, int row0) const
+    {
+        const int valid = key_end - row0;
+        const int nbytes = valid > 0 ? (valid - 1) * kstride_bytes + D * 2 : 0;
+        return __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(base + (long)row0 * (kstride_bytes / 2)), (short)0, nbytes, kBufferFlags);
+    }
+
+    // Issue the copies of keys [key0, key0 + BN) into the K and V tiles at
+    // lds_k / lds_v.  key0 is a multiple of 16.
+    __device__ __forceinline__ void issue(char *lds_k, char *lds_v, int key0, int wave,
+                                          int lane) const
+    {
+#pragma unroll
+        for (int i = 0; i < PER_WAVE; ++i) {
+            const int q = i * NW + wave;
+            const int row = q * RPI + lane / CPR;          // tile-relative row
+            const int voff = (lane / CPR) * kstride_bytes + (((lane % CPR) ^ swz<D>(row)) * 16);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(kbase, key0 + q * RPI),
+                                                     (lds_void_t *)(lds_k + q * 1024), 16, voff,
+                                                     0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(vbase, key0 + q * RPI),
+                                                     (lds_void_t *)(lds_v + q * 1024), 16, voff,
+                                                     0, 0, 0);
+        }
+    }
+};
+
+// Per-lane LDS byte offsets (relative to a tile) of the operand reads.
+//   K (A operand of S^T = K Q^T): lane (col, half) at k-step st reads the 16
+//     bytes of head dims 16*st + 8*half .. +7 of key kb*32 + col.
+//   V^T (A operand of O^T = V^T P^T) through ds_read_b64_tr_b16: in each
+//     16-lane group, source lane 4j + s supplies 4 consecutive head dims of
+//     key row k0 + j; the instruction hands lane 4s + e element e of those
+//     four rows, i.e. 4 consecutive keys of one head dim.
+template <int D>
+struct OperandOffsets {
+    static constexpr int QS = D / 16;
+    static constexpr int DB = D / 32;
+    int k[QS];           // + kb * 32 rows
+    int v[DB][2];        // [d block][second group of 4 keys]; + ps * 16 rows
+
+    __device__ __forceinline__ void init(int lane)
+    {
+        const int col = lane & 31, half = lane >> 5;
+#pragma unroll
+        for (int st = 0; st < QS; ++st)
+            k[st] = col * (2 * D) + (((2 * st + half) ^ swz<D>(col)) * 16);
+        const int li = lane & 15, g = (lane >> 4) & 1;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int sec = 0; sec < 2; ++sec) {
+                const int row = 4 * half + (li >> 2) + 8 * sec;
+                const int d = db * 32 + 16 * g + 4 * (li & 3);
+                v[db][sec] = row * (2 * D) + (((d >> 3) ^ swz<D>(row)) * 16) + (d & 7) * 2;
+            }
+    }
+};
+
 // ---------------------------------------------------------------------------
 // One wave's share of a K/V tile held in LDS: S^T, online softmax, O^T += V^T P^T.
-//
-// K tile in LDS: Ks[key][D] bf16, 16-byte chunk c of row key stored at chunk
-//   c ^ (key % KCH).  V tile: Vt[d][BN] bf16 (keys in vt_pos order), chunk c of
-//   row d stored at c ^ (d % VCH).
 // Lane (col, half): query column `col`; after the S^T MFMA its register r of
-//   key block kb holds key kb*32 + 8*(r/4) + 4*half + (r%4).
+// key block kb holds key kb*32 + 8*(r/4) + 4*half + (r%4).
 // ---------------------------------------------------------------------------
 template <int D, int BN>
 struct WaveTile {
-    static constexpr int KCH = D / 8;
-    static constexpr int VCH = BN / 8;
     static constexpr int QS = D / 16;
     static constexpr int KB = BN / 32;
     static constexpr int DB = D / 32;
     static constexpr int PS = BN / 16;
 
-    // mask_mode: 0 = every key allowed; 1 = per element check
     template <bool MASK>
-    __device__ __forceinline__ static void step(const uint16_t *__restrict__ Ks,
-                                                const uint16_t *__restrict__ Vt,
+    __device__ __forceinline__ static void step(const char *__restrict__ Ks,
+                                                const char *__restrict__ Vs,
+                                                const OperandOffsets<D> &off,
                                                 const bf16x8_t (&qf)[QS], f32x16_t (&o)[DB],
-                                                float &m_run, float &l_run, float c, int col,
-                                                int half, int key0, int key_end, int lim)
+                                                float &m_ref, float &l_run, float c, int half,
+                                                int key0, int key_end, int lim)
     {
         // ---- S^T = K Q^T over this tile's BN keys ----
         f32x16_t s[KB];
@@ -142,10 +244,8 @@ struct WaveTile {
         for (int st = 0; st < QS; ++st) {
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
-                const int key = kb * 32 + col;
-                const int ch = 2 * st + half;
-                const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(
-                    Ks + key * D + ((ch ^ (key % KCH)) * 8));
+                const bf16x8_t a =
+                    *reinterpret_cast<const bf16x8_t *>(Ks + off.k[st] + kb * 32 * 2 * D);
                 s[kb] = mfma32(a, qf[st], s[kb]);
             }
         }
@@ -161,19 +261,28 @@ struct WaveTile {
                 }
         }
 
-        // ---- online softmax (row = this lane's query) ----
+        // ---- online softmax (row = this lane's query) with a lazy reference max ----
         float mx = kNegInf;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
         mx = max_halves(mx);
-        const float m_new = fmaxf(m_run, mx);
-        // a row that has seen no allowed key yet keeps m = -inf; use 0 as its
-        // reference so that no -inf - -inf is formed
-        const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
-        const float alpha = (m_run == kNegInf) ? 0.0f : fast_exp2((m_run - m_use) * c);
-        const float mc = m_use * c;
+        // a row moves its reference when its max grew past the threshold (the
+        // first allowed key always does: m_ref starts at -inf)
+        const bool grow = (mx - m_ref) * c > kRescaleThreshold;
+        if (__any(grow)) {
+            const float m_new = grow ? mx : m_ref;
+            const float alpha = (m_ref == kNegInf) ? 0.0f : fast_exp2((m_ref - m_new) * c);
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+            m_ref = m_new;
+        }
+        // rows that have not seen an allowed key keep m_ref = -inf; 0 stands in
+        const float mc = (m_ref == kNegInf) ? 0.0f : m_ref * c;
         float lsum = 0.0f;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
@@ -184,18 +293,12 @@ struct WaveTile {
                 s[kb][r] = pv;
                 lsum += pv;
             }
-        l_run = fmaf(l_run, alpha, lsum);
-        m_run = m_new;
-        // rescale O only when some row's max moved
-        if (__any(alpha != 1.0f)) {
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-        }
+        l_run += lsum;
 
         // ---- P (bf16, from the S^T registers) as the B operand of O^T += V^T P^T ----
-        bf16x8_t pb[PS];
+        // PV step ps covers keys 16*ps .. +15; B element e of lane half h is key
+        // 16*ps + 8*(e/4) + 4*h + e%4, which the two transposing reads of V
+        // (keys 16*ps + 4*h + 0..3 and 16*ps + 8 + 4*h + 0..3) match.
 #pragma unroll
         for (int ps = 0; ps < PS; ++ps) {
             const int kb = ps >> 1, t2 = ps & 1;
@@ -203,21 +306,47 @@ struct WaveTile {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 w[e] = pack_bf16(s[kb][8 * t2 + 2 * e], s[kb][8 * t2 + 2 * e + 1]);
-            pb[ps] = __builtin_bit_cast(bf16x8_t, w);
-        }
-#pragma unroll
-        for (int ps = 0; ps < PS; ++ps) {
+            const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, w);
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                const int d = db * 32 + col;
-                const int ch = 2 * ps + half;
-                const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(
-                    Vt + d * BN + ((ch ^ (d % VCH)) * 8));
-                o[db] = mfma32(a, pb[ps], o[db]);
+                const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_i16x4_t *)(Vs + off.v[db][0] + ps * 16 * 2 * D));
+                const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_i16x4_t *)(Vs + off.v[db][1] + ps * 16 * 2 * D));
+                const u32x2_t lw = __builtin_bit_cast(u32x2_t, lo);
+                const u32x2_t hw = __builtin_bit_cast(u32x2_t, hi);
+                const bf16x8_t a = __builtin_bit_cast(bf16x8_t, (u32x4_t){lw[0], lw[1], hw[0], hw[1]});
+                o[db] = mfma32(a, pb, o[db]);
             }
         }
     }
 };
+
+// One pipeline step of a workgroup's key loop: wait for tile n (in `stage`),
+// start the copies of tile n + 1 into `next_stage`, then run this wave's share
+// of tile n.  `live` is false for a wave with nothing to do on tile n; it still
+// takes part in the barrier and the copies.
+template <int D, int BN, int NW>
+__device__ __forceinline__ void pipeline_step(
+    int n, int n_tiles, int key_base, char *stage, char *next_stage,
+    const TileLoader<D, BN, NW> &ld, int wave, int lane, bool live, int key_end, int wmin_lim,
+    const OperandOffsets<D> &off, const bf16x8_t (&qf)[D / 16], f32x16_t (&o)[D / 32],
+    float &m_ref, float &l_run, float c, int half, int lim_lane)
+{
+    constexpr int TB = TileLoader<D, BN, NW>::TILE_BYTES;
+    wait_vmem();           // this wave's copies of tile n are in LDS
+    __syncthreads();       // ... and every wave's; tile n - 1 is consumed
+    const int key0 = key_base + n * BN;
+    if (n + 1 < n_tiles) ld.issue(next_stage, next_stage + TB, key0 + BN, wave, lane);
+    if (!live) return;
+    const bool need_mask = (key0 + BN > key_end) || (key0 + BN - 1 > wmin_lim);
+    if (need_mask)
+        WaveTile<D, BN>::template step<true>(stage, stage + TB, off, qf, o, m_ref, l_run, c, half,
+                                             key0, key_end, lim_lane);
+    else
+        WaveTile<D, BN>::template step<false>(stage, stage + TB, off, qf, o, m_ref, l_run, c,
+                                              half, key0, key_end, lim_lane);
+}
 
 // Write 4 consecutive head dims of one output row.
 template <bool OUT_F32>
@@ -230,109 +359,6 @@ __device__ __forceinline__ void store4(void *o, long idx, float a, float b, floa
         u32x2_t v = {pack_bf16(a, b), pack_bf16(c, d)};
         *reinterpret_cast<u32x2_t *>(static_cast<uint16_t *>(o) + idx) = v;
     }
-}
-
-// ---------------------------------------------------------------------------
-// Staging of one K/V tile: global -> registers -> LDS.
-// K chunks go straight to Ks (swizzled); V chunks are transposed into Vt.
-// NTHR threads; each holds NK 16-byte chunks of K and NK of V, where the V
-// chunks are 4 consecutive keys x 8 head dims (so each transposed LDS write is
-// 4 keys wide).
-// ---------------------------------------------------------------------------
-template <int D, int BN, int NTHR>
-struct TileStager {
-    static constexpr int KCH = D / 8;
-    static constexpr int VCH = BN / 8;
-    static constexpr int NK = BN * KCH / NTHR;       // chunks per thread per tensor
-    static constexpr int KROWS = NTHR / KCH;          // K rows per pass
-    static constexpr int VGROUPS = NTHR / KCH;        // 4-key groups per V pass
-    static_assert(NK % 4 == 0 && NK >= 4, "stager needs groups of 4 keys");
-
-    u32x4_t kst[NK], vst[NK];
-
-    const uint16_t *kbase, *vbase;
-    int kstride_bytes;  // bytes between consecutive keys
-    int key_end;        // keys >= key_end read as zero
-
-    __device__ __forceinline__ void bind(const uint16_t *kb, const uint16_t *vb, long kstride,
-                                         int kend)
-    {
-        kbase = kb;
-        vbase = vb;
-        kstride_bytes = (int)(kstride * 2);
-        key_end = kend;
-    }
-
-    // Buffer descriptor over `rows` key rows starting at key `row0`: rows
-    // beyond key_end fall outside the descriptor's byte range and the hardware
-    // returns zero for them (no branch per load).  Built from uniform values,
-    // so it lives in scalar registers.
-    __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t *base,
-                                                                int row0) const
-    {
-        const int valid = key_end - row0;
-        const int nbytes = valid > 0 ? (valid - 1) * kstride_bytes + D * 2 : 0;
-        return __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(base + (long)row0 * (kstride_bytes / 2)), (short)0, nbytes, kBufferFlags);
-    }
-
-    // t: thread index, passed through an opaque copy so that the per-thread
-    // offsets are recomputed here instead of being hoisted (and kept live)
-    // across the whole loop.
-    __device__ __forceinline__ void load(int key0, int t)
-    {
-        const int ch = t % KCH;
-        const int vk = (t / KCH) * kstride_bytes + ch * 16;
-        const int vv = 4 * (t / KCH) * kstride_bytes + ch * 16;
-#pragma unroll
-        for (int i = 0; i < NK; ++i)
-            kst[i] = __builtin_amdgcn_raw_buffer_load_b128(rows_rsrc(kbase, key0 + i * KROWS), vk,
-                                                           0, 0);
-#pragma unroll
-        for (int i = 0; i < NK; ++i)
-            vst[i] = __builtin_amdgcn_raw_buffer_load_b128(
-                rows_rsrc(vbase, key0 + 4 * VGROUPS * (i / 4) + (i % 4)), vv, 0, 0);
-    }
-
-    __device__ __forceinline__ void store(uint16_t *__restrict__ Ks, uint16_t *__restrict__ Vt,
-                                          int t) const
-    {
-        const int ch = t % KCH;
-#pragma unroll
-        for (int i = 0; i < NK; ++i) {
-            const int row = t / KCH + i * KROWS;
-            *reinterpret_cast<u32x4_t *>(Ks + row * D + ((ch ^ (row % KCH)) * 8)) = kst[i];
-        }
-#pragma unroll
-        for (int g4 = 0; g4 < NK / 4; ++g4) {
-            const int key = 4 * VGROUPS * g4 + 4 * (t / KCH);
-            const int p0 = vt_pos(key);  // 4-aligned, the 4 keys stay adjacent
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int d = ch * 8 + e;
-                const int j = e >> 1;
-                const u32x4_t *w = &vst[4 * g4];
-                uint32_t lo, hi;
-                if (e & 1) {
-                    lo = (w[0][j] >> 16) | (w[1][j] & 0xffff0000u);
-                    hi = (w[2][j] >> 16) | (w[3][j] & 0xffff0000u);
-                } else {
-                    lo = (w[0][j] & 0xffffu) | (w[1][j] << 16);
-                    hi = (w[2][j] & 0xffffu) | (w[3][j] << 16);
-                }
-                *reinterpret_cast<u32x2_t *>(Vt + d * BN + (((p0 >> 3) ^ (d % VCH)) * 8) +
-                                             (p0 & 7)) = u32x2_t{lo, hi};
-            }
-        }
-    }
-};
-
-// An opaque copy of v: the compiler must assume it changes, so values derived
-// from it are recomputed where they are used rather than hoisted out of loops.
-__device__ __forceinline__ int opaque(int v)
-{
-    asm volatile("" : "+v"(v));
-    return v;
 }
 
 // Load this lane's Q fragment (B operand of S^T = K Q^T): head dims
@@ -350,9 +376,32 @@ __device__ __forceinline__ void load_q(bf16x8_t (&qf)[D / 16], const uint16_t *q
     }
 }
 
+// Epilogue of one wave's 32 query columns: O = O / l, LSE = ln 2 * (c*m + log2 l).
+template <int D, bool OUT_F32>
+__device__ __forceinline__ void finish_rows(const f32x16_t (&o)[D / 32], float m_ref,
+                                            float l_run, float c, int half, void *out,
+                                            long obase, float *lse_out, bool write)
+{
+    const float l = add_halves(l_run);
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    if (!write) return;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+            const int d0 = db * 32 + 8 * gq + 4 * half;
+            store4<OUT_F32>(out, obase + d0, o[db][4 * gq] * inv, o[db][4 * gq + 1] * inv,
+                            o[db][4 * gq + 2] * inv, o[db][4 * gq + 3] * inv);
+        }
+    if (lse_out && half == 0) {
+        const float mc = (m_ref == kNegInf) ? 0.0f : m_ref * c;
+        *lse_out = l > 0.0f ? (mc + __log2f(l)) * kLn2 : kNegInf;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Prefill: one workgroup = 4 waves = 128 query rows of one (b, hq); K/V tiles
-// of BN keys stream through a double-buffered LDS stage.
+// of BN keys stream through a two-stage LDS ring filled by HBM -> LDS copies.
 // ---------------------------------------------------------------------------
 template <int D>
 struct PrefillTraits {
@@ -363,19 +412,24 @@ template <int D, bool OUT_F32>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 fa_prefill_kernel(const Params p)
 {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
     constexpr int BM = kPrefillBM;
     constexpr int BN = PrefillTraits<D>::BN;
-    constexpr int TILE = BN * D;
     using WT = WaveTile<D, BN>;
-    using ST = TileStager<D, BN, 256>;
+    using TL = TileLoader<D, BN, 4>;
+    constexpr int TB = TL::TILE_BYTES;
+    constexpr int STAGE = 2 * TB;   // K tile then V tile
 
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 2 * TILE];
+    __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int col = lane & 31;
     const int half = lane >> 5;
+
+    OperandOffsets<D> off;
+    off.init(lane);
 
     const int BH = p.B * p.Hq;
     const int ND = p.domains;
@@ -384,7 +438,6 @@ fa_prefill_kernel(const Params p)
     const int Gx = gridDim.x / ND;
     const int BHx = BH / ND;                 // (b, hq) pairs of this domain
     const int Nx = BHx * p.n_mblocks;        // items of this domain
-    const long kstride = (long)p.Hkv * D;    // elements between consecutive keys
 
     for (int t = 0; t * Gx < Nx; ++t) {
         const int li = t * Gx + ((t & 1) ? (Gx - 1 - jw) : jw);
@@ -411,69 +464,43 @@ fa_prefill_kernel(const Params p)
         bf16x8_t qf[D / 16];
         load_q<D>(qf, p.q + (((long)b * p.Sq + qi) * p.Hq + hq) * D, qi < p.Sq, half, p.qflip);
 
-        const uint16_t *kbase = p.k + ((long)b * p.Sk * p.Hkv + g) * D;
-        const uint16_t *vbase = p.v + ((long)b * p.Sk * p.Hkv + g) * D;
+        TL ld;
+        ld.kbase = p.k + ((long)b * p.Sk * p.Hkv + g) * D;
+        ld.vbase = p.v + ((long)b * p.Sk * p.Hkv + g) * D;
+        ld.kstride_bytes = p.Hkv * D * 2;
+        ld.key_end = p.Sk;
 
         f32x16_t o[D / 32];
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) o[db] = f32x16_t{};
-        float m_run = kNegInf, l_run = 0.0f;
-
-        ST stg;
-        stg.bind(kbase, vbase, kstride, p.Sk);
-        if (n_tiles > 0) {
-            stg.load(0, opaque(tid));
-            stg.store(lds, lds + TILE, opaque(tid));
-        }
-        __syncthreads();
+        float m_ref = kNegInf, l_run = 0.0f;
 
         const int lim_lane = p.causal ? qi + p.off : 0x7fffffff;
         const int wmin_lim = p.causal ? wrow0 + p.off : 0x7fffffff;   // smallest limit of the wave
         const int wmax_lim = p.causal ? wlast + p.off : 0x7fffffff;   // largest limit of the wave
+        const bool wave_live = wrow0 < p.Sq;
 
-        for (int n = 0; n < n_tiles; ++n) {
-            const int buf = n & 1;
-            if (n + 1 < n_tiles) stg.load((n + 1) * BN, opaque(tid));
+        if (n_tiles > 0) ld.issue(lds, lds + TB, 0, wave, lane);
 
-            const int key0 = n * BN;
-            const uint16_t *Ks = lds + buf * 2 * TILE;
-            const uint16_t *Vt = Ks + TILE;
-            if (wrow0 < p.Sq && key0 <= wmax_lim) {   // tile not fully masked for this wave
-                const bool need_mask = (key0 + BN > p.Sk) || (key0 + BN - 1 > wmin_lim);
-                if (need_mask)
-                    WT::template step<true>(Ks, Vt, qf, o, m_run, l_run, p.c, col, half, key0,
-                                            p.Sk, lim_lane);
-                else
-                    WT::template step<false>(Ks, Vt, qf, o, m_run, l_run, p.c, col, half, key0,
-                                             p.Sk, lim_lane);
-            }
-
-            if (n + 1 < n_tiles) {
-                uint16_t *Kn = lds + (buf ^ 1) * 2 * TILE;
-                stg.store(Kn, Kn + TILE, opaque(tid));
-            }
-            __syncthreads();
+        // tile n lives in stage n & 1; the loop handles two tiles per trip so
+        // that every LDS offset is a compile-time constant
+        for (int n = 0; n < n_tiles; n += 2) {
+            pipeline_step<D, BN, 4>(n, n_tiles, 0, lds, lds + STAGE, ld, wave, lane,
+                                    wave_live && n * BN <= wmax_lim, p.Sk, wmin_lim, off, qf, o,
+                                    m_ref, l_run, p.c, half, lim_lane);
+            if (n + 1 < n_tiles)
+                pipeline_step<D, BN, 4>(n + 1, n_tiles, 0, lds + STAGE, lds, ld, wave, lane,
+                                        wave_live && (n + 1) * BN <= wmax_lim, p.Sk, wmin_lim,
+                                        off, qf, o, m_ref, l_run, p.c, half, lim_lane);
         }
+        __syncthreads();   // every wave is done with the LDS ring before the next item
 
-        // ---- epilogue: O = O / l, LSE = ln(2) * (c * m + log2 l) ----
-        const float l = add_halves(l_run);
-        const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-        if (qi < p.Sq) {
-            const long obase = (((long)b * p.Sq + qi) * p.Hq + hq) * D;
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-                for (int gq = 0; gq < 4; ++gq) {
-                    const int d0 = db * 32 + 8 * gq + 4 * half;
-                    store4<OUT_F32>(p.o, obase + d0, o[db][4 * gq] * inv,
-                                    o[db][4 * gq + 1] * inv, o[db][4 * gq + 2] * inv,
-                                    o[db][4 * gq + 3] * inv);
-                }
-            if (p.lse && half == 0)
-                p.lse[((long)b * p.Hq + hq) * p.Sq + qi] =
-                    l > 0.0f ? (m_run * p.c + __log2f(l)) * kLn2 : kNegInf;
-        }
+        finish_rows<D, OUT_F32>(o, m_ref, l_run, p.c, half, p.o,
+                                (((long)b * p.Sq + qi) * p.Hq + hq) * D,
+                                p.lse ? p.lse + ((long)b * p.Hq + hq) * p.Sq + qi : nullptr,
+                                qi < p.Sq);
     }
+#endif
 }
 
 // ---------------------------------------------------------------------------
@@ -485,16 +512,21 @@ template <int D, bool OUT_F32>
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
 fa_decode_split_kernel(const Params p)
 {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
     constexpr int BN = kDecodeBN;
-    constexpr int TILE = BN * D;
     using WT = WaveTile<D, BN>;
-    using ST = TileStager<D, BN, 64>;
+    using TL = TileLoader<D, BN, 1>;
+    constexpr int TB = TL::TILE_BYTES;
+    constexpr int STAGE = 2 * TB;
 
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * TILE];
+    __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE];
 
     const int lane = threadIdx.x;
     const int col = lane & 31;
     const int half = lane >> 5;
+
+    OperandOffsets<D> off;
+    off.init(lane);
 
     const int item = blockIdx.x;
     const int s = item % p.num_splits;
@@ -508,72 +540,46 @@ fa_decode_split_kernel(const Params p)
     const int hq = g * p.group + (valid ? col % p.group : 0);
 
     const int k_begin = s * p.split_len;
-    int k_end = min(k_begin + p.split_len, p.Sk);
-    if (p.causal) k_end = min(k_end, p.Sq - 1 + p.off + 1);   // beyond every row's limit
+    const int k_end = min(k_begin + p.split_len, p.Sk);
     const int n_tiles = k_end > k_begin ? (k_end - k_begin + BN - 1) / BN : 0;
 
     bf16x8_t qf[D / 16];
     load_q<D>(qf, p.q + (((long)b * p.Sq + qi) * p.Hq + hq) * D, valid, half, p.qflip);
 
-    const long kstride = (long)p.Hkv * D;
-    const uint16_t *kbase = p.k + ((long)b * p.Sk * p.Hkv + g) * D;
-    const uint16_t *vbase = p.v + ((long)b * p.Sk * p.Hkv + g) * D;
+    TL ld;
+    ld.kbase = p.k + ((long)b * p.Sk * p.Hkv + g) * D;
+    ld.vbase = p.v + ((long)b * p.Sk * p.Hkv + g) * D;
+    ld.kstride_bytes = p.Hkv * D * 2;
+    ld.key_end = k_end;
 
     f32x16_t o[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) o[db] = f32x16_t{};
-    float m_run = kNegInf, l_run = 0.0f;
+    float m_ref = kNegInf, l_run = 0.0f;
 
     const int lim_lane = p.causal ? qi + p.off : 0x7fffffff;
     const int wmin_lim = p.causal ? p.off : 0x7fffffff;   // row 0 has the smallest limit
 
-    ST stg;
-    stg.bind(kbase, vbase, kstride, k_end);
-    if (n_tiles > 0) stg.load(k_begin, opaque(lane));
-    for (int n = 0; n < n_tiles; ++n) {
-        const int key0 = k_begin + n * BN;
-        __syncthreads();                      // previous tile's LDS reads are done
-        stg.store(lds, lds + TILE, opaque(lane));
-        __syncthreads();
-        if (n + 1 < n_tiles) stg.load(key0 + BN, opaque(lane));
-        const bool need_mask = (key0 + BN > k_end) || (key0 + BN - 1 > wmin_lim);
-        // keys are counted relative to the tile inside step(); pass absolute bounds
-        if (need_mask)
-            WT::template step<true>(lds, lds + TILE, qf, o, m_run, l_run, p.c, col, half, key0,
-                                    k_end, lim_lane);
-        else
-            WT::template step<false>(lds, lds + TILE, qf, o, m_run, l_run, p.c, col, half, key0,
-                                     k_end, lim_lane);
+    if (n_tiles > 0) ld.issue(lds, lds + TB, k_begin, 0, lane);
+    for (int n = 0; n < n_tiles; n += 2) {
+        pipeline_step<D, BN, 1>(n, n_tiles, k_begin, lds, lds + STAGE, ld, 0, lane, true, k_end,
+                                wmin_lim, off, qf, o, m_ref, l_run, p.c, half, lim_lane);
+        if (n + 1 < n_tiles)
+            pipeline_step<D, BN, 1>(n + 1, n_tiles, k_begin, lds + STAGE, lds, ld, 0, lane, true,
+                                    k_end, wmin_lim, off, qf, o, m_ref, l_run, p.c, half,
+                                    lim_lane);
     }
 
-    const float l = add_halves(l_run);
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-    const float lse = l > 0.0f ? (m_run * p.c + __log2f(l)) * kLn2 : kNegInf;
-    if (!valid) return;
     if (p.num_splits == 1) {
-        const long obase = (((long)b * p.Sq + qi) * p.Hq + hq) * D;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                const int d0 = db * 32 + 8 * gq + 4 * half;
-                store4<OUT_F32>(p.o, obase + d0, o[db][4 * gq] * inv, o[db][4 * gq + 1] * inv,
-                                o[db][4 * gq + 2] * inv, o[db][4 * gq + 3] * inv);
-            }
-        if (p.lse && half == 0) p.lse[((long)b * p.Hq + hq) * p.Sq + qi] = lse;
+        finish_rows<D, OUT_F32>(o, m_ref, l_run, p.c, half, p.o,
+                                (((long)b * p.Sq + qi) * p.Hq + hq) * D,
+                                p.lse ? p.lse + ((long)b * p.Hq + hq) * p.Sq + qi : nullptr, valid);
     } else {
         const long prow = (((long)s * p.B + b) * p.Hq + hq) * p.Sq + qi;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                const int d0 = db * 32 + 8 * gq + 4 * half;
-                store4<true>(p.part_o, prow * D + d0, o[db][4 * gq] * inv,
-                             o[db][4 * gq + 1] * inv, o[db][4 * gq + 2] * inv,
-                             o[db][4 * gq + 3] * inv);
-            }
-        if (half == 0) p.part_lse[prow] = lse;
+        finish_rows<D, true>(o, m_ref, l_run, p.c, half, p.part_o, prow * D, p.part_lse + prow,
+                             valid);
     }
+#endif
 }
 
 // ---------------------------------------------------------------------------
@@ -585,6 +591,7 @@ fa_decode_split_kernel(const Params p)
 template <int D, bool OUT_F32>
 __global__ void __launch_bounds__(64) fa_merge_kernel(const Params p)
 {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
     const int lane = threadIdx.x;
     const long row = blockIdx.x;                 // (b, hq, i) with i fastest
     const long n_rows = (long)p.B * p.Hq * p.Sq;
@@ -630,6 +637,7 @@ __global__ void __launch_bounds__(64) fa_merge_kernel(const Params p)
     }
     if (p.lse && lane == 0)
         p.lse[row] = wsum > 0.0f ? Mu + __logf(wsum) : kNegInf;
+#endif
 }
 
 Params make_params(const Launch &L)
@@ -660,7 +668,9 @@ Params make_params(const Launch &L)
     return p;
 }
 
-}  // namespace
+}  // namespace kern
+
+using namespace kern;
 
 hipError_t launch_prefill(const Launch &L)
 {

@@ -115,6 +115,32 @@ def cpu_baseline_leg(w, q, k, v, o_gpu, lse_gpu, seconds):
     }
 
 
+def profile_one(args):
+    """Run one call `warmup + steps` times on its own (for rocprofv3 --pmc)."""
+    import torch
+    from attention_fwd_02_amd import _binding as fa
+    from attention_fwd_02_amd.inputs import WORKLOADS, make_inputs
+    dev = "cuda:0"
+    if args.profile_kernel == "copy":
+        n = 1 << 30
+        x = torch.empty(n // 2, dtype=torch.bfloat16, device=dev).fill_(1.0)
+        y = torch.empty_like(x)
+        fn = lambda: y.copy_(x)  # noqa: E731
+        label = f"copy of {n} bytes"
+    else:
+        w = WORKLOADS[PREFILL if args.profile_kernel == "prefill" else DECODE]
+        q, k, v = (t.to(dev) for t in make_inputs(w))
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=dev)
+        fn = lambda: fa.fa_fwd(q, k, v, o, lse, w.causal, w.scale)  # noqa: E731
+        label = w.name
+    for _ in range(args.warmup + args.steps):
+        fn()
+    torch.cuda.synchronize()
+    print(f"profiled {label}: {args.warmup + args.steps} calls", flush=True)
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -122,6 +148,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-kernel", choices=["prefill", "decode", "copy"],
+                    help="run only this call (warmup + steps) for counter collection; "
+                         "'copy' is a plain 1 GiB device-to-device copy that calibrates "
+                         "the HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
@@ -134,6 +164,8 @@ def main():
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.profile_kernel:
+        return profile_one(args)
     wp, wd = WORKLOADS[PREFILL], WORKLOADS[DECODE]
     qp_h, kp_h, vp_h = make_inputs(wp)
     qp, kp, vp = (t.to(dev) for t in (qp_h, kp_h, vp_h))
