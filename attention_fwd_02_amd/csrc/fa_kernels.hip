@@ -50,6 +50,8 @@ namespace fa {
 namespace kern {
 
 typedef __bf16 bf16x8_t __attribute__((__vector_size__(16)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((__vector_size__(64)));
 typedef uint32_t u32x4_t __attribute__((__vector_size__(16)));
@@ -103,11 +105,11 @@ __device__ __forceinline__ float add_halves(float x)
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Two floats to two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b)
 {
-    __bf16 x = (__bf16)a, y = (__bf16)b;  // round to nearest even (v_cvt_pk_bf16_f32)
-    return (uint32_t)__builtin_bit_cast(uint16_t, x) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+    const f32x2_t v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 __device__ __forceinline__ u32x4_t ld16(const uint16_t *p)
@@ -424,7 +426,9 @@ fa_prefill_kernel(const Params p)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    // the wave index is uniform across the wave: say so, so that everything
+    // derived from it (tile-copy descriptors, row ranges) stays scalar
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 31;
     const int half = lane >> 5;
 
