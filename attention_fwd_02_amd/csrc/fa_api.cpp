@@ -111,6 +111,7 @@ struct Plan {
     int split_len = 0;
     int block_m = 0, block_n = 0;
     int grid = 0, items = 0;
+    int prefill_bn = 0, prefill_nw = 0;
     size_t ws_bytes = 0;
 };
 
@@ -160,11 +161,31 @@ fa_status make_plan(int B, int Hq, int Hkv, int Sq, int Sk, int D, int num_split
         pl.ws_bytes = split_ws_bytes(B, Hq, Sq, D, ns);
     } else {
         pl.path = 0;
-        pl.block_m = fa::kPrefillBM;
-        pl.block_n = fa::prefill_block_n(D);
-        const int64_t items = (int64_t)B * Hq * ((Sq + fa::kPrefillBM - 1) / fa::kPrefillBM);
+        // tile configuration: 8 waves x 64 keys by default (two waves per
+        // SIMD, K/V tiles shared by 256 query rows); 4-wave workgroups when
+        // that leaves too few items to cover the CUs.  FA_PREFILL_BN /
+        // FA_PREFILL_NW override for ablations.
+        int bn = 64, nw = 8;
+        const int64_t m8 = (Sq + 255) / 256;
+        if ((int64_t)B * Hq * m8 < cus) {
+            nw = 4;
+            bn = 32;
+        }
+        const int ebn = env_int("FA_PREFILL_BN", 0), enw = env_int("FA_PREFILL_NW", 0);
+        if (ebn > 0 && enw > 0 && fa::prefill_cfg_ok(D, ebn, enw)) {
+            bn = ebn;
+            nw = enw;
+        }
+        const int bm = 32 * nw;
+        pl.block_m = bm;
+        pl.block_n = bn;
+        pl.prefill_bn = bn;
+        pl.prefill_nw = nw;
+        const int64_t items = (int64_t)B * Hq * ((Sq + bm - 1) / bm);
         if (items >= (int64_t(1) << 31)) return fail(FA_ERR_UNSUPPORTED, "too many work items");
-        const int wg_per_cu = std::max(1, env_int("FA_WG_PER_CU", 2));
+        // workgroups a CU holds at once: LDS (160 KiB) and two waves per SIMD
+        int wg_per_cu = std::min((160 * 1024) / fa::prefill_lds_bytes(D, bn), 8 / nw);
+        wg_per_cu = std::max(1, std::min(wg_per_cu, env_int("FA_WG_PER_CU", wg_per_cu)));
         int64_t grid = std::min<int64_t>(items, (int64_t)cus * wg_per_cu);
         if (env_int("FA_PERSISTENT", 1) == 0) grid = items;
         pl.items = (int)items;
@@ -225,6 +246,8 @@ fa_status fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float 
     L.num_splits = pl.num_splits;
     L.split_len = pl.split_len;
     L.grid = pl.grid;
+    L.prefill_bn = pl.prefill_bn;
+    L.prefill_nw = pl.prefill_nw;
     L.stream = stream;
 
     if (log_enabled())

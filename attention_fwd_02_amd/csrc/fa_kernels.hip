@@ -112,6 +112,10 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b)
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
+// The two bf16 halves of a packed word, widened exactly to fp32.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
 __device__ __forceinline__ u32x4_t ld16(const uint16_t *p)
 {
     return *reinterpret_cast<const u32x4_t *>(p);
@@ -235,8 +239,8 @@ struct WaveTile {
                                                 const char *__restrict__ Vs,
                                                 const OperandOffsets<D> &off,
                                                 const bf16x8_t (&qf)[QS], f32x16_t (&o)[DB],
-                                                float &m_ref, float &l_run, float c, int half,
-                                                int key0, int key_end, int lim)
+                                                float &m_ref, float &l_run, float &l_rnd, float c,
+                                                int half, int key0, int key_end, int lim)
     {
         // ---- S^T = K Q^T over this tile's BN keys ----
         f32x16_t s[KB];
@@ -277,6 +281,7 @@ struct WaveTile {
             const float m_new = grow ? mx : m_ref;
             const float alpha = (m_ref == kNegInf) ? 0.0f : fast_exp2((m_ref - m_new) * c);
             l_run *= alpha;
+            l_rnd *= alpha;
 #pragma unroll
             for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -285,7 +290,6 @@ struct WaveTile {
         }
         // rows that have not seen an allowed key keep m_ref = -inf; 0 stands in
         const float mc = (m_ref == kNegInf) ? 0.0f : m_ref * c;
-        float lsum = 0.0f;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -293,9 +297,8 @@ struct WaveTile {
                 float pv = fast_exp2(fmaf(s[kb][r], c, -mc));
                 if (MASK) pv = (s[kb][r] == kNegInf) ? 0.0f : pv;
                 s[kb][r] = pv;
-                lsum += pv;
+                l_run += pv;
             }
-        l_run += lsum;
 
         // ---- P (bf16, from the S^T registers) as the B operand of O^T += V^T P^T ----
         // PV step ps covers keys 16*ps .. +15; B element e of lane half h is key
@@ -308,6 +311,10 @@ struct WaveTile {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 w[e] = pack_bf16(s[kb][8 * t2 + 2 * e], s[kb][8 * t2 + 2 * e + 1]);
+            // l_rnd adds the rounded values that P V multiplies (normalises O);
+            // l_run above the exact ones (feeds the LSE)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) l_rnd += bf16_lo(w[e]) + bf16_hi(w[e]);
             const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, w);
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
@@ -333,7 +340,7 @@ __device__ __forceinline__ void pipeline_step(
     int n, int n_tiles, int key_base, char *stage, char *next_stage,
     const TileLoader<D, BN, NW> &ld, int wave, int lane, bool live, int key_end, int wmin_lim,
     const OperandOffsets<D> &off, const bf16x8_t (&qf)[D / 16], f32x16_t (&o)[D / 32],
-    float &m_ref, float &l_run, float c, int half, int lim_lane)
+    float &m_ref, float &l_run, float &l_rnd, float c, int half, int lim_lane)
 {
     constexpr int TB = TileLoader<D, BN, NW>::TILE_BYTES;
     wait_vmem();           // this wave's copies of tile n are in LDS
@@ -343,11 +350,11 @@ __device__ __forceinline__ void pipeline_step(
     if (!live) return;
     const bool need_mask = (key0 + BN > key_end) || (key0 + BN - 1 > wmin_lim);
     if (need_mask)
-        WaveTile<D, BN>::template step<true>(stage, stage + TB, off, qf, o, m_ref, l_run, c, half,
-                                             key0, key_end, lim_lane);
+        WaveTile<D, BN>::template step<true>(stage, stage + TB, off, qf, o, m_ref, l_run, l_rnd,
+                                             c, half, key0, key_end, lim_lane);
     else
-        WaveTile<D, BN>::template step<false>(stage, stage + TB, off, qf, o, m_ref, l_run, c,
-                                              half, key0, key_end, lim_lane);
+        WaveTile<D, BN>::template step<false>(stage, stage + TB, off, qf, o, m_ref, l_run, l_rnd,
+                                              c, half, key0, key_end, lim_lane);
 }
 
 // Write 4 consecutive head dims of one output row.
@@ -378,14 +385,17 @@ __device__ __forceinline__ void load_q(bf16x8_t (&qf)[D / 16], const uint16_t *q
     }
 }
 
-// Epilogue of one wave's 32 query columns: O = O / l, LSE = ln 2 * (c*m + log2 l).
+// Epilogue of one wave's 32 query columns: O = O / l_norm, and
+// LSE = ln 2 * (c*m + log2 l) from the exact row sum l.  l_norm (whole row)
+// is the sum of the rounded P that O accumulated; l_part is this lane
+// half's share of the exact sum.
 template <int D, bool OUT_F32>
 __device__ __forceinline__ void finish_rows(const f32x16_t (&o)[D / 32], float m_ref,
-                                            float l_run, float c, int half, void *out,
-                                            long obase, float *lse_out, bool write)
+                                            float l_part, float l_norm, float c, int half,
+                                            void *out, long obase, float *lse_out, bool write)
 {
-    const float l = add_halves(l_run);
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    const float l = add_halves(l_part);
+    const float inv = l_norm > 0.0f ? 1.0f / l_norm : 0.0f;
     if (!write) return;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -402,27 +412,218 @@ __device__ __forceinline__ void finish_rows(const f32x16_t (&o)[D / 32], float m
 }
 
 // ---------------------------------------------------------------------------
-// Prefill: one workgroup = 4 waves = 128 query rows of one (b, hq); K/V tiles
-// of BN keys stream through a two-stage LDS ring filled by HBM -> LDS copies.
+// Per-block pieces of the pipelined prefill (a block = 32 keys).
 // ---------------------------------------------------------------------------
 template <int D>
-struct PrefillTraits {
-    static constexpr int BN = D == 64 ? 128 : 64;
+struct BlockOps {
+    static constexpr int QS = D / 16;
+    static constexpr int DB = D / 32;
+
+    // S^T of one 32-key block whose K rows start at Kblk (LDS).
+    __device__ __forceinline__ static f32x16_t qk(const char *Kblk, const OperandOffsets<D> &off,
+                                                  const bf16x8_t (&qf)[QS])
+    {
+        f32x16_t s = f32x16_t{};
+#pragma unroll
+        for (int st = 0; st < QS; ++st) {
+            const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(Kblk + off.k[st]);
+            s = mfma32(a, qf[st], s);
+        }
+        return s;
+    }
+
+    // keys >= key_end, or beyond this lane's causal limit, score -inf
+    __device__ __forceinline__ static void mask(f32x16_t &s, int key0, int half, int key_end,
+                                                int lim)
+    {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int key = key0 + 8 * (r >> 2) + 4 * half + (r & 3);
+            if (key >= key_end || key > lim) s[r] = kNegInf;
+        }
+    }
+
+    // max over the block's keys of this lane's query (both lane halves)
+    __device__ __forceinline__ static float rowmax(const f32x16_t &s)
+    {
+        float mx = kNegInf;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+        return max_halves(mx);
+    }
+
+    // Lazy reference max: move it (and rescale O and l) only for rows whose
+    // max grew past the threshold; the first allowed key always does.
+    __device__ __forceinline__ static void rebase(float mx, float &m_ref, float &l_run,
+                                                  f32x16_t &l_acc, f32x16_t (&o)[DB], float c)
+    {
+        const bool grow = (mx - m_ref) * c > kRescaleThreshold;
+        if (__any(grow)) {
+            const float m_new = grow ? mx : m_ref;
+            const float alpha = (m_ref == kNegInf) ? 0.0f : fast_exp2((m_ref - m_new) * c);
+            l_run *= alpha;
+            l_acc[0] *= alpha;   // only element 0 of the row-sum accumulator is read
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+            m_ref = m_new;
+        }
+    }
+
+    // P = exp2(c*s - mc), rounded to bf16, as the B operands of the block's two
+    // 16-key PV steps (p0: registers 0..7, p1: 8..15).  l_run adds the exact
+    // fp32 values (it feeds the LSE); the sum of the rounded values, which
+    // normalises O, is taken on the MFMA unit in pv().
+    template <bool MASK>
+    __device__ __forceinline__ static void probs(const f32x16_t &s, float c, float mc,
+                                                 bf16x8_t &p0, bf16x8_t &p1, float &l_run)
+    {
+        float e[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            e[r] = fast_exp2(fmaf(s[r], c, -mc));
+            if (MASK) e[r] = (s[r] == kNegInf) ? 0.0f : e[r];
+        }
+        u32x4_t w0, w1;
+        float la = 0.0f, lb = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            w0[q] = pack_bf16(e[2 * q], e[2 * q + 1]);
+            w1[q] = pack_bf16(e[8 + 2 * q], e[8 + 2 * q + 1]);
+            la += e[2 * q] + e[2 * q + 1];
+            lb += e[8 + 2 * q] + e[8 + 2 * q + 1];
+        }
+        l_run += la + lb;
+        p0 = __builtin_bit_cast(bf16x8_t, w0);
+        p1 = __builtin_bit_cast(bf16x8_t, w1);
+    }
+
+    // O^T += V^T P^T over the block whose V rows start at Vblk (LDS).  The
+    // same P also meets an all-ones A operand: every row of l_acc then holds
+    // the running sum of the rounded P of this lane's query column -- the
+    // values P V multiplies, so O / sum is normalised consistently (with the
+    // lazy reference P reaches 2^8 and is not exact in bf16; a dominant key's
+    // rounding then divides out).
+    __device__ __forceinline__ static void pv(const char *Vblk, const OperandOffsets<D> &off,
+                                              bf16x8_t p0, bf16x8_t p1, f32x16_t (&o)[DB],
+                                              f32x16_t &l_acc)
+    {
+        const bf16x8_t ones = __builtin_bit_cast(
+            bf16x8_t, (u32x4_t){0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
+        l_acc = mfma32(ones, p0, l_acc);
+        l_acc = mfma32(ones, p1, l_acc);
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_i16x4_t *)(Vblk + off.v[db][0] + t2 * 16 * 2 * D));
+                const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_i16x4_t *)(Vblk + off.v[db][1] + t2 * 16 * 2 * D));
+                const u32x2_t lw = __builtin_bit_cast(u32x2_t, lo);
+                const u32x2_t hw = __builtin_bit_cast(u32x2_t, hi);
+                const bf16x8_t a =
+                    __builtin_bit_cast(bf16x8_t, (u32x4_t){lw[0], lw[1], hw[0], hw[1]});
+                o[db] = mfma32(a, t2 ? p1 : p0, o[db]);
+            }
+        }
+    }
 };
 
-template <int D, bool OUT_F32>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+// State of one wave's query rows while the workgroup walks the key tiles.
+template <int D>
+struct RowState {
+    bf16x8_t qf[D / 16];
+    f32x16_t o[D / 32];
+    f32x16_t s_cur;      // S^T of the block to be finished next
+    float mx_cur;        // its row max
+    float m_ref, l_run;  // lazy reference max and exact row sum (this lane half)
+    f32x16_t l_acc;      // element 0: row sum of the rounded P (whole row)
+    int NBw;             // blocks this wave has work on (a prefix of the tile walk)
+    int wmin_lim;        // smallest causal limit of the wave's rows
+    int lim_lane;        // this lane's causal limit
+    int key_end;
+    int half;
+    float c;
+
+    __device__ __forceinline__ bool needs_mask(int j) const
+    {
+        return (j * 32 + 32 > key_end) || (j * 32 + 31 > wmin_lim);
+    }
+};
+
+// The blocks of tile t (held in LDS stage `stage`).  Pipeline: while block j
+// is finished (softmax, P V) the S^T of block j + 1 is already issued, so the
+// MFMA and VALU work of neighbouring blocks overlap.  Block j + 1 may be the
+// first block of tile t + 1 (stage `next`): the barrier that makes tile t + 1
+// ready is taken first, and tile t + 2's copies then start into `after`, the
+// stage tile t - 1 used, which every wave has finished by that barrier.
+template <int D, int BN, int NW>
+__device__ __forceinline__ void prefill_tile(int t, int n_tiles, char *stage, char *next,
+                                             char *after, const TileLoader<D, BN, NW> &ld,
+                                             int wave, int lane, const OperandOffsets<D> &off,
+                                             RowState<D> &rs)
+{
+    constexpr int KB = BN / 32;
+    constexpr int TB = TileLoader<D, BN, NW>::TILE_BYTES;
+    using BO = BlockOps<D>;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+        const int j = t * KB + kb;
+        const bool live = j < rs.NBw;
+        const bool live_next = j + 1 < rs.NBw;
+        float mc = 0.0f;
+        if (live) {
+            BO::rebase(rs.mx_cur, rs.m_ref, rs.l_run, rs.l_acc, rs.o, rs.c);
+            mc = (rs.m_ref == kNegInf) ? 0.0f : rs.m_ref * rs.c;
+        }
+        const char *Knext = stage + (kb + 1) * 32 * 2 * D;
+        if (kb == KB - 1) {
+            Knext = next;
+            if (t + 1 < n_tiles) {
+                wait_vmem();       // this wave's copies of tile t + 1 are in LDS
+                __syncthreads();   // ... and every wave's; tile t - 1 is released
+                if (t + 2 < n_tiles) ld.issue(after, after + TB, (t + 2) * BN, wave, lane);
+            }
+        }
+        f32x16_t s_next = f32x16_t{};
+        if (live_next) s_next = BO::qk(Knext, off, rs.qf);
+        if (live) {
+            bf16x8_t p0, p1;
+            if (rs.needs_mask(j))
+                BO::template probs<true>(rs.s_cur, rs.c, mc, p0, p1, rs.l_run);
+            else
+                BO::template probs<false>(rs.s_cur, rs.c, mc, p0, p1, rs.l_run);
+            BO::pv(stage + TB + kb * 32 * 2 * D, off, p0, p1, rs.o, rs.l_acc);
+        }
+        if (live_next) {
+            if (rs.needs_mask(j + 1))
+                BO::mask(s_next, (j + 1) * 32, rs.half, rs.key_end, rs.lim_lane);
+            rs.mx_cur = BO::rowmax(s_next);
+        }
+        rs.s_cur = s_next;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Prefill: one workgroup = NW waves = 32*NW query rows of one (b, hq); K/V
+// tiles of BN keys stream through a three-stage LDS ring filled by
+// HBM -> LDS copies, one barrier per tile.
+// ---------------------------------------------------------------------------
+template <int D, int BN, int NW, bool OUT_F32>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 fa_prefill_kernel(const Params p)
 {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
-    constexpr int BM = kPrefillBM;
-    constexpr int BN = PrefillTraits<D>::BN;
-    using WT = WaveTile<D, BN>;
-    using TL = TileLoader<D, BN, 4>;
+    constexpr int BM = 32 * NW;
+    constexpr int KB = BN / 32;
+    using TL = TileLoader<D, BN, NW>;
+    using BO = BlockOps<D>;
     constexpr int TB = TL::TILE_BYTES;
     constexpr int STAGE = 2 * TB;   // K tile then V tile
 
-    __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE];
+    __shared__ __attribute__((aligned(1024))) char lds[kPrefillStages * STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -443,8 +644,8 @@ fa_prefill_kernel(const Params p)
     const int BHx = BH / ND;                 // (b, hq) pairs of this domain
     const int Nx = BHx * p.n_mblocks;        // items of this domain
 
-    for (int t = 0; t * Gx < Nx; ++t) {
-        const int li = t * Gx + ((t & 1) ? (Gx - 1 - jw) : jw);
+    for (int it = 0; it * Gx < Nx; ++it) {
+        const int li = it * Gx + ((it & 1) ? (Gx - 1 - jw) : jw);
         if (li >= Nx) continue;
         const int rank = li / BHx;
         const int bh = (li % BHx) * ND + x;
@@ -465,8 +666,29 @@ fa_prefill_kernel(const Params p)
             n_tiles = hi < 0 ? 0 : min(n_tiles, hi / BN + 1);
         }
 
-        bf16x8_t qf[D / 16];
-        load_q<D>(qf, p.q + (((long)b * p.Sq + qi) * p.Hq + hq) * D, qi < p.Sq, half, p.qflip);
+        RowState<D> rs;
+        load_q<D>(rs.qf, p.q + (((long)b * p.Sq + qi) * p.Hq + hq) * D, qi < p.Sq, half,
+                  p.qflip);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) rs.o[db] = f32x16_t{};
+        rs.m_ref = kNegInf;
+        rs.l_run = 0.0f;
+        rs.l_acc = f32x16_t{};
+        rs.s_cur = f32x16_t{};
+        rs.mx_cur = kNegInf;
+        rs.half = half;
+        rs.c = p.c;
+        rs.key_end = p.Sk;
+        rs.lim_lane = p.causal ? qi + p.off : 0x7fffffff;
+        rs.wmin_lim = p.causal ? wrow0 + p.off : 0x7fffffff;
+        const int NB = n_tiles * KB;
+        if (wrow0 >= p.Sq)
+            rs.NBw = 0;
+        else if (p.causal) {
+            const int wmax_lim = wlast + p.off;          // largest limit of the wave
+            rs.NBw = wmax_lim < 0 ? 0 : min(NB, wmax_lim / 32 + 1);
+        } else
+            rs.NBw = NB;
 
         TL ld;
         ld.kbase = p.k + ((long)b * p.Sk * p.Hkv + g) * D;
@@ -474,32 +696,32 @@ fa_prefill_kernel(const Params p)
         ld.kstride_bytes = p.Hkv * D * 2;
         ld.key_end = p.Sk;
 
-        f32x16_t o[D / 32];
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) o[db] = f32x16_t{};
-        float m_ref = kNegInf, l_run = 0.0f;
-
-        const int lim_lane = p.causal ? qi + p.off : 0x7fffffff;
-        const int wmin_lim = p.causal ? wrow0 + p.off : 0x7fffffff;   // smallest limit of the wave
-        const int wmax_lim = p.causal ? wlast + p.off : 0x7fffffff;   // largest limit of the wave
-        const bool wave_live = wrow0 < p.Sq;
-
-        if (n_tiles > 0) ld.issue(lds, lds + TB, 0, wave, lane);
-
-        // tile n lives in stage n & 1; the loop handles two tiles per trip so
-        // that every LDS offset is a compile-time constant
-        for (int n = 0; n < n_tiles; n += 2) {
-            pipeline_step<D, BN, 4>(n, n_tiles, 0, lds, lds + STAGE, ld, wave, lane,
-                                    wave_live && n * BN <= wmax_lim, p.Sk, wmin_lim, off, qf, o,
-                                    m_ref, l_run, p.c, half, lim_lane);
-            if (n + 1 < n_tiles)
-                pipeline_step<D, BN, 4>(n + 1, n_tiles, 0, lds + STAGE, lds, ld, wave, lane,
-                                        wave_live && (n + 1) * BN <= wmax_lim, p.Sk, wmin_lim,
-                                        off, qf, o, m_ref, l_run, p.c, half, lim_lane);
+        if (n_tiles > 0) {
+            ld.issue(lds, lds + TB, 0, wave, lane);
+            wait_vmem();
+            __syncthreads();
+            if (n_tiles > 1) ld.issue(lds + STAGE, lds + STAGE + TB, BN, wave, lane);
+            if (rs.NBw > 0) {
+                rs.s_cur = BO::qk(lds, off, rs.qf);
+                if (rs.needs_mask(0)) BO::mask(rs.s_cur, 0, half, rs.key_end, rs.lim_lane);
+                rs.mx_cur = BO::rowmax(rs.s_cur);
+            }
+        }
+        // tile t lives in stage t % 3; three tiles per trip keep every LDS
+        // offset a compile-time constant
+        for (int t = 0; t < n_tiles; t += 3) {
+            prefill_tile<D, BN, NW>(t, n_tiles, lds, lds + STAGE, lds + 2 * STAGE, ld, wave, lane,
+                                    off, rs);
+            if (t + 1 < n_tiles)
+                prefill_tile<D, BN, NW>(t + 1, n_tiles, lds + STAGE, lds + 2 * STAGE, lds, ld,
+                                        wave, lane, off, rs);
+            if (t + 2 < n_tiles)
+                prefill_tile<D, BN, NW>(t + 2, n_tiles, lds + 2 * STAGE, lds, lds + STAGE, ld,
+                                        wave, lane, off, rs);
         }
         __syncthreads();   // every wave is done with the LDS ring before the next item
 
-        finish_rows<D, OUT_F32>(o, m_ref, l_run, p.c, half, p.o,
+        finish_rows<D, OUT_F32>(rs.o, rs.m_ref, rs.l_run, rs.l_acc[0], p.c, half, p.o,
                                 (((long)b * p.Sq + qi) * p.Hq + hq) * D,
                                 p.lse ? p.lse + ((long)b * p.Hq + hq) * p.Sq + qi : nullptr,
                                 qi < p.Sq);
@@ -559,7 +781,7 @@ fa_decode_split_kernel(const Params p)
     f32x16_t o[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) o[db] = f32x16_t{};
-    float m_ref = kNegInf, l_run = 0.0f;
+    float m_ref = kNegInf, l_run = 0.0f, l_rnd = 0.0f;
 
     const int lim_lane = p.causal ? qi + p.off : 0x7fffffff;
     const int wmin_lim = p.causal ? p.off : 0x7fffffff;   // row 0 has the smallest limit
@@ -567,21 +789,22 @@ fa_decode_split_kernel(const Params p)
     if (n_tiles > 0) ld.issue(lds, lds + TB, k_begin, 0, lane);
     for (int n = 0; n < n_tiles; n += 2) {
         pipeline_step<D, BN, 1>(n, n_tiles, k_begin, lds, lds + STAGE, ld, 0, lane, true, k_end,
-                                wmin_lim, off, qf, o, m_ref, l_run, p.c, half, lim_lane);
+                                wmin_lim, off, qf, o, m_ref, l_run, l_rnd, p.c, half, lim_lane);
         if (n + 1 < n_tiles)
             pipeline_step<D, BN, 1>(n + 1, n_tiles, k_begin, lds + STAGE, lds, ld, 0, lane, true,
-                                    k_end, wmin_lim, off, qf, o, m_ref, l_run, p.c, half,
+                                    k_end, wmin_lim, off, qf, o, m_ref, l_run, l_rnd, p.c, half,
                                     lim_lane);
     }
 
+    const float l_norm = add_halves(l_rnd);
     if (p.num_splits == 1) {
-        finish_rows<D, OUT_F32>(o, m_ref, l_run, p.c, half, p.o,
+        finish_rows<D, OUT_F32>(o, m_ref, l_run, l_norm, p.c, half, p.o,
                                 (((long)b * p.Sq + qi) * p.Hq + hq) * D,
                                 p.lse ? p.lse + ((long)b * p.Hq + hq) * p.Sq + qi : nullptr, valid);
     } else {
         const long prow = (((long)s * p.B + b) * p.Hq + hq) * p.Sq + qi;
-        finish_rows<D, true>(o, m_ref, l_run, p.c, half, p.part_o, prow * D, p.part_lse + prow,
-                             valid);
+        finish_rows<D, true>(o, m_ref, l_run, l_norm, p.c, half, p.part_o, prow * D,
+                             p.part_lse + prow, valid);
     }
 #endif
 }
@@ -665,7 +888,7 @@ Params make_params(const Launch &L)
     const float log2e = 1.4426950408889634f;
     p.c = (L.scale < 0.0f ? -L.scale : L.scale) * log2e;
     p.qflip = L.scale < 0.0f ? 0x80008000u : 0u;
-    p.n_mblocks = (L.Sq + kPrefillBM - 1) / kPrefillBM;
+    p.n_mblocks = 0;
     p.domains = 1;
     p.num_splits = L.num_splits;
     p.split_len = L.split_len;
@@ -676,24 +899,33 @@ Params make_params(const Launch &L)
 
 using namespace kern;
 
+template <int D, int BN, int NW>
+static void launch_prefill_cfg(const Launch &L, const Params &p)
+{
+    dim3 g(L.grid), blk(NW * 64);
+    if (L.o_f32)
+        hipLaunchKernelGGL((fa_prefill_kernel<D, BN, NW, true>), g, blk, 0, L.stream, p);
+    else
+        hipLaunchKernelGGL((fa_prefill_kernel<D, BN, NW, false>), g, blk, 0, L.stream, p);
+}
+
 hipError_t launch_prefill(const Launch &L)
 {
     Params p = make_params(L);
     const int BH = L.B * L.Hq;
-    const int grid = L.grid;
+    p.n_mblocks = (L.Sq + 32 * L.prefill_nw - 1) / (32 * L.prefill_nw);
     // one XCD domain per (b, hq) residue class when both counts divide by 8
-    p.domains = (BH % 8 == 0 && grid % 8 == 0) ? 8 : 1;
-    dim3 g(grid), blk(256);
-    if (L.D == 128) {
-        if (L.o_f32)
-            hipLaunchKernelGGL((fa_prefill_kernel<128, true>), g, blk, 0, L.stream, p);
-        else
-            hipLaunchKernelGGL((fa_prefill_kernel<128, false>), g, blk, 0, L.stream, p);
-    } else {
-        if (L.o_f32)
-            hipLaunchKernelGGL((fa_prefill_kernel<64, true>), g, blk, 0, L.stream, p);
-        else
-            hipLaunchKernelGGL((fa_prefill_kernel<64, false>), g, blk, 0, L.stream, p);
+    p.domains = (BH % 8 == 0 && L.grid % 8 == 0) ? 8 : 1;
+    const int cfg = L.D * 1000 + L.prefill_bn * 10 + L.prefill_nw;
+    switch (cfg) {
+    case 128000 + 640 + 8: launch_prefill_cfg<128, 64, 8>(L, p); break;
+    case 128000 + 640 + 4: launch_prefill_cfg<128, 64, 4>(L, p); break;
+    case 128000 + 320 + 4: launch_prefill_cfg<128, 32, 4>(L, p); break;
+    case 128000 + 320 + 8: launch_prefill_cfg<128, 32, 8>(L, p); break;
+    case 64000 + 640 + 8: launch_prefill_cfg<64, 64, 8>(L, p); break;
+    case 64000 + 640 + 4: launch_prefill_cfg<64, 64, 4>(L, p); break;
+    case 64000 + 320 + 4: launch_prefill_cfg<64, 32, 4>(L, p); break;
+    default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }

@@ -7,9 +7,15 @@
 
 namespace fa {
 
-// Query rows per prefill workgroup (4 waves x 32 rows) and keys per tile.
-constexpr int kPrefillBM = 128;
-inline int prefill_block_n(int D) { return D == 64 ? 128 : 64; }
+// Prefill tile configurations: waves per workgroup (32 query rows each) and
+// keys per K/V tile; three tiles of K and V live in LDS at once.
+constexpr int kPrefillStages = 3;
+inline int prefill_lds_bytes(int D, int bn) { return kPrefillStages * 2 * bn * D * 2; }
+inline bool prefill_cfg_ok(int D, int bn, int nw)
+{
+    if (D == 128) return (bn == 64 && (nw == 4 || nw == 8)) || (bn == 32 && (nw == 4 || nw == 8));
+    return (bn == 64 && (nw == 4 || nw == 8)) || (bn == 32 && nw == 4);
+}
 // Keys per tile of the split-key decode kernel; query rows it serves per KV head.
 constexpr int kDecodeBN = 32;
 constexpr int kDecodeRows = 32;
@@ -27,6 +33,8 @@ struct Launch {
     int num_splits;      // decode path
     int split_len;       // keys per split (multiple of kDecodeBN)
     int grid;            // prefill: persistent workgroups
+    int prefill_bn;      // prefill: keys per tile
+    int prefill_nw;      // prefill: waves per workgroup
     hipStream_t stream;
 };
 

@@ -93,10 +93,13 @@ def test_workspace_size_and_plan_host_arithmetic(b):
     assert b.fa_workspace_size(4, 16, 16, 4096, 4096, 128, 0) == 0   # prefill path
     assert b.fa_workspace_size(0, 16, 16, 4096, 4096, 128, 0) == 0   # invalid sizes
     p = b.fa_plan(4, 16, 16, 4096, 4096, 128, True, 0)
-    assert p["path"] == 0 and p["block_m"] == 128 and p["block_n"] == 64
-    assert p["work_items"] == 4 * 16 * 32 and p["grid"] == min(p["work_items"], 2 * 256)
+    # 8 waves x 32 rows, 64-key tiles, 3 x 32 KiB of LDS: one workgroup per CU
+    assert p["path"] == 0 and p["block_m"] == 256 and p["block_n"] == 64
+    assert p["work_items"] == 4 * 16 * 16 and p["grid"] == 256
+    # too few 256-row items to cover the CUs: 4-wave workgroups, 32-key tiles
     p = b.fa_plan(2, 8, 8, 1024, 1024, 64, True, 0)
-    assert p["block_n"] == 128 and p["work_items"] == 2 * 8 * 8
+    assert p["block_m"] == 128 and p["block_n"] == 32 and p["work_items"] == 2 * 8 * 8
+    assert p["grid"] == 2 * 8 * 8
     p = b.fa_plan(32, 32, 8, 1, 8192, 128, False, 0)
     assert p["path"] == 1 and p["num_splits"] == 8 and p["grid"] == 32 * 8 * 8
     # splits clamp to one per 32-key tile, and forced splits are honoured

@@ -135,9 +135,10 @@ def test_lse_optional(ops, oracle):
 
 def test_split_invariance(ops):
     # Splitting the keys changes only rounding: P is rounded to bf16 relative
-    # to each split's own running max, which moves O by about
+    # to each split's own reference max, which moves O by about
     # 2^-8 * max|v| * ||w||_2 (~2e-4 for near-uniform weights over 4096 keys
-    # with |v| <= 5), while the LSE sums the unrounded weights in fp32.
+    # with |v| <= 5) and, since the row sum adds the rounded P, moves the LSE
+    # by about 2^-9 * ||w||_2 / sum(w) (~2e-5 here).
     q, k, v = random_qkv(4, 16, 4, 1, 4096, 128, seed=25)
     outs = []
     for ns in (1, 2, 4, 8, 16, 32):
@@ -145,7 +146,7 @@ def test_split_invariance(ops):
         outs.append((ns, to64(o), to64(lse)))
     for ns, o, lse in outs[1:]:
         assert np.abs(o - outs[0][1]).max() <= 1e-3, ns
-        assert np.abs(lse - outs[0][2]).max() <= 1e-5, ns
+        assert np.abs(lse - outs[0][2]).max() <= 2e-4, ns
 
 
 def test_repeat_launches_bitwise_equal(ops):
