@@ -67,6 +67,10 @@ constexpr int kBufferFlags = 0x00020000;
 // The lazy running max moves when a row max exceeds it by more than this
 // (exp2 units): P stays below 2^8.
 constexpr float kRescaleThreshold = 8.0f;
+#ifndef FA_USE_PRIO
+#define FA_USE_PRIO 1
+#endif
+constexpr bool kUsePrio = FA_USE_PRIO;
 
 struct Params {
     const uint16_t *q, *k, *v;
@@ -119,6 +123,15 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ u32x4_t ld16(const uint16_t *p)
 {
     return *reinterpret_cast<const u32x4_t *>(p);
+}
+
+// Wave issue priority (s_setprio): a wave raises it while it issues an MFMA
+// chain, so that with two waves on a SIMD the matrix pipe is fed first and the
+// other wave's VALU work fills the cycles in between.
+template <int P>
+__device__ __forceinline__ void set_prio()
+{
+    if (kUsePrio) __builtin_amdgcn_s_setprio(P);
 }
 
 // Wait until this wave's outstanding vector-memory operations (including the
@@ -424,11 +437,13 @@ struct BlockOps {
                                                   const bf16x8_t (&qf)[QS])
     {
         f32x16_t s = f32x16_t{};
+        set_prio<1>();
 #pragma unroll
         for (int st = 0; st < QS; ++st) {
             const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(Kblk + off.k[st]);
             s = mfma32(a, qf[st], s);
         }
+        set_prio<0>();
         return s;
     }
 
@@ -511,6 +526,7 @@ struct BlockOps {
     {
         const bf16x8_t ones = __builtin_bit_cast(
             bf16x8_t, (u32x4_t){0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
+        set_prio<1>();
         l_acc = mfma32(ones, p0, l_acc);
         l_acc = mfma32(ones, p1, l_acc);
 #pragma unroll
@@ -528,6 +544,7 @@ struct BlockOps {
                 o[db] = mfma32(a, t2 ? p1 : p0, o[db]);
             }
         }
+        set_prio<0>();
     }
 };
 
