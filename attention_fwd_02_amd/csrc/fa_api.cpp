@@ -111,7 +111,8 @@ struct Plan {
     int split_len = 0;
     int block_m = 0, block_n = 0;
     int grid = 0, items = 0;
-    int prefill_bn = 0, prefill_nw = 0;
+    int prefill_bn = 0, prefill_nw = 0, prefill_nr = 1;
+    int head_major = 0;
     size_t ws_bytes = 0;
 };
 
@@ -122,8 +123,8 @@ size_t split_ws_bytes(int B, int Hq, int Sq, int D, int ns)
 }
 
 // cus = 0 when unknown (pure host query): use the MI355X count
-fa_status make_plan(int B, int Hq, int Hkv, int Sq, int Sk, int D, int num_splits, int cus,
-                    Plan *out)
+fa_status make_plan(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal, int num_splits,
+                    int cus, Plan *out)
 {
     if (num_splits < 0) return fail(FA_ERR_INVALID_ARG, "num_splits must be >= 0");
     if (cus <= 0) cus = 256;
@@ -164,30 +165,39 @@ fa_status make_plan(int B, int Hq, int Hkv, int Sq, int Sk, int D, int num_split
         // tile configuration: 8 waves x 64 keys by default (two waves per
         // SIMD, K/V tiles shared by 256 query rows); 4-wave workgroups when
         // that leaves too few items to cover the CUs.  FA_PREFILL_BN /
-        // FA_PREFILL_NW override for ablations.
-        int bn = 64, nw = 8;
+        // FA_PREFILL_NW / FA_PREFILL_NR override for ablations.
+        int bn = 64, nw = 8, nr = 1;
         const int64_t m8 = (Sq + 255) / 256;
         if ((int64_t)B * Hq * m8 < cus) {
             nw = 4;
             bn = 32;
         }
         const int ebn = env_int("FA_PREFILL_BN", 0), enw = env_int("FA_PREFILL_NW", 0);
-        if (ebn > 0 && enw > 0 && fa::prefill_cfg_ok(D, ebn, enw)) {
+        const int enr = env_int("FA_PREFILL_NR", 1);
+        if (ebn > 0 && enw > 0 && fa::prefill_cfg_ok(D, ebn, enw, enr)) {
             bn = ebn;
             nw = enw;
+            nr = enr;
         }
-        const int bm = 32 * nw;
+        const int bm = 32 * nw * nr;
         pl.block_m = bm;
         pl.block_n = bn;
         pl.prefill_bn = bn;
         pl.prefill_nw = nw;
+        pl.prefill_nr = nr;
         const int64_t items = (int64_t)B * Hq * ((Sq + bm - 1) / bm);
         if (items >= (int64_t(1) << 31)) return fail(FA_ERR_UNSUPPORTED, "too many work items");
-        // workgroups a CU holds at once: LDS (160 KiB) and two waves per SIMD
-        int wg_per_cu = std::min((160 * 1024) / fa::prefill_lds_bytes(D, bn), 8 / nw);
+        // workgroups a CU holds at once: LDS (160 KiB) and the waves per SIMD
+        // the configuration's register budget allows (4 SIMDs per CU)
+        int wg_per_cu = std::min((160 * 1024) / fa::prefill_lds_bytes(D, bn),
+                                 4 * fa::prefill_waves_per_simd(nr) / nw);
         wg_per_cu = std::max(1, std::min(wg_per_cu, env_int("FA_WG_PER_CU", wg_per_cu)));
         int64_t grid = std::min<int64_t>(items, (int64_t)cus * wg_per_cu);
         if (env_int("FA_PERSISTENT", 1) == 0) grid = items;
+        // causal: head-major item order (measured faster, most for short
+        // sequences: more of an XCD's workgroups share one head's K/V at a
+        // time); non-causal: rank-major.  FA_HEAD_MAJOR overrides.
+        pl.head_major = env_int("FA_HEAD_MAJOR", causal ? 1 : 0) != 0;
         pl.items = (int)items;
         pl.grid = (int)grid;
     }
@@ -223,7 +233,7 @@ fa_status fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float 
     {
         // size-only plan check before touching the device
         Plan pre;
-        st = make_plan(B, Hq, Hkv, Sq, Sk, D, num_splits, 0, &pre);
+        st = make_plan(B, Hq, Hkv, Sq, Sk, D, causal, num_splits, 0, &pre);
         if (st != FA_OK) return st;
     }
 
@@ -233,7 +243,7 @@ fa_status fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float 
     if (st != FA_OK) return st;
 
     Plan pl;
-    st = make_plan(B, Hq, Hkv, Sq, Sk, D, num_splits, info->cus, &pl);
+    st = make_plan(B, Hq, Hkv, Sq, Sk, D, causal, num_splits, info->cus, &pl);
     if (st != FA_OK) return st;
 
     fa::Launch L;
@@ -248,15 +258,17 @@ fa_status fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float 
     L.grid = pl.grid;
     L.prefill_bn = pl.prefill_bn;
     L.prefill_nw = pl.prefill_nw;
+    L.prefill_nr = pl.prefill_nr;
+    L.head_major = pl.head_major;
     L.stream = stream;
 
     if (log_enabled())
         fprintf(stderr,
                 "[fa] path=%s B=%d Hq=%d Hkv=%d Sq=%d Sk=%d D=%d causal=%d splits=%d "
-                "split_len=%d block=%dx%d grid=%d items=%d ws=%zu\n",
+                "split_len=%d block=%dx%d waves=%d grid=%d items=%d ws=%zu\n",
                 pl.path ? "split-decode" : "prefill", B, Hq, Hkv, Sq, Sk, D, causal,
-                pl.num_splits, pl.split_len, pl.block_m, pl.block_n, pl.grid, pl.items,
-                pl.ws_bytes);
+                pl.num_splits, pl.split_len, pl.block_m, pl.block_n,
+                pl.path ? 1 : pl.prefill_nw, pl.grid, pl.items, pl.ws_bytes);
 
     hipError_t e;
     if (pl.path == 0) {
@@ -318,14 +330,14 @@ size_t fa_workspace_size(int B, int Hq, int Hkv, int Sq, int Sk, int D, int num_
             cus = g_dev[dev].cus;
     }
     Plan pl;
-    if (make_plan(B, Hq, Hkv, Sq, Sk, D, num_splits, cus, &pl) != FA_OK) return 0;
+    // the workspace depends on the split plan only, which ignores causality
+    if (make_plan(B, Hq, Hkv, Sq, Sk, D, 0, num_splits, cus, &pl) != FA_OK) return 0;
     return pl.ws_bytes;
 }
 
 fa_status fa_plan(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal, int num_splits,
                   fa_plan_info *out)
 {
-    (void)causal;
     g_last_error.clear();
     if (!out) return fail(FA_ERR_INVALID_ARG, "out must not be NULL");
     fa_status st = check_sizes(B, Hq, Hkv, Sq, Sk, D);
@@ -338,7 +350,7 @@ fa_status fa_plan(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal, int
             cus = g_dev[dev].cus;
     }
     Plan pl;
-    st = make_plan(B, Hq, Hkv, Sq, Sk, D, num_splits, cus, &pl);
+    st = make_plan(B, Hq, Hkv, Sq, Sk, D, causal, num_splits, cus, &pl);
     if (st != FA_OK) return st;
     out->path = pl.path;
     out->num_splits = pl.num_splits;

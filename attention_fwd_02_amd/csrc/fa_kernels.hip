@@ -85,6 +85,7 @@ struct Params {
     uint32_t qflip;   // 0x80008000 when scale < 0 (Q is negated exactly instead)
     int n_mblocks;    // prefill: query blocks per head
     int domains;      // prefill: XCD scheduling domains (8 or 1)
+    int head_major;   // prefill: walk a domain's items head by head (else rank by rank)
     int num_splits, split_len;
 };
 
@@ -427,6 +428,29 @@ __device__ __forceinline__ void finish_rows(const f32x16_t (&o)[D / 32], float m
 // ---------------------------------------------------------------------------
 // Per-block pieces of the pipelined prefill (a block = 32 keys).
 // ---------------------------------------------------------------------------
+typedef float f32x4_t __attribute__((__vector_size__(16)));
+
+__device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// A operand that turns a 16x16x32 MFMA into per-query row sums of P.  Fed to
+// that MFMA, the P registers of a 32x32x16 step (B operand) are read as: lane
+// group h = lane / 16 holds column lane % 16 and k-group h, so lane 16h + c
+// carries query c + 16 (h % 2) and one half of the step's 16 keys.  An A
+// operand that is one where (lane group) % 2 == (row / 4) % 2 and zero
+// elsewhere therefore makes accumulator rows 4h .. 4h+3 of column c the sum
+// over all 16 keys of query c + 16 (h % 2).  In the 16x16 accumulator layout
+// (lane 16h + c holds rows 4h .. 4h+3 of column c) that is the lane's own
+// query, the same one its 32x32 registers belong to.
+__device__ __forceinline__ bf16x8_t rowsum_selector(int lane)
+{
+    const bool on = ((lane >> 4) & 1) == ((lane >> 2) & 1);
+    const uint32_t w = on ? 0x3f803f80u : 0u;
+    return __builtin_bit_cast(bf16x8_t, (u32x4_t){w, w, w, w});
+}
+
 template <int D>
 struct BlockOps {
     static constexpr int QS = D / 16;
@@ -470,7 +494,7 @@ struct BlockOps {
     // Lazy reference max: move it (and rescale O and l) only for rows whose
     // max grew past the threshold; the first allowed key always does.
     __device__ __forceinline__ static void rebase(float mx, float &m_ref, float &l_run,
-                                                  f32x16_t &l_acc, f32x16_t (&o)[DB], float c)
+                                                  f32x4_t &l_acc, f32x16_t (&o)[DB], float c)
     {
         const bool grow = (mx - m_ref) * c > kRescaleThreshold;
         if (__any(grow)) {
@@ -515,20 +539,18 @@ struct BlockOps {
     }
 
     // O^T += V^T P^T over the block whose V rows start at Vblk (LDS).  The
-    // same P also meets an all-ones A operand: every row of l_acc then holds
-    // the running sum of the rounded P of this lane's query column -- the
-    // values P V multiplies, so O / sum is normalised consistently (with the
-    // lazy reference P reaches 2^8 and is not exact in bf16; a dominant key's
-    // rounding then divides out).
+    // same P also meets the row-sum selector: l_acc then holds the running
+    // sum of the rounded P of this lane's query -- the values P V multiplies,
+    // so O / sum is normalised consistently (with the lazy reference P
+    // reaches 2^8 and is not exact in bf16; a dominant key's rounding then
+    // divides out).
     __device__ __forceinline__ static void pv(const char *Vblk, const OperandOffsets<D> &off,
-                                              bf16x8_t p0, bf16x8_t p1, f32x16_t (&o)[DB],
-                                              f32x16_t &l_acc)
+                                              bf16x8_t sel, bf16x8_t p0, bf16x8_t p1,
+                                              f32x16_t (&o)[DB], f32x4_t &l_acc)
     {
-        const bf16x8_t ones = __builtin_bit_cast(
-            bf16x8_t, (u32x4_t){0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
         set_prio<1>();
-        l_acc = mfma32(ones, p0, l_acc);
-        l_acc = mfma32(ones, p1, l_acc);
+        l_acc = mfma16(sel, p0, l_acc);
+        l_acc = mfma16(sel, p1, l_acc);
 #pragma unroll
         for (int t2 = 0; t2 < 2; ++t2) {
 #pragma unroll
@@ -556,7 +578,8 @@ struct RowState {
     f32x16_t s_cur;      // S^T of the block to be finished next
     float mx_cur;        // its row max
     float m_ref, l_run;  // lazy reference max and exact row sum (this lane half)
-    f32x16_t l_acc;      // element 0: row sum of the rounded P (whole row)
+    f32x4_t l_acc;       // element 0: row sum of the rounded P (whole row)
+    bf16x8_t sel;        // row-sum selector operand
     int NBw;             // blocks this wave has work on (a prefix of the tile walk)
     int wmin_lim;        // smallest causal limit of the wave's rows
     int lim_lane;        // this lane's causal limit
@@ -612,7 +635,7 @@ __device__ __forceinline__ void prefill_tile(int t, int n_tiles, char *stage, ch
                 BO::template probs<true>(rs.s_cur, rs.c, mc, p0, p1, rs.l_run);
             else
                 BO::template probs<false>(rs.s_cur, rs.c, mc, p0, p1, rs.l_run);
-            BO::pv(stage + TB + kb * 32 * 2 * D, off, p0, p1, rs.o, rs.l_acc);
+            BO::pv(stage + TB + kb * 32 * 2 * D, off, rs.sel, p0, p1, rs.o, rs.l_acc);
         }
         if (live_next) {
             if (rs.needs_mask(j + 1))
@@ -664,8 +687,12 @@ fa_prefill_kernel(const Params p)
     for (int it = 0; it * Gx < Nx; ++it) {
         const int li = it * Gx + ((it & 1) ? (Gx - 1 - jw) : jw);
         if (li >= Nx) continue;
-        const int rank = li / BHx;
-        const int bh = (li % BHx) * ND + x;
+        // rank-major: all heads' longest blocks first; head-major: all
+        // blocks of one head before the next, so that more workgroups of an
+        // XCD stream the same K/V at once.  Either way the snake over it
+        // balances the causal lengths.
+        const int rank = p.head_major ? li % p.n_mblocks : li / BHx;
+        const int bh = (p.head_major ? li / p.n_mblocks : li % BHx) * ND + x;
         const int mb = p.causal ? (p.n_mblocks - 1 - rank) : rank;
         const int b = bh / p.Hq;
         const int hq = bh % p.Hq;
@@ -690,7 +717,8 @@ fa_prefill_kernel(const Params p)
         for (int db = 0; db < D / 32; ++db) rs.o[db] = f32x16_t{};
         rs.m_ref = kNegInf;
         rs.l_run = 0.0f;
-        rs.l_acc = f32x16_t{};
+        rs.l_acc = f32x4_t{};
+        rs.sel = rowsum_selector(lane);
         rs.s_cur = f32x16_t{};
         rs.mx_cur = kNegInf;
         rs.half = half;
@@ -742,6 +770,561 @@ fa_prefill_kernel(const Params p)
                                 (((long)b * p.Sq + qi) * p.Hq + hq) * D,
                                 p.lse ? p.lse + ((long)b * p.Hq + hq) * p.Sq + qi : nullptr,
                                 qi < p.Sq);
+    }
+#endif
+}
+
+// ---------------------------------------------------------------------------
+// Wide prefill: one wave per SIMD, 64 query rows per wave (column blocks
+// r = 0, 1 of 32 rows), so that each K and V operand read from LDS feeds two
+// MFMAs -- half the LDS reads per flop of the kernel above.  With one wave
+// per SIMD no other wave fills the matrix unit's shadow, so the block loop is
+// software-pipelined by hand: block j issues, step by step, the MFMAs of
+// S(j+1) = K Q^T and of O += V P(j-1), and between them the VALU work that
+// turns S(j) into P(j).  The reference max is the exact row max of the first
+// key block; after that it moves only when a block's exact P sum (which the
+// LSE needs anyway) exceeds kWideOverflow in some lane -- that block is then
+// redone against its exact row max.  P therefore stays below 2^12.
+// LDS: the three K tiles first, then the three V tiles; the V operand offsets
+// carry the distance between the two, so that the stage and block parts of
+// every LDS address are compile-time immediates.
+// ---------------------------------------------------------------------------
+constexpr float kWideOverflow = 4096.0f;
+// Operand reads of the fast block run this many steps ahead of their MFMAs;
+// each step is fenced off for the scheduler unless the fence is disabled.
+#ifndef FA_WIDE_PREFETCH
+#define FA_WIDE_PREFETCH 2
+#endif
+#ifndef FA_WIDE_STEP_FENCE
+#define FA_WIDE_STEP_FENCE 1
+#endif
+#ifndef FA_WIDE_SCHED
+#define FA_WIDE_SCHED 0
+#endif
+constexpr int kWidePrefetch = FA_WIDE_PREFETCH;
+constexpr bool kWideStepFence = FA_WIDE_STEP_FENCE;
+// 0: compiler's own order within a step; 1: an interleaving pattern per
+// step; 2: the pattern for every step, without the per-step fence
+constexpr int kWideSched = FA_WIDE_SCHED;
+
+template <int D>
+struct WideRows {
+    static constexpr int QS = D / 16;
+    static constexpr int DB = D / 32;
+    bf16x8_t qf[2][QS];
+    f32x16_t o[2][DB];
+    f32x16_t s[2];        // S^T of block j, to be turned into P(j)
+    bf16x8_t pp[2][2];    // P(j - 1), waiting for its P V
+    f32x4_t l_acc[2];     // element 0: row sum of the rounded P (whole row)
+    float m_ref[2];       // reference max (score units)
+    float mc[2];          // c * m_ref, 0 while m_ref = -inf
+    float l_run[2];       // exact row sum (this lane half)
+    int lim[2];           // causal limit of this lane's row in column block r
+    bf16x8_t sel;         // row-sum selector operand
+    int NBw;              // blocks this wave has work on (a prefix of the tile walk)
+    int wmin_lim;         // smallest causal limit of the wave's rows
+    int key_end;
+    int half;
+    float c;
+
+    __device__ __forceinline__ bool needs_mask(int j) const
+    {
+        return (j * 32 + 32 > key_end) || (j * 32 + 31 > wmin_lim);
+    }
+};
+
+template <int D>
+__device__ __forceinline__ bf16x8_t wide_ld_k(const char *Kblk, const OperandOffsets<D> &off, int st)
+{
+    return *reinterpret_cast<const bf16x8_t *>(Kblk + off.k[st]);
+}
+
+// A operand of PV step ps (16 keys x 32 head dims) of the block at Vblk.
+template <int D>
+__device__ __forceinline__ bf16x8_t wide_ld_v(const char *Vblk, const OperandOffsets<D> &off, int ps)
+{
+    constexpr int DB = D / 32;
+    const int t2 = ps / DB, db = ps % DB;
+    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4_t *)(Vblk + off.v[db][0] + t2 * 16 * 2 * D));
+    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4_t *)(Vblk + off.v[db][1] + t2 * 16 * 2 * D));
+    const u32x2_t lw = __builtin_bit_cast(u32x2_t, lo);
+    const u32x2_t hw = __builtin_bit_cast(u32x2_t, hi);
+    return __builtin_bit_cast(bf16x8_t, (u32x4_t){lw[0], lw[1], hw[0], hw[1]});
+}
+
+// S^T MFMAs of the fast block, with the accumulator in VGPRs.  The VALU
+// reads S next, and the compiler keeps every accumulator of this kernel in
+// AGPRs (moving S out would cost 32 v_accvgpr_read per block), so these two
+// are written out; Q comes straight from AGPRs.  The compiler does not see
+// the MFMA inside, so wide_block_fast waits out its result latency (s_nop)
+// before any VALU instruction can read the accumulator.
+__device__ __forceinline__ void mfma_s_first(f32x16_t &d, bf16x8_t a, bf16x8_t b)
+{
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_s_next(f32x16_t &d, bf16x8_t a, bf16x8_t b)
+{
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+}
+
+// The wait after the last S MFMA of a block, before the VALU may read S.
+__device__ __forceinline__ void mfma_s_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
+
+// Instruction order of one fast step for the scheduler: the step's LDS
+// reads first, then each MFMA followed by a share of the VALU work, so that
+// the single wave on the SIMD keeps the matrix unit fed while it computes P.
+__device__ __forceinline__ void wide_step_pattern(bool rowsum_step)
+{
+    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);   // LDS reads
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);   // VALU, transcendental included
+    }
+    if (rowsum_step) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x402, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+}
+
+// S^T of one 32-key block (K rows at Kblk) for both column blocks.
+template <int D>
+__device__ __forceinline__ void wide_qk(const char *Kblk, const OperandOffsets<D> &off,
+                                        const bf16x8_t (&qf)[2][D / 16], f32x16_t (&s)[2])
+{
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) {
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(Kblk + off.k[st]);
+        if (st == 0) {
+            mfma_s_first(s[0], a, qf[0][0]);
+            mfma_s_first(s[1], a, qf[1][0]);
+        } else {
+            mfma_s_next(s[0], a, qf[0][st]);
+            mfma_s_next(s[1], a, qf[1][st]);
+        }
+    }
+    mfma_s_drain();
+}
+
+// P of key pair q (registers 2q, 2q+1) of one column block: exp2(c*s - mc),
+// packed to bf16 into w[q / 4][q % 4]; la adds the exact values.
+template <bool MASK>
+__device__ __forceinline__ void wide_pair(const f32x16_t &s, int q, float c, float mc,
+                                          u32x4_t (&w)[2], float &la)
+{
+    float a = fast_exp2(fmaf(s[2 * q], c, -mc));
+    float b = fast_exp2(fmaf(s[2 * q + 1], c, -mc));
+    if (MASK) {
+        a = (s[2 * q] == kNegInf) ? 0.0f : a;
+        b = (s[2 * q + 1] == kNegInf) ? 0.0f : b;
+    }
+    w[q >> 2][q & 3] = pack_bf16(a, b);
+    la += a + b;
+}
+
+// Pins the computation of a VGPR value before this point (an empty volatile
+// asm that reads it), so that a software-pipelined step keeps its share of
+// the VALU work between its own MFMAs.
+__device__ __forceinline__ void keep(uint32_t a) { asm volatile("" ::"v"(a)); }
+__device__ __forceinline__ void keep(float a) { asm volatile("" ::"v"(a)); }
+
+// End of block j: where P(j) overflowed, redo it against the exact row max;
+// then P(j) becomes the pending P and S(j+1) the next S.
+template <int D, bool MASK>
+__device__ __forceinline__ void wide_settle(WideRows<D> &w, const f32x16_t (&sn)[2],
+                                            u32x4_t (&pw)[2][2], float (&la)[2])
+{
+    constexpr int DB = D / 32;
+    // !(x <= T) is also true for inf and NaN
+    const bool big = !(la[0] <= kWideOverflow) || !(la[1] <= kWideOverflow);
+    if (__any(big)) {
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            float mx = kNegInf;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, w.s[r][e]);
+            mx = max_halves(mx);
+            const float m_new = fmaxf(w.m_ref[r], mx);
+            const float alpha =
+                (w.m_ref[r] == kNegInf) ? 0.0f : fast_exp2((w.m_ref[r] - m_new) * w.c);
+            w.l_run[r] *= alpha;
+            w.l_acc[r][0] *= alpha;
+            // one accumulator at a time: O lives in AGPRs, and rescaling it
+            // all at once would need 64 VGPRs of temporaries in this loop
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) w.o[r][db][e] *= alpha;
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            w.m_ref[r] = m_new;
+            w.mc[r] = (m_new == kNegInf) ? 0.0f : m_new * w.c;
+            la[r] = 0.0f;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) wide_pair<MASK>(w.s[r], q, w.c, w.mc[r], pw[r], la[r]);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        w.l_run[r] += la[r];
+        w.pp[r][0] = __builtin_bit_cast(bf16x8_t, pw[r][0]);
+        w.pp[r][1] = __builtin_bit_cast(bf16x8_t, pw[r][1]);
+        w.s[r] = sn[r];
+    }
+}
+
+// Block j with every piece live and no mask: S(j+1) from the K block at Kn,
+// O += V P(j-1) from the V block at Vp, P(j) from S(j).  Step st issues the
+// operand reads of step st + kWidePrefetch, the two S MFMAs of k-step st and
+// the two P V MFMAs of PV step st, and between consecutive MFMAs one quarter
+// of the step's share of P(j): the exp of a key pair is split across two
+// MFMA shadows, so its latency never stalls the wave.  The order is fixed
+// with scheduling fences (the S MFMAs are inline asm, which the scheduler's
+// grouping does not recognise).
+template <int D>
+__device__ __forceinline__ void wide_block_fast(const char *Kn, const char *Vp,
+                                                const OperandOffsets<D> &off, WideRows<D> &w)
+{
+    constexpr int QS = D / 16, DB = D / 32, PPS = 8 / QS;
+    constexpr int PF = kWidePrefetch < QS ? kWidePrefetch : QS;
+    f32x16_t sn[2];
+    u32x4_t pw[2][2];
+    float la[2] = {-0.0f, -0.0f};   // -0 + x is x: the first add folds away
+    bf16x8_t kr[QS], vr[QS];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+        kr[i] = wide_ld_k<D>(Kn, off, i);
+        vr[i] = wide_ld_v<D>(Vp, off, i);
+    }
+#pragma unroll
+    for (int st = 0; st < QS; ++st) {
+        const bool pf = st + PF < QS;
+        float x1[2][PPS], y0[2][PPS];
+        // first half of a key pair: both exponents' arguments, the first exp
+        auto first = [&](int r) {
+#pragma unroll
+            for (int p = 0; p < PPS; ++p) {
+                const int q = st * PPS + p;
+                const float x0 = fmaf(w.s[r][2 * q], w.c, -w.mc[r]);
+                x1[r][p] = fmaf(w.s[r][2 * q + 1], w.c, -w.mc[r]);
+                y0[r][p] = fast_exp2(x0);
+            }
+        };
+        // second half: the second exp, the bf16 pair, the exact sum
+        auto second = [&](int r) {
+#pragma unroll
+            for (int p = 0; p < PPS; ++p) {
+                const int q = st * PPS + p;
+                const float y1 = fast_exp2(x1[r][p]);
+                pw[r][q >> 2][q & 3] = pack_bf16(y0[r][p], y1);
+                la[r] += y0[r][p] + y1;
+                keep(pw[r][q >> 2][q & 3]);
+            }
+        };
+        const int t2 = st / DB, db = st % DB;
+        if (st == 0)
+            mfma_s_first(sn[0], kr[st], w.qf[0][st]);
+        else
+            mfma_s_next(sn[0], kr[st], w.qf[0][st]);
+        __builtin_amdgcn_sched_barrier(0);
+        // the operand reads of step st + PF go into the MFMA shadows too
+        if (pf) kr[st + PF] = wide_ld_k<D>(Kn, off, st + PF);
+        first(0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (st == 0)
+            mfma_s_first(sn[1], kr[st], w.qf[1][st]);
+        else
+            mfma_s_next(sn[1], kr[st], w.qf[1][st]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (pf) vr[st + PF] = wide_ld_v<D>(Vp, off, st + PF);
+        second(0);
+        __builtin_amdgcn_sched_barrier(0);
+        w.o[0][db] = mfma32(vr[st], w.pp[0][t2], w.o[0][db]);
+        __builtin_amdgcn_sched_barrier(0);
+        first(1);
+        __builtin_amdgcn_sched_barrier(0);
+        w.o[1][db] = mfma32(vr[st], w.pp[1][t2], w.o[1][db]);
+        __builtin_amdgcn_sched_barrier(0);
+        second(1);
+        __builtin_amdgcn_sched_barrier(0);
+        if (st == QS - 2) {
+            w.l_acc[0] = mfma16(w.sel, w.pp[0][0], w.l_acc[0]);
+            w.l_acc[0] = mfma16(w.sel, w.pp[0][1], w.l_acc[0]);
+        }
+        if (st == QS - 1) {
+            w.l_acc[1] = mfma16(w.sel, w.pp[1][0], w.l_acc[1]);
+            w.l_acc[1] = mfma16(w.sel, w.pp[1][1], w.l_acc[1]);
+        }
+    }
+    // 24 wait states: the last S MFMAs have written their VGPRs before the
+    // first VALU read of sn (the 8-pass MFMA needs about half of that)
+    mfma_s_drain();
+    wide_settle<D, false>(w, sn, pw, la);
+}
+
+// Block j in general: any of S(j+1), P V(j-1), P(j) may be absent for this
+// wave, and keys past key_end or the causal limit are masked.
+template <int D>
+__device__ __forceinline__ void wide_block_general(const char *Kn, const char *Vp, int j,
+                                                   const OperandOffsets<D> &off, WideRows<D> &w)
+{
+    constexpr int QS = D / 16, DB = D / 32;
+    const bool live = j < w.NBw;
+    const bool live_next = j + 1 < w.NBw;
+    const bool live_prev = j >= 1 && j - 1 < w.NBw;
+    f32x16_t sn[2] = {f32x16_t{}, f32x16_t{}};
+    if (live_next) wide_qk<D>(Kn, off, w.qf, sn);
+    if (live_prev) {
+#pragma unroll
+        for (int ps = 0; ps < QS; ++ps) {
+            const bf16x8_t a = wide_ld_v<D>(Vp, off, ps);
+            const int t2 = ps / DB, db = ps % DB;
+            w.o[0][db] = mfma32(a, w.pp[0][t2], w.o[0][db]);
+            w.o[1][db] = mfma32(a, w.pp[1][t2], w.o[1][db]);
+        }
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            w.l_acc[r] = mfma16(w.sel, w.pp[r][0], w.l_acc[r]);
+            w.l_acc[r] = mfma16(w.sel, w.pp[r][1], w.l_acc[r]);
+        }
+    }
+    if (live) {
+        u32x4_t pw[2][2];
+        float la[2] = {0.0f, 0.0f};
+        const bool m = w.needs_mask(j);
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            if (m) BlockOps<D>::mask(w.s[r], j * 32, w.half, w.key_end, w.lim[r]);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) wide_pair<true>(w.s[r], q, w.c, w.mc[r], pw[r], la[r]);
+        }
+        wide_settle<D, true>(w, sn, pw, la);
+    } else {
+        w.s[0] = sn[0];
+        w.s[1] = sn[1];
+    }
+}
+
+// The blocks of tile t (LDS stage `stage`); `next` holds tile t + 1 and
+// `prev` tile t - 1, whose stage receives tile t + 2 once the barrier in the
+// tile's last block shows every wave is done with it.  Needs BN >= 64: the
+// P V of a tile's first block reads the last block of tile t - 1, which must
+// still be in place.
+template <int D, int BN, int NW, bool FAST>
+__device__ __forceinline__ void wide_tile(int t, int n_tiles, char *stage, char *next, char *prev,
+                                          const TileLoader<D, BN, NW> &ld, int wave, int lane,
+                                          const OperandOffsets<D> &off, WideRows<D> &w)
+{
+    constexpr int KB = BN / 32;
+    constexpr int TB = TileLoader<D, BN, NW>::TILE_BYTES;
+    static_assert(KB >= 2, "the wide prefill needs at least two key blocks per tile");
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+        const char *Kn = (kb == KB - 1) ? next : stage + (kb + 1) * 32 * 2 * D;
+        // V of the previous block; its offsets add the K-to-V distance
+        const char *Vp = (kb == 0) ? prev + (KB - 1) * 32 * 2 * D : stage + (kb - 1) * 32 * 2 * D;
+        if (kb == KB - 1 && (FAST || t + 1 < n_tiles)) {
+            wait_vmem();       // this wave's copies of tile t + 1 are in LDS
+            __syncthreads();   // ... and every wave's; tile t - 1 is released
+            if (t + 2 < n_tiles)
+                ld.issue(prev, prev + kPrefillStages * TB, (t + 2) * BN, wave, lane);
+        }
+        if (FAST)
+            wide_block_fast<D>(Kn, Vp, off, w);
+        else
+            wide_block_general<D>(Kn, Vp, t * KB + kb, off, w);
+    }
+}
+
+// A tile takes the fast body when t >= 1 (its first block has a pending
+// P V), its blocks and the block after it are live for this wave, and none
+// of its blocks needs a mask.  Liveness and masking are monotone in the block
+// index, so the fast tiles of a wave form one range [1, t_end).
+template <int KB>
+__device__ __forceinline__ bool wide_fast_ok(int t, int NBw, int key_end, int wmin_lim)
+{
+    const int jl = t * KB + KB - 1;   // the tile's last block
+    return t >= 1 && jl + 1 < NBw && jl * 32 + 32 <= key_end && jl * 32 + 31 <= wmin_lim;
+}
+
+template <int D, int BN, int NW, bool OUT_F32>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1)))
+fa_prefill_wide_kernel(const Params p)
+{
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
+    constexpr int BM = 64 * NW;
+    constexpr int KB = BN / 32;
+    constexpr int QS = D / 16;
+    using TL = TileLoader<D, BN, NW>;
+    constexpr int TB = TL::TILE_BYTES;
+    constexpr int VOFF = kPrefillStages * TB;   // V tile s sits at K tile s + VOFF
+
+    __shared__ __attribute__((aligned(1024))) char lds[2 * kPrefillStages * TB];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 31;
+    const int half = lane >> 5;
+
+    OperandOffsets<D> off;
+    off.init(lane);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int sec = 0; sec < 2; ++sec) {
+            off.v[db][sec] += VOFF;
+            // keep the bias inside the register: folded back into the
+            // immediates it would overflow their 16 bits
+            asm volatile("" : "+v"(off.v[db][sec]));
+        }
+
+    const int BH = p.B * p.Hq;
+    const int ND = p.domains;
+    const int x = blockIdx.x % ND;
+    const int jw = blockIdx.x / ND;
+    const int Gx = gridDim.x / ND;
+    const int BHx = BH / ND;
+    const int Nx = BHx * p.n_mblocks;
+
+    for (int it = 0; it * Gx < Nx; ++it) {
+        const int li = it * Gx + ((it & 1) ? (Gx - 1 - jw) : jw);
+        if (li >= Nx) continue;
+        // rank-major: all heads' longest blocks first; head-major: all
+        // blocks of one head before the next, so that more workgroups of an
+        // XCD stream the same K/V at once.  Either way the snake over it
+        // balances the causal lengths.
+        const int rank = p.head_major ? li % p.n_mblocks : li / BHx;
+        const int bh = (p.head_major ? li / p.n_mblocks : li % BHx) * ND + x;
+        const int mb = p.causal ? (p.n_mblocks - 1 - rank) : rank;
+        const int b = bh / p.Hq;
+        const int hq = bh % p.Hq;
+        const int g = hq / p.group;
+
+        const int row0 = mb * BM;
+        const int wrow0 = row0 + wave * 64;
+        const int last_row = min(row0 + BM, p.Sq) - 1;
+        const int wlast = min(wrow0 + 63, p.Sq - 1);
+
+        int n_tiles = (p.Sk + BN - 1) / BN;
+        if (p.causal) {
+            const int hi = last_row + p.off;
+            n_tiles = hi < 0 ? 0 : min(n_tiles, hi / BN + 1);
+        }
+        const int NB = n_tiles * KB;
+
+        WideRows<D> w;
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int qi = wrow0 + 32 * r + col;
+            load_q<D>(w.qf[r], p.q + (((long)b * p.Sq + qi) * p.Hq + hq) * D, qi < p.Sq, half,
+                      p.qflip);
+            // Q fragments are only ever MFMA B operands, which may sit in
+            // AGPRs: put them there, out of the way of the VALU's registers
+#pragma unroll
+            for (int st = 0; st < QS; ++st) asm volatile("" : "+a"(w.qf[r][st]));
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) w.o[r][db] = f32x16_t{};
+            w.s[r] = f32x16_t{};
+            w.l_acc[r] = f32x4_t{};
+            w.m_ref[r] = kNegInf;
+            w.mc[r] = 0.0f;
+            w.l_run[r] = 0.0f;
+            w.lim[r] = p.causal ? qi + p.off : 0x7fffffff;
+        }
+        w.sel = rowsum_selector(lane);
+        w.half = half;
+        w.c = p.c;
+        w.key_end = p.Sk;
+        w.wmin_lim = p.causal ? wrow0 + p.off : 0x7fffffff;
+        if (wrow0 >= p.Sq)
+            w.NBw = 0;
+        else if (p.causal) {
+            const int wmax_lim = wlast + p.off;
+            w.NBw = wmax_lim < 0 ? 0 : min(NB, wmax_lim / 32 + 1);
+        } else
+            w.NBw = NB;
+
+        TL ld;
+        ld.kbase = p.k + ((long)b * p.Sk * p.Hkv + g) * D;
+        ld.vbase = p.v + ((long)b * p.Sk * p.Hkv + g) * D;
+        ld.kstride_bytes = p.Hkv * D * 2;
+        ld.key_end = p.Sk;
+
+        if (n_tiles > 0) {
+            ld.issue(lds, lds + VOFF, 0, wave, lane);
+            wait_vmem();
+            __syncthreads();
+            if (n_tiles > 1) ld.issue(lds + TB, lds + TB + VOFF, BN, wave, lane);
+            if (w.NBw > 0) {
+                // S(0), and the reference max from its exact (masked) row max
+                wide_qk<D>(lds, off, w.qf, w.s);
+                const bool m = w.needs_mask(0);
+#pragma unroll
+                for (int r = 0; r < 2; ++r) {
+                    if (m) BlockOps<D>::mask(w.s[r], 0, half, w.key_end, w.lim[r]);
+                    const float mx = BlockOps<D>::rowmax(w.s[r]);
+                    w.m_ref[r] = mx;
+                    w.mc[r] = (mx == kNegInf) ? 0.0f : mx * w.c;
+                }
+            }
+        }
+        // tile t lives in stage t % 3.  Tile 0 and the tiles from the first
+        // non-fast one on take the general body (runtime stage addresses);
+        // the fast range in between runs three tiles per trip, starting at
+        // stage 1, so that every LDS offset there is a compile-time constant.
+        int t_end = 1;
+        while (t_end < n_tiles && wide_fast_ok<KB>(t_end, w.NBw, w.key_end, w.wmin_lim)) ++t_end;
+        int t = 0;
+        if (n_tiles > 0) {
+            wide_tile<D, BN, NW, false>(0, n_tiles, lds, lds + TB, lds + 2 * TB, ld, wave, lane,
+                                        off, w);
+            t = 1;
+        }
+        for (; t + 2 < t_end; t += 3) {
+            wide_tile<D, BN, NW, true>(t, n_tiles, lds + TB, lds + 2 * TB, lds, ld, wave, lane,
+                                       off, w);
+            wide_tile<D, BN, NW, true>(t + 1, n_tiles, lds + 2 * TB, lds, lds + TB, ld, wave, lane,
+                                       off, w);
+            wide_tile<D, BN, NW, true>(t + 2, n_tiles, lds, lds + TB, lds + 2 * TB, ld, wave, lane,
+                                       off, w);
+        }
+        for (; t < n_tiles; ++t) {
+            const int sc = t % kPrefillStages;
+            const int sn = sc == kPrefillStages - 1 ? 0 : sc + 1;
+            const int sp = sc == 0 ? kPrefillStages - 1 : sc - 1;
+            wide_tile<D, BN, NW, false>(t, n_tiles, lds + sc * TB, lds + sn * TB, lds + sp * TB, ld,
+                                        wave, lane, off, w);
+        }
+        // the last block's P V (its tile is still in place)
+        if (NB > 0 && w.NBw == NB) {
+            const char *Vl = lds + ((n_tiles - 1) % kPrefillStages) * TB + (KB - 1) * 32 * 2 * D;
+#pragma unroll
+            for (int ps = 0; ps < QS; ++ps) {
+                const bf16x8_t a = wide_ld_v<D>(Vl, off, ps);
+                const int t2 = ps / (D / 32), db = ps % (D / 32);
+                w.o[0][db] = mfma32(a, w.pp[0][t2], w.o[0][db]);
+                w.o[1][db] = mfma32(a, w.pp[1][t2], w.o[1][db]);
+            }
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                w.l_acc[r] = mfma16(w.sel, w.pp[r][0], w.l_acc[r]);
+                w.l_acc[r] = mfma16(w.sel, w.pp[r][1], w.l_acc[r]);
+            }
+        }
+        __syncthreads();   // every wave is done with the LDS ring before the next item
+
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int qi = wrow0 + 32 * r + col;
+            finish_rows<D, OUT_F32>(w.o[r], w.m_ref[r], w.l_run[r], w.l_acc[r][0], p.c, half, p.o,
+                                    (((long)b * p.Sq + qi) * p.Hq + hq) * D,
+                                    p.lse ? p.lse + ((long)b * p.Hq + hq) * p.Sq + qi : nullptr,
+                                    qi < p.Sq);
+        }
     }
 #endif
 }
@@ -907,6 +1490,7 @@ Params make_params(const Launch &L)
     p.qflip = L.scale < 0.0f ? 0x80008000u : 0u;
     p.n_mblocks = 0;
     p.domains = 1;
+    p.head_major = 0;
     p.num_splits = L.num_splits;
     p.split_len = L.split_len;
     return p;
@@ -916,34 +1500,63 @@ Params make_params(const Launch &L)
 
 using namespace kern;
 
-template <int D, int BN, int NW>
+template <int D, int BN, int NW, int NR>
 static void launch_prefill_cfg(const Launch &L, const Params &p)
 {
     dim3 g(L.grid), blk(NW * 64);
-    if (L.o_f32)
-        hipLaunchKernelGGL((fa_prefill_kernel<D, BN, NW, true>), g, blk, 0, L.stream, p);
-    else
-        hipLaunchKernelGGL((fa_prefill_kernel<D, BN, NW, false>), g, blk, 0, L.stream, p);
+    if constexpr (NR == 1) {
+        if (L.o_f32)
+            hipLaunchKernelGGL((fa_prefill_kernel<D, BN, NW, true>), g, blk, 0, L.stream, p);
+        else
+            hipLaunchKernelGGL((fa_prefill_kernel<D, BN, NW, false>), g, blk, 0, L.stream, p);
+    } else {
+        if (L.o_f32)
+            hipLaunchKernelGGL((fa_prefill_wide_kernel<D, BN, NW, true>), g, blk, 0, L.stream, p);
+        else
+            hipLaunchKernelGGL((fa_prefill_wide_kernel<D, BN, NW, false>), g, blk, 0, L.stream,
+                               p);
+    }
 }
+
+// The compiled prefill tile configurations: head dim, keys per tile, waves
+// per workgroup, 32-row column blocks per wave.
+struct PrefillCfg {
+    int D, bn, nw, nr;
+    void (*launch)(const Launch &, const Params &);
+};
+static const PrefillCfg kPrefillCfgs[] = {
+    {128, 64, 8, 1, launch_prefill_cfg<128, 64, 8, 1>},
+    {128, 64, 4, 1, launch_prefill_cfg<128, 64, 4, 1>},
+    {128, 32, 4, 1, launch_prefill_cfg<128, 32, 4, 1>},
+    {128, 32, 8, 1, launch_prefill_cfg<128, 32, 8, 1>},
+    {128, 64, 4, 2, launch_prefill_cfg<128, 64, 4, 2>},
+    {64, 64, 8, 1, launch_prefill_cfg<64, 64, 8, 1>},
+    {64, 64, 4, 1, launch_prefill_cfg<64, 64, 4, 1>},
+    {64, 32, 4, 1, launch_prefill_cfg<64, 32, 4, 1>},
+    {64, 64, 4, 2, launch_prefill_cfg<64, 64, 4, 2>},
+};
+
+static const PrefillCfg *find_prefill_cfg(int D, int bn, int nw, int nr)
+{
+    for (const PrefillCfg &c : kPrefillCfgs)
+        if (c.D == D && c.bn == bn && c.nw == nw && c.nr == nr) return &c;
+    return nullptr;
+}
+
+bool prefill_cfg_ok(int D, int bn, int nw, int nr) { return find_prefill_cfg(D, bn, nw, nr); }
 
 hipError_t launch_prefill(const Launch &L)
 {
+    const PrefillCfg *cfg = find_prefill_cfg(L.D, L.prefill_bn, L.prefill_nw, L.prefill_nr);
+    if (!cfg) return hipErrorInvalidValue;
     Params p = make_params(L);
     const int BH = L.B * L.Hq;
-    p.n_mblocks = (L.Sq + 32 * L.prefill_nw - 1) / (32 * L.prefill_nw);
+    const int bm = 32 * L.prefill_nw * L.prefill_nr;
+    p.n_mblocks = (L.Sq + bm - 1) / bm;
     // one XCD domain per (b, hq) residue class when both counts divide by 8
     p.domains = (BH % 8 == 0 && L.grid % 8 == 0) ? 8 : 1;
-    const int cfg = L.D * 1000 + L.prefill_bn * 10 + L.prefill_nw;
-    switch (cfg) {
-    case 128000 + 640 + 8: launch_prefill_cfg<128, 64, 8>(L, p); break;
-    case 128000 + 640 + 4: launch_prefill_cfg<128, 64, 4>(L, p); break;
-    case 128000 + 320 + 4: launch_prefill_cfg<128, 32, 4>(L, p); break;
-    case 128000 + 320 + 8: launch_prefill_cfg<128, 32, 8>(L, p); break;
-    case 64000 + 640 + 8: launch_prefill_cfg<64, 64, 8>(L, p); break;
-    case 64000 + 640 + 4: launch_prefill_cfg<64, 64, 4>(L, p); break;
-    case 64000 + 320 + 4: launch_prefill_cfg<64, 32, 4>(L, p); break;
-    default: return hipErrorInvalidValue;
-    }
+    p.head_major = L.head_major;
+    cfg->launch(L, p);
     return hipGetLastError();
 }
 

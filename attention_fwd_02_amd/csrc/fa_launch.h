@@ -7,15 +7,13 @@
 
 namespace fa {
 
-// Prefill tile configurations: waves per workgroup (32 query rows each) and
-// keys per K/V tile; three tiles of K and V live in LDS at once.
+// Prefill tile configurations: keys per K/V tile (bn), waves per workgroup
+// (nw), 32-row query column blocks per wave (nr; 1 = two waves per SIMD,
+// 2 = one wave per SIMD).  Three tiles of K and V live in LDS at once.
 constexpr int kPrefillStages = 3;
 inline int prefill_lds_bytes(int D, int bn) { return kPrefillStages * 2 * bn * D * 2; }
-inline bool prefill_cfg_ok(int D, int bn, int nw)
-{
-    if (D == 128) return (bn == 64 && (nw == 4 || nw == 8)) || (bn == 32 && (nw == 4 || nw == 8));
-    return (bn == 64 && (nw == 4 || nw == 8)) || (bn == 32 && nw == 4);
-}
+inline int prefill_waves_per_simd(int nr) { return nr == 1 ? 2 : 1; }
+bool prefill_cfg_ok(int D, int bn, int nw, int nr);   // is this configuration compiled?
 // Keys per tile of the split-key decode kernel; query rows it serves per KV head.
 constexpr int kDecodeBN = 32;
 constexpr int kDecodeRows = 32;
@@ -35,6 +33,8 @@ struct Launch {
     int grid;            // prefill: persistent workgroups
     int prefill_bn;      // prefill: keys per tile
     int prefill_nw;      // prefill: waves per workgroup
+    int prefill_nr;      // prefill: 32-row column blocks per wave
+    int head_major;      // prefill: item order (1: head by head, 0: rank by rank)
     hipStream_t stream;
 };
 

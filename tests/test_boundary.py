@@ -110,6 +110,26 @@ def test_workspace_size_and_plan_host_arithmetic(b):
     assert e.value.status == 2
 
 
+def test_plan_tile_overrides(b, monkeypatch):
+    """FA_PREFILL_BN / _NW / _NR pick a compiled tile configuration; anything
+    not compiled falls back to the planner's own choice."""
+    # 64 rows per wave (two 32-row column blocks), 4 waves: 256-row blocks
+    monkeypatch.setenv("FA_PREFILL_BN", "64")
+    monkeypatch.setenv("FA_PREFILL_NW", "4")
+    monkeypatch.setenv("FA_PREFILL_NR", "2")
+    p = b.fa_plan(1, 32, 8, 16384, 16384, 128, False, 0)
+    assert p["block_m"] == 256 and p["block_n"] == 64 and p["work_items"] == 32 * 64
+    assert p["grid"] == 256          # one wave per SIMD: one workgroup per CU
+    # the wide kernel needs two key blocks per tile: 32-key tiles are not compiled
+    monkeypatch.setenv("FA_PREFILL_BN", "32")
+    p = b.fa_plan(4, 16, 16, 4096, 4096, 128, True, 0)
+    assert p["block_m"] == 256 and p["block_n"] == 64      # the default again
+    monkeypatch.setenv("FA_PREFILL_NR", "1")
+    monkeypatch.setenv("FA_PREFILL_NW", "8")
+    p = b.fa_plan(4, 16, 16, 4096, 4096, 128, True, 0)
+    assert p["block_m"] == 256 and p["block_n"] == 32
+
+
 def test_product_path_never_touches_the_oracle():
     pkg = os.path.join(ROOT, "attention_fwd_02_amd")
     for dirpath, _, files in os.walk(pkg):

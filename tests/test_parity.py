@@ -90,6 +90,75 @@ def test_prefill_shapes_elementwise(ops, oracle, shape):
     full_check(ops, oracle, q, k, v, causal, 1.0 / math.sqrt(D), out=out, label=str(shape))
 
 
+# The other compiled prefill configurations, forced through the planner's
+# override variables: 64 rows per wave (one wave per SIMD, software-pipelined
+# block loop), 32-key tiles with 8 waves, 64-key tiles with 4 waves.
+CONFIGS = {
+    "rows64_bn64_w4": {"FA_PREFILL_BN": "64", "FA_PREFILL_NW": "4", "FA_PREFILL_NR": "2"},
+    "bn32_w8": {"FA_PREFILL_BN": "32", "FA_PREFILL_NW": "8", "FA_PREFILL_NR": "1"},
+    "bn64_w4": {"FA_PREFILL_BN": "64", "FA_PREFILL_NW": "4", "FA_PREFILL_NR": "1"},
+}
+CONFIG_SHAPES = [
+    (1, 1, 1, 128, 128, 64, True, "bf16"),
+    (2, 3, 3, 77, 77, 64, True, "bf16"),
+    (1, 2, 1, 200, 333, 128, True, "f32"),
+    (1, 2, 2, 300, 100, 64, True, "bf16"),
+    (1, 8, 2, 129, 257, 128, False, "bf16"),
+    (2, 4, 4, 513, 513, 128, True, "bf16"),
+    (1, 2, 2, 1200, 1200, 128, False, "f32"),     # tiles of the fast body
+    (1, 2, 2, 1100, 1300, 128, True, "bf16"),     # fast tiles, diagonal and tail
+    (1, 1, 1, 5, 1, 128, True, "f32"),
+]
+
+
+@pytest.fixture
+def env_vars():
+    saved = {}
+
+    def set_(vars_):
+        for k, val in vars_.items():
+            saved.setdefault(k, os.environ.get(k))
+            os.environ[k] = val
+
+    yield set_
+    for k, val in saved.items():
+        if val is None:
+            os.environ.pop(k, None)
+        else:
+            os.environ[k] = val
+
+
+@pytest.mark.parametrize("shape", CONFIG_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("cfg", list(CONFIGS))
+def test_prefill_configs_elementwise(ops, oracle, env_vars, cfg, shape):
+    B, Hq, Hkv, Sq, Sk, D, causal, out = shape
+    env_vars(CONFIGS[cfg])
+    say(f"[parity] config {cfg} shape {shape}")
+    q, k, v = random_qkv(B, Hq, Hkv, Sq, Sk, D, seed=Sq * 17 + Sk + D)
+    full_check(ops, oracle, q, k, v, causal, 1.0 / math.sqrt(D), out=out,
+               label=f"{cfg} {shape}")
+
+
+@pytest.mark.parametrize("scale", [-0.3, 2.5])
+def test_rows64_config_scales_and_overflow_redo(ops, oracle, env_vars, scale):
+    # large |scale| and hot rows make P pass the block-sum bound, which redoes
+    # the block against its exact row max
+    env_vars(CONFIGS["rows64_bn64_w4"])
+    q, k, v = random_qkv(1, 4, 2, 700, 900, 128, seed=29)
+    q[:, ::7] *= 8.0
+    full_check(ops, oracle, q, k, v, True, scale, out="f32", label=f"rows64 scale={scale}")
+
+
+def test_item_order_does_not_change_results(ops, env_vars):
+    # head-major and rank-major walks run the same per-item arithmetic
+    q, k, v = random_qkv(2, 8, 8, 1000, 1000, 128, seed=30)
+    outs = []
+    for hm in ("0", "1"):
+        env_vars({"FA_HEAD_MAJOR": hm})
+        outs.append(run_gpu(ops, q, k, v, True, 0.088))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
 DECODE_SHAPES = [
     # B, Hq, Hkv, Sq, Sk, D, causal, num_splits
     (2, 8, 2, 1, 1000, 128, False, 0),
@@ -228,6 +297,22 @@ def test_full_size_workloads_sampled(ops, oracle, name):
     say(f"[parity] {name}: {len(rows)} rows, max|dO|={eo:.2e} max|dLSE|={el:.2e}")
     assert np.isfinite(lg).all() or w.causal  # no -inf rows in these workloads
     assert not torch.isnan(o).any()
+
+
+@pytest.mark.parametrize("name", ["causal_b4_h16_s4096_d128", "gqa_b1_hq32_hkv8_s16384_d128"])
+def test_full_size_rows64_config_sampled(ops, oracle, env_vars, name):
+    # the 64-rows-per-wave kernel at full size, on sampled rows
+    env_vars(CONFIGS["rows64_bn64_w4"])
+    w = WORKLOADS[name]
+    say(f"[parity] full-size workload {name}, 64 rows per wave")
+    q, k, v = make_inputs(w)
+    o, lse = run_gpu(ops, q, k, v, w.causal, w.scale, out=w.o_dtype)
+    rows = sample_rows(w, q, 96, seed=w.seed + 1)
+    o_ref, lse_ref = oracle.attn_fwd(q, k, v, w.causal, w.scale, rows=rows)
+    og, lg = to64(o), to64(lse)
+    o_s = np.stack([og[b, i, h] for b, h, i in rows])
+    l_s = np.array([lg[b, h, i] for b, h, i in rows])
+    check(o_s, l_s, o_ref, lse_ref, w.o_dtype, name + " rows64")
 
 
 def test_compute_bound_workload_float32_output_strict(ops, oracle):
