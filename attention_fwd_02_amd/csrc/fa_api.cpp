@@ -142,9 +142,13 @@ fa_status make_plan(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal, i
         if (ns == 0) {
             ns = env_int("FA_NUM_SPLITS", 0);
             if (ns <= 0) {
-                // enough (b, g, split) waves for ~8 per CU, each split >= 4 tiles
+                // enough (b, g, split) waves to fill every CU's resident slots
+                // once (LDS ring and two waves per SIMD bound them), each
+                // split >= 4 tiles; FA_DECODE_WAVES_PER_CU overrides the slots
                 const int64_t bg = (int64_t)B * Hkv;
-                const int64_t want = ((int64_t)cus * 8 + bg - 1) / bg;
+                int per_cu = std::min(8, (160 * 1024) / fa::decode_lds_bytes(D));
+                per_cu = std::max(1, env_int("FA_DECODE_WAVES_PER_CU", per_cu));
+                const int64_t want = ((int64_t)cus * per_cu + bg - 1) / bg;
                 const int64_t by_len = std::max<int64_t>(1, Sk / (4 * fa::kDecodeBN));
                 ns = (int)std::max<int64_t>(1, std::min<int64_t>(want, by_len));
             }
@@ -162,15 +166,22 @@ fa_status make_plan(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal, i
         pl.ws_bytes = split_ws_bytes(B, Hq, Sq, D, ns);
     } else {
         pl.path = 0;
-        // tile configuration: 8 waves x 64 keys by default (two waves per
-        // SIMD, K/V tiles shared by 256 query rows); 4-wave workgroups when
-        // that leaves too few items to cover the CUs.  FA_PREFILL_BN /
-        // FA_PREFILL_NW / FA_PREFILL_NR override for ablations.
+        // tile configuration: 8 waves x 32 rows x 64 keys (two waves per
+        // SIMD, K/V tiles shared by 256 query rows), or 4 waves x 64 rows
+        // (one wave per SIMD); 4-wave, 32-key workgroups when 256-row items
+        // leave CUs idle.  FA_PREFILL_BN / FA_PREFILL_NW / FA_PREFILL_NR
+        // override (for measurements).
         int bn = 64, nw = 8, nr = 1;
         const int64_t m8 = (Sq + 255) / 256;
         if ((int64_t)B * Hq * m8 < cus) {
             nw = 4;
             bn = 32;
+        } else if (!causal || Sq >= 8192) {
+            // 64 rows per wave: faster wherever most tiles take its pipelined
+            // body (non-causal, or long causal rows); short causal rows spend
+            // too much of their time on diagonal tiles
+            nw = 4;
+            nr = 2;
         }
         const int ebn = env_int("FA_PREFILL_BN", 0), enw = env_int("FA_PREFILL_NW", 0);
         const int enr = env_int("FA_PREFILL_NR", 1);

@@ -5,7 +5,8 @@
 // forward main loop laid out in "SM80 内核实现对比" (Inference Cookbook): Q kept
 // in registers for the whole key loop (section 5.3, Q_in_regs), K/V tiles
 // staged through on-chip memory by asynchronous 16-byte copies with zero fill
-// at the edges, two stages deep (sections 2.1 and 4.1), the S = Q K^T product,
+// at the edges (sections 2.1 and 4.1; the pages' pipeline is two stages deep,
+// the rings here three), the S = Q K^T product,
 // the online softmax, then P V with P taken from registers (section 5.2), and
 // an XOR-swizzled on-chip layout (section 6.3).  The online-softmax pieces --
 // row max, exp, row sum, rescale, causal mask -- are those named in
@@ -33,13 +34,17 @@
 //    grows by more than 2^8 in exp2 units, so the O rescale is skipped on
 //    almost every tile.  P values then stay below 2^8, which bf16 and the fp32
 //    accumulators hold without loss; the result is the same function.
-//  * Prefill runs a persistent grid (two 256-thread workgroups per CU) that
-//    walks (batch, head, query block) items in a snake order, longest causal
-//    blocks first, and keeps all blocks of a head on one XCD so that their K/V
-//    re-reads hit that XCD's L2.
+//  * Prefill runs a persistent grid (one workgroup per CU) that walks
+//    (batch, head, query block) items in a snake order that balances the
+//    causal lengths, and keeps all blocks of a head on one XCD so that their
+//    K/V re-reads hit that XCD's L2.  Two kernels: 32 query rows per wave and
+//    two waves per SIMD (the default), or 64 rows per wave and one wave per
+//    SIMD with a hand-pipelined block loop (half the LDS reads per flop).
+//  * The HBM -> LDS copies are issued as inline asm so that the compiler does
+//    not make LDS reads wait for copies still in flight (see lds_dma16).
 //  * Decode (few query rows per KV head) runs a split-key kernel, one wave per
-//    (batch, KV head, key range), which writes partial (O_s, LSE_s); a merge
-//    pass combines them with log-sum-exp weights.
+//    (batch, KV head, key range) with a three-tile LDS ring, which writes
+//    partial (O_s, LSE_s); a merge pass combines them with log-sum-exp weights.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -156,6 +161,30 @@ __device__ __forceinline__ int swz(int r)
     return (r1 << 2) | ((r0 ^ r2) << 1) | (r0 ^ r3);
 }
 
+// One HBM -> LDS copy instruction: buffer_load_dwordx4 ... lds writes the 64
+// lanes' 16 bytes at consecutive LDS addresses from M0 on.  It is issued as
+// inline asm on purpose: the compiler tracks its own LDS-DMA loads and, unable
+// to prove that a later transposing LDS read does not touch the destination,
+// waits for every copy in flight (vmcnt(0)) before that read -- which would
+// expose the full HBM latency of the tiles prefetched ahead.  The kernels wait
+// for the copies themselves (wait_vmem / wait_tiles_ahead, then a barrier).
+// M0 is saved and restored around the copy (the compiler reserves it).
+__device__ __forceinline__ void lds_dma16(char *lds_dst, int voff, u32x4_t rsrc)
+{
+    const uint32_t m0v =
+        (uint32_t)reinterpret_cast<uintptr_t>((lds_void_t *)lds_dst);   // LDS byte address
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(m0v), "v"(voff), "s"(rsrc)
+        : "memory");
+}
+
 // HBM -> LDS copy of one K and one V tile of BN keys by NW waves.  One
 // buffer_load_dwordx4 ... lds instruction writes 1 KiB: 64 lanes x 16 bytes at
 // consecutive LDS addresses.  Lane l of instruction q fills tile row
@@ -176,12 +205,14 @@ struct TileLoader {
 
     // Descriptor over the rows from `row0` on: rows at or beyond key_end fall
     // outside its byte range.  Uniform values only (scalar registers).
-    __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const uint16_t *base, int row0) const
+    // Words: base address bits 31:0; bits 47:32 (stride 0); byte range; flags.
+    __device__ __forceinline__ u32x4_t rsrc(const uint16_t *base, int row0) const
     {
         const int valid = key_end - row0;
         const int nbytes = valid > 0 ? (valid - 1) * kstride_bytes + D * 2 : 0;
-        return __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(base + (long)row0 * (kstride_bytes / 2)), (short)0, nbytes, kBufferFlags);
+        const uint64_t a = reinterpret_cast<uint64_t>(base + (long)row0 * (kstride_bytes / 2));
+        return (u32x4_t){(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, (uint32_t)nbytes,
+                         (uint32_t)kBufferFlags};
     }
 
     // Issue the copies of keys [key0, key0 + BN) into the K and V tiles at
@@ -194,12 +225,8 @@ struct TileLoader {
             const int q = i * NW + wave;
             const int row = q * RPI + lane / CPR;          // tile-relative row
             const int voff = (lane / CPR) * kstride_bytes + (((lane % CPR) ^ swz<D>(row)) * 16);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(kbase, key0 + q * RPI),
-                                                     (lds_void_t *)(lds_k + q * 1024), 16, voff,
-                                                     0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(vbase, key0 + q * RPI),
-                                                     (lds_void_t *)(lds_v + q * 1024), 16, voff,
-                                                     0, 0, 0);
+            lds_dma16(lds_k + q * 1024, voff, rsrc(kbase, key0 + q * RPI));
+            lds_dma16(lds_v + q * 1024, voff, rsrc(vbase, key0 + q * RPI));
         }
     }
 };
@@ -345,23 +372,45 @@ struct WaveTile {
     }
 };
 
-// One pipeline step of a workgroup's key loop: wait for tile n (in `stage`),
-// start the copies of tile n + 1 into `next_stage`, then run this wave's share
-// of tile n.  `live` is false for a wave with nothing to do on tile n; it still
-// takes part in the barrier and the copies.
-template <int D, int BN, int NW>
-__device__ __forceinline__ void pipeline_step(
-    int n, int n_tiles, int key_base, char *stage, char *next_stage,
-    const TileLoader<D, BN, NW> &ld, int wave, int lane, bool live, int key_end, int wmin_lim,
-    const OperandOffsets<D> &off, const bf16x8_t (&qf)[D / 16], f32x16_t (&o)[D / 32],
-    float &m_ref, float &l_run, float &l_rnd, float c, int half, int lim_lane)
+// Wait until at most `ahead` tiles of copies (LPT loads each) are in flight:
+// the oldest tile has landed.  gfx9 s_waitcnt: vmcnt in bits 3:0 and 15:14,
+// expcnt 7 and lgkmcnt 15 (no wait on those).
+template <int LPT, int MAXA>
+__device__ __forceinline__ void wait_tiles_ahead(int ahead)
 {
-    constexpr int TB = TileLoader<D, BN, NW>::TILE_BYTES;
-    wait_vmem();           // this wave's copies of tile n are in LDS
-    __syncthreads();       // ... and every wave's; tile n - 1 is consumed
+#define FA_VMCNT(n) (((n) & 15) | (((n) >> 4) << 14) | 0x0F70)
+    static_assert(MAXA * LPT <= 63, "vmcnt holds at most 63");
+    if (MAXA >= 3 && ahead >= 3) __builtin_amdgcn_s_waitcnt(FA_VMCNT(3 * LPT));
+    else if (MAXA >= 2 && ahead >= 2) __builtin_amdgcn_s_waitcnt(FA_VMCNT(2 * LPT));
+    else if (MAXA >= 1 && ahead >= 1) __builtin_amdgcn_s_waitcnt(FA_VMCNT(LPT));
+    else wait_vmem();
+#undef FA_VMCNT
+}
+
+// One step of the split-key decode loop over an S-stage LDS ring: tile n sits
+// in stage `st` (= n % S); tiles n + 1 .. n + S - 2 may still be in flight;
+// the copies of tile n + S - 1 start into the stage tile n - 1 used.
+template <int D, int BN, int S>
+__device__ __forceinline__ void decode_step(
+    int n, int n_tiles, int key_base, char *lds, int st, const TileLoader<D, BN, 1> &ld,
+    int lane, int key_end, int wmin_lim, const OperandOffsets<D> &off,
+    const bf16x8_t (&qf)[D / 16], f32x16_t (&o)[D / 32], float &m_ref, float &l_run,
+    float &l_rnd, float c, int half, int lim_lane)
+{
+    constexpr int TB = TileLoader<D, BN, 1>::TILE_BYTES;
+    constexpr int STAGE = 2 * TB;
+    constexpr int LPT = 2 * TileLoader<D, BN, 1>::PER_WAVE;
+    const int ahead = min(S - 2, n_tiles - 1 - n);
+    wait_tiles_ahead<LPT, S - 2>(ahead);
+    // one wave: orders its LDS reads of tile n - 1 before the copies below
+    // overwrite that stage
+    __syncthreads();
+    if (n + S - 1 < n_tiles) {
+        char *dst = lds + ((st + S - 1) % S) * STAGE;
+        ld.issue(dst, dst + TB, key_base + (n + S - 1) * BN, 0, lane);
+    }
+    const char *stage = lds + st * STAGE;
     const int key0 = key_base + n * BN;
-    if (n + 1 < n_tiles) ld.issue(next_stage, next_stage + TB, key0 + BN, wave, lane);
-    if (!live) return;
     const bool need_mask = (key0 + BN > key_end) || (key0 + BN - 1 > wmin_lim);
     if (need_mask)
         WaveTile<D, BN>::template step<true>(stage, stage + TB, off, qf, o, m_ref, l_run, l_rnd,
@@ -1345,7 +1394,8 @@ fa_decode_split_kernel(const Params p)
     constexpr int TB = TL::TILE_BYTES;
     constexpr int STAGE = 2 * TB;
 
-    __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE];
+    constexpr int S = kDecodeStages;
+    __shared__ __attribute__((aligned(1024))) char lds[S * STAGE];
 
     const int lane = threadIdx.x;
     const int col = lane & 31;
@@ -1386,14 +1436,17 @@ fa_decode_split_kernel(const Params p)
     const int lim_lane = p.causal ? qi + p.off : 0x7fffffff;
     const int wmin_lim = p.causal ? p.off : 0x7fffffff;   // row 0 has the smallest limit
 
-    if (n_tiles > 0) ld.issue(lds, lds + TB, k_begin, 0, lane);
-    for (int n = 0; n < n_tiles; n += 2) {
-        pipeline_step<D, BN, 1>(n, n_tiles, k_begin, lds, lds + STAGE, ld, 0, lane, true, k_end,
-                                wmin_lim, off, qf, o, m_ref, l_run, l_rnd, p.c, half, lim_lane);
-        if (n + 1 < n_tiles)
-            pipeline_step<D, BN, 1>(n + 1, n_tiles, k_begin, lds + STAGE, lds, ld, 0, lane, true,
-                                    k_end, wmin_lim, off, qf, o, m_ref, l_run, l_rnd, p.c, half,
-                                    lim_lane);
+    // the first S - 1 tiles' copies go out together
+#pragma unroll
+    for (int u = 0; u < S - 1; ++u)
+        if (u < n_tiles) ld.issue(lds + u * STAGE, lds + u * STAGE + TB, k_begin + u * BN, 0, lane);
+    // S tiles per trip keep every stage offset a compile-time constant
+    for (int n = 0; n < n_tiles; n += S) {
+#pragma unroll
+        for (int u = 0; u < S; ++u)
+            if (n + u < n_tiles)
+                decode_step<D, BN, S>(n + u, n_tiles, k_begin, lds, u, ld, lane, k_end, wmin_lim,
+                                      off, qf, o, m_ref, l_run, l_rnd, p.c, half, lim_lane);
     }
 
     const float l_norm = add_halves(l_rnd);

@@ -14,9 +14,15 @@ constexpr int kPrefillStages = 3;
 inline int prefill_lds_bytes(int D, int bn) { return kPrefillStages * 2 * bn * D * 2; }
 inline int prefill_waves_per_simd(int nr) { return nr == 1 ? 2 : 1; }
 bool prefill_cfg_ok(int D, int bn, int nw, int nr);   // is this configuration compiled?
-// Keys per tile of the split-key decode kernel; query rows it serves per KV head.
+// Keys per tile of the split-key decode kernel; query rows it serves per KV
+// head; depth of its LDS ring (tiles: one being read, the rest in flight).
 constexpr int kDecodeBN = 32;
 constexpr int kDecodeRows = 32;
+#ifndef FA_DECODE_STAGES
+#define FA_DECODE_STAGES 3
+#endif
+constexpr int kDecodeStages = FA_DECODE_STAGES;
+inline int decode_lds_bytes(int D) { return kDecodeStages * 2 * kDecodeBN * D * 2; }
 
 struct Launch {
     const void *q, *k, *v;

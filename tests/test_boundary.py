@@ -86,8 +86,10 @@ def test_valid_call_without_device_reports_hip_error(b):
 
 
 def test_workspace_size_and_plan_host_arithmetic(b):
-    # decode shape: 8 splits on a 256-CU part, partials [splits][B][Hq][Sq][D+1] fp32
-    assert b.fa_workspace_size(32, 32, 8, 1, 8192, 128, 0) == 8 * 32 * 32 * 1 * 129 * 4
+    # decode shape: a 3-stage ring of 2 x 8 KiB tiles (48 KiB of LDS) leaves 3
+    # single-wave workgroups per CU, so 256 (b, g) pairs x 3 splits fill a
+    # 256-CU part once; partials [splits][B][Hq][Sq][D+1] fp32
+    assert b.fa_workspace_size(32, 32, 8, 1, 8192, 128, 0) == 3 * 32 * 32 * 1 * 129 * 4
     assert b.fa_workspace_size(32, 32, 8, 1, 8192, 128, 16) == 16 * 32 * 32 * 129 * 4
     assert b.fa_workspace_size(32, 32, 8, 1, 8192, 128, 1) == 0
     assert b.fa_workspace_size(4, 16, 16, 4096, 4096, 128, 0) == 0   # prefill path
@@ -96,12 +98,16 @@ def test_workspace_size_and_plan_host_arithmetic(b):
     # 8 waves x 32 rows, 64-key tiles, 3 x 32 KiB of LDS: one workgroup per CU
     assert p["path"] == 0 and p["block_m"] == 256 and p["block_n"] == 64
     assert p["work_items"] == 4 * 16 * 16 and p["grid"] == 256
+    # non-causal (and long causal): 4 waves x 64 rows, still 256-row blocks
+    for causal, S in ((False, 4096), (True, 16384)):
+        p = b.fa_plan(1, 32, 8, S, S, 128, causal, 0)
+        assert p["block_m"] == 256 and p["block_n"] == 64 and p["grid"] == 256
     # too few 256-row items to cover the CUs: 4-wave workgroups, 32-key tiles
     p = b.fa_plan(2, 8, 8, 1024, 1024, 64, True, 0)
     assert p["block_m"] == 128 and p["block_n"] == 32 and p["work_items"] == 2 * 8 * 8
     assert p["grid"] == 2 * 8 * 8
     p = b.fa_plan(32, 32, 8, 1, 8192, 128, False, 0)
-    assert p["path"] == 1 and p["num_splits"] == 8 and p["grid"] == 32 * 8 * 8
+    assert p["path"] == 1 and p["num_splits"] == 3 and p["grid"] == 32 * 8 * 3
     # splits clamp to one per 32-key tile, and forced splits are honoured
     assert b.fa_plan(1, 4, 1, 1, 100, 64, False, 64)["num_splits"] == 4
     assert b.fa_plan(1, 4, 1, 1, 1000, 64, False, 3)["num_splits"] == 3
