@@ -300,12 +300,13 @@ struct WaveTile {
         // ---- masking: keys >= key_end, and keys beyond the causal limit ----
         if (MASK) {
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
+            for (int kb = 0; kb < KB; ++kb) {
+                // offsets 8*(r/4) + r%4 stay immediates (see BlockOps::mask)
+                const int last = min(lim, key_end - 1) - (key0 + kb * 32 + 4 * half);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-                    if (key >= key_end || key > lim) s[kb][r] = kNegInf;
-                }
+                for (int r = 0; r < 16; ++r)
+                    if (8 * (r >> 2) + (r & 3) > last) s[kb][r] = kNegInf;
+            }
         }
 
         // ---- online softmax (row = this lane's query) with a lazy reference max ----
@@ -434,18 +435,34 @@ __device__ __forceinline__ void store4(void *o, long idx, float a, float b, floa
 }
 
 // Load this lane's Q fragment (B operand of S^T = K Q^T): head dims
-// 16*st + 8*half .. +7 of one query row, for st = 0..D/16-1.  Rows outside
-// the problem load as zero.  A negative scale is applied by negating Q here.
+// 16*st + 8*half .. +7 of one query row, for st = 0..D/16-1.  The loads go
+// straight into the fragment registers, all issued before anything waits on
+// them (callers issue their first K/V copies before this, so one memory round
+// trip covers both).  Callers pass an in-range row: rows past the problem
+// load the last real row, whose columns are never written.
 template <int D>
-__device__ __forceinline__ void load_q(bf16x8_t (&qf)[D / 16], const uint16_t *qrow, bool valid,
-                                       int half, uint32_t qflip)
+__device__ __forceinline__ void load_q(bf16x8_t (&qf)[D / 16], const uint16_t *qrow, int half)
 {
 #pragma unroll
-    for (int st = 0; st < D / 16; ++st) {
-        u32x4_t w = valid ? ld16(qrow + 16 * st + 8 * half) : u32x4_t{};
-        w ^= qflip;
-        qf[st] = __builtin_bit_cast(bf16x8_t, w);
+    for (int st = 0; st < D / 16; ++st)
+        qf[st] = __builtin_bit_cast(bf16x8_t, ld16(qrow + 16 * st + 8 * half));
+}
+
+// A negative scale is applied by negating Q exactly (sign bits), once the
+// fragment has landed.  The empty asm reads every fragment register on every
+// path: the compiler then knows the loads are complete before the key loop,
+// instead of re-waiting on them (vmcnt, which would also drain the K/V copies
+// in flight) at each S MFMA.
+template <int D>
+__device__ __forceinline__ void flip_q(bf16x8_t (&qf)[D / 16], uint32_t qflip)
+{
+    if (qflip) {
+#pragma unroll
+        for (int st = 0; st < D / 16; ++st)
+            qf[st] = __builtin_bit_cast(bf16x8_t, __builtin_bit_cast(u32x4_t, qf[st]) ^ qflip);
     }
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) asm volatile("" ::"v"(qf[st]));
 }
 
 // Epilogue of one wave's 32 query columns: O = O / l_norm, and
@@ -520,15 +537,18 @@ struct BlockOps {
         return s;
     }
 
-    // keys >= key_end, or beyond this lane's causal limit, score -inf
+    // keys >= key_end, or beyond this lane's causal limit, score -inf.
+    // Register r holds key key0 + 4*half + 8*(r/4) + r%4; comparing the
+    // constant part against one per-lane bound keeps the 16 offsets as
+    // instruction immediates (no registers to hold, or spill, them in).
     __device__ __forceinline__ static void mask(f32x16_t &s, int key0, int half, int key_end,
                                                 int lim)
     {
+        const int base = key0 + 4 * half;
+        const int last = min(lim, key_end - 1) - base;   // largest allowed offset
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int key = key0 + 8 * (r >> 2) + 4 * half + (r & 3);
-            if (key >= key_end || key > lim) s[r] = kNegInf;
-        }
+        for (int r = 0; r < 16; ++r)
+            if (8 * (r >> 2) + (r & 3) > last) s[r] = kNegInf;
     }
 
     // max over the block's keys of this lane's query (both lane halves)
@@ -760,8 +780,6 @@ fa_prefill_kernel(const Params p)
         }
 
         RowState<D> rs;
-        load_q<D>(rs.qf, p.q + (((long)b * p.Sq + qi) * p.Hq + hq) * D, qi < p.Sq, half,
-                  p.qflip);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) rs.o[db] = f32x16_t{};
         rs.m_ref = kNegInf;
@@ -790,11 +808,14 @@ fa_prefill_kernel(const Params p)
         ld.kstride_bytes = p.Hkv * D * 2;
         ld.key_end = p.Sk;
 
+        // the first two tiles' copies, then Q: one memory round trip for all
+        if (n_tiles > 0) ld.issue(lds, lds + TB, 0, wave, lane);
+        if (n_tiles > 1) ld.issue(lds + STAGE, lds + STAGE + TB, BN, wave, lane);
+        load_q<D>(rs.qf, p.q + (((long)b * p.Sq + min(qi, p.Sq - 1)) * p.Hq + hq) * D, half);
+        wait_vmem();
+        flip_q<D>(rs.qf, p.qflip);
         if (n_tiles > 0) {
-            ld.issue(lds, lds + TB, 0, wave, lane);
-            wait_vmem();
             __syncthreads();
-            if (n_tiles > 1) ld.issue(lds + STAGE, lds + STAGE + TB, BN, wave, lane);
             if (rs.NBw > 0) {
                 rs.s_cur = BO::qk(lds, off, rs.qf);
                 if (rs.needs_mask(0)) BO::mask(rs.s_cur, 0, half, rs.key_end, rs.lim_lane);
@@ -1269,12 +1290,6 @@ fa_prefill_wide_kernel(const Params p)
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
             const int qi = wrow0 + 32 * r + col;
-            load_q<D>(w.qf[r], p.q + (((long)b * p.Sq + qi) * p.Hq + hq) * D, qi < p.Sq, half,
-                      p.qflip);
-            // Q fragments are only ever MFMA B operands, which may sit in
-            // AGPRs: put them there, out of the way of the VALU's registers
-#pragma unroll
-            for (int st = 0; st < QS; ++st) asm volatile("" : "+a"(w.qf[r][st]));
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) w.o[r][db] = f32x16_t{};
             w.s[r] = f32x16_t{};
@@ -1303,11 +1318,25 @@ fa_prefill_wide_kernel(const Params p)
         ld.kstride_bytes = p.Hkv * D * 2;
         ld.key_end = p.Sk;
 
+        // the first two tiles' copies, then Q: one memory round trip for all
+        if (n_tiles > 0) ld.issue(lds, lds + VOFF, 0, wave, lane);
+        if (n_tiles > 1) ld.issue(lds + TB, lds + TB + VOFF, BN, wave, lane);
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int qi = min(wrow0 + 32 * r + col, p.Sq - 1);
+            load_q<D>(w.qf[r], p.q + (((long)b * p.Sq + qi) * p.Hq + hq) * D, half);
+        }
+        wait_vmem();
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            flip_q<D>(w.qf[r], p.qflip);
+            // Q fragments are only ever MFMA B operands, which may sit in
+            // AGPRs: put them there, out of the way of the VALU's registers
+#pragma unroll
+            for (int st = 0; st < QS; ++st) asm volatile("" : "+a"(w.qf[r][st]));
+        }
         if (n_tiles > 0) {
-            ld.issue(lds, lds + VOFF, 0, wave, lane);
-            wait_vmem();
             __syncthreads();
-            if (n_tiles > 1) ld.issue(lds + TB, lds + TB + VOFF, BN, wave, lane);
             if (w.NBw > 0) {
                 // S(0), and the reference max from its exact (masked) row max
                 wide_qk<D>(lds, off, w.qf, w.s);
@@ -1420,7 +1449,6 @@ fa_decode_split_kernel(const Params p)
     const int n_tiles = k_end > k_begin ? (k_end - k_begin + BN - 1) / BN : 0;
 
     bf16x8_t qf[D / 16];
-    load_q<D>(qf, p.q + (((long)b * p.Sq + qi) * p.Hq + hq) * D, valid, half, p.qflip);
 
     TL ld;
     ld.kbase = p.k + ((long)b * p.Sk * p.Hkv + g) * D;
@@ -1436,10 +1464,13 @@ fa_decode_split_kernel(const Params p)
     const int lim_lane = p.causal ? qi + p.off : 0x7fffffff;
     const int wmin_lim = p.causal ? p.off : 0x7fffffff;   // row 0 has the smallest limit
 
-    // the first S - 1 tiles' copies go out together
+    // the first S - 1 tiles' copies go out together, then Q (padding columns
+    // load a real row: they are never written)
 #pragma unroll
     for (int u = 0; u < S - 1; ++u)
         if (u < n_tiles) ld.issue(lds + u * STAGE, lds + u * STAGE + TB, k_begin + u * BN, 0, lane);
+    load_q<D>(qf, p.q + (((long)b * p.Sq + qi) * p.Hq + hq) * D, half);
+    flip_q<D>(qf, p.qflip);
     // S tiles per trip keep every stage offset a compile-time constant
     for (int n = 0; n < n_tiles; n += S) {
 #pragma unroll
