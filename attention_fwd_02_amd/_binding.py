@@ -35,7 +35,8 @@ class FaPlanInfo(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int), ("num_splits", ctypes.c_int),
                 ("block_m", ctypes.c_int), ("block_n", ctypes.c_int),
                 ("grid", ctypes.c_int), ("work_items", ctypes.c_int),
-                ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace_bytes", ctypes.c_size_t), ("waves", ctypes.c_int),
+                ("rows_per_wave", ctypes.c_int)]
 
 
 def _load():

@@ -1,0 +1,139 @@
+"""Static check of the generated gfx950 code around hand-written MFMAs.
+
+Some MFMAs in fa_kernels.hip are inline assembly, so that their accumulator
+can live in VGPRs.  The compiler's hazard recognizer does not look inside
+inline assembly: it inserts no wait states between such an MFMA and the
+instructions around it.  The kernels provide those waits themselves (an
+``s_nop`` drain that takes the accumulators as operands), but the register
+allocator may still copy or spill an accumulator between the MFMA and the
+drain, or write an MFMA operand right before it.  Either reads or writes a
+register the matrix unit is still working on and gives wrong results
+intermittently, with no fault.
+
+``scan`` looks at the device assembly (``hipcc --cuda-device-only -S``) and
+reports, for every inline-assembly MFMA:
+
+* any compiler-emitted instruction that reads or writes the MFMA's
+  destination registers, or a branch or label, before ``result_wait`` wait
+  states have passed (an 8-pass XDL result needs about 12 on gfx950 before a
+  VALU or memory instruction may read it; 18 covers a 16-pass one);
+* any compiler-emitted VALU instruction that writes one of the MFMA's source
+  registers fewer than ``operand_wait`` wait states before it (2 are needed).
+
+Wait states are counted conservatively: one per instruction, ``N + 1`` for
+``s_nop N``.  Other inline-assembly instructions count but are not reported
+(the MFMA chains and the drain are written to respect the rules).
+"""
+from __future__ import annotations
+
+import os
+import re
+import subprocess
+import tempfile
+
+_RANGE = re.compile(r"^([va])\[(\d+):(\d+)\]$")
+_SINGLE = re.compile(r"^([va])(\d+)$")
+
+
+def _regs(tok: str) -> set:
+    m = _RANGE.match(tok)
+    if m:
+        return {f"{m.group(1)}{i}" for i in range(int(m.group(2)), int(m.group(3)) + 1)}
+    m = _SINGLE.match(tok)
+    return {tok} if m else set()
+
+
+def _operands(text: str) -> list:
+    op = text.split()[0]
+    out = []
+    for part in text[len(op):].split(","):
+        part = part.strip().split()
+        out.append(_regs(part[0]) if part else set())
+    return out
+
+
+def _instructions(asm: str):
+    """(line number, text, inside inline asm, is control flow) per instruction."""
+    out = []
+    in_asm = False
+    for no, line in enumerate(asm.splitlines(), 1):
+        t = line.strip()
+        if t.startswith(";;#ASMSTART"):
+            in_asm = True
+            continue
+        if t.startswith(";;#ASMEND"):
+            in_asm = False
+            continue
+        if not t or t.startswith(";") or t.startswith("."):
+            continue
+        if re.match(r"^[\w.$]+:", t):
+            out.append((no, t, in_asm, True))
+            continue
+        t = t.split(";")[0].strip()
+        if not t:
+            continue
+        op = t.split()[0]
+        out.append((no, t, in_asm, op.startswith(("s_branch", "s_cbranch", "s_setpc", "s_endpgm"))))
+    return out
+
+
+def _wait_states(text: str) -> int:
+    parts = text.split()
+    if parts[0] == "s_nop":
+        return int(parts[1], 0) + 1
+    return 1
+
+
+def scan(asm: str, result_wait: int = 18, operand_wait: int = 2) -> list:
+    """Findings (one string each) for every inline-asm MFMA in ``asm``."""
+    ins = _instructions(asm)
+    findings = []
+    for k, (no, text, in_asm, _) in enumerate(ins):
+        if not (in_asm and text.startswith("v_mfma")):
+            continue
+        ops = _operands(text)
+        dst, srcs = ops[0], set().union(*ops[1:]) if len(ops) > 1 else set()
+        # after: nothing emitted by the compiler touches dst until the wait is over
+        ws, j = 0, k + 1
+        while j < len(ins) and ws < result_wait:
+            no2, t2, a2, cf = ins[j]
+            if cf:
+                findings.append(f"line {no}: {text}: control flow {ws} wait states later "
+                                f"(line {no2}: {t2})")
+                break
+            if not a2:
+                hit = set().union(*_operands(t2)) & dst
+                if hit:
+                    findings.append(f"line {no}: {text}: its result is accessed {ws} wait "
+                                    f"states later (line {no2}: {t2})")
+                    break
+            ws += _wait_states(t2)
+            j += 1
+        # before: no VALU write to an operand within operand_wait wait states
+        ws, j = 0, k - 1
+        while j >= 0 and ws < operand_wait:
+            no2, t2, a2, cf = ins[j]
+            if cf:
+                break
+            if not a2 and t2.startswith("v_"):
+                hit = _operands(t2)[0] & srcs
+                if hit:
+                    findings.append(f"line {no}: {text}: operand written {ws} wait states "
+                                    f"earlier (line {no2}: {t2})")
+                    break
+            ws += _wait_states(t2)
+            j -= 1
+    return findings
+
+
+def device_asm(hipcc: str, flags: list, include: str, source: str) -> str:
+    """The gfx950 assembly hipcc generates for ``source``."""
+    with tempfile.TemporaryDirectory() as tmp:
+        out = os.path.join(tmp, "device.s")
+        keep = [f for f in flags if f not in ("-shared", "-fPIC")]
+        cmd = [hipcc, *keep, "--cuda-device-only", "-S", "-I", include, "-o", out, source]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"hipcc -S failed ({res.returncode}):\n{res.stderr[-4000:]}")
+        with open(out) as f:
+            return f.read()

@@ -176,10 +176,10 @@ fa_status make_plan(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal, i
         if ((int64_t)B * Hq * m8 < cus) {
             nw = 4;
             bn = 32;
-        } else if (!causal || Sq >= 8192) {
+        } else if (!causal || Sq >= 2048) {
             // 64 rows per wave: faster wherever most tiles take its pipelined
-            // body (non-causal, or long causal rows); short causal rows spend
-            // too much of their time on diagonal tiles
+            // body (non-causal, or causal rows of 2048 and more); shorter
+            // causal rows spend too much of their time on diagonal tiles
             nw = 4;
             nr = 2;
         }
@@ -370,6 +370,8 @@ fa_status fa_plan(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal, int
     out->grid = pl.grid;
     out->work_items = pl.items;
     out->workspace_bytes = pl.ws_bytes;
+    out->waves = pl.path == 0 ? pl.prefill_nw : 1;
+    out->rows_per_wave = pl.path == 0 ? 32 * pl.prefill_nr : 0;
     return FA_OK;
 }
 

@@ -928,8 +928,11 @@ __device__ __forceinline__ bf16x8_t wide_ld_v(const char *Vblk, const OperandOff
 // reads S next, and the compiler keeps every accumulator of this kernel in
 // AGPRs (moving S out would cost 32 v_accvgpr_read per block), so these two
 // are written out; Q comes straight from AGPRs.  The compiler does not see
-// the MFMA inside, so wide_block_fast waits out its result latency (s_nop)
-// before any VALU instruction can read the accumulator.
+// the MFMA inside, so it would also not wait for its result: the chain of
+// one accumulator ends in mfma_s_drain, which takes the accumulators as
+// operands, so nothing the compiler emits can touch them before the wait.
+// (It could still copy or spill one between the MFMA and the drain; the
+// build scans the generated code for any such access and rejects it.)
 __device__ __forceinline__ void mfma_s_first(f32x16_t &d, bf16x8_t a, bf16x8_t b)
 {
     asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
@@ -939,8 +942,12 @@ __device__ __forceinline__ void mfma_s_next(f32x16_t &d, bf16x8_t a, bf16x8_t b)
     asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
 }
 
-// The wait after the last S MFMA of a block, before the VALU may read S.
-__device__ __forceinline__ void mfma_s_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
+// The wait after the last S MFMAs of a block (24 wait states; the 8-pass
+// MFMA needs about half of that), before anything may read or move S.
+__device__ __forceinline__ void mfma_s_drain(f32x16_t &a, f32x16_t &b)
+{
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a), "+v"(b)::"memory");
+}
 
 // Instruction order of one fast step for the scheduler: the step's LDS
 // reads first, then each MFMA followed by a share of the VALU work, so that
@@ -976,7 +983,7 @@ __device__ __forceinline__ void wide_qk(const char *Kblk, const OperandOffsets<D
             mfma_s_next(s[1], a, qf[1][st]);
         }
     }
-    mfma_s_drain();
+    mfma_s_drain(s[0], s[1]);
 }
 
 // P of key pair q (registers 2q, 2q+1) of one column block: exp2(c*s - mc),
@@ -1129,9 +1136,7 @@ __device__ __forceinline__ void wide_block_fast(const char *Kn, const char *Vp,
             w.l_acc[1] = mfma16(w.sel, w.pp[1][1], w.l_acc[1]);
         }
     }
-    // 24 wait states: the last S MFMAs have written their VGPRs before the
-    // first VALU read of sn (the 8-pass MFMA needs about half of that)
-    mfma_s_drain();
+    mfma_s_drain(sn[0], sn[1]);
     wide_settle<D, false>(w, sn, pw, la);
 }
 
@@ -1210,9 +1215,11 @@ __device__ __forceinline__ void wide_tile(int t, int n_tiles, char *stage, char 
 }
 
 // A tile takes the fast body when t >= 1 (its first block has a pending
-// P V), its blocks and the block after it are live for this wave, and none
-// of its blocks needs a mask.  Liveness and masking are monotone in the block
-// index, so the fast tiles of a wave form one range [1, t_end).
+// P V), its blocks and the block after it are live for this wave and none of
+// its blocks needs a mask.  Liveness and masking are monotone in the block
+// index, so the fast tiles of a wave form one range [1, t_end).  (The block
+// after it being live implies t + 1 < n_tiles: the fast body always takes
+// the tile-boundary barrier.)
 template <int KB>
 __device__ __forceinline__ bool wide_fast_ok(int t, int NBw, int key_end, int wmin_lim)
 {
@@ -1350,10 +1357,10 @@ fa_prefill_wide_kernel(const Params p)
                 }
             }
         }
-        // tile t lives in stage t % 3.  Tile 0 and the tiles from the first
-        // non-fast one on take the general body (runtime stage addresses);
-        // the fast range in between runs three tiles per trip, starting at
-        // stage 1, so that every LDS offset there is a compile-time constant.
+        // tile t lives in stage t % 3.  Tile 0 takes the general body; the
+        // fast tiles [1, t_end) run with compile-time stage addresses, three
+        // per trip from stage 1, then the one or two left (stages 1 and 2);
+        // the tiles from t_end on take the general body (runtime stages).
         int t_end = 1;
         while (t_end < n_tiles && wide_fast_ok<KB>(t_end, w.NBw, w.key_end, w.wmin_lim)) ++t_end;
         int t = 0;
@@ -1369,6 +1376,17 @@ fa_prefill_wide_kernel(const Params p)
                                        off, w);
             wide_tile<D, BN, NW, true>(t + 2, n_tiles, lds, lds + TB, lds + 2 * TB, ld, wave, lane,
                                        off, w);
+        }
+        // here t % 3 == 1: at most two fast tiles remain, in stages 1 and 2
+        if (t < t_end) {
+            wide_tile<D, BN, NW, true>(t, n_tiles, lds + TB, lds + 2 * TB, lds, ld, wave, lane,
+                                       off, w);
+            ++t;
+        }
+        if (t < t_end) {
+            wide_tile<D, BN, NW, true>(t, n_tiles, lds + 2 * TB, lds, lds + TB, ld, wave, lane,
+                                       off, w);
+            ++t;
         }
         for (; t < n_tiles; ++t) {
             const int sc = t % kPrefillStages;

@@ -123,6 +123,10 @@ typedef struct {
     int grid;            /* workgroups of the main kernel                          */
     int work_items;      /* tiles of work the grid walks                           */
     size_t workspace_bytes;
+    int waves;           /* waves per workgroup of the main kernel                 */
+    int rows_per_wave;   /* prefill: query rows per wave (32, or 64 for the kernel
+                            that holds two 32-row column blocks per wave); 0 for
+                            the split-key path                                    */
 } fa_plan_info;
 
 fa_status fa_plan(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal, int num_splits,

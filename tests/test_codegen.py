@@ -1,0 +1,82 @@
+"""The generated gfx950 code respects the wait states around the kernels'
+inline-assembly MFMAs (asm_check.py), and the scanner itself catches each
+kind of violation on small hand-written listings."""
+from __future__ import annotations
+
+import os
+import shutil
+
+import pytest
+
+from attention_fwd_02_amd import asm_check, build
+
+MFMA = "v_mfma_f32_32x32x16_bf16 v[32:47], v[0:3], a[0:3], v[32:47]"
+
+
+def listing(*lines, asm_idx=()):
+    """Assembly text; the lines at asm_idx are wrapped as inline assembly."""
+    out = []
+    for i, l in enumerate(lines):
+        if i in asm_idx:
+            out += [";;#ASMSTART", "\t" + l, ";;#ASMEND"]
+        else:
+            out.append("\t" + l)
+    return "\n".join(out)
+
+
+def test_drained_chain_passes():
+    asm = listing(MFMA, "v_exp_f32_e32 v8, v9", MFMA, "s_nop 7\n\ts_nop 7\n\ts_nop 7",
+                  "v_fma_f32 v8, v32, s4, -v9", asm_idx=(0, 2, 3))
+    assert asm_check.scan(asm) == []
+
+
+def test_copy_of_result_before_wait_is_found():
+    asm = listing(MFMA, "v_accvgpr_write_b32 a235, v47", "s_nop 7\n\ts_nop 7\n\ts_nop 7",
+                  asm_idx=(0, 2))
+    found = asm_check.scan(asm)
+    assert len(found) == 1 and "accessed 0 wait states later" in found[0]
+
+
+def test_spill_of_result_is_found():
+    asm = listing(MFMA, "v_exp_f32_e32 v8, v9", "scratch_store_dwordx4 off, v[44:47], off",
+                  asm_idx=(0,))
+    assert "accessed 1 wait states later" in asm_check.scan(asm)[0]
+
+
+def test_write_of_accumulator_in_flight_is_found():
+    asm = listing(MFMA, "v_mov_b32_e32 v40, 0", asm_idx=(0,))
+    assert asm_check.scan(asm)
+
+
+def test_access_after_the_wait_passes():
+    asm = listing(MFMA, "s_nop 7\n\ts_nop 7\n\ts_nop 1", "v_mov_b32_e32 v0, v40", asm_idx=(0,))
+    assert asm_check.scan(asm) == []
+
+
+def test_branch_before_wait_is_found():
+    asm = listing(MFMA, "s_cbranch_scc1 .LBB0_3", asm_idx=(0,))
+    assert "control flow" in asm_check.scan(asm)[0]
+
+
+def test_operand_written_just_before_is_found():
+    asm = listing("v_accvgpr_write_b32 a2, v7", MFMA, "s_nop 7\n\ts_nop 7\n\ts_nop 7",
+                  asm_idx=(1, 2))
+    assert "operand written 0 wait states earlier" in asm_check.scan(asm)[0]
+    asm = listing("v_mov_b32_e32 v1, v7", "s_nop 1", MFMA, "s_nop 7\n\ts_nop 7\n\ts_nop 7",
+                  asm_idx=(2, 3))
+    assert asm_check.scan(asm) == []
+
+
+def test_compiler_emitted_mfma_is_not_checked():
+    asm = listing(MFMA, "v_mov_b32_e32 v40, 0")
+    assert asm_check.scan(asm) == []
+
+
+@pytest.mark.skipif(not shutil.which(build.HIPCC) and not os.path.exists(build.HIPCC),
+                    reason="hipcc not available")
+def test_kernels_have_no_inline_mfma_hazards():
+    asm = asm_check.device_asm(build.HIPCC, build.FLAGS, build.INCLUDE,
+                               os.path.join(build.CSRC, "fa_kernels.hip"))
+    n = sum(1 for i in asm_check._instructions(asm) if i[2] and i[1].startswith("v_mfma"))
+    assert n > 0, "no inline-asm MFMA found: the scan would be vacuous"
+    assert asm_check.scan(asm) == []
