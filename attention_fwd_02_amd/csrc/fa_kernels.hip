@@ -967,14 +967,20 @@ __device__ __forceinline__ void wide_step_pattern(bool rowsum_step)
     }
 }
 
-// S^T of one 32-key block (K rows at Kblk) for both column blocks.
+// S^T of one 32-key block (K rows at Kblk) for both column blocks.  All K
+// fragments are read first: the MFMAs are volatile asm, which the compiler
+// does not move loads across, so a read inside the loop would cost one LDS
+// round trip per k-step.
 template <int D>
 __device__ __forceinline__ void wide_qk(const char *Kblk, const OperandOffsets<D> &off,
                                         const bf16x8_t (&qf)[2][D / 16], f32x16_t (&s)[2])
 {
+    bf16x8_t ka[D / 16];
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) ka[st] = wide_ld_k<D>(Kblk, off, st);
 #pragma unroll
     for (int st = 0; st < D / 16; ++st) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(Kblk + off.k[st]);
+        const bf16x8_t a = ka[st];
         if (st == 0) {
             mfma_s_first(s[0], a, qf[0][0]);
             mfma_s_first(s[1], a, qf[1][0]);
@@ -1227,6 +1233,73 @@ __device__ __forceinline__ bool wide_fast_ok(int t, int NBw, int key_end, int wm
     return t >= 1 && jl + 1 < NBw && jl * 32 + 32 <= key_end && jl * 32 + 31 <= wmin_lim;
 }
 
+// One work item of the 64-row kernel: 256 query rows of one (b, hq).
+struct WideItem {
+    int b, hq, g;
+    int wrow0;     // this wave's first query row
+    int n_tiles;   // key tiles the workgroup walks
+    int NBw;       // key blocks this wave has work on (a prefix of the walk)
+};
+
+// Item `it` of this workgroup, if it has one.  The snake over `it` balances
+// the causal lengths; rank-major walks all heads' longest blocks first,
+// head-major all blocks of one head before the next (more workgroups of an
+// XCD then stream the same K/V at once).  Items past the end only occur on
+// the last trip, so the valid items of a workgroup are a prefix of `it`.
+__device__ __forceinline__ bool wide_item(const Params &p, int it, int Gx, int jw, int x, int Nx,
+                                          int BHx, int ND, int BM, int BN, int wave, WideItem &I)
+{
+    if (it * Gx >= Nx) return false;
+    const int li = it * Gx + ((it & 1) ? (Gx - 1 - jw) : jw);
+    if (li >= Nx) return false;
+    const int rank = p.head_major ? li % p.n_mblocks : li / BHx;
+    const int bh = (p.head_major ? li / p.n_mblocks : li % BHx) * ND + x;
+    const int mb = p.causal ? (p.n_mblocks - 1 - rank) : rank;
+    I.b = bh / p.Hq;
+    I.hq = bh % p.Hq;
+    I.g = I.hq / p.group;
+    const int row0 = mb * BM;
+    I.wrow0 = row0 + wave * 64;
+    const int last_row = min(row0 + BM, p.Sq) - 1;
+    const int wlast = min(I.wrow0 + 63, p.Sq - 1);
+    int n_tiles = (p.Sk + BN - 1) / BN;
+    if (p.causal) {
+        const int hi = last_row + p.off;
+        n_tiles = hi < 0 ? 0 : min(n_tiles, hi / BN + 1);
+    }
+    I.n_tiles = n_tiles;
+    const int NB = n_tiles * (BN / 32);
+    if (I.wrow0 >= p.Sq)
+        I.NBw = 0;
+    else if (p.causal) {
+        const int wmax_lim = wlast + p.off;
+        I.NBw = wmax_lim < 0 ? 0 : min(NB, wmax_lim / 32 + 1);
+    } else
+        I.NBw = NB;
+    return true;
+}
+
+// The item's first two tiles' copies, then its Q loads (raw, into qf):
+// one memory round trip for all, waited for at the item's start.
+template <int D, int BN, int NW>
+__device__ __forceinline__ void wide_item_issue(const Params &p, const WideItem &I,
+                                                TileLoader<D, BN, NW> &ld, char *lds, int VOFF,
+                                                int TB, int wave, int lane, int half, int col,
+                                                bf16x8_t (&qf)[2][D / 16])
+{
+    ld.kbase = p.k + ((long)I.b * p.Sk * p.Hkv + I.g) * D;
+    ld.vbase = p.v + ((long)I.b * p.Sk * p.Hkv + I.g) * D;
+    ld.kstride_bytes = p.Hkv * D * 2;
+    ld.key_end = p.Sk;
+    if (I.n_tiles > 0) ld.issue(lds, lds + VOFF, 0, wave, lane);
+    if (I.n_tiles > 1) ld.issue(lds + TB, lds + TB + VOFF, BN, wave, lane);
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int qi = min(I.wrow0 + 32 * r + col, p.Sq - 1);
+        load_q<D>(qf[r], p.q + (((long)I.b * p.Sq + qi) * p.Hq + I.hq) * D, half);
+    }
+}
+
 template <int D, int BN, int NW, bool OUT_F32>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1)))
 fa_prefill_wide_kernel(const Params p)
@@ -1267,33 +1340,21 @@ fa_prefill_wide_kernel(const Params p)
     const int BHx = BH / ND;
     const int Nx = BHx * p.n_mblocks;
 
-    for (int it = 0; it * Gx < Nx; ++it) {
-        const int li = it * Gx + ((it & 1) ? (Gx - 1 - jw) : jw);
-        if (li >= Nx) continue;
-        // rank-major: all heads' longest blocks first; head-major: all
-        // blocks of one head before the next, so that more workgroups of an
-        // XCD stream the same K/V at once.  Either way the snake over it
-        // balances the causal lengths.
-        const int rank = p.head_major ? li % p.n_mblocks : li / BHx;
-        const int bh = (p.head_major ? li / p.n_mblocks : li % BHx) * ND + x;
-        const int mb = p.causal ? (p.n_mblocks - 1 - rank) : rank;
-        const int b = bh / p.Hq;
-        const int hq = bh % p.Hq;
-        const int g = hq / p.group;
+    // Items are software-pipelined: the next item's first two K/V tiles and
+    // its Q are requested as soon as the LDS ring is free, before this
+    // item's epilogue, so their memory latency overlaps the O/LSE stores.
+    WideItem cur, nxt;
+    bool have = wide_item(p, 0, Gx, jw, x, Nx, BHx, ND, BM, BN, wave, cur);
+    TL ld;
+    WideRows<D> w;
+    if (have) wide_item_issue<D, BN, NW>(p, cur, ld, lds, VOFF, TB, wave, lane, half, col, w.qf);
 
-        const int row0 = mb * BM;
-        const int wrow0 = row0 + wave * 64;
-        const int last_row = min(row0 + BM, p.Sq) - 1;
-        const int wlast = min(wrow0 + 63, p.Sq - 1);
-
-        int n_tiles = (p.Sk + BN - 1) / BN;
-        if (p.causal) {
-            const int hi = last_row + p.off;
-            n_tiles = hi < 0 ? 0 : min(n_tiles, hi / BN + 1);
-        }
+    for (int it = 0; have; ++it) {
+        const int b = cur.b, hq = cur.hq;
+        const int wrow0 = cur.wrow0;
+        const int n_tiles = cur.n_tiles;
         const int NB = n_tiles * KB;
 
-        WideRows<D> w;
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
             const int qi = wrow0 + 32 * r + col;
@@ -1311,28 +1372,10 @@ fa_prefill_wide_kernel(const Params p)
         w.c = p.c;
         w.key_end = p.Sk;
         w.wmin_lim = p.causal ? wrow0 + p.off : 0x7fffffff;
-        if (wrow0 >= p.Sq)
-            w.NBw = 0;
-        else if (p.causal) {
-            const int wmax_lim = wlast + p.off;
-            w.NBw = wmax_lim < 0 ? 0 : min(NB, wmax_lim / 32 + 1);
-        } else
-            w.NBw = NB;
+        w.NBw = cur.NBw;
 
-        TL ld;
-        ld.kbase = p.k + ((long)b * p.Sk * p.Hkv + g) * D;
-        ld.vbase = p.v + ((long)b * p.Sk * p.Hkv + g) * D;
-        ld.kstride_bytes = p.Hkv * D * 2;
-        ld.key_end = p.Sk;
-
-        // the first two tiles' copies, then Q: one memory round trip for all
-        if (n_tiles > 0) ld.issue(lds, lds + VOFF, 0, wave, lane);
-        if (n_tiles > 1) ld.issue(lds + TB, lds + TB + VOFF, BN, wave, lane);
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            const int qi = min(wrow0 + 32 * r + col, p.Sq - 1);
-            load_q<D>(w.qf[r], p.q + (((long)b * p.Sq + qi) * p.Hq + hq) * D, half);
-        }
+        // the item's copies and Q loads were issued before the previous
+        // item's epilogue (or just above, for the first item)
         wait_vmem();
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
@@ -1411,7 +1454,11 @@ fa_prefill_wide_kernel(const Params p)
                 w.l_acc[r] = mfma16(w.sel, w.pp[r][1], w.l_acc[r]);
             }
         }
-        __syncthreads();   // every wave is done with the LDS ring before the next item
+        __syncthreads();   // every wave is done with the LDS ring
+
+        // the next item's first copies and Q loads, then this item's epilogue
+        have = wide_item(p, it + 1, Gx, jw, x, Nx, BHx, ND, BM, BN, wave, nxt);
+        if (have) wide_item_issue<D, BN, NW>(p, nxt, ld, lds, VOFF, TB, wave, lane, half, col, w.qf);
 
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
@@ -1421,6 +1468,7 @@ fa_prefill_wide_kernel(const Params p)
                                     p.lse ? p.lse + ((long)b * p.Hq + hq) * p.Sq + qi : nullptr,
                                     qi < p.Sq);
         }
+        cur = nxt;
     }
 #endif
 }

@@ -18,6 +18,10 @@ against HBM.  `cpu_baseline` times the fp64 oracle on a bounded sample of the
 prefill workload's rows and also compares those rows with the timed output.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+
+The default warm-up is 100 steps (about 50 ms of GPU work): from idle the
+shader clock takes about 30 ms of load to reach its steady level, and steps
+timed before that run up to 30 % slower.
 """
 from __future__ import annotations
 
@@ -145,7 +149,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--cpu-seconds", type=float, default=25.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-kernel", choices=["prefill", "decode", "copy"],
