@@ -860,22 +860,8 @@ fa_prefill_kernel(const Params p)
 // every LDS address are compile-time immediates.
 // ---------------------------------------------------------------------------
 constexpr float kWideOverflow = 4096.0f;
-// Operand reads of the fast block run this many steps ahead of their MFMAs;
-// each step is fenced off for the scheduler unless the fence is disabled.
-#ifndef FA_WIDE_PREFETCH
-#define FA_WIDE_PREFETCH 2
-#endif
-#ifndef FA_WIDE_STEP_FENCE
-#define FA_WIDE_STEP_FENCE 1
-#endif
-#ifndef FA_WIDE_SCHED
-#define FA_WIDE_SCHED 0
-#endif
-constexpr int kWidePrefetch = FA_WIDE_PREFETCH;
-constexpr bool kWideStepFence = FA_WIDE_STEP_FENCE;
-// 0: compiler's own order within a step; 1: an interleaving pattern per
-// step; 2: the pattern for every step, without the per-step fence
-constexpr int kWideSched = FA_WIDE_SCHED;
+// Operand reads of the fast block run this many steps ahead of their MFMAs.
+constexpr int kWidePrefetch = 2;
 
 template <int D>
 struct WideRows {
@@ -947,24 +933,6 @@ __device__ __forceinline__ void mfma_s_next(f32x16_t &d, bf16x8_t a, bf16x8_t b)
 __device__ __forceinline__ void mfma_s_drain(f32x16_t &a, f32x16_t &b)
 {
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a), "+v"(b)::"memory");
-}
-
-// Instruction order of one fast step for the scheduler: the step's LDS
-// reads first, then each MFMA followed by a share of the VALU work, so that
-// the single wave on the SIMD keeps the matrix unit fed while it computes P.
-__device__ __forceinline__ void wide_step_pattern(bool rowsum_step)
-{
-    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);   // LDS reads
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);   // VALU, transcendental included
-    }
-    if (rowsum_step) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x402, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    }
 }
 
 // S^T of one 32-key block (K rows at Kblk) for both column blocks.  All K
@@ -1063,10 +1031,11 @@ __device__ __forceinline__ void wide_settle(WideRows<D> &w, const f32x16_t (&sn)
 // O += V P(j-1) from the V block at Vp, P(j) from S(j).  Step st issues the
 // operand reads of step st + kWidePrefetch, the two S MFMAs of k-step st and
 // the two P V MFMAs of PV step st, and between consecutive MFMAs one quarter
-// of the step's share of P(j): the exp of a key pair is split across two
-// MFMA shadows, so its latency never stalls the wave.  The order is fixed
-// with scheduling fences (the S MFMAs are inline asm, which the scheduler's
-// grouping does not recognise).
+// of the step's share of P(j), placed so that no value is consumed in the
+// MFMA shadow that produces it (one wave per SIMD: a dependent instruction
+// right behind a transcendental would stall the wave, and the next MFMA with
+// it).  The order is fixed with scheduling fences (the S MFMAs are inline
+// asm, which the scheduler's grouping does not recognise).
 template <int D>
 __device__ __forceinline__ void wide_block_fast(const char *Kn, const char *Vp,
                                                 const OperandOffsets<D> &off, WideRows<D> &w)
@@ -1077,45 +1046,43 @@ __device__ __forceinline__ void wide_block_fast(const char *Kn, const char *Vp,
     u32x4_t pw[2][2];
     float la[2] = {-0.0f, -0.0f};   // -0 + x is x: the first add folds away
     bf16x8_t kr[QS], vr[QS];
+    // in the order the steps consume them, so that the first MFMA waits for
+    // one LDS read only (LDS reads complete in order)
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
         kr[i] = wide_ld_k<D>(Kn, off, i);
+        __builtin_amdgcn_sched_barrier(0);
         vr[i] = wide_ld_v<D>(Vp, off, i);
+        __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int st = 0; st < QS; ++st) {
         const bool pf = st + PF < QS;
-        float x1[2][PPS], y0[2][PPS];
-        // first half of a key pair: both exponents' arguments, the first exp
-        auto first = [&](int r) {
-#pragma unroll
-            for (int p = 0; p < PPS; ++p) {
-                const int q = st * PPS + p;
-                const float x0 = fmaf(w.s[r][2 * q], w.c, -w.mc[r]);
-                x1[r][p] = fmaf(w.s[r][2 * q + 1], w.c, -w.mc[r]);
-                y0[r][p] = fast_exp2(x0);
-            }
-        };
-        // second half: the second exp, the bf16 pair, the exact sum
-        auto second = [&](int r) {
-#pragma unroll
-            for (int p = 0; p < PPS; ++p) {
-                const int q = st * PPS + p;
-                const float y1 = fast_exp2(x1[r][p]);
-                pw[r][q >> 2][q & 3] = pack_bf16(y0[r][p], y1);
-                la[r] += y0[r][p] + y1;
-                keep(pw[r][q >> 2][q & 3]);
-            }
-        };
         const int t2 = st / DB, db = st % DB;
+        // the step's VALU work, spread over the four MFMA shadows so that no
+        // result is read in the shadow it is produced in: both column blocks'
+        // exponent arguments; the exps, r = 0 first; then per column block
+        // the bf16 pairs and the exact sums
+        float xa[2][PPS][2], ya[2][PPS][2];
         if (st == 0)
             mfma_s_first(sn[0], kr[st], w.qf[0][st]);
         else
             mfma_s_next(sn[0], kr[st], w.qf[0][st]);
         __builtin_amdgcn_sched_barrier(0);
-        // the operand reads of step st + PF go into the MFMA shadows too
         if (pf) kr[st + PF] = wide_ld_k<D>(Kn, off, st + PF);
-        first(0);
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int p = 0; p < PPS; ++p) {
+                const int q = st * PPS + p;
+                xa[r][p][0] = fmaf(w.s[r][2 * q], w.c, -w.mc[r]);
+                xa[r][p][1] = fmaf(w.s[r][2 * q + 1], w.c, -w.mc[r]);
+            }
+#pragma unroll
+        for (int p = 0; p < PPS; ++p) {
+            ya[0][p][0] = fast_exp2(xa[0][p][0]);
+            keep(ya[0][p][0]);
+        }
         __builtin_amdgcn_sched_barrier(0);
         if (st == 0)
             mfma_s_first(sn[1], kr[st], w.qf[1][st]);
@@ -1123,15 +1090,35 @@ __device__ __forceinline__ void wide_block_fast(const char *Kn, const char *Vp,
             mfma_s_next(sn[1], kr[st], w.qf[1][st]);
         __builtin_amdgcn_sched_barrier(0);
         if (pf) vr[st + PF] = wide_ld_v<D>(Vp, off, st + PF);
-        second(0);
+#pragma unroll
+        for (int p = 0; p < PPS; ++p) {
+            ya[0][p][1] = fast_exp2(xa[0][p][1]);
+            ya[1][p][0] = fast_exp2(xa[1][p][0]);
+            keep(ya[0][p][1]);
+            keep(ya[1][p][0]);
+        }
         __builtin_amdgcn_sched_barrier(0);
         w.o[0][db] = mfma32(vr[st], w.pp[0][t2], w.o[0][db]);
         __builtin_amdgcn_sched_barrier(0);
-        first(1);
+#pragma unroll
+        for (int p = 0; p < PPS; ++p) {
+            const int q = st * PPS + p;
+            ya[1][p][1] = fast_exp2(xa[1][p][1]);
+            keep(ya[1][p][1]);
+            pw[0][q >> 2][q & 3] = pack_bf16(ya[0][p][0], ya[0][p][1]);
+            la[0] += ya[0][p][0] + ya[0][p][1];
+            keep(pw[0][q >> 2][q & 3]);
+        }
         __builtin_amdgcn_sched_barrier(0);
         w.o[1][db] = mfma32(vr[st], w.pp[1][t2], w.o[1][db]);
         __builtin_amdgcn_sched_barrier(0);
-        second(1);
+#pragma unroll
+        for (int p = 0; p < PPS; ++p) {
+            const int q = st * PPS + p;
+            pw[1][q >> 2][q & 3] = pack_bf16(ya[1][p][0], ya[1][p][1]);
+            la[1] += ya[1][p][0] + ya[1][p][1];
+            keep(pw[1][q >> 2][q & 3]);
+        }
         __builtin_amdgcn_sched_barrier(0);
         if (st == QS - 2) {
             w.l_acc[0] = mfma16(w.sel, w.pp[0][0], w.l_acc[0]);
