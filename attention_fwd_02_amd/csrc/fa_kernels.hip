@@ -169,20 +169,36 @@ __device__ __forceinline__ int swz(int r)
 // expose the full HBM latency of the tiles prefetched ahead.  The kernels wait
 // for the copies themselves (wait_vmem / wait_tiles_ahead, then a barrier).
 // M0 is saved and restored around the copy (the compiler reserves it).
+// STREAM marks the copy non-temporal: data read once (the decode's K/V)
+// then does not displace cache lines that are still needed, such as output
+// another kernel left dirty, whose write-back would otherwise be charged to
+// the streaming read.
+template <bool STREAM = false>
 __device__ __forceinline__ void lds_dma16(char *lds_dst, int voff, u32x4_t rsrc)
 {
     const uint32_t m0v =
         (uint32_t)reinterpret_cast<uintptr_t>((lds_void_t *)lds_dst);   // LDS byte address
     uint32_t saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %1\n\t"
-        "s_nop 0\n\t"
-        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "s"(m0v), "v"(voff), "s"(rsrc)
-        : "memory");
+    if (STREAM)
+        asm volatile(
+            "s_mov_b32 %0, m0\n\t"
+            "s_mov_b32 m0, %1\n\t"
+            "s_nop 0\n\t"
+            "buffer_load_dwordx4 %2, %3, 0 offen nt lds\n\t"
+            "s_mov_b32 m0, %0"
+            : "=&s"(saved)
+            : "s"(m0v), "v"(voff), "s"(rsrc)
+            : "memory");
+    else
+        asm volatile(
+            "s_mov_b32 %0, m0\n\t"
+            "s_mov_b32 m0, %1\n\t"
+            "s_nop 0\n\t"
+            "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+            "s_mov_b32 m0, %0"
+            : "=&s"(saved)
+            : "s"(m0v), "v"(voff), "s"(rsrc)
+            : "memory");
 }
 
 // HBM -> LDS copy of one K and one V tile of BN keys by NW waves.  One
@@ -190,7 +206,7 @@ __device__ __forceinline__ void lds_dma16(char *lds_dst, int voff, u32x4_t rsrc)
 // consecutive LDS addresses.  Lane l of instruction q fills tile row
 // q * RPI + l / CPR at physical chunk l % CPR, i.e. it loads the logical chunk
 // (l % CPR) ^ swz(row) of that key's row.
-template <int D, int BN, int NW>
+template <int D, int BN, int NW, bool STREAM = false>
 struct TileLoader {
     static constexpr int CPR = D / 8;                 // 16-byte chunks per row
     static constexpr int RPI = 64 / CPR;              // rows per instruction
@@ -225,8 +241,8 @@ struct TileLoader {
             const int q = i * NW + wave;
             const int row = q * RPI + lane / CPR;          // tile-relative row
             const int voff = (lane / CPR) * kstride_bytes + (((lane % CPR) ^ swz<D>(row)) * 16);
-            lds_dma16(lds_k + q * 1024, voff, rsrc(kbase, key0 + q * RPI));
-            lds_dma16(lds_v + q * 1024, voff, rsrc(vbase, key0 + q * RPI));
+            lds_dma16<STREAM>(lds_k + q * 1024, voff, rsrc(kbase, key0 + q * RPI));
+            lds_dma16<STREAM>(lds_v + q * 1024, voff, rsrc(vbase, key0 + q * RPI));
         }
     }
 };
@@ -393,14 +409,14 @@ __device__ __forceinline__ void wait_tiles_ahead(int ahead)
 // the copies of tile n + S - 1 start into the stage tile n - 1 used.
 template <int D, int BN, int S>
 __device__ __forceinline__ void decode_step(
-    int n, int n_tiles, int key_base, char *lds, int st, const TileLoader<D, BN, 1> &ld,
+    int n, int n_tiles, int key_base, char *lds, int st, const TileLoader<D, BN, 1, true> &ld,
     int lane, int key_end, int wmin_lim, const OperandOffsets<D> &off,
     const bf16x8_t (&qf)[D / 16], f32x16_t (&o)[D / 32], float &m_ref, float &l_run,
     float &l_rnd, float c, int half, int lim_lane)
 {
-    constexpr int TB = TileLoader<D, BN, 1>::TILE_BYTES;
+    constexpr int TB = TileLoader<D, BN, 1, true>::TILE_BYTES;
     constexpr int STAGE = 2 * TB;
-    constexpr int LPT = 2 * TileLoader<D, BN, 1>::PER_WAVE;
+    constexpr int LPT = 2 * TileLoader<D, BN, 1, true>::PER_WAVE;
     const int ahead = min(S - 2, n_tiles - 1 - n);
     wait_tiles_ahead<LPT, S - 2>(ahead);
     // one wave: orders its LDS reads of tile n - 1 before the copies below
@@ -1472,7 +1488,7 @@ fa_decode_split_kernel(const Params p)
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
     constexpr int BN = kDecodeBN;
     using WT = WaveTile<D, BN>;
-    using TL = TileLoader<D, BN, 1>;
+    using TL = TileLoader<D, BN, 1, true>;
     constexpr int TB = TL::TILE_BYTES;
     constexpr int STAGE = 2 * TB;
 
