@@ -870,12 +870,19 @@ fa_prefill_kernel(const Params p)
 // turns S(j) into P(j).  The reference max is the exact row max of the first
 // key block; after that it moves only when a block's exact P sum (which the
 // LSE needs anyway) exceeds kWideOverflow in some lane -- that block is then
-// redone against its exact row max.  P therefore stays below 2^12.
+// redone against its exact row max.  P therefore stays below 2^64: bf16 and
+// fp32 carry the same relative precision at any magnitude, and the sums stay
+// far from fp32 overflow (O and the row sums grow to at most keys * 2^64 *
+// max|v|, below 2^127 for any key count under 2^50 with |v| < 2^13).  The
+// threshold only has to catch exponents near overflow (an exp2 of 128 or
+// more is inf, which the test also catches); a low one would redo a block
+// each time a row's running max climbs, as it does on rows with large
+// scores.
 // LDS: the three K tiles first, then the three V tiles; the V operand offsets
 // carry the distance between the two, so that the stage and block parts of
 // every LDS address are compile-time immediates.
 // ---------------------------------------------------------------------------
-constexpr float kWideOverflow = 4096.0f;
+constexpr float kWideOverflow = 18446744073709551616.0f;   // 2^64
 // Operand reads of the fast block run this many steps ahead of their MFMAs.
 constexpr int kWidePrefetch = 2;
 
