@@ -59,6 +59,7 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((__vector_size__(64)));
+typedef float f32x4_t __attribute__((__vector_size__(16)));
 typedef uint32_t u32x4_t __attribute__((__vector_size__(16)));
 typedef uint32_t u32x2_t __attribute__((__vector_size__(8)));
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
@@ -437,19 +438,6 @@ __device__ __forceinline__ void decode_step(
                                               c, half, key0, key_end, lim_lane);
 }
 
-// Write 4 consecutive head dims of one output row.
-template <bool OUT_F32>
-__device__ __forceinline__ void store4(void *o, long idx, float a, float b, float c, float d)
-{
-    if (OUT_F32) {
-        float4 v = make_float4(a, b, c, d);
-        *reinterpret_cast<float4 *>(static_cast<float *>(o) + idx) = v;
-    } else {
-        u32x2_t v = {pack_bf16(a, b), pack_bf16(c, d)};
-        *reinterpret_cast<u32x2_t *>(static_cast<uint16_t *>(o) + idx) = v;
-    }
-}
-
 // Load this lane's Q fragment (B operand of S^T = K Q^T): head dims
 // 16*st + 8*half .. +7 of one query row, for st = 0..D/16-1.  The loads go
 // straight into the fragment registers, all issued before anything waits on
@@ -493,14 +481,40 @@ __device__ __forceinline__ void finish_rows(const f32x16_t (&o)[D / 32], float m
     const float l = add_halves(l_part);
     const float inv = l_norm > 0.0f ? 1.0f / l_norm : 0.0f;
     if (!write) return;
+    // all values first, each store's data in registers of its own, then the
+    // stores back to back: rewriting a store's data registers right behind
+    // it stalls the wave until the store has read them
+    if (OUT_F32) {
+        f32x4_t ov[D / 32][4];
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+        for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-            const int d0 = db * 32 + 8 * gq + 4 * half;
-            store4<OUT_F32>(out, obase + d0, o[db][4 * gq] * inv, o[db][4 * gq + 1] * inv,
-                            o[db][4 * gq + 2] * inv, o[db][4 * gq + 3] * inv);
-        }
+            for (int gq = 0; gq < 4; ++gq)
+                ov[db][gq] = (f32x4_t){o[db][4 * gq] * inv, o[db][4 * gq + 1] * inv,
+                                       o[db][4 * gq + 2] * inv, o[db][4 * gq + 3] * inv};
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq)
+                *reinterpret_cast<f32x4_t *>(static_cast<float *>(out) + obase + db * 32 + 8 * gq +
+                                             4 * half) = ov[db][gq];
+    } else {
+        u32x2_t ov[D / 32][4];
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq)
+                ov[db][gq] = (u32x2_t){pack_bf16(o[db][4 * gq] * inv, o[db][4 * gq + 1] * inv),
+                                       pack_bf16(o[db][4 * gq + 2] * inv, o[db][4 * gq + 3] * inv)};
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq)
+                *reinterpret_cast<u32x2_t *>(static_cast<uint16_t *>(out) + obase + db * 32 + 8 * gq +
+                                             4 * half) = ov[db][gq];
+    }
     if (lse_out && half == 0) {
         const float mc = (m_ref == kNegInf) ? 0.0f : m_ref * c;
         *lse_out = l > 0.0f ? (mc + __log2f(l)) * kLn2 : kNegInf;
@@ -510,8 +524,6 @@ __device__ __forceinline__ void finish_rows(const f32x16_t (&o)[D / 32], float m
 // ---------------------------------------------------------------------------
 // Per-block pieces of the pipelined prefill (a block = 32 keys).
 // ---------------------------------------------------------------------------
-typedef float f32x4_t __attribute__((__vector_size__(16)));
-
 __device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
