@@ -20,6 +20,9 @@ reports, for every inline-assembly MFMA:
 * any compiler-emitted VALU instruction that writes one of the MFMA's source
   registers fewer than ``operand_wait`` wait states before it (2 are needed).
 
+``scan_divergent_copies`` reports register copies placed right before the
+end of a divergent region (see there).
+
 Wait states are counted conservatively: one per instruction, ``N + 1`` for
 ``s_nop N``.  Other inline-assembly instructions count but are not reported
 (the MFMA chains and the drain are written to respect the rules).
@@ -123,6 +126,49 @@ def scan(asm: str, result_wait: int = 18, operand_wait: int = 2) -> list:
                     break
             ws += _wait_states(t2)
             j -= 1
+    return findings
+
+
+_COPIES = ("v_mov_b32", "v_mov_b64", "v_accvgpr_write_b32", "v_accvgpr_read_b32",
+           "v_accvgpr_mov_b32")
+
+
+def scan_divergent_copies(asm: str) -> list:
+    """Register copies placed at the very end of a divergent region.
+
+    A region opened by ``s_and_saveexec_b64 sX`` runs with some lanes off
+    until ``s_or_b64 exec, exec, sX`` restores them.  A VGPR/AGPR copy right
+    before that restore only reaches the active lanes; when the register
+    allocator splits the live range of a value that every lane still needs
+    (a loop-carried sum, say) and puts the copy there, the other lanes lose
+    it.  This once produced wrong row sums in the lanes a causal-mask branch
+    had skipped.  The kernels keep their masks as selects so that no such
+    branch exists inside the key loop; any copy in this position is reported.
+    """
+    ins = _instructions(asm)
+    findings = []
+    for k, (no, text, _, _) in enumerate(ins):
+        if not text.startswith("s_or_b64 exec, exec,"):
+            continue
+        j = k - 1
+        while j >= 0:
+            no2, t2, _, cf = ins[j]
+            op = t2.split()[0]
+            if cf and not op.startswith("s_"):
+                j -= 1          # a label: keep looking back
+                continue
+            if cf or op.startswith("s_and_saveexec"):
+                break           # a branch (no fall-through) or the region's start
+                break
+            if op.startswith("s_"):
+                j -= 1
+                continue
+            if re.sub(r"_e(32|64)$", "", op) in _COPIES:
+                findings.append(f"line {no2}: {t2}: copy at the end of a divergent region "
+                                f"(exec restored at line {no})")
+                j -= 1
+                continue
+            break
     return findings
 
 

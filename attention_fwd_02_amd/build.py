@@ -40,6 +40,10 @@ def check_device_code() -> None:
     if found:
         raise RuntimeError("inline-asm MFMA hazards in the generated code:\n  "
                            + "\n  ".join(found[:20]))
+    found = asm_check.scan_divergent_copies(asm)
+    if found:
+        raise RuntimeError("register copies at the end of divergent regions:\n  "
+                           + "\n  ".join(found[:20]))
 
 
 def build_lib(verbose: bool = False) -> str:

@@ -41,7 +41,7 @@
 //    two waves per SIMD (the default), or 64 rows per wave and one wave per
 //    SIMD with a hand-pipelined block loop (half the LDS reads per flop).
 //  * The HBM -> LDS copies are issued as inline asm so that the compiler does
-//    not make LDS reads wait for copies still in flight (see lds_dma16).
+//    not make LDS reads wait for copies still in flight (see lds_dma16_pair).
 //  * Decode (few query rows per KV head) runs a split-key kernel, one wave per
 //    (batch, KV head, key range) with a three-tile LDS ring, which writes
 //    partial (O_s, LSE_s); a merge pass combines them with log-sum-exp weights.
@@ -169,36 +169,45 @@ __device__ __forceinline__ int swz(int r)
 // waits for every copy in flight (vmcnt(0)) before that read -- which would
 // expose the full HBM latency of the tiles prefetched ahead.  The kernels wait
 // for the copies themselves (wait_vmem / wait_tiles_ahead, then a barrier).
-// M0 is saved and restored around the copy (the compiler reserves it).
-// STREAM marks the copy non-temporal: data read once (the decode's K/V)
-// then does not displace cache lines that are still needed, such as output
-// another kernel left dirty, whose write-back would otherwise be charged to
-// the streaming read.
+// M0 is saved and restored around the copies (the compiler reserves it).
+//
+// lds_dma16_pair issues the K and the V copy of one lane chunk: same
+// offsets, two descriptors, two LDS destinations.  STREAM marks them
+// non-temporal: data read once (the decode's K/V) then does not displace
+// cache lines that are still needed, such as output another kernel left
+// dirty, whose write-back would otherwise be charged to the streaming read.
 template <bool STREAM = false>
-__device__ __forceinline__ void lds_dma16(char *lds_dst, int voff, u32x4_t rsrc)
+__device__ __forceinline__ void lds_dma16_pair(char *lds_k, char *lds_v, int voff, u32x4_t kd,
+                                               u32x4_t vd)
 {
-    const uint32_t m0v =
-        (uint32_t)reinterpret_cast<uintptr_t>((lds_void_t *)lds_dst);   // LDS byte address
+    const uint32_t m0k = (uint32_t)reinterpret_cast<uintptr_t>((lds_void_t *)lds_k);
+    const uint32_t m0v = (uint32_t)reinterpret_cast<uintptr_t>((lds_void_t *)lds_v);
     uint32_t saved;
     if (STREAM)
         asm volatile(
             "s_mov_b32 %0, m0\n\t"
             "s_mov_b32 m0, %1\n\t"
             "s_nop 0\n\t"
-            "buffer_load_dwordx4 %2, %3, 0 offen nt lds\n\t"
+            "buffer_load_dwordx4 %3, %4, 0 offen nt lds\n\t"
+            "s_mov_b32 m0, %2\n\t"
+            "s_nop 0\n\t"
+            "buffer_load_dwordx4 %3, %5, 0 offen nt lds\n\t"
             "s_mov_b32 m0, %0"
             : "=&s"(saved)
-            : "s"(m0v), "v"(voff), "s"(rsrc)
+            : "s"(m0k), "s"(m0v), "v"(voff), "s"(kd), "s"(vd)
             : "memory");
     else
         asm volatile(
             "s_mov_b32 %0, m0\n\t"
             "s_mov_b32 m0, %1\n\t"
             "s_nop 0\n\t"
-            "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+            "buffer_load_dwordx4 %3, %4, 0 offen lds\n\t"
+            "s_mov_b32 m0, %2\n\t"
+            "s_nop 0\n\t"
+            "buffer_load_dwordx4 %3, %5, 0 offen lds\n\t"
             "s_mov_b32 m0, %0"
             : "=&s"(saved)
-            : "s"(m0v), "v"(voff), "s"(rsrc)
+            : "s"(m0k), "s"(m0v), "v"(voff), "s"(kd), "s"(vd)
             : "memory");
 }
 
@@ -216,20 +225,25 @@ struct TileLoader {
     static constexpr int TILE_BYTES = BN * D * 2;
     static_assert(NQ % NW == 0, "instructions must split evenly over the waves");
 
-    const uint16_t *kbase, *vbase;
-    int kstride_bytes;   // bytes between consecutive keys in HBM
-    int key_end;         // keys >= key_end read as zero
+    u32x4_t kdesc, vdesc;   // K and V rows [0, key_end) of one (batch, KV head)
+    int kstride_bytes;      // bytes between consecutive keys in HBM
 
-    // Descriptor over the rows from `row0` on: rows at or beyond key_end fall
-    // outside its byte range.  Uniform values only (scalar registers).
-    // Words: base address bits 31:0; bits 47:32 (stride 0); byte range; flags.
-    __device__ __forceinline__ u32x4_t rsrc(const uint16_t *base, int row0) const
+    // Descriptors whose byte range ends with row key_end - 1, so that rows
+    // at or beyond key_end read as zero.  Uniform values only (scalar
+    // registers).  Words: base address bits 31:0; bits 47:32 (stride 0);
+    // byte range; flags.  Byte offsets stay below 2^31: the host checks
+    // that K and V of one batch are under 2 GiB.
+    __device__ __forceinline__ void setup(const uint16_t *kbase, const uint16_t *vbase,
+                                          int kstride, int key_end)
     {
-        const int valid = key_end - row0;
-        const int nbytes = valid > 0 ? (valid - 1) * kstride_bytes + D * 2 : 0;
-        const uint64_t a = reinterpret_cast<uint64_t>(base + (long)row0 * (kstride_bytes / 2));
-        return (u32x4_t){(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, (uint32_t)nbytes,
-                         (uint32_t)kBufferFlags};
+        kstride_bytes = kstride;
+        const uint32_t nbytes = key_end > 0 ? (uint32_t)((key_end - 1) * kstride + D * 2) : 0u;
+        const uint64_t ka = reinterpret_cast<uint64_t>(kbase);
+        const uint64_t va = reinterpret_cast<uint64_t>(vbase);
+        kdesc = (u32x4_t){(uint32_t)ka, (uint32_t)(ka >> 32) & 0xffffu, nbytes,
+                          (uint32_t)kBufferFlags};
+        vdesc = (u32x4_t){(uint32_t)va, (uint32_t)(va >> 32) & 0xffffu, nbytes,
+                          (uint32_t)kBufferFlags};
     }
 
     // Issue the copies of keys [key0, key0 + BN) into the K and V tiles at
@@ -237,13 +251,13 @@ struct TileLoader {
     __device__ __forceinline__ void issue(char *lds_k, char *lds_v, int key0, int wave,
                                           int lane) const
     {
+        const int toff = key0 * kstride_bytes;   // uniform
 #pragma unroll
         for (int i = 0; i < PER_WAVE; ++i) {
             const int q = i * NW + wave;
             const int row = q * RPI + lane / CPR;          // tile-relative row
-            const int voff = (lane / CPR) * kstride_bytes + (((lane % CPR) ^ swz<D>(row)) * 16);
-            lds_dma16<STREAM>(lds_k + q * 1024, voff, rsrc(kbase, key0 + q * RPI));
-            lds_dma16<STREAM>(lds_v + q * 1024, voff, rsrc(vbase, key0 + q * RPI));
+            const int voff = toff + row * kstride_bytes + (((lane % CPR) ^ swz<D>(row)) * 16);
+            lds_dma16_pair<STREAM>(lds_k + q * 1024, lds_v + q * 1024, voff, kdesc, vdesc);
         }
     }
 };
@@ -322,7 +336,7 @@ struct WaveTile {
                 const int last = min(lim, key_end - 1) - (key0 + kb * 32 + 4 * half);
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    if (8 * (r >> 2) + (r & 3) > last) s[kb][r] = kNegInf;
+                    s[kb][r] = (8 * (r >> 2) + (r & 3) > last) ? kNegInf : s[kb][r];
             }
         }
 
@@ -569,14 +583,18 @@ struct BlockOps {
     // Register r holds key key0 + 4*half + 8*(r/4) + r%4; comparing the
     // constant part against one per-lane bound keeps the 16 offsets as
     // instruction immediates (no registers to hold, or spill, them in).
+    // Selects, not conditional assignments: written as `if (...) s[r] = -inf`
+    // the compiler turned the mask into a branch on the lane's limit (skip
+    // when nothing is masked), and the register allocator then placed copies
+    // of loop-carried values (the exact row sums) inside that branch, where
+    // the lanes that skipped it never received them.
     __device__ __forceinline__ static void mask(f32x16_t &s, int key0, int half, int key_end,
                                                 int lim)
     {
         const int base = key0 + 4 * half;
         const int last = min(lim, key_end - 1) - base;   // largest allowed offset
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-            if (8 * (r >> 2) + (r & 3) > last) s[r] = kNegInf;
+        for (int r = 0; r < 16; ++r) s[r] = (8 * (r >> 2) + (r & 3) > last) ? kNegInf : s[r];
     }
 
     // max over the block's keys of this lane's query (both lane halves)
@@ -831,10 +849,8 @@ fa_prefill_kernel(const Params p)
             rs.NBw = NB;
 
         TL ld;
-        ld.kbase = p.k + ((long)b * p.Sk * p.Hkv + g) * D;
-        ld.vbase = p.v + ((long)b * p.Sk * p.Hkv + g) * D;
-        ld.kstride_bytes = p.Hkv * D * 2;
-        ld.key_end = p.Sk;
+        ld.setup(p.k + ((long)b * p.Sk * p.Hkv + g) * D, p.v + ((long)b * p.Sk * p.Hkv + g) * D,
+                 p.Hkv * D * 2, p.Sk);
 
         // the first two tiles' copies, then Q: one memory round trip for all
         if (n_tiles > 0) ld.issue(lds, lds + TB, 0, wave, lane);
@@ -1309,10 +1325,8 @@ __device__ __forceinline__ void wide_item_issue(const Params &p, const WideItem 
                                                 int TB, int wave, int lane, int half, int col,
                                                 bf16x8_t (&qf)[2][D / 16])
 {
-    ld.kbase = p.k + ((long)I.b * p.Sk * p.Hkv + I.g) * D;
-    ld.vbase = p.v + ((long)I.b * p.Sk * p.Hkv + I.g) * D;
-    ld.kstride_bytes = p.Hkv * D * 2;
-    ld.key_end = p.Sk;
+    ld.setup(p.k + ((long)I.b * p.Sk * p.Hkv + I.g) * D, p.v + ((long)I.b * p.Sk * p.Hkv + I.g) * D,
+             p.Hkv * D * 2, p.Sk);
     if (I.n_tiles > 0) ld.issue(lds, lds + VOFF, 0, wave, lane);
     if (I.n_tiles > 1) ld.issue(lds + TB, lds + TB + VOFF, BN, wave, lane);
 #pragma unroll
@@ -1539,10 +1553,8 @@ fa_decode_split_kernel(const Params p)
     bf16x8_t qf[D / 16];
 
     TL ld;
-    ld.kbase = p.k + ((long)b * p.Sk * p.Hkv + g) * D;
-    ld.vbase = p.v + ((long)b * p.Sk * p.Hkv + g) * D;
-    ld.kstride_bytes = p.Hkv * D * 2;
-    ld.key_end = k_end;
+    ld.setup(p.k + ((long)b * p.Sk * p.Hkv + g) * D, p.v + ((long)b * p.Sk * p.Hkv + g) * D,
+             p.Hkv * D * 2, k_end);
 
     f32x16_t o[D / 32];
 #pragma unroll

@@ -72,6 +72,24 @@ def test_compiler_emitted_mfma_is_not_checked():
     assert asm_check.scan(asm) == []
 
 
+def test_copy_at_end_of_divergent_region_is_found():
+    # the allocator's copy of a loop-carried value inside a masked branch:
+    # lanes outside the branch never receive it
+    asm = listing("v_cmp_gt_i32_e32 vcc, 27, v0", "s_and_saveexec_b64 s[28:29], vcc",
+                  "v_cndmask_b32_e32 v4, v5, v6, vcc", "v_accvgpr_write_b32 a201, v238",
+                  "v_mov_b32_e32 v251, v237", "s_mov_b32 s0, s53",
+                  "s_or_b64 exec, exec, s[28:29]")
+    found = asm_check.scan_divergent_copies(asm)
+    assert len(found) == 2 and "a201" in found[1] and "v251" in found[0]
+
+
+def test_store_at_end_of_divergent_region_passes():
+    asm = listing("s_and_saveexec_b64 s[6:7], vcc", "v_mov_b32_e32 v3, v9",
+                  "v_cvt_pk_bf16_f32 v8, v1, v2", "global_store_dword v[2:3], v8, off",
+                  ".LBB0_4:", "s_or_b64 exec, exec, s[6:7]")
+    assert asm_check.scan_divergent_copies(asm) == []
+
+
 @pytest.mark.skipif(not shutil.which(build.HIPCC) and not os.path.exists(build.HIPCC),
                     reason="hipcc not available")
 def test_kernels_have_no_inline_mfma_hazards():
@@ -80,3 +98,4 @@ def test_kernels_have_no_inline_mfma_hazards():
     n = sum(1 for i in asm_check._instructions(asm) if i[2] and i[1].startswith("v_mfma"))
     assert n > 0, "no inline-asm MFMA found: the scan would be vacuous"
     assert asm_check.scan(asm) == []
+    assert asm_check.scan_divergent_copies(asm) == []

@@ -100,6 +100,7 @@ CONFIGS = {
 }
 CONFIG_SHAPES = [
     (1, 1, 1, 128, 128, 64, True, "bf16"),
+    (1, 1, 1, 64, 64, 128, True, "f32"),          # one diagonal tile: every row's LSE
     (2, 3, 3, 77, 77, 64, True, "bf16"),
     (1, 2, 1, 200, 333, 128, True, "f32"),
     (1, 2, 2, 300, 100, 64, True, "bf16"),
