@@ -12,6 +12,16 @@ Recipe (the same on every machine, CPU generator only):
     query rows, drawn after v from the same generator with ``torch.rand``;
     selected rows are multiplied by ``hot_row_mult`` in float32 before the cast
     (8 is a power of two, so the bf16 values are exactly 8x the plain draw).
+
+Paged K/V caches (``PagedWorkload``), same generator:
+  * sequence lengths: every sequence ``max_len`` keys ("equal"), or
+    ``torch.randint(1, max_len + 1)`` per sequence ("ragged", mean about
+    max_len / 2);
+  * each sequence takes ceil(len / page_size) pages; the cache holds exactly
+    those pages, handed out in the order of ``torch.randperm`` (a fragmented
+    pool: a sequence's pages are scattered over the cache); unused block-table
+    entries are -1;
+  * then q, k_cache, v_cache with ``torch.randn`` as above.
 """
 from __future__ import annotations
 
@@ -108,3 +118,74 @@ def random_qkv(B, Hq, Hkv, Sq, Sk, D, seed, std=1.0, device="cpu"):
     w = Workload("adhoc", B=B, Hq=Hq, Hkv=Hkv, Sq=Sq, Sk=Sk, D=D, causal=False,
                  std=std, seed=seed)
     return make_inputs(w, device=device)
+
+
+@dataclasses.dataclass(frozen=True)
+class PagedWorkload:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Sq: int
+    max_len: int
+    page_size: int
+    D: int
+    lengths: str = "equal"         # "equal" or "ragged"
+    causal: bool = False
+    o_dtype: str = "bf16"
+    seed: int = 0
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+    @property
+    def max_pages(self) -> int:
+        return (self.max_len + self.page_size - 1) // self.page_size
+
+
+PAGED_WORKLOADS = {
+    w.name: w for w in [
+        # the decode workload's shape (B=32, Hq=32, Hkv=8, 8192 keys, D=128)
+        # with its K/V in 16-key pages scattered over the cache
+        PagedWorkload("paged_decode_b32_hq32_hkv8_len8192_ps16_d128", B=32, Hq=32, Hkv=8,
+                      Sq=1, max_len=8192, page_size=16, D=128, seed=5),
+        # the same with lengths drawn from [1, 16384] (mean about 8192)
+        PagedWorkload("paged_decode_b32_hq32_hkv8_ragged16384_ps16_d128", B=32, Hq=32, Hkv=8,
+                      Sq=1, max_len=16384, page_size=16, D=128, lengths="ragged", seed=6),
+    ]
+}
+
+
+def make_paged_inputs(w: PagedWorkload, seed: int | None = None, device: str = "cpu",
+                      lens=None):
+    """Return (q, k_cache, v_cache, block_table, seq_lens).
+
+    q [B,Sq,Hq,D] bf16; caches [num_pages, page_size, Hkv, D] bf16;
+    block_table [B, max_pages] int32; seq_lens [B] int32.  ``lens`` (a list)
+    replaces the drawn lengths (edge cases in tests)."""
+    g = torch.Generator("cpu")
+    g.manual_seed(w.seed if seed is None else seed)
+    if lens is not None:
+        seq = torch.tensor(lens, dtype=torch.int64)
+    elif w.lengths == "equal":
+        seq = torch.full((w.B,), w.max_len, dtype=torch.int64)
+    else:
+        seq = torch.randint(1, w.max_len + 1, (w.B,), generator=g, dtype=torch.int64)
+    npages = (seq + w.page_size - 1) // w.page_size
+    total = int(npages.sum())
+    perm = torch.randperm(max(total, 1), generator=g)
+    table = torch.full((w.B, w.max_pages), -1, dtype=torch.int32)
+    at = 0
+    for b in range(w.B):
+        n = int(npages[b])
+        table[b, :n] = perm[at:at + n].to(torch.int32)
+        at += n
+    q = torch.randn((w.B, w.Sq, w.Hq, w.D), generator=g, dtype=torch.float32)
+    kc = torch.randn((max(total, 1), w.page_size, w.Hkv, w.D), generator=g, dtype=torch.float32)
+    vc = torch.randn((max(total, 1), w.page_size, w.Hkv, w.D), generator=g, dtype=torch.float32)
+    q, kc, vc = (t.to(torch.bfloat16) for t in (q, kc, vc))
+    seq = seq.to(torch.int32)
+    if device != "cpu":
+        q, kc, vc, table, seq = (t.to(device) for t in (q, kc, vc, table, seq))
+    return q, kc, vc, table, seq

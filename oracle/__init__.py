@@ -13,6 +13,10 @@ Parity status: pinned.  ``tests/test_oracle.py`` checks it against a 40-digit
 ``decimal`` brute force, a torch fp64 library evaluation of the same
 definition, closed forms worked out by hand, invariants and layout probes;
 ``tests/test_oracle_mutants.py`` shows that planted slips fail those pins.
+``attn_fwd_paged`` (paged K/V cache, one length per sequence) gathers each
+sequence's keys in plain numpy and hands them to the same definition; its
+gather is pinned by hand-placed page contents with closed-form answers in
+``tests/test_oracle.py`` and by planted slips in the mutant tests.
 """
 from __future__ import annotations
 
@@ -123,3 +127,45 @@ def attn_fwd(q, k, v, causal: bool, scale: float, *, rows=None,
 def allowed_pairs(Sq: int, Sk: int, causal: bool) -> int:
     """Allowed (query, key) pairs of one head: the unit of algorithmic work."""
     return int(_load().oracle_allowed_pairs(Sq, Sk, int(bool(causal))))
+
+
+def gather_pages(cache: np.ndarray, table_row: np.ndarray, n: int) -> np.ndarray:
+    """Rows 0..n-1 of one sequence out of a paged cache [pages, page_size, H, D]:
+    logical key j is slot j % page_size of page table_row[j // page_size]."""
+    page_size = cache.shape[1]
+    j = np.arange(n)
+    return cache[table_row[j // page_size], j % page_size]
+
+
+def attn_fwd_paged(q, k_cache, v_cache, block_table, seq_lens, causal: bool, scale: float, *,
+                   nthreads: int | None = None, _lib_override=None):
+    """The oracle over a paged K/V cache with one length per sequence.
+
+    The pages name paged K/V only as a way of loading K and V ("SM80 内核实现对比",
+    section 7.3, the PagedKV row of the scenario table: both kernels fetch it with
+    cp.async).  Layout and meaning are this project's reading: k_cache and
+    v_cache are [num_pages, page_size, Hkv, D] bf16; block_table [B, max_pages]
+    maps sequence b's logical page p to a cache page; seq_lens[b] = Sk_b keys.
+    Sequence b is then exactly the contiguous problem over its first Sk_b keys
+    (causal: key j allowed for query i iff j <= i + Sk_b - Sq); Sk_b = 0 gives
+    O = 0 and LSE = -inf, as for any row without an allowed key.
+
+    q: [B, Sq, Hq, D] bf16.  Returns (o [B,Sq,Hq,D], lse [B,Hq,Sq]) float64.
+    """
+    qb, kb, vb = _bits(q), _bits(k_cache), _bits(v_cache)
+    table = np.asarray(block_table.cpu() if hasattr(block_table, "cpu") else block_table,
+                       dtype=np.int64)
+    lens = np.asarray(seq_lens.cpu() if hasattr(seq_lens, "cpu") else seq_lens, dtype=np.int64)
+    B, Sq, Hq, D = qb.shape
+    o = np.zeros((B, Sq, Hq, D), dtype=np.float64)
+    lse = np.full((B, Hq, Sq), -np.inf, dtype=np.float64)
+    for b in range(B):
+        n = int(lens[b])
+        if n == 0:
+            continue
+        kc = gather_pages(kb, table[b], n)[None]
+        vc = gather_pages(vb, table[b], n)[None]
+        ob, lb = attn_fwd(qb[b:b + 1], np.ascontiguousarray(kc), np.ascontiguousarray(vc),
+                          causal, scale, nthreads=nthreads, _lib_override=_lib_override)
+        o[b], lse[b] = ob[0], lb[0]
+    return o, lse

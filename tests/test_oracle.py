@@ -347,3 +347,111 @@ def test_allowed_pairs_count(oracle_mod):
     assert oracle_mod.allowed_pairs(3, 5, True) == 3 + 4 + 5
     assert oracle_mod.allowed_pairs(5, 3, True) == 0 + 0 + 1 + 2 + 3
     assert oracle_mod.allowed_pairs(7, 9, False) == 63
+
+
+# ----------------------------------------------------------------------------
+# paged K/V cache: the gather, pinned by where each value was placed
+# ----------------------------------------------------------------------------
+# 4 pages of 2 slots; the value of every element of page p, slot s is
+# 1 + 10 p + s (exact in bf16).  Sequence 0 has 3 keys: page 3 (slots 0, 1),
+# then page 1 (slot 0) -> values 31, 32, 11.  Sequence 1 has 1 key: page 0
+# slot 0 -> 1.  Sequence 2 has 5 keys: pages 2, 0, 3 -> 21, 22, 1, 2, 31.
+PAGED_TABLE = np.array([[3, 1, -1], [0, 2, -1], [2, 0, 3]], dtype=np.int32)
+PAGED_LENS = np.array([3, 1, 5], dtype=np.int32)
+
+
+def paged_ids_cache(Hkv=1, D=4):
+    ids = 1.0 + 10.0 * np.arange(4)[:, None] + np.arange(2)[None, :]
+    return bf16(np.broadcast_to(ids[:, :, None, None], (4, 2, Hkv, D)).copy())
+
+
+def test_paged_uniform_scores_average_the_sequences_own_rows(oracle_mod):
+    # K = 0: every allowed key scores 0, so O is the mean of the sequence's V
+    # rows and LSE = ln(count)
+    v = paged_ids_cache()
+    k = bf16(np.zeros((4, 2, 1, 4)))
+    q = bf16(np.random.default_rng(0).standard_normal((3, 1, 2, 4)))
+    o, lse = oracle_mod.attn_fwd_paged(q, k, v, PAGED_TABLE, PAGED_LENS, False, 0.5)
+    expect = [74.0 / 3.0, 1.0, 77.0 / 5.0]
+    for b in range(3):
+        np.testing.assert_allclose(o[b], np.full((1, 2, 4), expect[b]), rtol=1e-13)
+        np.testing.assert_allclose(lse[b], np.full((2, 1), math.log(PAGED_LENS[b])),
+                                   rtol=0, atol=1e-13)
+
+
+def test_paged_dominant_key_picks_its_slot(oracle_mod):
+    # q = e0; K rows -1 in dim 0 except logical key 2 of sequence 0 (page 1,
+    # slot 0) and logical key 3 of sequence 2 (page 0, slot 1), which are +1.
+    # With scale 30 the others weigh e^-60: O is that key's V row (11, 2).
+    v = paged_ids_cache()
+    k = np.zeros((4, 2, 1, 4), dtype=np.float32)
+    k[:, :, 0, 0] = -1.0
+    k[1, 0, 0, 0] = 1.0
+    k[0, 1, 0, 0] = 1.0
+    q = np.zeros((3, 1, 1, 4), dtype=np.float32)
+    q[:, 0, 0, 0] = 1.0
+    lens = np.array([3, 1, 5], dtype=np.int32)
+    o, lse = oracle_mod.attn_fwd_paged(bf16(q), bf16(k), v, PAGED_TABLE, lens, False, 30.0)
+    assert o[0, 0, 0, 0] == pytest.approx(11.0, abs=1e-20)
+    assert o[2, 0, 0, 0] == pytest.approx(2.0, abs=1e-20)
+    # sequence 1 (one key, page 0 slot 0 with -1): the single row itself
+    assert o[1, 0, 0, 0] == 1.0 and lse[1, 0, 0] == pytest.approx(-30.0, abs=1e-13)
+    # sequence 0: one key at +30, two at -30
+    assert lse[0, 0, 0] == pytest.approx(30.0 + math.log1p(2 * math.exp(-60.0)), abs=1e-13)
+
+
+def test_paged_causal_offset_is_per_sequence(oracle_mod):
+    # Sq = 2, causal: row i of sequence b sees keys j <= i + len_b - 2.
+    # Sequence 2 (5 keys): row 0 -> first 4 keys (21, 22, 1, 2), row 1 -> all 5.
+    # Sequence 1 (1 key): row 0 sees none (O = 0, LSE = -inf), row 1 key 0.
+    v = paged_ids_cache()
+    k = bf16(np.zeros((4, 2, 1, 4)))
+    q = bf16(np.ones((3, 2, 1, 4)))
+    o, lse = oracle_mod.attn_fwd_paged(q, k, v, PAGED_TABLE, PAGED_LENS, True, 0.5)
+    assert o[2, 0, 0, 0] == pytest.approx(46.0 / 4.0, rel=1e-13)
+    assert o[2, 1, 0, 0] == pytest.approx(77.0 / 5.0, rel=1e-13)
+    assert lse[2, 0, 0] == pytest.approx(math.log(4), abs=1e-13)
+    assert np.all(o[1, 0] == 0.0) and lse[1, 0, 0] == -math.inf
+    assert o[1, 1, 0, 0] == 1.0 and lse[1, 0, 1] == 0.0
+    # sequence 0 (3 keys): row 0 -> 31, 32; row 1 -> 31, 32, 11
+    assert o[0, 0, 0, 0] == pytest.approx(31.5, rel=1e-13)
+    assert o[0, 1, 0, 0] == pytest.approx(74.0 / 3.0, rel=1e-13)
+
+
+def test_paged_empty_sequence(oracle_mod):
+    v = paged_ids_cache()
+    q = bf16(np.ones((3, 1, 2, 4)))
+    lens = np.array([3, 0, 5], dtype=np.int32)
+    o, lse = oracle_mod.attn_fwd_paged(q, v, v, PAGED_TABLE, lens, False, 0.5)
+    assert np.all(o[1] == 0.0) and np.all(lse[1] == -math.inf)
+    assert np.isfinite(lse[0]).all() and np.isfinite(lse[2]).all()
+
+
+def test_paged_identity_table_equals_contiguous(oracle_mod):
+    # pages laid out in order, every sequence full: the contiguous problem
+    B, Hq, Hkv, S, D, ps = 2, 4, 2, 24, 8, 4
+    q, k, v = random_qkv(B, Hq, Hkv, 3, S, D, seed=21)
+    table = np.arange(B * S // ps, dtype=np.int32).reshape(B, S // ps)
+    kc = k.reshape(B * S // ps, ps, Hkv, D)
+    vc = v.reshape(B * S // ps, ps, Hkv, D)
+    lens = np.full(B, S, dtype=np.int32)
+    for causal in (False, True):
+        o1, l1 = oracle_mod.attn_fwd_paged(q, kc, vc, table, lens, causal, 0.3)
+        o2, l2 = oracle_mod.attn_fwd(q, k, v, causal, 0.3)
+        np.testing.assert_array_equal(o1, o2)
+        np.testing.assert_array_equal(l1, l2)
+
+
+def test_paged_page_permutation_invariance(oracle_mod):
+    # moving pages around the cache and remapping the table changes nothing
+    rng = np.random.default_rng(3)
+    q = bf16(rng.standard_normal((3, 1, 2, 8)))
+    k = bf16(rng.standard_normal((4, 2, 1, 8)))
+    v = bf16(rng.standard_normal((4, 2, 1, 8)))
+    o1, l1 = oracle_mod.attn_fwd_paged(q, k, v, PAGED_TABLE, PAGED_LENS, False, 0.4)
+    perm = np.array([2, 0, 3, 1])                 # page p moves to slot perm[p]
+    inv = np.argsort(perm)
+    table2 = np.where(PAGED_TABLE >= 0, perm[np.maximum(PAGED_TABLE, 0)], -1).astype(np.int32)
+    o2, l2 = oracle_mod.attn_fwd_paged(q, k[inv], v[inv], table2, PAGED_LENS, False, 0.4)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)

@@ -77,3 +77,41 @@ def test_pins_reject_mutant(tmp_path, name):
         except (AssertionError, RuntimeError):
             caught += 1
     assert caught > 0, f"no pin detects mutant {name}"
+
+
+# slips in the paged gather (oracle/__init__.py), caught by the paged pins
+PY_MUTANTS = {
+    "page_and_slot_swapped": ("return cache[table_row[j // page_size], j % page_size]",
+                              "return cache[table_row[j % page_size], j // page_size]"),
+    "slots_reversed_in_page": ("return cache[table_row[j // page_size], j % page_size]",
+                               "return cache[table_row[j // page_size], page_size - 1 - j % page_size]"),
+    "next_sequence_table_row": ("kc = gather_pages(kb, table[b], n)[None]\n        vc = gather_pages(vb, table[b], n)[None]",
+                                "kc = gather_pages(kb, table[(b + 1) % B], n)[None]\n        vc = gather_pages(vb, table[(b + 1) % B], n)[None]"),
+    "length_off_by_one": ("n = int(lens[b])\n", "n = max(int(lens[b]) - 1, 1)\n"),
+    "v_gathered_from_k": ("vc = gather_pages(vb, table[b], n)[None]", "vc = gather_pages(kb, table[b], n)[None]"),
+}
+
+PAGED_PIN_TESTS = [
+    pins.test_paged_uniform_scores_average_the_sequences_own_rows,
+    pins.test_paged_dominant_key_picks_its_slot,
+    pins.test_paged_causal_offset_is_per_sequence,
+    pins.test_paged_empty_sequence,
+]
+
+
+@pytest.mark.parametrize("name", sorted(PY_MUTANTS))
+def test_paged_pins_reject_mutant(name):
+    import types
+    before, after = PY_MUTANTS[name]
+    src = open(oracle_pkg.__file__).read()
+    assert src.count(before) == 1, f"mutation anchor for {name} not found exactly once"
+    mod = types.ModuleType("oracle_mutant")
+    mod.__file__ = oracle_pkg.__file__
+    exec(compile(src.replace(before, after), "oracle_mutant", "exec"), mod.__dict__)
+    caught = 0
+    for pin in PAGED_PIN_TESTS:
+        try:
+            pin(mod)
+        except (AssertionError, IndexError, ValueError):
+            caught += 1
+    assert caught > 0, f"no pin detects mutant {name}"
