@@ -20,8 +20,8 @@ STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_INVALID_ARG", 2: "FA_ERR_UNSUPPORTED",
                 3: "FA_ERR_NOMEM", 4: "FA_ERR_HIP"}
 
 # every symbol include/fa.h declares
-EXPORTS = ["fa_fwd", "fa_fwd_ex", "fa_workspace_size", "fa_plan", "fa_last_error",
-           "fa_release_workspace", "fa_version"]
+EXPORTS = ["fa_fwd", "fa_fwd_ex", "fa_workspace_size", "fa_plan", "fa_fwd_paged",
+           "fa_plan_paged", "fa_last_error", "fa_release_workspace", "fa_version"]
 
 
 class FaError(RuntimeError):
@@ -56,6 +56,11 @@ def _load():
     lib.fa_workspace_size.restype = c_size_t
     lib.fa_plan.argtypes = [c_int] * 8 + [ctypes.POINTER(FaPlanInfo)]
     lib.fa_plan.restype = c_int
+    lib.fa_fwd_paged.argtypes = ([c_void_p] * 7 + [c_int] * 8 + [c_int, c_float, c_void_p,
+                                                                c_int, c_int, c_void_p, c_size_t])
+    lib.fa_fwd_paged.restype = c_int
+    lib.fa_plan_paged.argtypes = [c_int] * 9 + [ctypes.POINTER(FaPlanInfo)]
+    lib.fa_plan_paged.restype = c_int
     lib.fa_last_error.argtypes = []
     lib.fa_last_error.restype = ctypes.c_char_p
     lib.fa_release_workspace.argtypes = []
@@ -154,3 +159,53 @@ def fa_fwd_ex(q, k, v, o, lse, causal: bool, scale: float, stream=None, num_spli
                          lse.data_ptr() if lse is not None else None,
                          B, Hq, Hkv, Sq, Sk, D, int(bool(causal)), float(scale),
                          _stream_handle(stream), odt, int(num_splits), ws_ptr, ws_bytes))
+
+
+def fa_plan_paged(B, Hq, Hkv, Sq, D, num_pages, page_size, max_pages, num_splits=0) -> dict:
+    info = FaPlanInfo()
+    _check(lib.fa_plan_paged(B, Hq, Hkv, Sq, D, num_pages, page_size, max_pages, num_splits,
+                             ctypes.byref(info)))
+    return {f: getattr(info, f) for f, _ in FaPlanInfo._fields_}
+
+
+def fa_fwd_paged(q, k_cache, v_cache, block_table, seq_lens, o, lse, causal: bool, scale: float,
+                 stream=None, num_splits: int = 0, workspace=None) -> None:
+    """Attention of q over a paged K/V cache; o bfloat16 or float32."""
+    import torch
+    if o.dtype == torch.bfloat16:
+        odt = FA_DTYPE_BF16
+    elif o.dtype == torch.float32:
+        odt = FA_DTYPE_F32
+    else:
+        raise TypeError("o must be bfloat16 or float32")
+    if q.dim() != 4 or k_cache.dim() != 4 or v_cache.dim() != 4 or o.dim() != 4:
+        raise ValueError("q, o must be [B, Sq, Hq, D]; caches [num_pages, page_size, Hkv, D]")
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be bfloat16")
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("o", o),
+                    ("block_table", block_table), ("seq_lens", seq_lens)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    B, Sq, Hq, D = q.shape
+    num_pages, page_size, Hkv, Dk = k_cache.shape
+    if Dk != D or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("k_cache and v_cache must both be [num_pages, page_size, Hkv, D]")
+    if tuple(o.shape) != (B, Sq, Hq, D):
+        raise ValueError("o must be [B, Sq, Hq, D]")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be int32 [B, max_pages]")
+    if seq_lens.dtype != torch.int32 or tuple(seq_lens.shape) != (B,):
+        raise ValueError("seq_lens must be int32 [B]")
+    if lse is not None:
+        if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Sq) or not lse.is_contiguous():
+            raise ValueError("lse must be a contiguous float32 [B, Hq, Sq] tensor")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    _check(lib.fa_fwd_paged(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                            block_table.data_ptr(), seq_lens.data_ptr(), o.data_ptr(),
+                            lse.data_ptr() if lse is not None else None,
+                            B, Hq, Hkv, Sq, D, num_pages, page_size, block_table.shape[1],
+                            int(bool(causal)), float(scale), _stream_handle(stream), odt,
+                            int(num_splits), ws_ptr, ws_bytes))

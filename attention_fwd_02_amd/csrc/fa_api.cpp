@@ -218,6 +218,123 @@ fa_status make_plan(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal, i
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Point L's split partials at the caller's workspace (checked against
+// `need`) or at the device's library-owned buffer, grown on demand.  `lk`
+// (on g_mu) stays locked while the launch uses the library buffer.
+fa_status attach_workspace(DeviceInfo *info, void *workspace, size_t workspace_bytes, size_t need,
+                           int num_splits, std::unique_lock<std::mutex> &lk, fa::Launch *L)
+{
+    void *ws = workspace;
+    if (ws) {
+        if (workspace_bytes < need)
+            return fail(FA_ERR_INVALID_ARG, "workspace_bytes is smaller than the workspace size");
+    } else {
+        lk.lock();
+        const char *force_fail = getenv("FA_TEST_FAIL_ALLOC");
+        if (force_fail && force_fail[0] == '1')
+            return fail(FA_ERR_NOMEM, "workspace allocation failed (forced by FA_TEST_FAIL_ALLOC)");
+        if (info->ws_bytes < need) {
+            if (info->ws) {
+                // hipFree waits for the device, so work still queued on
+                // any stream with the old buffer finishes first
+                (void)hipFree(info->ws);
+                info->ws = nullptr;
+                info->ws_bytes = 0;
+            }
+            void *p = nullptr;
+            hipError_t e = hipMalloc(&p, need);
+            if (e != hipSuccess || !p)
+                return fail(FA_ERR_NOMEM, std::string("workspace hipMalloc: ") + hipGetErrorString(e));
+            info->ws = p;
+            info->ws_bytes = need;
+        }
+        ws = info->ws;
+    }
+    const size_t n_rows = (size_t)L->B * L->Hq * L->Sq;
+    L->part_o = static_cast<float *>(ws);
+    L->part_lse = L->part_o + (size_t)num_splits * n_rows * L->D;
+    return FA_OK;
+}
+
+// ---- paged K/V cache ---------------------------------------------------------
+fa_status check_paged(int B, int Hq, int Hkv, int Sq, int D, int num_pages, int page_size,
+                      int max_pages)
+{
+    if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || D < 1 || num_pages < 1 || max_pages < 1)
+        return fail(FA_ERR_INVALID_ARG, "every dimension must be >= 1");
+    if (Hq % Hkv != 0) return fail(FA_ERR_INVALID_ARG, "Hq must be a multiple of Hkv");
+    if (page_size < 16 || (page_size & (page_size - 1)) != 0)
+        return fail(FA_ERR_INVALID_ARG, "page_size must be a power of two >= 16");
+    if (D != 64 && D != 128) return fail(FA_ERR_UNSUPPORTED, "head dim must be 64 or 128");
+    if ((int64_t)Sq * (Hq / Hkv) > fa::kDecodeRows)
+        return fail(FA_ERR_UNSUPPORTED,
+                    "the paged path serves at most 32 query rows per KV head (Sq * Hq / Hkv)");
+    // one page is addressed through 32-bit buffer byte offsets
+    if ((int64_t)page_size * Hkv * D * 2 >= (int64_t(1) << 31))
+        return fail(FA_ERR_UNSUPPORTED, "one cache page exceeds 2 GiB");
+    if ((int64_t)max_pages * page_size + Sq >= (int64_t(1) << 30) ||
+        (int64_t)B * max_pages >= (int64_t(1) << 31) || (int64_t)B * Hq * Sq >= (int64_t(1) << 30))
+        return fail(FA_ERR_UNSUPPORTED, "sizes beyond 32-bit indexing");
+    return FA_OK;
+}
+
+// Splits per sequence: each sequence's keys are cut into num_splits equal
+// ranges (multiples of the tile).  The lengths live on the device, so the
+// automatic count is sized for the table's capacity like the contiguous
+// decode, then raised until one range touches at most
+// kPagedMaxPagesPerSplit pages.
+fa_status make_paged_plan(int B, int Hkv, int page_size, int max_pages, int D, int num_splits,
+                          int cus, int Hq, int Sq, Plan *out)
+{
+    if (num_splits < 0) return fail(FA_ERR_INVALID_ARG, "num_splits must be >= 0");
+    if (cus <= 0) cus = 256;
+    const int64_t cap = (int64_t)max_pages * page_size;
+    const int max_splits = (int)((cap + fa::kDecodeBN - 1) / fa::kDecodeBN);
+    int ns = num_splits;
+    if (ns == 0) {
+        ns = env_int("FA_NUM_SPLITS", 0);
+        if (ns <= 0) {
+            const int64_t bg = (int64_t)B * Hkv;
+            int per_cu = std::min(8, (160 * 1024) / fa::decode_lds_bytes(D));
+            per_cu = std::max(1, env_int("FA_DECODE_WAVES_PER_CU", per_cu));
+            const int64_t want = ((int64_t)cus * per_cu + bg - 1) / bg;
+            const int64_t by_len = std::max<int64_t>(1, cap / (4 * fa::kDecodeBN));
+            ns = (int)std::max<int64_t>(1, std::min<int64_t>(want, by_len));
+        }
+    }
+    if (ns > max_splits) ns = max_splits;
+    auto pages_per_split = [&](int n) {
+        int64_t len = (cap + n - 1) / n;
+        len = (len + fa::kDecodeBN - 1) / fa::kDecodeBN * fa::kDecodeBN;
+        return (len + page_size - 1) / page_size + 1;
+    };
+    while (ns < max_splits && pages_per_split(ns) > fa::kPagedMaxPagesPerSplit) ++ns;
+    if (pages_per_split(ns) > fa::kPagedMaxPagesPerSplit)
+        return fail(FA_ERR_UNSUPPORTED, "page_size too small for one split's page-id registers");
+    Plan pl;
+    pl.path = 1;
+    pl.num_splits = ns;
+    pl.split_len = 0;   // per sequence, on the device
+    pl.block_m = fa::kDecodeRows;
+    pl.block_n = fa::kDecodeBN;
+    const int64_t items = (int64_t)B * Hkv * ns;
+    if (items >= (int64_t(1) << 31)) return fail(FA_ERR_UNSUPPORTED, "too many work items");
+    pl.items = (int)items;
+    pl.grid = pl.items;
+    pl.ws_bytes = split_ws_bytes(B, Hq, Sq, D, ns);
+    *out = pl;
+    return FA_OK;
+}
+
+int probed_cus()
+{
+    std::lock_guard<std::mutex> lk(g_mu);
+    int dev = 0;
+    if (hipGetDevice(&dev) == hipSuccess && dev < (int)g_dev.size() && g_dev[dev].probed)
+        return g_dev[dev].cus;
+    return 0;
+}
+
 }  // namespace
 
 extern "C" {
@@ -287,35 +404,9 @@ fa_status fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float 
     } else {
         std::unique_lock<std::mutex> lk(g_mu, std::defer_lock);
         if (pl.ws_bytes > 0) {
-            void *ws = workspace;
-            if (ws) {
-                if (workspace_bytes < pl.ws_bytes)
-                    return fail(FA_ERR_INVALID_ARG, "workspace_bytes is smaller than fa_workspace_size()");
-            } else {
-                lk.lock();
-                const char *force_fail = getenv("FA_TEST_FAIL_ALLOC");
-                if (force_fail && force_fail[0] == '1')
-                    return fail(FA_ERR_NOMEM, "workspace allocation failed (forced by FA_TEST_FAIL_ALLOC)");
-                if (info->ws_bytes < pl.ws_bytes) {
-                    if (info->ws) {
-                        // hipFree waits for the device, so work still queued on
-                        // any stream with the old buffer finishes first
-                        (void)hipFree(info->ws);
-                        info->ws = nullptr;
-                        info->ws_bytes = 0;
-                    }
-                    void *p = nullptr;
-                    e = hipMalloc(&p, pl.ws_bytes);
-                    if (e != hipSuccess || !p)
-                        return fail(FA_ERR_NOMEM, std::string("workspace hipMalloc: ") + hipGetErrorString(e));
-                    info->ws = p;
-                    info->ws_bytes = pl.ws_bytes;
-                }
-                ws = info->ws;
-            }
-            const size_t n_rows = (size_t)B * Hq * Sq;
-            L.part_o = static_cast<float *>(ws);
-            L.part_lse = L.part_o + (size_t)pl.num_splits * n_rows * D;
+            st = attach_workspace(info, workspace, workspace_bytes, pl.ws_bytes, pl.num_splits,
+                                  lk, &L);
+            if (st != FA_OK) return st;
         }
         e = fa::launch_decode(L);
     }
@@ -372,6 +463,102 @@ fa_status fa_plan(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal, int
     out->workspace_bytes = pl.ws_bytes;
     out->waves = pl.path == 0 ? pl.prefill_nw : 1;
     out->rows_per_wave = pl.path == 0 ? 32 * pl.prefill_nr : 0;
+    return FA_OK;
+}
+
+fa_status fa_fwd_paged(const void *q, const void *k_cache, const void *v_cache,
+                       const int *block_table, const int *seq_lens, void *o, float *lse, int B,
+                       int Hq, int Hkv, int Sq, int D, int num_pages, int page_size,
+                       int max_pages, int causal, float scale, hipStream_t stream,
+                       fa_dtype o_dtype, int num_splits, void *workspace, size_t workspace_bytes)
+{
+    g_last_error.clear();
+    if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !o)
+        return fail(FA_ERR_INVALID_ARG,
+                    "q, k_cache, v_cache, block_table, seq_lens and o must not be NULL");
+    fa_status st = check_paged(B, Hq, Hkv, Sq, D, num_pages, page_size, max_pages);
+    if (st != FA_OK) return st;
+    if (!isfinite(scale)) return fail(FA_ERR_INVALID_ARG, "scale must be finite");
+    if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "causal must be 0 or 1");
+    if (o_dtype != FA_DTYPE_BF16 && o_dtype != FA_DTYPE_F32)
+        return fail(FA_ERR_INVALID_ARG, "o_dtype must be FA_DTYPE_BF16 or FA_DTYPE_F32");
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) ||
+        (lse && !aligned16(lse)) || (workspace && !aligned16(workspace)))
+        return fail(FA_ERR_UNSUPPORTED,
+                    "q, k_cache, v_cache, o, lse and workspace must be 16-byte aligned");
+    if (((uintptr_t)block_table & 3u) || ((uintptr_t)seq_lens & 3u))
+        return fail(FA_ERR_UNSUPPORTED, "block_table and seq_lens must be 4-byte aligned");
+    if (num_splits < 0) return fail(FA_ERR_INVALID_ARG, "num_splits must be >= 0");
+    {
+        Plan pre;
+        st = make_paged_plan(B, Hkv, page_size, max_pages, D, num_splits, 0, Hq, Sq, &pre);
+        if (st != FA_OK) return st;
+    }
+
+    int dev = 0;
+    DeviceInfo *info = nullptr;
+    st = device_info(&dev, &info);
+    if (st != FA_OK) return st;
+    Plan pl;
+    st = make_paged_plan(B, Hkv, page_size, max_pages, D, num_splits, info->cus, Hq, Sq, &pl);
+    if (st != FA_OK) return st;
+
+    fa::Launch L;
+    L.q = q; L.k = k_cache; L.v = v_cache; L.o = o; L.lse = lse;
+    L.part_o = nullptr; L.part_lse = nullptr;
+    L.B = B; L.Hq = Hq; L.Hkv = Hkv; L.Sq = Sq; L.Sk = 0; L.D = D;
+    L.causal = causal;
+    L.o_f32 = (o_dtype == FA_DTYPE_F32);
+    L.scale = scale;
+    L.num_splits = pl.num_splits;
+    L.split_len = 0;
+    L.grid = pl.grid;
+    L.prefill_bn = L.prefill_nw = L.prefill_nr = 0;
+    L.head_major = 0;
+    L.stream = stream;
+    fa::PagedLaunch P;
+    P.table = block_table;
+    P.seq_lens = seq_lens;
+    P.num_pages = num_pages;
+    P.page_size = page_size;
+    P.max_pages = max_pages;
+
+    if (log_enabled())
+        fprintf(stderr,
+                "[fa] path=paged-decode B=%d Hq=%d Hkv=%d Sq=%d D=%d pages=%d page_size=%d "
+                "max_pages=%d causal=%d splits=%d grid=%d ws=%zu\n",
+                B, Hq, Hkv, Sq, D, num_pages, page_size, max_pages, causal, pl.num_splits,
+                pl.grid, pl.ws_bytes);
+
+    std::unique_lock<std::mutex> lk(g_mu, std::defer_lock);
+    if (pl.ws_bytes > 0) {
+        st = attach_workspace(info, workspace, workspace_bytes, pl.ws_bytes, pl.num_splits, lk, &L);
+        if (st != FA_OK) return st;
+    }
+    hipError_t e = fa::launch_decode_paged(L, P);
+    if (e != hipSuccess) return fail(FA_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
+    return FA_OK;
+}
+
+fa_status fa_plan_paged(int B, int Hq, int Hkv, int Sq, int D, int num_pages, int page_size,
+                        int max_pages, int num_splits, fa_plan_info *out)
+{
+    g_last_error.clear();
+    if (!out) return fail(FA_ERR_INVALID_ARG, "out must not be NULL");
+    fa_status st = check_paged(B, Hq, Hkv, Sq, D, num_pages, page_size, max_pages);
+    if (st != FA_OK) return st;
+    Plan pl;
+    st = make_paged_plan(B, Hkv, page_size, max_pages, D, num_splits, probed_cus(), Hq, Sq, &pl);
+    if (st != FA_OK) return st;
+    out->path = 2;
+    out->num_splits = pl.num_splits;
+    out->block_m = pl.block_m;
+    out->block_n = pl.block_n;
+    out->grid = pl.grid;
+    out->work_items = pl.items;
+    out->workspace_bytes = pl.ws_bytes;
+    out->waves = 1;
+    out->rows_per_wave = 0;
     return FA_OK;
 }
 

@@ -262,6 +262,102 @@ struct TileLoader {
     }
 };
 
+// The same copies out of a paged K/V cache: [pages][page_size][Hkv][D], with
+// one sequence's logical page p stored in cache page table[p].  page_size is
+// a power of two >= 16: a BN-key tile (BN = 32, starting at a multiple of 32)
+// lies in one page (PPT = 1, page_size >= BN) or covers PPT = BN / page_size
+// whole pages, each holding NQ / PPT of the tile's copy instructions.
+//
+// The page ids of the split's pages are loaded once per wave into VGPRs (lane
+// l of register r holds page p_first + 64 r + l) and read back with
+// v_readlane: no memory access in the key loop besides the copies, whose
+// vmcnt bookkeeping the ring relies on.  A page id outside [0, num_pages) and
+// rows at or beyond key_end get an empty byte range: they read as zeros, so a
+// bad table entry can give wrong numbers but no out-of-bounds access.
+template <int D, int BN, int PPT>
+struct PagedTileLoader {
+    static constexpr int CPR = D / 8;
+    static constexpr int RPI = 64 / CPR;
+    static constexpr int NQ = BN / RPI;
+    static constexpr int PER_WAVE = NQ;                // one wave per ring
+    static constexpr int TILE_BYTES = BN * D * 2;
+    static constexpr int R = kPagedIdRegs;
+    static_assert(PPT >= 1 && NQ % PPT == 0, "a page must hold whole copy instructions");
+
+    int pid[R];              // per lane: page ids of the split's pages
+    const uint16_t *kc, *vc; // caches, already offset to the KV head
+    long page_elems;         // elements per cache page (page_size * Hkv * D)
+    int p_first;             // first logical page of the split
+    int shift;               // log2(page_size)
+    int num_pages;
+    int key_end;             // keys at or beyond read as zero
+    int kstride_bytes;       // bytes between consecutive keys of a page
+
+    // Issue the page-id loads (vector loads; the first issue() waits for
+    // them).  table: the sequence's block-table row.  Keys [k_begin, k_end).
+    __device__ __forceinline__ void setup(const uint16_t *kcache, const uint16_t *vcache,
+                                          const int *table, int max_pages, int k_begin, int k_end,
+                                          int lg_page, int n_pages, long page_el, int kstride,
+                                          int lane)
+    {
+        kc = kcache;
+        vc = vcache;
+        page_elems = page_el;
+        shift = lg_page;
+        num_pages = n_pages;
+        key_end = k_end;
+        kstride_bytes = kstride;
+        p_first = k_begin >> lg_page;
+        // unconditional loads (no branch around them), clamped into the
+        // row: entries past the split's last page are loaded but never used
+        const int p_last = min(k_end > k_begin ? (k_end - 1) >> lg_page : p_first, max_pages - 1);
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            pid[r] = table[max(min(p_first + 64 * r + lane, p_last), 0)];
+    }
+
+    // One descriptor per page the tile touches (PPT of them: the tile's NQ
+    // copy instructions split evenly), based at that page.
+    __device__ __forceinline__ void issue(char *lds_k, char *lds_v, int key0, int, int lane) const
+    {
+        constexpr int QPP = NQ / PPT;                       // instructions per page
+#pragma unroll
+        for (int c = 0; c < PPT; ++c) {
+            const int r0 = key0 + c * QPP * RPI;            // uniform: first key of the page chunk
+            const int pg = r0 >> shift;
+            const int rel = pg - p_first;
+            // every register read back, then a scalar select: selecting the
+            // register first becomes a dynamically indexed array in scratch
+            int page = __builtin_amdgcn_readlane(pid[0], rel & 63);
+#pragma unroll
+            for (int r = 1; r < R; ++r) {
+                const int cand = __builtin_amdgcn_readlane(pid[r], rel & 63);
+                page = (rel >> 6) == r ? cand : page;
+            }
+            const int first = pg << shift;
+            const int rows = min(key_end - first, 1 << shift);
+            const bool ok = (unsigned)page < (unsigned)num_pages && rows > 0;
+            page = ok ? page : 0;
+            const uint32_t nbytes = ok ? (uint32_t)((rows - 1) * kstride_bytes + D * 2) : 0u;
+            const uint64_t ka = reinterpret_cast<uint64_t>(kc + page * page_elems);
+            const uint64_t va = reinterpret_cast<uint64_t>(vc + page * page_elems);
+            const u32x4_t kd = {(uint32_t)ka, (uint32_t)(ka >> 32) & 0xffffu, nbytes,
+                                (uint32_t)kBufferFlags};
+            const u32x4_t vd = {(uint32_t)va, (uint32_t)(va >> 32) & 0xffffu, nbytes,
+                                (uint32_t)kBufferFlags};
+            const int base = (key0 - first + lane / CPR) * kstride_bytes;
+#pragma unroll
+            for (int i = 0; i < QPP; ++i) {
+                const int q = c * QPP + i;
+                const int row = q * RPI + lane / CPR;       // tile-relative row
+                const int voff = base + q * RPI * kstride_bytes +
+                                 (((lane % CPR) ^ swz<D>(row)) * 16);
+                lds_dma16_pair<true>(lds_k + q * 1024, lds_v + q * 1024, voff, kd, vd);
+            }
+        }
+    }
+};
+
 // Per-lane LDS byte offsets (relative to a tile) of the operand reads.
 //   K (A operand of S^T = K Q^T): lane (col, half) at k-step st reads the 16
 //     bytes of head dims 16*st + 8*half .. +7 of key kb*32 + col.
@@ -422,16 +518,16 @@ __device__ __forceinline__ void wait_tiles_ahead(int ahead)
 // One step of the split-key decode loop over an S-stage LDS ring: tile n sits
 // in stage `st` (= n % S); tiles n + 1 .. n + S - 2 may still be in flight;
 // the copies of tile n + S - 1 start into the stage tile n - 1 used.
-template <int D, int BN, int S>
+template <int D, int BN, int S, class LD>
 __device__ __forceinline__ void decode_step(
-    int n, int n_tiles, int key_base, char *lds, int st, const TileLoader<D, BN, 1, true> &ld,
+    int n, int n_tiles, int key_base, char *lds, int st, const LD &ld,
     int lane, int key_end, int wmin_lim, const OperandOffsets<D> &off,
     const bf16x8_t (&qf)[D / 16], f32x16_t (&o)[D / 32], float &m_ref, float &l_run,
     float &l_rnd, float c, int half, int lim_lane)
 {
-    constexpr int TB = TileLoader<D, BN, 1, true>::TILE_BYTES;
+    constexpr int TB = LD::TILE_BYTES;
     constexpr int STAGE = 2 * TB;
-    constexpr int LPT = 2 * TileLoader<D, BN, 1, true>::PER_WAVE;
+    constexpr int LPT = 2 * LD::PER_WAVE;
     const int ahead = min(S - 2, n_tiles - 1 - n);
     wait_tiles_ahead<LPT, S - 2>(ahead);
     // one wave: orders its LDS reads of tile n - 1 before the copies below
@@ -1571,13 +1667,113 @@ fa_decode_split_kernel(const Params p)
         if (u < n_tiles) ld.issue(lds + u * STAGE, lds + u * STAGE + TB, k_begin + u * BN, 0, lane);
     load_q<D>(qf, p.q + (((long)b * p.Sq + qi) * p.Hq + hq) * D, half);
     flip_q<D>(qf, p.qflip);
+    // Q has landed, and with it every copy issued before it.  Saying so
+    // explicitly clears the compiler's record of loads in flight; without it
+    // the compiler kept one path's Q loads pending and put a vmcnt(0) at the
+    // top of the key loop, draining the ring once per trip.
+    wait_vmem();
     // S tiles per trip keep every stage offset a compile-time constant
     for (int n = 0; n < n_tiles; n += S) {
 #pragma unroll
         for (int u = 0; u < S; ++u)
             if (n + u < n_tiles)
-                decode_step<D, BN, S>(n + u, n_tiles, k_begin, lds, u, ld, lane, k_end, wmin_lim,
+                decode_step<D, BN, S, TL>(n + u, n_tiles, k_begin, lds, u, ld, lane, k_end, wmin_lim,
                                       off, qf, o, m_ref, l_run, l_rnd, p.c, half, lim_lane);
+    }
+
+    const float l_norm = add_halves(l_rnd);
+    if (p.num_splits == 1) {
+        finish_rows<D, OUT_F32>(o, m_ref, l_run, l_norm, p.c, half, p.o,
+                                (((long)b * p.Sq + qi) * p.Hq + hq) * D,
+                                p.lse ? p.lse + ((long)b * p.Hq + hq) * p.Sq + qi : nullptr, valid);
+    } else {
+        const long prow = (((long)s * p.B + b) * p.Hq + hq) * p.Sq + qi;
+        finish_rows<D, true>(o, m_ref, l_run, l_norm, p.c, half, p.part_o, prow * D,
+                             p.part_lse + prow, valid);
+    }
+#endif
+}
+
+// ---------------------------------------------------------------------------
+// Split-key decode over a paged K/V cache (PagedTileLoader): as
+// fa_decode_split_kernel, except that sequence b has its own length
+// seq_lens[b] (clamped to [0, max_pages * page_size]) and its own causal
+// offset, and its keys are cut into num_splits equal ranges, multiples of the
+// tile, so that every split of a sequence streams about the same bytes.
+// Splits past the end of a short sequence write an empty partial (O_s = 0,
+// LSE_s = -inf), which the merge weighs 0.
+// ---------------------------------------------------------------------------
+struct PagedParams {
+    const int *table;        // [B][max_pages]
+    const int *seq_lens;     // [B]
+    int max_pages, num_pages, lg_page;
+};
+
+template <int D, bool OUT_F32, int PPT>
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
+fa_decode_paged_kernel(const Params p, const PagedParams pp)
+{
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
+    constexpr int BN = kDecodeBN;
+    using TL = PagedTileLoader<D, BN, PPT>;
+    constexpr int TB = TL::TILE_BYTES;
+    constexpr int STAGE = 2 * TB;
+
+    constexpr int S = kDecodeStages;
+    __shared__ __attribute__((aligned(1024))) char lds[S * STAGE];
+
+    const int lane = threadIdx.x;
+    const int col = lane & 31;
+    const int half = lane >> 5;
+
+    OperandOffsets<D> off;
+    off.init(lane);
+
+    const int item = blockIdx.x;
+    const int s = item % p.num_splits;
+    const int bg = item / p.num_splits;
+    const int b = bg / p.Hkv;
+    const int g = bg % p.Hkv;
+
+    const int rows = p.Sq * p.group;
+    const bool valid = col < rows;
+    const int qi = valid ? col / p.group : 0;
+    const int hq = g * p.group + (valid ? col % p.group : 0);
+
+    const int sk = min(max(pp.seq_lens[b], 0), pp.max_pages << pp.lg_page);
+    int len = (sk + p.num_splits - 1) / p.num_splits;
+    len = (len + BN - 1) / BN * BN;
+    const int k_begin = min(s * len, sk);
+    const int k_end = min(k_begin + len, sk);
+    const int n_tiles = (k_end - k_begin + BN - 1) / BN;
+
+    TL ld;
+    ld.setup(p.k + g * D, p.v + g * D, pp.table + (long)b * pp.max_pages, pp.max_pages, k_begin, k_end,
+             pp.lg_page, pp.num_pages, ((long)p.Hkv * D) << pp.lg_page, p.Hkv * D * 2, lane);
+
+    bf16x8_t qf[D / 16];
+    f32x16_t o[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) o[db] = f32x16_t{};
+    float m_ref = kNegInf, l_run = 0.0f, l_rnd = 0.0f;
+
+    const int offk = sk - p.Sq;
+    const int lim_lane = p.causal ? qi + offk : 0x7fffffff;
+    const int wmin_lim = p.causal ? offk : 0x7fffffff;
+
+#pragma unroll
+    for (int u = 0; u < S - 1; ++u)
+        if (u < n_tiles) ld.issue(lds + u * STAGE, lds + u * STAGE + TB, k_begin + u * BN, 0, lane);
+    load_q<D>(qf, p.q + (((long)b * p.Sq + qi) * p.Hq + hq) * D, half);
+    flip_q<D>(qf, p.qflip);
+    wait_vmem();   // as in fa_decode_split_kernel: no ring drain per trip
+    for (int n = 0; n < n_tiles; n += S) {
+#pragma unroll
+        for (int u = 0; u < S; ++u)
+            if (n + u < n_tiles)
+                decode_step<D, BN, S, TL>(n + u, n_tiles, k_begin, lds, u, ld, lane, k_end,
+                                          wmin_lim, off, qf, o, m_ref, l_run, l_rnd, p.c, half,
+                                          lim_lane);
     }
 
     const float l_norm = add_halves(l_rnd);
@@ -1744,6 +1940,23 @@ hipError_t launch_prefill(const Launch &L)
     return hipGetLastError();
 }
 
+static hipError_t launch_merge(const Launch &L, const Params &p)
+{
+    dim3 gm((unsigned)((long)L.B * L.Hq * L.Sq)), blk(64);
+    if (L.D == 128) {
+        if (L.o_f32)
+            hipLaunchKernelGGL((fa_merge_kernel<128, true>), gm, blk, 0, L.stream, p);
+        else
+            hipLaunchKernelGGL((fa_merge_kernel<128, false>), gm, blk, 0, L.stream, p);
+    } else {
+        if (L.o_f32)
+            hipLaunchKernelGGL((fa_merge_kernel<64, true>), gm, blk, 0, L.stream, p);
+        else
+            hipLaunchKernelGGL((fa_merge_kernel<64, false>), gm, blk, 0, L.stream, p);
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_decode(const Launch &L)
 {
     Params p = make_params(L);
@@ -1761,19 +1974,45 @@ hipError_t launch_decode(const Launch &L)
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || L.num_splits == 1) return e;
-    dim3 gm((unsigned)((long)L.B * L.Hq * L.Sq));
+    return launch_merge(L, p);
+}
+
+template <int PPT>
+static void launch_paged_cfg(const Launch &L, const Params &p, const PagedParams &pp, dim3 g)
+{
+    dim3 blk(64);
     if (L.D == 128) {
         if (L.o_f32)
-            hipLaunchKernelGGL((fa_merge_kernel<128, true>), gm, blk, 0, L.stream, p);
+            hipLaunchKernelGGL((fa_decode_paged_kernel<128, true, PPT>), g, blk, 0, L.stream, p, pp);
         else
-            hipLaunchKernelGGL((fa_merge_kernel<128, false>), gm, blk, 0, L.stream, p);
+            hipLaunchKernelGGL((fa_decode_paged_kernel<128, false, PPT>), g, blk, 0, L.stream, p, pp);
     } else {
         if (L.o_f32)
-            hipLaunchKernelGGL((fa_merge_kernel<64, true>), gm, blk, 0, L.stream, p);
+            hipLaunchKernelGGL((fa_decode_paged_kernel<64, true, PPT>), g, blk, 0, L.stream, p, pp);
         else
-            hipLaunchKernelGGL((fa_merge_kernel<64, false>), gm, blk, 0, L.stream, p);
+            hipLaunchKernelGGL((fa_decode_paged_kernel<64, false, PPT>), g, blk, 0, L.stream, p, pp);
     }
-    return hipGetLastError();
+}
+
+hipError_t launch_decode_paged(const Launch &L, const PagedLaunch &P)
+{
+    Params p = make_params(L);
+    PagedParams pp;
+    pp.table = P.table;
+    pp.seq_lens = P.seq_lens;
+    pp.max_pages = P.max_pages;
+    pp.num_pages = P.num_pages;
+    pp.lg_page = 0;
+    while ((1 << pp.lg_page) < P.page_size) ++pp.lg_page;
+    dim3 g(L.B * L.Hkv * L.num_splits);
+    // pages per 32-key tile: 1, or 2 for 16-key pages
+    if (P.page_size >= kDecodeBN)
+        launch_paged_cfg<1>(L, p, pp, g);
+    else
+        launch_paged_cfg<kDecodeBN / 16>(L, p, pp, g);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || L.num_splits == 1) return e;
+    return launch_merge(L, p);
 }
 
 }  // namespace fa

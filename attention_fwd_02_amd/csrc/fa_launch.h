@@ -23,6 +23,10 @@ constexpr int kDecodeRows = 32;
 #endif
 constexpr int kDecodeStages = FA_DECODE_STAGES;
 inline int decode_lds_bytes(int D) { return kDecodeStages * 2 * kDecodeBN * D * 2; }
+// Paged decode: a wave keeps the page ids of its key range in this many
+// VGPRs (64 pages each), which bounds the pages one split may touch.
+constexpr int kPagedIdRegs = 4;
+constexpr int kPagedMaxPagesPerSplit = 64 * kPagedIdRegs;
 
 struct Launch {
     const void *q, *k, *v;
@@ -46,5 +50,14 @@ struct Launch {
 
 hipError_t launch_prefill(const Launch &L);
 hipError_t launch_decode(const Launch &L);  // split kernel, then the merge pass if splits > 1
+
+// Paged K/V cache: L.k / L.v are the caches [num_pages][page_size][Hkv][D];
+// L.Sk is unused.
+struct PagedLaunch {
+    const int *table;     // [B][max_pages] device
+    const int *seq_lens;  // [B] device
+    int num_pages, page_size, max_pages;
+};
+hipError_t launch_decode_paged(const Launch &L, const PagedLaunch &P);
 
 }  // namespace fa

@@ -116,7 +116,8 @@ size_t fa_workspace_size(int B, int Hq, int Hkv, int Sq, int Sk, int D, int num_
  * Fills *out; returns FA_ERR_INVALID_ARG / FA_ERR_UNSUPPORTED as fa_fwd_ex would.
  */
 typedef struct {
-    int path;            /* 0 = prefill (single pass), 1 = split-key decode + merge */
+    int path;            /* 0 = prefill (single pass), 1 = split-key decode + merge,
+                            2 = paged split-key decode + merge (fa_plan_paged)    */
     int num_splits;      /* 1 for the prefill path                                */
     int block_m;         /* query rows per workgroup tile                          */
     int block_n;         /* keys per K/V tile                                      */
@@ -131,6 +132,51 @@ typedef struct {
 
 fa_status fa_plan(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal, int num_splits,
                   fa_plan_info *out);
+
+/*
+ * fa_fwd_paged -- the same attention forward over a paged K/V cache, with a
+ * key count per sequence (decode, and short multi-token queries).
+ *
+ * The pages list paged K/V only as a loading mode of the SM80 and SM90
+ * kernels ("SM80 内核实现对比", section 7.3, the PagedKV row: both fetch it
+ * with cp.async); the layout and the meaning below are this library's:
+ *
+ *   q, o         [B][Sq][Hq][D] as for fa_fwd (o bf16 or f32 per o_dtype);
+ *                lse [B][Hq][Sq] float32 or NULL
+ *   k_cache,     [num_pages][page_size][Hkv][D] bf16, device: num_pages
+ *   v_cache      pages of page_size keys each
+ *   block_table  [B][max_pages] int32, device: key j of sequence b is slot
+ *                j % page_size of cache page block_table[b][j / page_size]
+ *   seq_lens     [B] int32, device: Sk_b, the keys of sequence b; read by the
+ *                kernels (no host synchronisation) and clamped to
+ *                [0, max_pages * page_size]
+ *
+ * Sequence b is then exactly fa_fwd over its first Sk_b keys: causal allows
+ * key j for query i iff j <= i + Sk_b - Sq, and a row with no allowed key
+ * (Sk_b = 0, say) gets O = 0 and LSE = -inf.
+ *
+ * page_size: a power of two >= 16.  Sq * Hq / Hkv <= 32 (the split-key
+ * decode's tile), else FA_ERR_UNSUPPORTED.  num_splits: 0 = automatic, else
+ * each sequence's keys are cut into num_splits equal ranges (multiples of 32
+ * keys); it is raised if needed so that one range spans at most 256 pages.
+ * workspace / workspace_bytes: as for fa_fwd_ex, sized by fa_plan_paged's
+ * workspace_bytes.  Only block-table entries of pages below Sk_b are read.
+ * An entry outside [0, num_pages) reads as zero keys and values: results for
+ * that sequence are then meaningless, but no memory outside the caches is
+ * touched.
+ */
+fa_status fa_fwd_paged(const void *q, const void *k_cache, const void *v_cache,
+                       const int *block_table, const int *seq_lens, void *o, float *lse, int B,
+                       int Hq, int Hkv, int Sq, int D, int num_pages, int page_size,
+                       int max_pages, int causal, float scale, hipStream_t stream,
+                       fa_dtype o_dtype, int num_splits, void *workspace, size_t workspace_bytes);
+
+/*
+ * fa_plan_paged -- the launch fa_fwd_paged would make (path 2): splits per
+ * sequence, grid, workspace bytes.  Pure host arithmetic, like fa_plan.
+ */
+fa_status fa_plan_paged(int B, int Hq, int Hkv, int Sq, int D, int num_pages, int page_size,
+                        int max_pages, int num_splits, fa_plan_info *out);
 
 /* fa_last_error -- message for the last non-OK status of this host thread
  * ("" if none).  The pointer stays valid until the next call on this thread. */

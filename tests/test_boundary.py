@@ -148,3 +148,46 @@ def test_product_path_never_touches_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(import|from)\s+oracle", text, re.M), f
                 assert "oracle.c" not in text and "liboracle" not in text, f
+
+
+def call_paged(b, q=P, kc=P, vc=P, table=P, lens=P, o=P, lse=None, B=2, Hq=8, Hkv=2, Sq=1, D=128,
+               num_pages=64, page_size=16, max_pages=32, causal=0, scale=0.125, o_dtype=0,
+               num_splits=0, ws=None, ws_bytes=0):
+    st = b.lib.fa_fwd_paged(q, kc, vc, table, lens, o, lse, B, Hq, Hkv, Sq, D, num_pages,
+                            page_size, max_pages, causal, scale, None, o_dtype, num_splits, ws,
+                            ws_bytes)
+    return st, b.fa_last_error()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(kc=None), 1), (dict(vc=None), 1), (dict(table=None), 1),
+    (dict(lens=None), 1), (dict(o=None), 1),
+    (dict(B=0), 1), (dict(num_pages=0), 1), (dict(max_pages=0), 1), (dict(Hq=6, Hkv=4), 1),
+    (dict(page_size=24), 1), (dict(page_size=8), 1), (dict(page_size=0), 1),
+    (dict(scale=math.nan), 1), (dict(causal=3), 1), (dict(o_dtype=5), 1),
+    (dict(num_splits=-2), 1),
+    (dict(D=96), 2), (dict(Sq=9), 2), (dict(Hq=64, Hkv=1), 2),
+    (dict(q=P + 2), 2), (dict(kc=P + 8), 2), (dict(table=P + 2), 2), (dict(lens=P + 1), 2),
+    (dict(page_size=1 << 20, Hkv=8), 2),           # one page over 2 GiB
+])
+def test_paged_bad_arguments_rejected_before_any_hip_call(b, kw, status):
+    st, msg = call_paged(b, **kw)
+    assert st == status, (st, msg)
+    assert msg
+
+
+def test_paged_plan_host_arithmetic(b):
+    # the paged decode workload: 256 (b, g) pairs x 3 splits, like the
+    # contiguous decode; partials [splits][B][Hq][Sq][D+1] fp32
+    p = b.fa_plan_paged(32, 32, 8, 1, 128, 16384, 16, 512, 0)
+    assert p["path"] == 2 and p["num_splits"] == 3 and p["grid"] == 32 * 8 * 3
+    assert p["workspace_bytes"] == 3 * 32 * 32 * 129 * 4
+    # capacity 16384 keys in 16-key pages: one split may span at most 256
+    # pages, so at least 5 splits (3277 -> 3296 keys = 206 + 1 pages)
+    p = b.fa_plan_paged(32, 32, 8, 1, 128, 32768, 16, 1024, 0)
+    assert p["num_splits"] == 5
+    assert b.fa_plan_paged(1, 8, 2, 1, 128, 1024, 16, 256, 1)["num_splits"] == 2
+    # bigger pages lift the bound; forced counts are honoured
+    assert b.fa_plan_paged(1, 8, 2, 1, 128, 1024, 256, 64, 1)["num_splits"] == 1
+    assert b.fa_plan_paged(1, 8, 2, 1, 128, 1024, 256, 64, 7)["num_splits"] == 7
+    assert b.fa_plan_paged(1, 8, 2, 1, 128, 1024, 16, 2, 64)["num_splits"] == 1
