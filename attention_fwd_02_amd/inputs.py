@@ -143,6 +143,17 @@ class PagedWorkload:
     def max_pages(self) -> int:
         return (self.max_len + self.page_size - 1) // self.page_size
 
+    def hbm_bytes(self, seq_lens) -> int:
+        """Algorithmic bytes: every sequence's K and V rows, Q, the block-table
+        entries of its pages and its length read once; O and LSE written once."""
+        lens = [int(x) for x in seq_lens]
+        kv = 2 * sum(lens) * self.Hkv * self.D * 2
+        q = self.B * self.Sq * self.Hq * self.D * 2
+        o = self.B * self.Sq * self.Hq * self.D * (4 if self.o_dtype == "f32" else 2)
+        lse = self.B * self.Hq * self.Sq * 4
+        table = 4 * sum((n + self.page_size - 1) // self.page_size for n in lens) + 4 * self.B
+        return kv + q + o + lse + table
+
 
 PAGED_WORKLOADS = {
     w.name: w for w in [

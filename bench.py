@@ -6,15 +6,19 @@ in HBM:
   * the compute-bound causal prefill, B=4, Hq=Hkv=16, Sq=Sk=4096, D=128, bf16
     (one fa_fwd call: the persistent prefill kernel), and
   * the memory-bound decode, B=32, Hq=32, Hkv=8, Sq=1, Sk=8192, D=128, bf16
-    (one fa_fwd call: the split-key kernel and the log-sum-exp merge).
+    (one fa_fwd call: the split-key kernel and the log-sum-exp merge), and
+  * the same decode over a paged K/V cache (16-key pages scattered over the
+    cache): every sequence at 8192 keys, then lengths drawn from [1, 16384]
+    (one fa_fwd_paged call each: paged split kernel and merge).
 Both go to the same stream; HIP events recorded on that stream around each
 call give the per-call durations.
 
 Printed: one JSON line.  `value` is the prefill's algorithmic TFLOP/s (4*D
 flops per allowed query-key pair); `decode` holds the decode's algorithmic
-GB/s (Q, K, V read once, O and LSE written once).  `roofline` is the prefill
-kernel against the dense bf16 MFMA peak; `decode.roofline` the decode call
-against HBM.  `cpu_baseline` times the fp64 oracle on a bounded sample of the
+GB/s (Q, K, V read once, O and LSE written once), `paged_decode` and
+`paged_decode_ragged` the paged calls' (plus the block-table entries read).
+`roofline` is the prefill kernel against the dense bf16 MFMA peak; the decode
+entries' `roofline` their call against HBM.  `cpu_baseline` times the fp64 oracle on a bounded sample of the
 prefill workload's rows and also compares those rows with the timed output.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
@@ -42,6 +46,8 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA (datasheet)
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E (datasheet)
 PREFILL = "causal_b4_h16_s4096_d128"
 DECODE = "decode_b32_hq32_hkv8_sk8192_d128"
+PAGED = "paged_decode_b32_hq32_hkv8_len8192_ps16_d128"
+PAGED_RAGGED = "paged_decode_b32_hq32_hkv8_ragged16384_ps16_d128"
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 KERNEL_SRC = os.path.join(ROOT, "attention_fwd_02_amd", "csrc", "fa_kernels.hip")
 
@@ -125,12 +131,20 @@ def profile_one(args):
     from attention_fwd_02_amd import _binding as fa
     from attention_fwd_02_amd.inputs import WORKLOADS, make_inputs
     dev = "cuda:0"
+    from attention_fwd_02_amd.inputs import PAGED_WORKLOADS, make_paged_inputs
     if args.profile_kernel == "copy":
         n = 1 << 30
         x = torch.empty(n // 2, dtype=torch.bfloat16, device=dev).fill_(1.0)
         y = torch.empty_like(x)
         fn = lambda: y.copy_(x)  # noqa: E731
         label = f"copy of {n} bytes"
+    elif args.profile_kernel in ("paged", "paged_ragged"):
+        w = PAGED_WORKLOADS[PAGED if args.profile_kernel == "paged" else PAGED_RAGGED]
+        q, kc, vc, table, lens = (t.to(dev) for t in make_paged_inputs(w))
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=dev)
+        fn = lambda: fa.fa_fwd_paged(q, kc, vc, table, lens, o, lse, w.causal, w.scale)  # noqa: E731
+        label = w.name
     else:
         w = WORKLOADS[PREFILL if args.profile_kernel == "prefill" else DECODE]
         q, k, v = (t.to(dev) for t in make_inputs(w))
@@ -152,7 +166,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--cpu-seconds", type=float, default=25.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--profile-kernel", choices=["prefill", "decode", "copy"],
+    ap.add_argument("--profile-kernel",
+                    choices=["prefill", "decode", "paged", "paged_ragged", "copy"],
                     help="run only this call (warmup + steps) for counter collection; "
                          "'copy' is a plain 1 GiB device-to-device copy that calibrates "
                          "the HBM byte counters")
@@ -164,7 +179,8 @@ def main():
 
     import torch
     from attention_fwd_02_amd import _binding as fa
-    from attention_fwd_02_amd.inputs import WORKLOADS, make_inputs
+    from attention_fwd_02_amd.inputs import (PAGED_WORKLOADS, WORKLOADS, make_inputs,
+                                             make_paged_inputs)
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
@@ -179,6 +195,14 @@ def main():
     od = torch.empty_like(qd)
     ld = torch.empty((wd.B, wd.Hq, wd.Sq), dtype=torch.float32, device=dev)
 
+    paged = {}
+    for key in (PAGED, PAGED_RAGGED):
+        w = PAGED_WORKLOADS[key]
+        q, kc, vc, table, lens = make_paged_inputs(w)
+        paged[key] = (w, lens.tolist(), tuple(t.to(dev) for t in (q, kc, vc, table, lens)),
+                      torch.empty((w.B, w.Sq, w.Hq, w.D), dtype=torch.bfloat16, device=dev),
+                      torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=dev))
+
     stream = torch.cuda.current_stream()
 
     def prefill():
@@ -187,22 +211,30 @@ def main():
     def decode():
         fa.fa_fwd(qd, kd, vd, od, ld, wd.causal, wd.scale, stream=stream)
 
+    def paged_call(key):
+        w, _, (q, kc, vc, table, lens), o, lse = paged[key]
+        fa.fa_fwd_paged(q, kc, vc, table, lens, o, lse, w.causal, w.scale, stream=stream)
+
+    def step(evs=None):
+        calls = (prefill, decode, lambda: paged_call(PAGED), lambda: paged_call(PAGED_RAGGED))
+        for i, call in enumerate(calls):
+            if evs:
+                evs[i].record(stream)
+            call()
+        if evs:
+            evs[len(calls)].record(stream)
+
     for _ in range(args.warmup):
-        prefill()
-        decode()
+        step()
     torch.cuda.synchronize()
 
     K = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
     for s in range(K):
-        evs[s][0].record(stream)
-        prefill()
-        evs[s][1].record(stream)
-        decode()
-        evs[s][2].record(stream)
+        step(evs[s])
     stop.record(stream)
     torch.cuda.synchronize()
 
@@ -211,6 +243,24 @@ def main():
     d_ms = sorted(e[1].elapsed_time(e[2]) for e in evs)
     p_avg = sum(p_ms) / K
     d_avg = sum(d_ms) / K
+
+    def paged_entry(key, i):
+        w, lens, (_, kc, _, table, _), _, _ = paged[key]
+        ms = sorted(e[i].elapsed_time(e[i + 1]) for e in evs)
+        avg = sum(ms) / K
+        nbytes = w.hbm_bytes(lens)
+        gb = nbytes / (avg * 1e-3) / 1e9
+        return {
+            "workload": key, "value": round(gb, 1), "unit": "GB/s",
+            "config": {"B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Sq": w.Sq, "D": w.D,
+                       "page_size": w.page_size, "max_len": w.max_len, "lengths": w.lengths,
+                       "total_keys": sum(lens), "algorithmic_bytes": nbytes,
+                       "plan": fa.fa_plan_paged(w.B, w.Hq, w.Hkv, w.Sq, w.D, kc.shape[0],
+                                                w.page_size, table.shape[1], 0)},
+            "ms": {"avg": round(avg, 4), "median": round(ms[K // 2], 4), "min": round(ms[0], 4)},
+            "roofline": roofline(gb, PEAK_HBM_GBPS, "GB/s", "hbm",
+                                 measured_traffic("paged" if key == PAGED else "paged_ragged")),
+        }
 
     flops = wp.flops()
     tflops = flops / (p_avg * 1e-3) / 1e12
@@ -236,7 +286,9 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": (f"{PREFILL} (causal prefill B=4 Hq=Hkv=16 Sq=Sk=4096 D=128) + "
-                         f"{DECODE} (decode B=32 Hq=32 Hkv=8 Sq=1 Sk=8192 D=128)"),
+                         f"{DECODE} (decode B=32 Hq=32 Hkv=8 Sq=1 Sk=8192 D=128) + "
+                         f"{PAGED} and {PAGED_RAGGED} (the decode over 16-key pages; "
+                         "8192 keys each, then lengths drawn from [1, 16384])"),
             "prefill": {"B": wp.B, "Hq": wp.Hq, "Hkv": wp.Hkv, "Sq": wp.Sq, "Sk": wp.Sk,
                         "D": wp.D, "causal": wp.causal, "algorithmic_flops": flops,
                         "plan": plan_p},
@@ -255,6 +307,8 @@ def main():
             "roofline": roofline(gbps, PEAK_HBM_GBPS, "GB/s", "hbm",
                                  measured_traffic("decode")),
         },
+        "paged_decode": paged_entry(PAGED, 2),
+        "paged_decode_ragged": paged_entry(PAGED_RAGGED, 3),
         "roofline": roofline(tflops, PEAK_BF16_TFLOPS, "TFLOP/s", "mfma",
                              measured_traffic("prefill")),
         "cpu_baseline": None,
