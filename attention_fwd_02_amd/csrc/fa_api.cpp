@@ -91,7 +91,8 @@ fa_status check_sizes(int B, int Hq, int Hkv, int Sq, int Sk, int D)
     if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Sk < 1 || D < 1)
         return fail(FA_ERR_INVALID_ARG, "every dimension must be >= 1");
     if (Hq % Hkv != 0) return fail(FA_ERR_INVALID_ARG, "Hq must be a multiple of Hkv");
-    if (D != 64 && D != 128) return fail(FA_ERR_UNSUPPORTED, "head dim must be 64 or 128");
+    if (D != 64 && D != 128 && D != 256)
+        return fail(FA_ERR_UNSUPPORTED, "head dim must be 64, 128 or 256");
     const int64_t q_elems = (int64_t)B * Sq * Hq * D;
     const int64_t k_elems = (int64_t)B * Sk * Hkv * D;
     if (q_elems >= (int64_t(1) << 40) || k_elems >= (int64_t(1) << 40))
@@ -173,7 +174,13 @@ fa_status make_plan(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal, i
         // override (for measurements).
         int bn = 64, nw = 8, nr = 1;
         const int64_t m8 = (Sq + 255) / 256;
-        if ((int64_t)B * Hq * m8 < cus) {
+        if (D == 256) {
+            // 32-key tiles (16 KiB per tile at D = 256: the three-stage ring
+            // takes 96 KiB), 4 waves x 32 rows, one wave per SIMD (Q and O
+            // alone take 192 registers per lane: two waves per SIMD spill)
+            bn = 32;
+            nw = 4;
+        } else if ((int64_t)B * Hq * m8 < cus) {
             nw = 4;
             bn = 32;
         } else if (!causal || Sq >= 2048) {
@@ -265,7 +272,8 @@ fa_status check_paged(int B, int Hq, int Hkv, int Sq, int D, int num_pages, int 
     if (Hq % Hkv != 0) return fail(FA_ERR_INVALID_ARG, "Hq must be a multiple of Hkv");
     if (page_size < 16 || (page_size & (page_size - 1)) != 0)
         return fail(FA_ERR_INVALID_ARG, "page_size must be a power of two >= 16");
-    if (D != 64 && D != 128) return fail(FA_ERR_UNSUPPORTED, "head dim must be 64 or 128");
+    if (D != 64 && D != 128 && D != 256)
+        return fail(FA_ERR_UNSUPPORTED, "head dim must be 64, 128 or 256");
     if ((int64_t)Sq * (Hq / Hkv) > fa::kDecodeRows)
         return fail(FA_ERR_UNSUPPORTED,
                     "the paged path serves at most 32 query rows per KV head (Sq * Hq / Hkv)");

@@ -49,6 +49,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fa_launch.h"
 
 namespace fa {
@@ -150,6 +152,9 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 // 16-byte chunk c of row r sits at chunk c ^ swz(r).  Bits ri of the row:
 //   D = 128 (16 chunks): swz = r0<<3 | r1<<2 | (r0^r2)<<1 | (r2^r3)
 //   D =  64 ( 8 chunks): swz = r1<<2 | (r0^r2)<<1 | (r0^r3)
+//   D = 256 (32 chunks): as D = 128.  A row is 512 bytes, twice the 64 banks'
+//     width, so a chunk's bank depends on its index mod 16 only, which the
+//     D = 128 pattern already permutes conflict-free.
 // Any 16 consecutive rows at one chunk (the K read) and any 4 rows starting at
 // a multiple of 4 over an aligned block of 4 chunks (the V transposing read)
 // land on distinct banks.
@@ -158,7 +163,7 @@ template <int D>
 __device__ __forceinline__ int swz(int r)
 {
     const int r0 = r & 1, r1 = (r >> 1) & 1, r2 = (r >> 2) & 1, r3 = (r >> 3) & 1;
-    if (D == 128) return (r0 << 3) | (r1 << 2) | ((r0 ^ r2) << 1) | (r2 ^ r3);
+    if (D >= 128) return (r0 << 3) | (r1 << 2) | ((r0 ^ r2) << 1) | (r2 ^ r3);
     return (r1 << 2) | ((r0 ^ r2) << 1) | (r0 ^ r3);
 }
 
@@ -366,21 +371,38 @@ struct PagedTileLoader {
 //     key row k0 + j; the instruction hands lane 4s + e element e of those
 //     four rows, i.e. 4 consecutive keys of one head dim.
 template <int D>
+//   The swizzle permutes chunk indices mod 16 only, so at D = 256 the second
+//   256 bytes of a row repeat the first half's offsets + 256: only the first
+//   16 chunks' offsets are kept in registers (kofs / vofs add the rest as an
+//   immediate).
 struct OperandOffsets {
     static constexpr int QS = D / 16;
     static constexpr int DB = D / 32;
-    int k[QS];           // + kb * 32 rows
-    int v[DB][2];        // [d block][second group of 4 keys]; + ps * 16 rows
+    static constexpr int NK = QS < 8 ? QS : 8;     // k-steps within the first 256 bytes
+    static constexpr int NV = DB < 4 ? DB : 4;     // d blocks within the first 256 bytes
+    int k[NK];           // + kb * 32 rows
+    int v[NV][2];        // [d block][second group of 4 keys]; + ps * 16 rows
+
+    __device__ __forceinline__ int kofs(int st) const
+    {
+        if constexpr (NK == QS) return k[st];
+        else return k[st % NK] + (st / NK) * 256;
+    }
+    __device__ __forceinline__ int vofs(int db, int sec) const
+    {
+        if constexpr (NV == DB) return v[db][sec];
+        else return v[db % NV][sec] + (db / NV) * 256;
+    }
 
     __device__ __forceinline__ void init(int lane)
     {
         const int col = lane & 31, half = lane >> 5;
 #pragma unroll
-        for (int st = 0; st < QS; ++st)
+        for (int st = 0; st < NK; ++st)
             k[st] = col * (2 * D) + (((2 * st + half) ^ swz<D>(col)) * 16);
         const int li = lane & 15, g = (lane >> 4) & 1;
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < NV; ++db)
 #pragma unroll
             for (int sec = 0; sec < 2; ++sec) {
                 const int row = 4 * half + (li >> 2) + 8 * sec;
@@ -419,7 +441,7 @@ struct WaveTile {
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
                 const bf16x8_t a =
-                    *reinterpret_cast<const bf16x8_t *>(Ks + off.k[st] + kb * 32 * 2 * D);
+                    *reinterpret_cast<const bf16x8_t *>(Ks + off.kofs(st) + kb * 32 * 2 * D);
                 s[kb] = mfma32(a, qf[st], s[kb]);
             }
         }
@@ -488,9 +510,9 @@ struct WaveTile {
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
                 const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_i16x4_t *)(Vs + off.v[db][0] + ps * 16 * 2 * D));
+                    (lds_i16x4_t *)(Vs + off.vofs(db, 0) + ps * 16 * 2 * D));
                 const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_i16x4_t *)(Vs + off.v[db][1] + ps * 16 * 2 * D));
+                    (lds_i16x4_t *)(Vs + off.vofs(db, 1) + ps * 16 * 2 * D));
                 const u32x2_t lw = __builtin_bit_cast(u32x2_t, lo);
                 const u32x2_t hw = __builtin_bit_cast(u32x2_t, hi);
                 const bf16x8_t a = __builtin_bit_cast(bf16x8_t, (u32x4_t){lw[0], lw[1], hw[0], hw[1]});
@@ -539,7 +561,9 @@ __device__ __forceinline__ void decode_step(
     }
     const char *stage = lds + st * STAGE;
     const int key0 = key_base + n * BN;
-    const bool need_mask = (key0 + BN > key_end) || (key0 + BN - 1 > wmin_lim);
+    // one (masked) copy of the step at D = 256: two inlined copies there
+    // keep two register assignments of O alive and spill
+    const bool need_mask = D >= 256 || (key0 + BN > key_end) || (key0 + BN - 1 > wmin_lim);
     if (need_mask)
         WaveTile<D, BN>::template step<true>(stage, stage + TB, off, qf, o, m_ref, l_run, l_rnd,
                                              c, half, key0, key_end, lim_lane);
@@ -668,7 +692,7 @@ struct BlockOps {
         set_prio<1>();
 #pragma unroll
         for (int st = 0; st < QS; ++st) {
-            const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(Kblk + off.k[st]);
+            const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(Kblk + off.kofs(st));
             s = mfma32(a, qf[st], s);
         }
         set_prio<0>();
@@ -767,9 +791,9 @@ struct BlockOps {
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
                 const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_i16x4_t *)(Vblk + off.v[db][0] + t2 * 16 * 2 * D));
+                    (lds_i16x4_t *)(Vblk + off.vofs(db, 0) + t2 * 16 * 2 * D));
                 const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_i16x4_t *)(Vblk + off.v[db][1] + t2 * 16 * 2 * D));
+                    (lds_i16x4_t *)(Vblk + off.vofs(db, 1) + t2 * 16 * 2 * D));
                 const u32x2_t lw = __builtin_bit_cast(u32x2_t, lo);
                 const u32x2_t hw = __builtin_bit_cast(u32x2_t, hi);
                 const bf16x8_t a =
@@ -1039,7 +1063,7 @@ struct WideRows {
 template <int D>
 __device__ __forceinline__ bf16x8_t wide_ld_k(const char *Kblk, const OperandOffsets<D> &off, int st)
 {
-    return *reinterpret_cast<const bf16x8_t *>(Kblk + off.k[st]);
+    return *reinterpret_cast<const bf16x8_t *>(Kblk + off.kofs(st));
 }
 
 // A operand of PV step ps (16 keys x 32 head dims) of the block at Vblk.
@@ -1049,9 +1073,9 @@ __device__ __forceinline__ bf16x8_t wide_ld_v(const char *Vblk, const OperandOff
     constexpr int DB = D / 32;
     const int t2 = ps / DB, db = ps % DB;
     const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_i16x4_t *)(Vblk + off.v[db][0] + t2 * 16 * 2 * D));
+        (lds_i16x4_t *)(Vblk + off.vofs(db, 0) + t2 * 16 * 2 * D));
     const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_i16x4_t *)(Vblk + off.v[db][1] + t2 * 16 * 2 * D));
+        (lds_i16x4_t *)(Vblk + off.vofs(db, 1) + t2 * 16 * 2 * D));
     const u32x2_t lw = __builtin_bit_cast(u32x2_t, lo);
     const u32x2_t hw = __builtin_bit_cast(u32x2_t, hi);
     return __builtin_bit_cast(bf16x8_t, (u32x4_t){lw[0], lw[1], hw[0], hw[1]});
@@ -1455,7 +1479,7 @@ fa_prefill_wide_kernel(const Params p)
     OperandOffsets<D> off;
     off.init(lane);
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int db = 0; db < OperandOffsets<D>::NV; ++db)
 #pragma unroll
         for (int sec = 0; sec < 2; ++sec) {
             off.v[db][sec] += VOFF;
@@ -1611,7 +1635,7 @@ fa_prefill_wide_kernel(const Params p)
 // j / group, head g * group + j % group; columns >= Sq * group are padding.
 // ---------------------------------------------------------------------------
 template <int D, bool OUT_F32>
-__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1 : 2)))
 fa_decode_split_kernel(const Params p)
 {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
@@ -1672,13 +1696,25 @@ fa_decode_split_kernel(const Params p)
     // the compiler kept one path's Q loads pending and put a vmcnt(0) at the
     // top of the key loop, draining the ring once per trip.
     wait_vmem();
-    // S tiles per trip keep every stage offset a compile-time constant
-    for (int n = 0; n < n_tiles; n += S) {
-#pragma unroll
-        for (int u = 0; u < S; ++u)
-            if (n + u < n_tiles)
-                decode_step<D, BN, S, TL>(n + u, n_tiles, k_begin, lds, u, ld, lane, k_end, wmin_lim,
+    if constexpr (D >= 256) {
+        // one tile per trip, stage offsets at run time: the S-way unrolled
+        // trip below does not fit the register file at D = 256
+        int st = 0;
+        for (int n = 0; n < n_tiles; ++n) {
+            decode_step<D, BN, S, TL>(n, n_tiles, k_begin, lds, st, ld, lane, k_end, wmin_lim,
                                       off, qf, o, m_ref, l_run, l_rnd, p.c, half, lim_lane);
+            st = st + 1 == S ? 0 : st + 1;
+        }
+    } else {
+        // S tiles per trip keep every stage offset a compile-time constant
+        for (int n = 0; n < n_tiles; n += S) {
+#pragma unroll
+            for (int u = 0; u < S; ++u)
+                if (n + u < n_tiles)
+                    decode_step<D, BN, S, TL>(n + u, n_tiles, k_begin, lds, u, ld, lane, k_end,
+                                              wmin_lim, off, qf, o, m_ref, l_run, l_rnd, p.c,
+                                              half, lim_lane);
+        }
     }
 
     const float l_norm = add_halves(l_rnd);
@@ -1710,7 +1746,7 @@ struct PagedParams {
 };
 
 template <int D, bool OUT_F32, int PPT>
-__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1 : 2)))
 fa_decode_paged_kernel(const Params p, const PagedParams pp)
 {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
@@ -1767,13 +1803,25 @@ fa_decode_paged_kernel(const Params p, const PagedParams pp)
     load_q<D>(qf, p.q + (((long)b * p.Sq + qi) * p.Hq + hq) * D, half);
     flip_q<D>(qf, p.qflip);
     wait_vmem();   // as in fa_decode_split_kernel: no ring drain per trip
-    for (int n = 0; n < n_tiles; n += S) {
+    if constexpr (D >= 256) {
+        // one tile per trip, stage offsets at run time: the S-way unrolled
+        // trip below does not fit the register file at D = 256
+        int st = 0;
+        for (int n = 0; n < n_tiles; ++n) {
+            decode_step<D, BN, S, TL>(n, n_tiles, k_begin, lds, st, ld, lane, k_end, wmin_lim,
+                                      off, qf, o, m_ref, l_run, l_rnd, p.c, half, lim_lane);
+            st = st + 1 == S ? 0 : st + 1;
+        }
+    } else {
+        // S tiles per trip keep every stage offset a compile-time constant
+        for (int n = 0; n < n_tiles; n += S) {
 #pragma unroll
-        for (int u = 0; u < S; ++u)
-            if (n + u < n_tiles)
-                decode_step<D, BN, S, TL>(n + u, n_tiles, k_begin, lds, u, ld, lane, k_end,
-                                          wmin_lim, off, qf, o, m_ref, l_run, l_rnd, p.c, half,
-                                          lim_lane);
+            for (int u = 0; u < S; ++u)
+                if (n + u < n_tiles)
+                    decode_step<D, BN, S, TL>(n + u, n_tiles, k_begin, lds, u, ld, lane, k_end,
+                                              wmin_lim, off, qf, o, m_ref, l_run, l_rnd, p.c,
+                                              half, lim_lane);
+        }
     }
 
     const float l_norm = add_halves(l_rnd);
@@ -1914,6 +1962,7 @@ static const PrefillCfg kPrefillCfgs[] = {
     {64, 64, 4, 1, launch_prefill_cfg<64, 64, 4, 1>},
     {64, 32, 4, 1, launch_prefill_cfg<64, 32, 4, 1>},
     {64, 64, 4, 2, launch_prefill_cfg<64, 64, 4, 2>},
+    {256, 32, 4, 1, launch_prefill_cfg<256, 32, 4, 1>},
 };
 
 static const PrefillCfg *find_prefill_cfg(int D, int bn, int nw, int nr)
@@ -1940,20 +1989,32 @@ hipError_t launch_prefill(const Launch &L)
     return hipGetLastError();
 }
 
+// Calls f(D, OUT_F32) with the call's head dim and output type as
+// compile-time constants (std::integral_constant values).
+template <class F>
+static void with_head_dim(const Launch &L, F &&f)
+{
+    auto out = [&](auto d) {
+        if (L.o_f32)
+            f(d, std::true_type{});
+        else
+            f(d, std::false_type{});
+    };
+    if (L.D == 256)
+        out(std::integral_constant<int, 256>{});
+    else if (L.D == 128)
+        out(std::integral_constant<int, 128>{});
+    else
+        out(std::integral_constant<int, 64>{});
+}
+
 static hipError_t launch_merge(const Launch &L, const Params &p)
 {
     dim3 gm((unsigned)((long)L.B * L.Hq * L.Sq)), blk(64);
-    if (L.D == 128) {
-        if (L.o_f32)
-            hipLaunchKernelGGL((fa_merge_kernel<128, true>), gm, blk, 0, L.stream, p);
-        else
-            hipLaunchKernelGGL((fa_merge_kernel<128, false>), gm, blk, 0, L.stream, p);
-    } else {
-        if (L.o_f32)
-            hipLaunchKernelGGL((fa_merge_kernel<64, true>), gm, blk, 0, L.stream, p);
-        else
-            hipLaunchKernelGGL((fa_merge_kernel<64, false>), gm, blk, 0, L.stream, p);
-    }
+    with_head_dim(L, [&](auto d, auto of) {
+        hipLaunchKernelGGL((fa_merge_kernel<decltype(d)::value, decltype(of)::value>), gm, blk,
+                           0, L.stream, p);
+    });
     return hipGetLastError();
 }
 
@@ -1961,17 +2022,10 @@ hipError_t launch_decode(const Launch &L)
 {
     Params p = make_params(L);
     dim3 g(L.B * L.Hkv * L.num_splits), blk(64);
-    if (L.D == 128) {
-        if (L.o_f32)
-            hipLaunchKernelGGL((fa_decode_split_kernel<128, true>), g, blk, 0, L.stream, p);
-        else
-            hipLaunchKernelGGL((fa_decode_split_kernel<128, false>), g, blk, 0, L.stream, p);
-    } else {
-        if (L.o_f32)
-            hipLaunchKernelGGL((fa_decode_split_kernel<64, true>), g, blk, 0, L.stream, p);
-        else
-            hipLaunchKernelGGL((fa_decode_split_kernel<64, false>), g, blk, 0, L.stream, p);
-    }
+    with_head_dim(L, [&](auto d, auto of) {
+        hipLaunchKernelGGL((fa_decode_split_kernel<decltype(d)::value, decltype(of)::value>), g,
+                           blk, 0, L.stream, p);
+    });
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || L.num_splits == 1) return e;
     return launch_merge(L, p);
@@ -1981,17 +2035,10 @@ template <int PPT>
 static void launch_paged_cfg(const Launch &L, const Params &p, const PagedParams &pp, dim3 g)
 {
     dim3 blk(64);
-    if (L.D == 128) {
-        if (L.o_f32)
-            hipLaunchKernelGGL((fa_decode_paged_kernel<128, true, PPT>), g, blk, 0, L.stream, p, pp);
-        else
-            hipLaunchKernelGGL((fa_decode_paged_kernel<128, false, PPT>), g, blk, 0, L.stream, p, pp);
-    } else {
-        if (L.o_f32)
-            hipLaunchKernelGGL((fa_decode_paged_kernel<64, true, PPT>), g, blk, 0, L.stream, p, pp);
-        else
-            hipLaunchKernelGGL((fa_decode_paged_kernel<64, false, PPT>), g, blk, 0, L.stream, p, pp);
-    }
+    with_head_dim(L, [&](auto d, auto of) {
+        hipLaunchKernelGGL((fa_decode_paged_kernel<decltype(d)::value, decltype(of)::value, PPT>),
+                           g, blk, 0, L.stream, p, pp);
+    });
 }
 
 hipError_t launch_decode_paged(const Launch &L, const PagedLaunch &P)

@@ -93,6 +93,18 @@ WORKLOADS = {
 }
 
 
+# Head dim 256 (the head-dim variants beyond the five): a causal prefill with
+# the causal workload's sequence length and the decode workload's shape.
+HEADDIM_WORKLOADS = {
+    w.name: w for w in [
+        Workload("causal_b2_h16_s4096_d256", B=2, Hq=16, Hkv=16, Sq=4096, Sk=4096, D=256,
+                 causal=True, seed=7),
+        Workload("decode_b32_hq32_hkv8_sk8192_d256", B=32, Hq=32, Hkv=8, Sq=1, Sk=8192,
+                 D=256, causal=False, seed=8),
+    ]
+}
+
+
 def make_inputs(w: Workload, seed: int | None = None, device: str = "cpu"):
     """Return (q, k, v) bf16 tensors: q [B,Sq,Hq,D], k/v [B,Sk,Hkv,D]."""
     g = torch.Generator("cpu")

@@ -9,14 +9,17 @@ in HBM:
     (one fa_fwd call: the split-key kernel and the log-sum-exp merge), and
   * the same decode over a paged K/V cache (16-key pages scattered over the
     cache): every sequence at 8192 keys, then lengths drawn from [1, 16384]
-    (one fa_fwd_paged call each: paged split kernel and merge).
+    (one fa_fwd_paged call each: paged split kernel and merge), and
+  * head dim 256: a causal prefill, B=2, H=16, S=4096, and the decode shape
+    (one fa_fwd call each).
 Both go to the same stream; HIP events recorded on that stream around each
 call give the per-call durations.
 
 Printed: one JSON line.  `value` is the prefill's algorithmic TFLOP/s (4*D
 flops per allowed query-key pair); `decode` holds the decode's algorithmic
 GB/s (Q, K, V read once, O and LSE written once), `paged_decode` and
-`paged_decode_ragged` the paged calls' (plus the block-table entries read).
+`paged_decode_ragged` the paged calls' (plus the block-table entries read),
+`d256_prefill` / `d256_decode` the head-dim-256 calls' TFLOP/s and GB/s.
 `roofline` is the prefill kernel against the dense bf16 MFMA peak; the decode
 entries' `roofline` their call against HBM.  `cpu_baseline` times the fp64 oracle on a bounded sample of the
 prefill workload's rows and also compares those rows with the timed output.
@@ -48,6 +51,8 @@ PREFILL = "causal_b4_h16_s4096_d128"
 DECODE = "decode_b32_hq32_hkv8_sk8192_d128"
 PAGED = "paged_decode_b32_hq32_hkv8_len8192_ps16_d128"
 PAGED_RAGGED = "paged_decode_b32_hq32_hkv8_ragged16384_ps16_d128"
+PREFILL_D256 = "causal_b2_h16_s4096_d256"
+DECODE_D256 = "decode_b32_hq32_hkv8_sk8192_d256"
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 KERNEL_SRC = os.path.join(ROOT, "attention_fwd_02_amd", "csrc", "fa_kernels.hip")
 
@@ -145,6 +150,15 @@ def profile_one(args):
         lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=dev)
         fn = lambda: fa.fa_fwd_paged(q, kc, vc, table, lens, o, lse, w.causal, w.scale)  # noqa: E731
         label = w.name
+    elif args.profile_kernel in ("prefill_d256", "decode_d256"):
+        from attention_fwd_02_amd.inputs import HEADDIM_WORKLOADS
+        w = HEADDIM_WORKLOADS[PREFILL_D256 if args.profile_kernel == "prefill_d256"
+                              else DECODE_D256]
+        q, k, v = (t.to(dev) for t in make_inputs(w))
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=dev)
+        fn = lambda: fa.fa_fwd(q, k, v, o, lse, w.causal, w.scale)  # noqa: E731
+        label = w.name
     else:
         w = WORKLOADS[PREFILL if args.profile_kernel == "prefill" else DECODE]
         q, k, v = (t.to(dev) for t in make_inputs(w))
@@ -167,7 +181,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=25.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-kernel",
-                    choices=["prefill", "decode", "paged", "paged_ragged", "copy"],
+                    choices=["prefill", "decode", "paged", "paged_ragged", "prefill_d256",
+                             "decode_d256", "copy"],
                     help="run only this call (warmup + steps) for counter collection; "
                          "'copy' is a plain 1 GiB device-to-device copy that calibrates "
                          "the HBM byte counters")
@@ -179,8 +194,8 @@ def main():
 
     import torch
     from attention_fwd_02_amd import _binding as fa
-    from attention_fwd_02_amd.inputs import (PAGED_WORKLOADS, WORKLOADS, make_inputs,
-                                             make_paged_inputs)
+    from attention_fwd_02_amd.inputs import (HEADDIM_WORKLOADS, PAGED_WORKLOADS, WORKLOADS,
+                                             make_inputs, make_paged_inputs)
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
@@ -203,6 +218,13 @@ def main():
                       torch.empty((w.B, w.Sq, w.Hq, w.D), dtype=torch.bfloat16, device=dev),
                       torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=dev))
 
+    d256 = {}
+    for key in (PREFILL_D256, DECODE_D256):
+        w = HEADDIM_WORKLOADS[key]
+        q, k, v = (t.to(dev) for t in make_inputs(w))
+        d256[key] = (w, q, k, v, torch.empty_like(q),
+                     torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=dev))
+
     stream = torch.cuda.current_stream()
 
     def prefill():
@@ -215,8 +237,13 @@ def main():
         w, _, (q, kc, vc, table, lens), o, lse = paged[key]
         fa.fa_fwd_paged(q, kc, vc, table, lens, o, lse, w.causal, w.scale, stream=stream)
 
+    def d256_call(key):
+        w, q, k, v, o, lse = d256[key]
+        fa.fa_fwd(q, k, v, o, lse, w.causal, w.scale, stream=stream)
+
     def step(evs=None):
-        calls = (prefill, decode, lambda: paged_call(PAGED), lambda: paged_call(PAGED_RAGGED))
+        calls = (prefill, decode, lambda: paged_call(PAGED), lambda: paged_call(PAGED_RAGGED),
+                 lambda: d256_call(PREFILL_D256), lambda: d256_call(DECODE_D256))
         for i, call in enumerate(calls):
             if evs:
                 evs[i].record(stream)
@@ -229,7 +256,7 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(K)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
@@ -262,6 +289,29 @@ def main():
                                  measured_traffic("paged" if key == PAGED else "paged_ragged")),
         }
 
+    def d256_entry(key, i):
+        w = d256[key][0]
+        ms = sorted(e[i].elapsed_time(e[i + 1]) for e in evs)
+        avg = sum(ms) / K
+        plan = fa.fa_plan(w.B, w.Hq, w.Hkv, w.Sq, w.Sk, w.D, w.causal, 0)
+        cfg = {"B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Sq": w.Sq, "Sk": w.Sk, "D": w.D,
+               "causal": w.causal, "plan": plan}
+        if w.Sq > 1:
+            tf = w.flops() / (avg * 1e-3) / 1e12
+            cfg["algorithmic_flops"] = w.flops()
+            return {"workload": key, "value": round(tf, 3), "unit": "TFLOP/s", "config": cfg,
+                    "ms": {"avg": round(avg, 4), "median": round(ms[K // 2], 4),
+                           "min": round(ms[0], 4)},
+                    "roofline": roofline(tf, PEAK_BF16_TFLOPS, "TFLOP/s", "mfma",
+                                         measured_traffic("prefill_d256"))}
+        gb = w.hbm_bytes() / (avg * 1e-3) / 1e9
+        cfg["algorithmic_bytes"] = w.hbm_bytes()
+        return {"workload": key, "value": round(gb, 1), "unit": "GB/s", "config": cfg,
+                "ms": {"avg": round(avg, 4), "median": round(ms[K // 2], 4),
+                       "min": round(ms[0], 4)},
+                "roofline": roofline(gb, PEAK_HBM_GBPS, "GB/s", "hbm",
+                                     measured_traffic("decode_d256"))}
+
     flops = wp.flops()
     tflops = flops / (p_avg * 1e-3) / 1e12
     dbytes = wd.hbm_bytes()
@@ -288,7 +338,8 @@ def main():
             "workload": (f"{PREFILL} (causal prefill B=4 Hq=Hkv=16 Sq=Sk=4096 D=128) + "
                          f"{DECODE} (decode B=32 Hq=32 Hkv=8 Sq=1 Sk=8192 D=128) + "
                          f"{PAGED} and {PAGED_RAGGED} (the decode over 16-key pages; "
-                         "8192 keys each, then lengths drawn from [1, 16384])"),
+                         "8192 keys each, then lengths drawn from [1, 16384]) + "
+                         f"{PREFILL_D256} and {DECODE_D256} (head dim 256)"),
             "prefill": {"B": wp.B, "Hq": wp.Hq, "Hkv": wp.Hkv, "Sq": wp.Sq, "Sk": wp.Sk,
                         "D": wp.D, "causal": wp.causal, "algorithmic_flops": flops,
                         "plan": plan_p},
@@ -309,6 +360,8 @@ def main():
         },
         "paged_decode": paged_entry(PAGED, 2),
         "paged_decode_ragged": paged_entry(PAGED_RAGGED, 3),
+        "d256_prefill": d256_entry(PREFILL_D256, 4),
+        "d256_decode": d256_entry(DECODE_D256, 5),
         "roofline": roofline(tflops, PEAK_BF16_TFLOPS, "TFLOP/s", "mfma",
                              measured_traffic("prefill")),
         "cpu_baseline": None,

@@ -57,7 +57,7 @@ typedef enum {
     FA_OK = 0,
     FA_ERR_INVALID_ARG = 1, /* NULL q/k/v/o, a dimension < 1, Hq % Hkv != 0,
                                non-finite scale, bad workspace size          */
-    FA_ERR_UNSUPPORTED = 2, /* D not in {64, 128}, pointer not 16-B aligned,
+    FA_ERR_UNSUPPORTED = 2, /* D not in {64, 128, 256}, pointer not 16-B aligned,
                                device not gfx950, split request the split
                                path cannot serve, sizes beyond 32-bit indexing */
     FA_ERR_NOMEM = 3,       /* the library-owned workspace could not be

@@ -60,7 +60,7 @@ def call(b, q=P, k=P, v=P, o=P, lse=None, B=1, Hq=1, Hkv=1, Sq=128, Sk=128, D=64
     (dict(Hq=6, Hkv=4), 1),
     (dict(scale=math.inf), 1), (dict(scale=-math.inf), 1), (dict(scale=math.nan), 1),
     (dict(causal=2), 1), (dict(o_dtype=7), 1), (dict(num_splits=-1), 1),
-    (dict(D=96), 2), (dict(D=256), 2), (dict(D=32), 2),
+    (dict(D=96), 2), (dict(D=512), 2), (dict(D=32), 2),
     (dict(q=P + 2), 2), (dict(k=P + 8), 2), (dict(v=P + 4), 2), (dict(o=P + 2), 2),
     (dict(lse=P + 4), 2), (dict(ws=P + 8, ws_bytes=1 << 20, num_splits=2, Sq=1), 2),
     # split path limited to 32 query rows per KV head

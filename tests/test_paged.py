@@ -84,6 +84,8 @@ CASES = [
     (dict(B=2, Hq=32, Hkv=1, max_len=200), [200, 77], 0),      # 32 query heads per KV head
     (dict(B=2, max_len=4096, page_size=16), [4096, 4000], 64),  # many splits
     (dict(B=1, max_len=4096, page_size=16), [4096], 1),        # 1 split raised to 2 (<= 256 pages each)
+    (dict(D=256, Hq=8, Hkv=2), [300, 17, 0], 0),               # head dim 256
+    (dict(D=256, page_size=32, Sq=2, causal=True), [100, 1, 64], 2),
 ]
 
 

@@ -15,7 +15,7 @@ import numpy as np
 import pytest
 import torch
 
-from attention_fwd_02_amd.inputs import WORKLOADS, make_inputs, random_qkv
+from attention_fwd_02_amd.inputs import HEADDIM_WORKLOADS, WORKLOADS, make_inputs, random_qkv
 from tests.helpers import check, to64
 
 pytestmark = pytest.mark.gpu
@@ -79,6 +79,11 @@ SHAPES = [
     (1, 64, 1, 1, 300, 128, False, "bf16"),       # Sq = 1 but 64 rows per KV head: prefill path
     (1, 1, 1, 1, 1, 64, False, "bf16"),           # one query, one key
     (1, 1, 1, 5, 1, 128, True, "f32"),            # one key, causal: only the last row sees it
+    # head dim 256: 4 waves x 32 rows, 32-key tiles
+    (1, 2, 2, 128, 128, 256, False, "f32"),
+    (2, 4, 2, 200, 333, 256, True, "bf16"),       # ragged, GQA, causal with Sk > Sq
+    (1, 2, 2, 300, 100, 256, True, "f32"),        # Sq > Sk: leading rows see no key
+    (1, 2, 1, 513, 513, 256, True, "bf16"),       # several items + tail
 ]
 
 
@@ -170,6 +175,9 @@ DECODE_SHAPES = [
     (1, 32, 4, 4, 300, 128, True, 5),     # 32 columns: the largest the split path serves
     (2, 1, 1, 1, 33, 64, False, 2),       # last split holds one key
     (1, 2, 2, 7, 5, 64, True, 2),         # Sq > Sk on the split path: empty rows
+    (2, 8, 2, 1, 1000, 256, False, 0),    # head dim 256: one tile per trip
+    (1, 32, 4, 4, 300, 256, True, 5),
+    (2, 4, 4, 1, 65, 256, False, 3),
 ]
 
 
@@ -278,9 +286,9 @@ def sample_rows(w, q, n_random, seed):
     return np.array(sorted(rows), dtype=np.int64)
 
 
-@pytest.mark.parametrize("name", list(WORKLOADS))
+@pytest.mark.parametrize("name", list(WORKLOADS) + list(HEADDIM_WORKLOADS))
 def test_full_size_workloads_sampled(ops, oracle, name):
-    w = WORKLOADS[name]
+    w = WORKLOADS[name] if name in WORKLOADS else HEADDIM_WORKLOADS[name]
     say(f"[parity] full-size workload {name}")
     q, k, v = make_inputs(w)
     o, lse = run_gpu(ops, q, k, v, w.causal, w.scale, out=w.o_dtype)
