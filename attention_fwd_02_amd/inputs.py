@@ -22,6 +22,12 @@ Paged K/V caches (``PagedWorkload``), same generator:
     pool: a sequence's pages are scattered over the cache); unused block-table
     entries are -1;
   * then q, k_cache, v_cache with ``torch.randn`` as above.
+
+FP8 inputs (``make_fp8_inputs``): q, k, v drawn as above in float32 (times
+``std``, hot rows included), then quantized per tensor to OCP FP8 E4M3:
+descale = amax / 448 (a power of two is not forced), codes = the float32
+values divided by descale, converted with torch's round-to-nearest-even
+``float8_e4m3fn`` cast.  The real inputs are descale * codes.
 """
 from __future__ import annotations
 
@@ -212,3 +218,45 @@ def make_paged_inputs(w: PagedWorkload, seed: int | None = None, device: str = "
     if device != "cpu":
         q, kc, vc, table, seq = (t.to(device) for t in (q, kc, vc, table, seq))
     return q, kc, vc, table, seq
+
+
+# FP8 E4M3 inputs: the causal benchmark workload's shape.
+FP8_WORKLOADS = {
+    w.name: w for w in [
+        Workload("causal_b4_h16_s4096_d128_fp8", B=4, Hq=16, Hkv=16, Sq=4096, Sk=4096, D=128,
+                 causal=True, hot_row_frac=0.01, hot_row_mult=8.0, seed=9),
+    ]
+}
+
+
+def make_fp8_inputs(w: Workload, seed: int | None = None, device: str = "cpu"):
+    """Return (q8, k8, v8, q_descale, k_descale, v_descale): float8_e4m3fn
+    tensors of the usual shapes and per-tensor float descale factors."""
+    g = torch.Generator("cpu")
+    g.manual_seed(w.seed if seed is None else seed)
+    q = torch.randn((w.B, w.Sq, w.Hq, w.D), generator=g, dtype=torch.float32)
+    k = torch.randn((w.B, w.Sk, w.Hkv, w.D), generator=g, dtype=torch.float32)
+    v = torch.randn((w.B, w.Sk, w.Hkv, w.D), generator=g, dtype=torch.float32)
+    if w.std != 1.0:
+        q.mul_(w.std)
+        k.mul_(w.std)
+        v.mul_(w.std)
+    if w.hot_row_frac > 0.0:
+        hot = torch.rand((w.B, w.Sq, w.Hq), generator=g) < w.hot_row_frac
+        q = torch.where(hot.unsqueeze(-1), q * w.hot_row_mult, q)
+    out = []
+    scales = []
+    for t in (q, k, v):
+        descale = float(t.abs().max()) / 448.0
+        out.append((t / descale).to(torch.float8_e4m3fn))
+        scales.append(descale)
+    if device != "cpu":
+        out = [t.to(device) for t in out]
+    return (*out, *scales)
+
+
+def random_fp8(B, Hq, Hkv, Sq, Sk, D, seed, std=1.0, device="cpu"):
+    """Ad-hoc FP8 shapes for tests: same recipe, no hot rows."""
+    w = Workload("adhoc", B=B, Hq=Hq, Hkv=Hkv, Sq=Sq, Sk=Sk, D=D, causal=False, std=std,
+                 seed=seed)
+    return make_fp8_inputs(w, device=device)

@@ -17,6 +17,10 @@ definition, closed forms worked out by hand, invariants and layout probes;
 sequence's keys in plain numpy and hands them to the same definition; its
 gather is pinned by hand-placed page contents with closed-form answers in
 ``tests/test_oracle.py`` and by planted slips in the mutant tests.
+``attn_fwd_fp8`` (OCP FP8 E4M3 inputs with per-tensor descales) decodes the
+codes with its own table, written from the format's definition and pinned
+code by code against it and against torch's float8_e4m3fn, then applies the
+same definition; planted decode and descale slips must fail its pins.
 """
 from __future__ import annotations
 
@@ -169,3 +173,64 @@ def attn_fwd_paged(q, k_cache, v_cache, block_table, seq_lens, causal: bool, sca
                           causal, scale, nthreads=nthreads, _lib_override=_lib_override)
         o[b], lse[b] = ob[0], lb[0]
     return o, lse
+
+
+def fp8_e4m3_value(code: int) -> float:
+    """Value of one OCP FP8 E4M3 code ("fn" variant: no infinities).
+
+    Bit 7 sign, bits 6..3 exponent (bias 7), bits 2..0 mantissa; exponent
+    field 0 is subnormal (m / 8 * 2^-6); S.1111.111 is NaN, so the largest
+    finite magnitude is 1.75 * 2^8 = 448."""
+    sign = -1.0 if code & 0x80 else 1.0
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    if e == 0xF and m == 0x7:
+        return float("nan")
+    if e == 0:
+        return sign * (m / 8.0) * 2.0 ** -6
+    return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+_FP8_TABLE = np.array([fp8_e4m3_value(c) for c in range(256)], dtype=np.float64)
+
+
+def fp8_values(x) -> np.ndarray:
+    """float64 values of an array of FP8 E4M3 codes (uint8 numpy, or a torch
+    float8_e4m3fn / uint8 tensor)."""
+    if hasattr(x, "detach"):
+        import torch
+        t = x.detach().cpu()
+        if t.dtype != torch.uint8:
+            t = t.view(torch.uint8)
+        x = t.numpy()
+    return _FP8_TABLE[np.asarray(x, dtype=np.uint8)]
+
+
+def attn_fwd_fp8(q8, k8, v8, causal: bool, scale: float, q_descale: float, k_descale: float,
+                 v_descale: float, *, rows=None, nthreads: int | None = None,
+                 _lib_override=None):
+    """The oracle for FP8 E4M3 inputs with per-tensor descale factors.
+
+    The pages name FP8 only as a capability of the SM90 kernel ("SM80 内核实现对比",
+    section 7.3, the FP8 row of the scenario table); the convention is this
+    project's reading, the usual per-tensor one: the real inputs are
+    q_descale * q8, k_descale * k8, v_descale * v8, and the attention is the
+    plain definition on them.  Every E4M3 value is exact in bfloat16 (3
+    mantissa bits, exponents 2^-9 .. 2^8), so the codes are handed to the fp64
+    definition as bf16 and the descales are folded in: scores use
+    scale * q_descale * k_descale (rounded once to float32, the oracle's scale
+    argument), and O is multiplied by v_descale.  LSE is unaffected by v.
+    """
+    import torch
+
+    def as_bf16(x):
+        vals = fp8_values(x)
+        t = torch.from_numpy(vals.astype(np.float32))      # exact: E4M3 fits in fp32
+        b = t.to(torch.bfloat16)                            # exact: E4M3 fits in bf16
+        assert torch.equal(b.to(torch.float32), t), "an FP8 value is not exact in bf16"
+        return b
+
+    o, lse = attn_fwd(as_bf16(q8), as_bf16(k8), as_bf16(v8), causal,
+                      float(scale) * float(q_descale) * float(k_descale), rows=rows,
+                      nthreads=nthreads, _lib_override=_lib_override)
+    return o * float(v_descale), lse

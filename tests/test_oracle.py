@@ -455,3 +455,62 @@ def test_paged_page_permutation_invariance(oracle_mod):
     o2, l2 = oracle_mod.attn_fwd_paged(q, k[inv], v[inv], table2, PAGED_LENS, False, 0.4)
     np.testing.assert_array_equal(o1, o2)
     np.testing.assert_array_equal(l1, l2)
+
+
+# ----------------------------------------------------------------------------
+# FP8 E4M3 inputs: the decode of every code and the descale convention
+# ----------------------------------------------------------------------------
+def test_fp8_decode_matches_the_format_and_torch(oracle_mod):
+    # hand-worked codes of the OCP E4M3 format
+    expect = {0x00: 0.0, 0x80: -0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6,
+              0x38: 1.0, 0x39: 1.125, 0x40: 2.0, 0x7E: 448.0, 0xFE: -448.0, 0xB8: -1.0,
+              0x30: 0.5, 0x3C: 1.5}
+    for code, val in expect.items():
+        assert oracle_mod.fp8_e4m3_value(code) == val, hex(code)
+    assert math.isnan(oracle_mod.fp8_e4m3_value(0x7F))
+    assert math.isnan(oracle_mod.fp8_e4m3_value(0xFF))
+    # and every code against torch's float8_e4m3fn
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).float().double().numpy()
+    got = oracle_mod.fp8_values(codes.numpy())
+    assert np.array_equal(np.isnan(ref), np.isnan(got))
+    assert np.array_equal(ref[~np.isnan(ref)], got[~np.isnan(got)])
+
+
+def test_fp8_uniform_scores_average_descaled_v(oracle_mod):
+    # K = 0: O is the mean of the (descaled) V rows, LSE = ln(Sk)
+    Sk = 6
+    q8 = torch.full((1, 2, 1, 4), 3.0).to(torch.float8_e4m3fn)
+    k8 = torch.zeros((1, Sk, 1, 4)).to(torch.float8_e4m3fn)
+    vals = torch.tensor([1.0, 2.0, 3.0, 4.0, 6.0, 8.0])
+    v8 = vals.view(1, Sk, 1, 1).expand(1, Sk, 1, 4).contiguous().to(torch.float8_e4m3fn)
+    o, lse = oracle_mod.attn_fwd_fp8(q8, k8, v8, False, 0.5, 0.25, 3.0, 0.125)
+    assert np.allclose(o, 24.0 / 6.0 * 0.125, rtol=0, atol=1e-15)
+    assert np.allclose(lse, math.log(Sk), rtol=0, atol=1e-14)
+
+
+def test_fp8_descales_enter_scores_and_output(oracle_mod):
+    # two keys: s_j = scale*dq*dk*(q.k_j); weights by hand
+    q8 = torch.tensor([[[[2.0, 0.0]]]]).to(torch.float8_e4m3fn)          # [1,1,1,2]
+    k8 = torch.tensor([[[[1.0, 0.0]], [[0.0, 1.0]]]]).to(torch.float8_e4m3fn)  # [1,2,1,2]
+    v8 = torch.tensor([[[[4.0, 0.0]], [[0.0, 8.0]]]]).to(torch.float8_e4m3fn)
+    scale, dq, dk, dv = 0.5, 1.5, 0.75, 0.25
+    s0 = scale * dq * dk * 2.0
+    w0 = math.exp(s0) / (math.exp(s0) + 1.0)
+    o, lse = oracle_mod.attn_fwd_fp8(q8, k8, v8, False, scale, dq, dk, dv)
+    # the oracle rounds scale*dq*dk to float32 once
+    assert o[0, 0, 0, 0] == pytest.approx(dv * 4.0 * w0, rel=1e-6)
+    assert o[0, 0, 0, 1] == pytest.approx(dv * 8.0 * (1.0 - w0), rel=1e-6)
+    assert lse[0, 0, 0] == pytest.approx(math.log(math.exp(s0) + 1.0), rel=1e-6)
+
+
+def test_fp8_equals_bf16_oracle_on_exact_values(oracle_mod):
+    # descales of 1: the FP8 oracle is the bf16 oracle on the same values
+    q8, k8, v8, *_ = (t for t in (torch.randn(1, 5, 2, 8), torch.randn(1, 7, 2, 8),
+                                  torch.randn(1, 7, 2, 8)))
+    q8, k8, v8 = (t.to(torch.float8_e4m3fn) for t in (q8, k8, v8))
+    o1, l1 = oracle_mod.attn_fwd_fp8(q8, k8, v8, True, 0.3, 1.0, 1.0, 1.0)
+    o2, l2 = oracle_mod.attn_fwd(q8.float().to(torch.bfloat16), k8.float().to(torch.bfloat16),
+                                 v8.float().to(torch.bfloat16), True, 0.3)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)

@@ -115,3 +115,41 @@ def test_paged_pins_reject_mutant(name):
         except (AssertionError, IndexError, ValueError):
             caught += 1
     assert caught > 0, f"no pin detects mutant {name}"
+
+
+# slips in the FP8 decode and descale convention (oracle/__init__.py)
+FP8_MUTANTS = {
+    "exponent_bias_8": ("return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)",
+                        "return sign * (1.0 + m / 8.0) * 2.0 ** (e - 8)"),
+    "subnormal_as_normal": ("return sign * (m / 8.0) * 2.0 ** -6",
+                            "return sign * (1.0 + m / 8.0) * 2.0 ** -7"),
+    "no_nan_code": ("if e == 0xF and m == 0x7:\n        return float(\"nan\")",
+                    "if False:\n        return float(\"nan\")"),
+    "v_descale_dropped": ("return o * float(v_descale), lse", "return o, lse"),
+    "k_descale_dropped": ("float(scale) * float(q_descale) * float(k_descale)",
+                          "float(scale) * float(q_descale)"),
+}
+
+FP8_PIN_TESTS = [
+    pins.test_fp8_decode_matches_the_format_and_torch,
+    pins.test_fp8_uniform_scores_average_descaled_v,
+    pins.test_fp8_descales_enter_scores_and_output,
+]
+
+
+@pytest.mark.parametrize("name", sorted(FP8_MUTANTS))
+def test_fp8_pins_reject_mutant(name):
+    import types
+    before, after = FP8_MUTANTS[name]
+    src = open(oracle_pkg.__file__).read()
+    assert src.count(before) == 1, f"mutation anchor for {name} not found exactly once"
+    mod = types.ModuleType("oracle_mutant")
+    mod.__file__ = oracle_pkg.__file__
+    exec(compile(src.replace(before, after), "oracle_mutant", "exec"), mod.__dict__)
+    caught = 0
+    for pin in FP8_PIN_TESTS:
+        try:
+            pin(mod)
+        except (AssertionError, IndexError, ValueError):
+            caught += 1
+    assert caught > 0, f"no pin detects mutant {name}"
