@@ -21,7 +21,8 @@ STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_INVALID_ARG", 2: "FA_ERR_UNSUPPORTED",
 
 # every symbol include/fa.h declares
 EXPORTS = ["fa_fwd", "fa_fwd_ex", "fa_workspace_size", "fa_plan", "fa_fwd_paged",
-           "fa_plan_paged", "fa_last_error", "fa_release_workspace", "fa_version"]
+           "fa_plan_paged", "fa_fwd_fp8", "fa_last_error", "fa_release_workspace",
+           "fa_version"]
 
 
 class FaError(RuntimeError):
@@ -61,6 +62,9 @@ def _load():
     lib.fa_fwd_paged.restype = c_int
     lib.fa_plan_paged.argtypes = [c_int] * 9 + [ctypes.POINTER(FaPlanInfo)]
     lib.fa_plan_paged.restype = c_int
+    lib.fa_fwd_fp8.argtypes = ([c_void_p] * 5 + [c_int] * 7 + [c_float] * 4 +
+                               [c_void_p, c_int])
+    lib.fa_fwd_fp8.restype = c_int
     lib.fa_last_error.argtypes = []
     lib.fa_last_error.restype = ctypes.c_char_p
     lib.fa_release_workspace.argtypes = []
@@ -209,3 +213,37 @@ def fa_fwd_paged(q, k_cache, v_cache, block_table, seq_lens, o, lse, causal: boo
                             B, Hq, Hkv, Sq, D, num_pages, page_size, block_table.shape[1],
                             int(bool(causal)), float(scale), _stream_handle(stream), odt,
                             int(num_splits), ws_ptr, ws_bytes))
+
+
+def fa_fwd_fp8(q, k, v, o, lse, causal: bool, scale: float, q_descale: float, k_descale: float,
+               v_descale: float, stream=None) -> None:
+    """Attention on float8_e4m3fn q, k, v with per-tensor descales; o bf16 or f32."""
+    import torch
+    if o.dtype == torch.bfloat16:
+        odt = FA_DTYPE_BF16
+    elif o.dtype == torch.float32:
+        odt = FA_DTYPE_F32
+    else:
+        raise TypeError("o must be bfloat16 or float32")
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or o.dim() != 4:
+        raise ValueError("q, k, v, o must be 4-D: [B, S, H, D]")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.float8_e4m3fn:
+            raise TypeError(f"{name} must be float8_e4m3fn")
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    B, Sq, Hq, D = q.shape
+    _, Sk, Hkv, _ = k.shape
+    if tuple(k.shape) != (B, Sk, Hkv, D) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v must both be [B, Sk, Hkv, D]")
+    if tuple(o.shape) != (B, Sq, Hq, D):
+        raise ValueError("o must be [B, Sq, Hq, D]")
+    if lse is not None:
+        if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Sq) or not lse.is_contiguous():
+            raise ValueError("lse must be a contiguous float32 [B, Hq, Sq] tensor")
+    _check(lib.fa_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                          lse.data_ptr() if lse is not None else None,
+                          B, Hq, Hkv, Sq, Sk, D, int(bool(causal)), float(scale),
+                          float(q_descale), float(k_descale), float(v_descale),
+                          _stream_handle(stream), odt))

@@ -548,6 +548,68 @@ fa_status fa_fwd_paged(const void *q, const void *k_cache, const void *v_cache,
     return FA_OK;
 }
 
+fa_status fa_fwd_fp8(const void *q, const void *k, const void *v, void *o, float *lse, int B,
+                     int Hq, int Hkv, int Sq, int Sk, int D, int causal, float scale,
+                     float q_descale, float k_descale, float v_descale, hipStream_t stream,
+                     fa_dtype o_dtype)
+{
+    g_last_error.clear();
+    if (!q || !k || !v || !o) return fail(FA_ERR_INVALID_ARG, "q, k, v and o must not be NULL");
+    fa_status st = check_sizes(B, Hq, Hkv, Sq, Sk, D);
+    if (st != FA_OK) return st;
+    if (D != 128) return fail(FA_ERR_UNSUPPORTED, "the FP8 path serves head dim 128");
+    if (!isfinite(scale)) return fail(FA_ERR_INVALID_ARG, "scale must be finite");
+    if (!(q_descale > 0.0f) || !(k_descale > 0.0f) || !(v_descale > 0.0f) ||
+        !isfinite(q_descale) || !isfinite(k_descale) || !isfinite(v_descale))
+        return fail(FA_ERR_INVALID_ARG, "descales must be finite and > 0");
+    const float s_eff = scale * q_descale * k_descale;
+    if (!isfinite(s_eff)) return fail(FA_ERR_INVALID_ARG, "scale * q_descale * k_descale overflows");
+    if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "causal must be 0 or 1");
+    if (o_dtype != FA_DTYPE_BF16 && o_dtype != FA_DTYPE_F32)
+        return fail(FA_ERR_INVALID_ARG, "o_dtype must be FA_DTYPE_BF16 or FA_DTYPE_F32");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+        (lse && !aligned16(lse)))
+        return fail(FA_ERR_UNSUPPORTED, "q, k, v, o and lse must be 16-byte aligned");
+
+    int dev = 0;
+    DeviceInfo *info = nullptr;
+    st = device_info(&dev, &info);
+    if (st != FA_OK) return st;
+
+    // 32 rows per wave, 64-key tiles, 8 waves (two per SIMD, 256 registers
+    // each); FA_FP8_NW=4 selects one wave per SIMD (measured 1.7x slower on
+    // the causal S=4096 shape: no second wave fills the first's stalls)
+    const int nw = env_int("FA_FP8_NW", 8) == 4 ? 4 : 8;
+    const int bm = 32 * nw;
+    const int64_t items = (int64_t)B * Hq * ((Sq + bm - 1) / bm);
+    if (items >= (int64_t(1) << 31)) return fail(FA_ERR_UNSUPPORTED, "too many work items");
+    const int wg_per_cu = 1;
+    const int64_t grid = std::min<int64_t>(items, (int64_t)info->cus * wg_per_cu);
+
+    fa::Launch L;
+    L.q = q; L.k = k; L.v = v; L.o = o; L.lse = lse;
+    L.part_o = nullptr; L.part_lse = nullptr;
+    L.B = B; L.Hq = Hq; L.Hkv = Hkv; L.Sq = Sq; L.Sk = Sk; L.D = D;
+    L.causal = causal;
+    L.o_f32 = (o_dtype == FA_DTYPE_F32);
+    L.scale = s_eff;
+    L.num_splits = 1;
+    L.split_len = 0;
+    L.grid = (int)grid;
+    L.prefill_bn = fa::kFp8BN;
+    L.prefill_nw = nw;
+    L.prefill_nr = 1;
+    L.head_major = env_int("FA_HEAD_MAJOR", causal ? 1 : 0) != 0;
+    L.stream = stream;
+    if (log_enabled())
+        fprintf(stderr, "[fa] path=fp8-prefill B=%d Hq=%d Hkv=%d Sq=%d Sk=%d D=%d causal=%d "
+                "waves=%d grid=%lld items=%lld\n", B, Hq, Hkv, Sq, Sk, D, causal, nw,
+                (long long)grid, (long long)items);
+    hipError_t e = fa::launch_prefill_fp8(L, v_descale);
+    if (e != hipSuccess) return fail(FA_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
+    return FA_OK;
+}
+
 fa_status fa_plan_paged(int B, int Hq, int Hkv, int Sq, int D, int num_pages, int page_size,
                         int max_pages, int num_splits, fa_plan_info *out)
 {

@@ -1009,6 +1009,382 @@ fa_prefill_kernel(const Params p)
 }
 
 // ---------------------------------------------------------------------------
+// FP8 E4M3 prefill: Q, K, V as OCP E4M3 codes with per-tensor descales.
+// S^T = K Q^T and O^T += V^T P^T run on v_mfma_f32_32x32x64_f8f6f4 (64 keys
+// or head dims per instruction, twice the bf16 rate), P is rounded to E4M3.
+// Lane layout of that MFMA: A lane (m = lane % 32, h = lane / 32) holds
+// A[m][32h .. 32h + 31], B lane (n, h) holds B[32h .. 32h + 31][n]; the
+// output is laid out as for the bf16 32x32 MFMAs.
+//
+// One block is 64 keys, two 32-key S^T accumulators: lane (col, h) holds,
+// in accumulator kb register r, key kb*32 + 8*(r/4) + 4h + r%4 =: key(h, i)
+// with i = 16 kb + r.  Packed to E4M3 in that order (byte i), they are
+// directly the B operand P^T of the PV product if the A operand V^T holds
+// V[key(h, i)][dim] at byte i.  ds_read_b64_tr_b8 delivers exactly that:
+// in each group of 16 lanes, lane j receives byte j % 8 of the 8-byte words
+// the group's lanes 2t + j / 8 point at (t = 0..7, output byte t), so a
+// source lane s points at the 8 dims it shares with its destinations in key
+// row key(h, 8 t4 + s / 2), for the read t4 = 0..3 of the 32 bytes.
+// Tiles are rows of D bytes: the bf16 geometry of head dim D/2 (loader,
+// swizzle), so both reads stay conflict-free as there.
+// ---------------------------------------------------------------------------
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2_t lds_i32x2_t;
+
+__device__ __forceinline__ f32x16_t mfma32_f8(i32x8_t a, i32x8_t b, f32x16_t c)
+{
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+template <int D>
+struct Fp8Offsets {
+    static constexpr int RB = D;          // bytes per tile row
+    static constexpr int KS = D / 64;     // k-steps of S^T
+    static constexpr int DB = D / 32;     // 32-dim blocks of O^T
+    int k[KS][2];                         // the two 16-byte chunks of a k-step (+ kb*32 rows)
+    int vb[4];                            // read t4: this lane's source row and byte offset
+    int vs[4];                            //   and its row's swizzle / 2
+
+    // Address of this lane's 8 source bytes for read t4 of dim block db: the
+    // chunk (2 db + grp % 2) ^ swz(key) is split into its low bit (kept in
+    // vb) and 2 (db ^ swz/2), so that four registers serve every db.
+    __device__ __forceinline__ int vofs(int db, int t4) const { return vb[t4] + 32 * (db ^ vs[t4]); }
+
+    __device__ __forceinline__ void init(int lane)
+    {
+        const int col = lane & 31, half = lane >> 5;
+#pragma unroll
+        for (int st = 0; st < KS; ++st)
+#pragma unroll
+            for (int c2 = 0; c2 < 2; ++c2) {
+                const int chunk = 4 * st + 2 * half + c2;
+                k[st][c2] = col * RB + ((chunk ^ swz<D / 2>(col)) * 16);
+            }
+        const int sl = lane & 15, grp = lane >> 4;
+        static_assert(D == 128, "vofs assumes 8 chunks per row (4 dim blocks)");
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4) {
+            const int i = 8 * t4 + (sl >> 1);
+            const int r = i & 15;
+            const int key = (i >> 4) * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+            const int sw = swz<D / 2>(key);
+            vb[t4] = key * RB + 16 * ((grp ^ sw) & 1) + 8 * (sl & 1);
+            vs[t4] = sw >> 1;
+        }
+    }
+};
+
+template <int D>
+struct Fp8Ops {
+    static constexpr int KS = D / 64;
+    static constexpr int DB = D / 32;
+    static constexpr int RB = D;
+
+    // S^T of the 64 keys whose K rows start at Kblk (LDS)
+    __device__ __forceinline__ static void qk(const char *Kblk, const Fp8Offsets<D> &off,
+                                              const i32x8_t (&qf)[KS], f32x16_t (&s)[2])
+    {
+        set_prio<1>();
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            s[kb] = f32x16_t{};
+#pragma unroll
+            for (int st = 0; st < KS; ++st) {
+                const u32x4_t lo =
+                    *reinterpret_cast<const u32x4_t *>(Kblk + kb * 32 * RB + off.k[st][0]);
+                const u32x4_t hi =
+                    *reinterpret_cast<const u32x4_t *>(Kblk + kb * 32 * RB + off.k[st][1]);
+                const i32x8_t a = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                   (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+                s[kb] = mfma32_f8(a, qf[st], s[kb]);
+            }
+        }
+        set_prio<0>();
+    }
+
+    __device__ __forceinline__ static void mask(f32x16_t (&s)[2], int key0, int half,
+                                                int key_end, int lim)
+    {
+        BlockOps<64>::mask(s[0], key0, half, key_end, lim);
+        BlockOps<64>::mask(s[1], key0 + 32, half, key_end, lim);
+    }
+
+    __device__ __forceinline__ static float rowmax(const f32x16_t (&s)[2])
+    {
+        float mx = kNegInf;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+        return max_halves(mx);
+    }
+
+    // Lazy reference max (threshold 2^8: P stays below 2^8, inside E4M3's
+    // range of 448); the first allowed key always moves it.
+    __device__ __forceinline__ static void rebase(float mx, float &m_ref, float &l_run,
+                                                  f32x16_t &l_acc, f32x16_t (&o)[DB], float c)
+    {
+        const bool grow = (mx - m_ref) * c > kRescaleThreshold;
+        if (__any(grow)) {
+            const float m_new = grow ? mx : m_ref;
+            const float alpha = (m_ref == kNegInf) ? 0.0f : fast_exp2((m_ref - m_new) * c);
+            l_run *= alpha;
+            l_acc[0] *= alpha;   // only element 0 of the row-sum accumulator is read
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+            m_ref = m_new;
+        }
+    }
+
+    // P = exp2(c*s - mc) rounded to E4M3 (round to nearest even), byte
+    // 16 kb + r of the B operand; l_run adds the exact fp32 values (LSE).
+    template <bool MASK>
+    __device__ __forceinline__ static i32x8_t probs(const f32x16_t (&s)[2], float c, float mc,
+                                                    float &l_run)
+    {
+        float e[32];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float x = fast_exp2(fmaf(s[kb][r], c, -mc));
+                if (MASK) x = (s[kb][r] == kNegInf) ? 0.0f : x;
+                e[16 * kb + r] = x;
+            }
+        i32x8_t pw;
+        float la = 0.0f, lb = 0.0f;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+            int word = __builtin_amdgcn_cvt_pk_fp8_f32(e[4 * w], e[4 * w + 1], 0, false);
+            word = __builtin_amdgcn_cvt_pk_fp8_f32(e[4 * w + 2], e[4 * w + 3], word, true);
+            pw[w] = word;
+            la += e[4 * w] + e[4 * w + 1];
+            lb += e[4 * w + 2] + e[4 * w + 3];
+        }
+        l_run += la + lb;
+        return pw;
+    }
+
+    // O^T += V^T P^T over the 64 keys whose V rows start at Vblk; l_acc
+    // (element 0) adds the column sums of the rounded P: the row sum O is
+    // normalised by, from the same values P V multiplies.
+    __device__ __forceinline__ static void pv(const char *Vblk, const Fp8Offsets<D> &off,
+                                              i32x8_t pw, f32x16_t (&o)[DB], f32x16_t &l_acc)
+    {
+        constexpr int kOnes = 0x38383838;   // E4M3 1.0 in every byte
+        const i32x8_t ones = {kOnes, kOnes, kOnes, kOnes, kOnes, kOnes, kOnes, kOnes};
+        set_prio<1>();
+        l_acc = mfma32_f8(ones, pw, l_acc);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            i32x8_t a;
+#pragma unroll
+            for (int t4 = 0; t4 < 4; ++t4) {
+                const i32x2_t w =
+                    __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t *)(Vblk + off.vofs(db, t4)));
+                a[2 * t4] = w[0];
+                a[2 * t4 + 1] = w[1];
+            }
+            o[db] = mfma32_f8(a, pw, o[db]);
+        }
+        set_prio<0>();
+    }
+};
+
+template <int D>
+struct Fp8RowState {
+    i32x8_t qf[D / 64];
+    f32x16_t o[D / 32];
+    f32x16_t s_cur[2];   // S^T of the block to be finished next
+    float mx_cur;
+    float m_ref, l_run;
+    f32x16_t l_acc;      // element 0: row sum of the rounded P (whole row)
+    int NBw, wmin_lim, lim_lane, key_end, half;
+    float c;
+
+    __device__ __forceinline__ bool needs_mask(int j) const
+    {
+        return (j * 64 + 64 > key_end) || (j * 64 + 63 > wmin_lim);
+    }
+};
+
+// Tile t (64 keys, one block) held in LDS stage `stage`; the S^T of block
+// t + 1 is issued before block t is finished, as in prefill_tile.
+template <int D, int NW>
+__device__ __forceinline__ void prefill_tile_fp8(int t, int n_tiles, char *stage, char *next,
+                                                 char *after,
+                                                 const TileLoader<D / 2, 64, NW> &ld, int wave,
+                                                 int lane, const Fp8Offsets<D> &off,
+                                                 Fp8RowState<D> &rs)
+{
+    constexpr int TB = TileLoader<D / 2, 64, NW>::TILE_BYTES;
+    using FO = Fp8Ops<D>;
+    const bool live = t < rs.NBw;
+    const bool live_next = t + 1 < rs.NBw;
+    float mc = 0.0f;
+    if (live) {
+        FO::rebase(rs.mx_cur, rs.m_ref, rs.l_run, rs.l_acc, rs.o, rs.c);
+        mc = (rs.m_ref == kNegInf) ? 0.0f : rs.m_ref * rs.c;
+    }
+    if (t + 1 < n_tiles) {
+        wait_vmem();       // this wave's copies of tile t + 1 are in LDS
+        __syncthreads();   // ... and every wave's; tile t - 1 is released
+        if (t + 2 < n_tiles) ld.issue(after, after + TB, (t + 2) * 64, wave, lane);
+    }
+    f32x16_t s_next[2] = {f32x16_t{}, f32x16_t{}};
+    if (live_next) FO::qk(next, off, rs.qf, s_next);
+    if (live) {
+        const i32x8_t pw = rs.needs_mask(t)
+                               ? FO::template probs<true>(rs.s_cur, rs.c, mc, rs.l_run)
+                               : FO::template probs<false>(rs.s_cur, rs.c, mc, rs.l_run);
+        FO::pv(stage + TB, off, pw, rs.o, rs.l_acc);
+    }
+    if (live_next) {
+        if (rs.needs_mask(t + 1)) FO::mask(s_next, (t + 1) * 64, rs.half, rs.key_end, rs.lim_lane);
+        rs.mx_cur = FO::rowmax(s_next);
+    }
+    rs.s_cur[0] = s_next[0];
+    rs.s_cur[1] = s_next[1];
+}
+
+template <int D, int NW, bool OUT_F32>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 8 ? 2 : 1)))
+fa_prefill_fp8_kernel(const Params p, const float v_descale)
+{
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
+    constexpr int BN = 64;
+    constexpr int BM = 32 * NW;
+    using TL = TileLoader<D / 2, BN, NW>;
+    using FO = Fp8Ops<D>;
+    constexpr int TB = TL::TILE_BYTES;
+    constexpr int STAGE = 2 * TB;
+
+    __shared__ __attribute__((aligned(1024))) char lds[kPrefillStages * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 31;
+    const int half = lane >> 5;
+
+    Fp8Offsets<D> off;
+    off.init(lane);
+
+    const uint8_t *q8 = reinterpret_cast<const uint8_t *>(p.q);
+    const uint8_t *k8 = reinterpret_cast<const uint8_t *>(p.k);
+    const uint8_t *v8 = reinterpret_cast<const uint8_t *>(p.v);
+
+    const int BH = p.B * p.Hq;
+    const int ND = p.domains;
+    const int x = blockIdx.x % ND;
+    const int jw = blockIdx.x / ND;
+    const int Gx = gridDim.x / ND;
+    const int BHx = BH / ND;
+    const int Nx = BHx * p.n_mblocks;
+
+    for (int it = 0; it * Gx < Nx; ++it) {
+        const int li = it * Gx + ((it & 1) ? (Gx - 1 - jw) : jw);
+        if (li >= Nx) continue;
+        const int rank = p.head_major ? li % p.n_mblocks : li / BHx;
+        const int bh = (p.head_major ? li / p.n_mblocks : li % BHx) * ND + x;
+        const int mb = p.causal ? (p.n_mblocks - 1 - rank) : rank;
+        const int b = bh / p.Hq;
+        const int hq = bh % p.Hq;
+        const int g = hq / p.group;
+
+        const int row0 = mb * BM;
+        const int wrow0 = row0 + wave * 32;
+        const int qi = wrow0 + col;
+        const int last_row = min(row0 + BM, p.Sq) - 1;
+        const int wlast = min(wrow0 + 31, p.Sq - 1);
+
+        int n_tiles = (p.Sk + BN - 1) / BN;
+        if (p.causal) {
+            const int hi = last_row + p.off;
+            n_tiles = hi < 0 ? 0 : min(n_tiles, hi / BN + 1);
+        }
+
+        Fp8RowState<D> rs;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) rs.o[db] = f32x16_t{};
+        rs.m_ref = kNegInf;
+        rs.l_run = 0.0f;
+        rs.l_acc = f32x16_t{};
+        rs.s_cur[0] = f32x16_t{};
+        rs.s_cur[1] = f32x16_t{};
+        rs.mx_cur = kNegInf;
+        rs.half = half;
+        rs.c = p.c;
+        rs.key_end = p.Sk;
+        rs.lim_lane = p.causal ? qi + p.off : 0x7fffffff;
+        rs.wmin_lim = p.causal ? wrow0 + p.off : 0x7fffffff;
+        if (wrow0 >= p.Sq)
+            rs.NBw = 0;
+        else if (p.causal) {
+            const int wmax_lim = wlast + p.off;
+            rs.NBw = wmax_lim < 0 ? 0 : min(n_tiles, wmax_lim / BN + 1);
+        } else
+            rs.NBw = n_tiles;
+
+        TL ld;
+        ld.setup(reinterpret_cast<const uint16_t *>(k8 + ((long)b * p.Sk * p.Hkv + g) * D),
+                 reinterpret_cast<const uint16_t *>(v8 + ((long)b * p.Sk * p.Hkv + g) * D),
+                 p.Hkv * D, p.Sk);
+
+        if (n_tiles > 0) ld.issue(lds, lds + TB, 0, wave, lane);
+        if (n_tiles > 1) ld.issue(lds + STAGE, lds + STAGE + TB, BN, wave, lane);
+        {
+            // this lane's Q bytes: k-step st, dims 64 st + 32 half .. + 31
+            const uint8_t *qrow = q8 + (((long)b * p.Sq + min(qi, p.Sq - 1)) * p.Hq + hq) * D;
+#pragma unroll
+            for (int st = 0; st < D / 64; ++st) {
+                const u32x4_t lo = ld16(reinterpret_cast<const uint16_t *>(qrow + 64 * st + 32 * half));
+                const u32x4_t hi =
+                    ld16(reinterpret_cast<const uint16_t *>(qrow + 64 * st + 32 * half + 16));
+                rs.qf[st] = (i32x8_t){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                      (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+            }
+        }
+        wait_vmem();
+        // a negative scale negates Q exactly (E4M3 sign bits)
+#pragma unroll
+        for (int st = 0; st < D / 64; ++st) {
+            if (p.qflip) rs.qf[st] ^= (int)0x80808080u;
+            asm volatile("" ::"v"(rs.qf[st]));
+        }
+        if (n_tiles > 0) {
+            __syncthreads();
+            if (rs.NBw > 0) {
+                FO::qk(lds, off, rs.qf, rs.s_cur);
+                if (rs.needs_mask(0)) FO::mask(rs.s_cur, 0, half, rs.key_end, rs.lim_lane);
+                rs.mx_cur = FO::rowmax(rs.s_cur);
+            }
+        }
+        for (int t = 0; t < n_tiles; t += 3) {
+            prefill_tile_fp8<D, NW>(t, n_tiles, lds, lds + STAGE, lds + 2 * STAGE, ld, wave, lane,
+                                    off, rs);
+            if (t + 1 < n_tiles)
+                prefill_tile_fp8<D, NW>(t + 1, n_tiles, lds + STAGE, lds + 2 * STAGE, lds, ld,
+                                        wave, lane, off, rs);
+            if (t + 2 < n_tiles)
+                prefill_tile_fp8<D, NW>(t + 2, n_tiles, lds + 2 * STAGE, lds, lds + STAGE, ld,
+                                        wave, lane, off, rs);
+        }
+        __syncthreads();   // every wave is done with the LDS ring before the next item
+
+        // O = v_descale * O / l: the descale folds into the normaliser
+        finish_rows<D, OUT_F32>(rs.o, rs.m_ref, rs.l_run, rs.l_acc[0] / v_descale, p.c, half,
+                                p.o, (((long)b * p.Sq + qi) * p.Hq + hq) * D,
+                                p.lse ? p.lse + ((long)b * p.Hq + hq) * p.Sq + qi : nullptr,
+                                qi < p.Sq);
+    }
+#endif
+}
+
+// ---------------------------------------------------------------------------
 // Wide prefill: one wave per SIMD, 64 query rows per wave (column blocks
 // r = 0, 1 of 32 rows), so that each K and V operand read from LDS feeds two
 // MFMAs -- half the LDS reads per flop of the kernel above.  With one wave
@@ -2006,6 +2382,30 @@ static void with_head_dim(const Launch &L, F &&f)
         out(std::integral_constant<int, 128>{});
     else
         out(std::integral_constant<int, 64>{});
+}
+
+hipError_t launch_prefill_fp8(const Launch &L, float v_descale)
+{
+    if (L.D != 128 || (L.prefill_nw != 4 && L.prefill_nw != 8)) return hipErrorInvalidValue;
+    Params p = make_params(L);
+    const int BH = L.B * L.Hq;
+    const int bm = 32 * L.prefill_nw;
+    p.n_mblocks = (L.Sq + bm - 1) / bm;
+    p.domains = (BH % 8 == 0 && L.grid % 8 == 0) ? 8 : 1;
+    p.head_major = L.head_major;
+    dim3 g(L.grid), blk(64 * L.prefill_nw);
+    auto go = [&](auto nw, auto of) {
+        hipLaunchKernelGGL((fa_prefill_fp8_kernel<128, decltype(nw)::value, decltype(of)::value>),
+                           g, blk, 0, L.stream, p, v_descale);
+    };
+    if (L.prefill_nw == 8) {
+        if (L.o_f32) go(std::integral_constant<int, 8>{}, std::true_type{});
+        else go(std::integral_constant<int, 8>{}, std::false_type{});
+    } else {
+        if (L.o_f32) go(std::integral_constant<int, 4>{}, std::true_type{});
+        else go(std::integral_constant<int, 4>{}, std::false_type{});
+    }
+    return hipGetLastError();
 }
 
 static hipError_t launch_merge(const Launch &L, const Params &p)

@@ -60,4 +60,11 @@ struct PagedLaunch {
 };
 hipError_t launch_decode_paged(const Launch &L, const PagedLaunch &P);
 
+// FP8 E4M3 prefill: L.q/k/v hold E4M3 codes, L.scale already includes the
+// q and k descales; O is multiplied by v_descale.  64-key tiles, 32 rows per
+// wave, L.prefill_nw waves (4 or 8) per workgroup, L.grid workgroups.
+constexpr int kFp8BN = 64;
+inline int fp8_lds_bytes(int D) { return kPrefillStages * 2 * kFp8BN * D; }
+hipError_t launch_prefill_fp8(const Launch &L, float v_descale);
+
 }  // namespace fa

@@ -11,7 +11,8 @@ in HBM:
     cache): every sequence at 8192 keys, then lengths drawn from [1, 16384]
     (one fa_fwd_paged call each: paged split kernel and merge), and
   * head dim 256: a causal prefill, B=2, H=16, S=4096, and the decode shape
-    (one fa_fwd call each).
+    (one fa_fwd call each), and
+  * the causal prefill's shape on FP8 E4M3 inputs (one fa_fwd_fp8 call).
 Both go to the same stream; HIP events recorded on that stream around each
 call give the per-call durations.
 
@@ -19,7 +20,8 @@ Printed: one JSON line.  `value` is the prefill's algorithmic TFLOP/s (4*D
 flops per allowed query-key pair); `decode` holds the decode's algorithmic
 GB/s (Q, K, V read once, O and LSE written once), `paged_decode` and
 `paged_decode_ragged` the paged calls' (plus the block-table entries read),
-`d256_prefill` / `d256_decode` the head-dim-256 calls' TFLOP/s and GB/s.
+`d256_prefill` / `d256_decode` the head-dim-256 calls' TFLOP/s and GB/s,
+`fp8_prefill` the FP8 call's TFLOP/s against the dense FP8 MFMA peak.
 `roofline` is the prefill kernel against the dense bf16 MFMA peak; the decode
 entries' `roofline` their call against HBM.  `cpu_baseline` times the fp64 oracle on a bounded sample of the
 prefill workload's rows and also compares those rows with the timed output.
@@ -47,12 +49,14 @@ METRIC = ("attention fwd TFLOP/s + % bf16 MFMA peak (causal S=4096 D=128); "
           "decode HBM GB/s")
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA (datasheet)
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E (datasheet)
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense FP8 MFMA (datasheet)
 PREFILL = "causal_b4_h16_s4096_d128"
 DECODE = "decode_b32_hq32_hkv8_sk8192_d128"
 PAGED = "paged_decode_b32_hq32_hkv8_len8192_ps16_d128"
 PAGED_RAGGED = "paged_decode_b32_hq32_hkv8_ragged16384_ps16_d128"
 PREFILL_D256 = "causal_b2_h16_s4096_d256"
 DECODE_D256 = "decode_b32_hq32_hkv8_sk8192_d256"
+PREFILL_FP8 = "causal_b4_h16_s4096_d128_fp8"
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 KERNEL_SRC = os.path.join(ROOT, "attention_fwd_02_amd", "csrc", "fa_kernels.hip")
 
@@ -150,6 +154,14 @@ def profile_one(args):
         lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=dev)
         fn = lambda: fa.fa_fwd_paged(q, kc, vc, table, lens, o, lse, w.causal, w.scale)  # noqa: E731
         label = w.name
+    elif args.profile_kernel == "prefill_fp8":
+        from attention_fwd_02_amd.inputs import FP8_WORKLOADS, make_fp8_inputs
+        w = FP8_WORKLOADS[PREFILL_FP8]
+        q, k, v, dq, dk, dv = make_fp8_inputs(w, device=dev)
+        o = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=dev)
+        fn = lambda: fa.fa_fwd_fp8(q, k, v, o, lse, w.causal, w.scale, dq, dk, dv)  # noqa: E731
+        label = w.name
     elif args.profile_kernel in ("prefill_d256", "decode_d256"):
         from attention_fwd_02_amd.inputs import HEADDIM_WORKLOADS
         w = HEADDIM_WORKLOADS[PREFILL_D256 if args.profile_kernel == "prefill_d256"
@@ -182,7 +194,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-kernel",
                     choices=["prefill", "decode", "paged", "paged_ragged", "prefill_d256",
-                             "decode_d256", "copy"],
+                             "decode_d256", "prefill_fp8", "copy"],
                     help="run only this call (warmup + steps) for counter collection; "
                          "'copy' is a plain 1 GiB device-to-device copy that calibrates "
                          "the HBM byte counters")
@@ -194,8 +206,9 @@ def main():
 
     import torch
     from attention_fwd_02_amd import _binding as fa
-    from attention_fwd_02_amd.inputs import (HEADDIM_WORKLOADS, PAGED_WORKLOADS, WORKLOADS,
-                                             make_inputs, make_paged_inputs)
+    from attention_fwd_02_amd.inputs import (FP8_WORKLOADS, HEADDIM_WORKLOADS, PAGED_WORKLOADS,
+                                             WORKLOADS, make_fp8_inputs, make_inputs,
+                                             make_paged_inputs)
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
@@ -225,6 +238,11 @@ def main():
         d256[key] = (w, q, k, v, torch.empty_like(q),
                      torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=dev))
 
+    wf = FP8_WORKLOADS[PREFILL_FP8]
+    qf8, kf8, vf8, dqf, dkf, dvf = make_fp8_inputs(wf, device=dev)
+    of8 = torch.empty(qf8.shape, dtype=torch.bfloat16, device=dev)
+    lf8 = torch.empty((wf.B, wf.Hq, wf.Sq), dtype=torch.float32, device=dev)
+
     stream = torch.cuda.current_stream()
 
     def prefill():
@@ -241,9 +259,12 @@ def main():
         w, q, k, v, o, lse = d256[key]
         fa.fa_fwd(q, k, v, o, lse, w.causal, w.scale, stream=stream)
 
+    def fp8_call():
+        fa.fa_fwd_fp8(qf8, kf8, vf8, of8, lf8, wf.causal, wf.scale, dqf, dkf, dvf, stream=stream)
+
     def step(evs=None):
         calls = (prefill, decode, lambda: paged_call(PAGED), lambda: paged_call(PAGED_RAGGED),
-                 lambda: d256_call(PREFILL_D256), lambda: d256_call(DECODE_D256))
+                 lambda: d256_call(PREFILL_D256), lambda: d256_call(DECODE_D256), fp8_call)
         for i, call in enumerate(calls):
             if evs:
                 evs[i].record(stream)
@@ -256,7 +277,7 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(K)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(K)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
@@ -312,6 +333,19 @@ def main():
                 "roofline": roofline(gb, PEAK_HBM_GBPS, "GB/s", "hbm",
                                      measured_traffic("decode_d256"))}
 
+    def fp8_entry(i):
+        ms = sorted(e[i].elapsed_time(e[i + 1]) for e in evs)
+        avg = sum(ms) / K
+        tf = wf.flops() / (avg * 1e-3) / 1e12
+        return {"workload": PREFILL_FP8, "value": round(tf, 3), "unit": "TFLOP/s",
+                "config": {"B": wf.B, "Hq": wf.Hq, "Hkv": wf.Hkv, "Sq": wf.Sq, "Sk": wf.Sk,
+                           "D": wf.D, "causal": wf.causal, "inputs": "FP8 E4M3, per-tensor descale",
+                           "algorithmic_flops": wf.flops()},
+                "ms": {"avg": round(avg, 4), "median": round(ms[K // 2], 4),
+                       "min": round(ms[0], 4)},
+                "roofline": roofline(tf, PEAK_FP8_TFLOPS, "TFLOP/s", "mfma",
+                                     measured_traffic("prefill_fp8"))}
+
     flops = wp.flops()
     tflops = flops / (p_avg * 1e-3) / 1e12
     dbytes = wd.hbm_bytes()
@@ -339,7 +373,8 @@ def main():
                          f"{DECODE} (decode B=32 Hq=32 Hkv=8 Sq=1 Sk=8192 D=128) + "
                          f"{PAGED} and {PAGED_RAGGED} (the decode over 16-key pages; "
                          "8192 keys each, then lengths drawn from [1, 16384]) + "
-                         f"{PREFILL_D256} and {DECODE_D256} (head dim 256)"),
+                         f"{PREFILL_D256} and {DECODE_D256} (head dim 256) + "
+                         f"{PREFILL_FP8} (the causal prefill on FP8 E4M3 inputs)"),
             "prefill": {"B": wp.B, "Hq": wp.Hq, "Hkv": wp.Hkv, "Sq": wp.Sq, "Sk": wp.Sk,
                         "D": wp.D, "causal": wp.causal, "algorithmic_flops": flops,
                         "plan": plan_p},
@@ -362,6 +397,7 @@ def main():
         "paged_decode_ragged": paged_entry(PAGED_RAGGED, 3),
         "d256_prefill": d256_entry(PREFILL_D256, 4),
         "d256_decode": d256_entry(DECODE_D256, 5),
+        "fp8_prefill": fp8_entry(6),
         "roofline": roofline(tflops, PEAK_BF16_TFLOPS, "TFLOP/s", "mfma",
                              measured_traffic("prefill")),
         "cpu_baseline": None,

@@ -178,6 +178,29 @@ fa_status fa_fwd_paged(const void *q, const void *k_cache, const void *v_cache,
 fa_status fa_plan_paged(int B, int Hq, int Hkv, int Sq, int D, int num_pages, int page_size,
                         int max_pages, int num_splits, fa_plan_info *out);
 
+/*
+ * fa_fwd_fp8 -- the attention forward on OCP FP8 E4M3 inputs with per-tensor
+ * descale factors.  The pages list FP8 only as a capability of the SM90
+ * kernel ("SM80 内核实现对比", section 7.3, the FP8 row); the convention is
+ * this library's, the usual per-tensor one: the real inputs are
+ * q_descale * q, k_descale * k, v_descale * v, and the result is fa_fwd's on
+ * those values:
+ *
+ *   q [B][Sq][Hq][D], k, v [B][Sk][Hkv][D]: E4M3 codes, one byte each, device
+ *   o [B][Sq][Hq][D] bf16 or f32 (o_dtype), lse [B][Hq][Sq] f32 or NULL
+ *
+ * Scores are formed exactly from the codes (products and sums in fp32) and
+ * scaled by scale * q_descale * k_descale; P is rounded to E4M3 for the P V
+ * product and O is normalised by the sum of the rounded P; the LSE uses the
+ * unrounded fp32 P.  D = 128 only (else FA_ERR_UNSUPPORTED); descales must be
+ * finite and > 0 (else FA_ERR_INVALID_ARG).  Layout, causal convention,
+ * alignment, asynchrony and errors as for fa_fwd; no workspace.
+ */
+fa_status fa_fwd_fp8(const void *q, const void *k, const void *v, void *o, float *lse, int B,
+                     int Hq, int Hkv, int Sq, int Sk, int D, int causal, float scale,
+                     float q_descale, float k_descale, float v_descale, hipStream_t stream,
+                     fa_dtype o_dtype);
+
 /* fa_last_error -- message for the last non-OK status of this host thread
  * ("" if none).  The pointer stays valid until the next call on this thread. */
 const char *fa_last_error(void);

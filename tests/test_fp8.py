@@ -1,0 +1,182 @@
+"""GPU parity of the FP8 E4M3 forward (fa_fwd_fp8) against the FP8 oracle.
+
+The kernel rounds P to E4M3 (3 mantissa bits) before the P V product, so O
+is held to a bound derived from that rounding rather than to the flat 1e-2
+of the bf16 path.  For a row with allowed keys j, scores s_j (exact, from
+the descaled inputs), M = max s_j, e_j = exp(s_j - M) and the exact output O:
+
+    the kernel's P_j is e_j * F with F = exp(M - m_ref) >= 1 (its reference
+    max is at most the true one), rounded to nearest: |dP_j| <= 2^-4 P_j in
+    E4M3's normal range and <= 2^-10 (half the subnormal spacing) below it;
+    O normalised by the sum of the rounded P gives
+        O_gpu - O = sum_j dP_j (v_j - O) / sum_j (P_j + dP_j),
+    so, per head dim d, with F = 1 the worst case,
+        |O_gpu - O|_d <= (2^-4 sum_j e_j |v_jd - O_d| + 2^-10 sum_j |v_jd - O_d|)
+                         / ((1 - 2^-4) sum_j e_j - N 2^-10).
+
+The test allows that bound plus 1e-3 * max|v| (fp32 arithmetic) plus half an
+output ulp for bf16 O.  The LSE uses the unrounded fp32 P: 1e-3 as for bf16.
+"""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from attention_fwd_02_amd.inputs import FP8_WORKLOADS, make_fp8_inputs, random_fp8
+from tests.helpers import LSE_TOL, bf16_half_ulp, to64
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def ops():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from attention_fwd_02_amd import _binding
+    return _binding
+
+
+@pytest.fixture(scope="module")
+def oracle():
+    import oracle as o
+    o._load()
+    return o
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def fp8_bound(oracle, q8, k8, v8, causal, scale, dq, dk, dv, rows, o_ref):
+    """Per-(row, dim) bound of the E4M3 rounding of P (module docstring)."""
+    q = oracle.fp8_values(q8) * dq
+    k = oracle.fp8_values(k8) * dk
+    v = oracle.fp8_values(v8) * dv
+    B, Sq, Hq, D = q.shape
+    Sk, Hkv = k.shape[1], k.shape[2]
+    group = Hq // Hkv
+    tol = np.zeros((len(rows), D))
+    vmax = np.zeros(len(rows))
+    for n, (b, h, i) in enumerate(rows):
+        g = h // group
+        nk = Sk if not causal else max(0, min(Sk, i + Sk - Sq + 1))
+        if nk == 0:
+            continue
+        s = (k[b, :nk, g, :] @ q[b, i, h, :]) * scale
+        e = np.exp(s - s.max())
+        dev = np.abs(v[b, :nk, g, :] - o_ref[n][None, :])
+        den = (1 - 2.0 ** -4) * e.sum() - nk * 2.0 ** -10
+        den = max(den, 1e-3 * e.sum())
+        tol[n] = (2.0 ** -4 * (e[:, None] * dev).sum(0) + 2.0 ** -10 * dev.sum(0)) / den
+        vmax[n] = np.abs(v[b, :nk, g, :]).max()
+    return tol, vmax
+
+
+def check_fp8(ops, oracle, q8, k8, v8, causal, scale, dq, dk, dv, out="bf16", rows=None,
+              label=""):
+    B, Sq, Hq, D = q8.shape
+    o = torch.empty((B, Sq, Hq, D), dtype=torch.float32 if out == "f32" else torch.bfloat16,
+                    device=DEV)
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=DEV)
+    ops.fa_fwd_fp8(q8.to(DEV), k8.to(DEV), v8.to(DEV), o, lse, causal, scale, dq, dk, dv)
+    torch.cuda.synchronize()
+    if rows is None:
+        rows = np.array([(b, h, i) for b in range(B) for h in range(Hq) for i in range(Sq)],
+                        dtype=np.int64)
+    o_ref, lse_ref = oracle.attn_fwd_fp8(q8, k8, v8, causal, scale, dq, dk, dv, rows=rows)
+    og, lg = to64(o), to64(lse)
+    o_s = np.stack([og[b, i, h] for b, h, i in rows])
+    l_s = np.array([lg[b, h, i] for b, h, i in rows])
+    assert not np.isnan(o_s).any() and not np.isnan(l_s).any(), f"{label}: NaN"
+    tol, vmax = fp8_bound(oracle, q8, k8, v8, causal, scale, dq, dk, dv, rows, o_ref)
+    tol = tol + 1e-3 * vmax[:, None] + (bf16_half_ulp(o_ref) if out == "bf16" else 0.0) + 1e-6
+    err = np.abs(o_s - o_ref)
+    bad = err > tol
+    if bad.any():
+        n, d = np.unravel_index(np.argmax(err - tol), err.shape)
+        raise AssertionError(f"{label}: O mismatch at row {tuple(rows[n])} dim {d}: "
+                             f"gpu={o_s[n, d]!r} oracle={o_ref[n, d]!r} err={err[n, d]:.3e} "
+                             f"bound={tol[n, d]:.3e} ({bad.sum()} of {bad.size} outside)")
+    ninf = np.isneginf(lse_ref)
+    assert np.array_equal(np.isneginf(l_s), ninf), f"{label}: -inf LSE rows differ"
+    assert np.all(o_s[ninf] == 0.0), f"{label}: rows without keys must be 0"
+    if (~ninf).any():
+        lerr = np.abs(l_s[~ninf] - lse_ref[~ninf]).max()
+        assert lerr <= LSE_TOL, f"{label}: LSE error {lerr:.3e}"
+    say(f"[fp8] {label}: {len(rows)} rows, max|dO|={err.max():.3e}, "
+        f"max(|dO|/bound)={(err / tol).max():.3f}")
+
+
+SHAPES = [
+    # B, Hq, Hkv, Sq, Sk, causal, out
+    (1, 1, 1, 128, 128, False, "f32"),
+    (1, 2, 2, 200, 333, True, "bf16"),        # ragged, causal with Sk > Sq
+    (2, 8, 2, 129, 257, False, "bf16"),       # GQA, one row past a block
+    (1, 2, 2, 300, 100, True, "f32"),         # Sq > Sk: leading rows see no key
+    (2, 4, 4, 513, 513, True, "bf16"),        # several items + tail
+    (1, 1, 1, 1, 1, False, "f32"),            # one query, one key
+    (1, 2, 1, 640, 640, False, "bf16"),       # several tiles, MQA
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_fp8_shapes_elementwise(ops, oracle, shape):
+    B, Hq, Hkv, Sq, Sk, causal, out = shape
+    say(f"[fp8] shape {shape}")
+    q8, k8, v8, dq, dk, dv = random_fp8(B, Hq, Hkv, Sq, Sk, 128, seed=Sq * 7 + Sk)
+    check_fp8(ops, oracle, q8, k8, v8, causal, 1.0 / math.sqrt(128), dq, dk, dv, out=out,
+              label=str(shape))
+
+
+@pytest.mark.parametrize("scale", [-0.1, 0.0, 0.4])
+def test_fp8_scale_sign_and_zero(ops, oracle, scale):
+    q8, k8, v8, dq, dk, dv = random_fp8(1, 2, 2, 150, 150, 128, seed=31)
+    check_fp8(ops, oracle, q8, k8, v8, True, scale, dq, dk, dv, out="f32",
+              label=f"scale={scale}")
+
+
+def test_fp8_waves4_config(ops, oracle, monkeypatch):
+    # the 4-wave configuration (one wave per SIMD), forced
+    monkeypatch.setenv("FA_FP8_NW", "4")
+    q8, k8, v8, dq, dk, dv = random_fp8(2, 4, 2, 600, 700, 128, seed=41)
+    check_fp8(ops, oracle, q8, k8, v8, True, 1.0 / math.sqrt(128), dq, dk, dv, label="nw=4")
+
+
+def test_fp8_rejects_bad_descales_and_head_dims(ops):
+    q8, k8, v8, dq, dk, dv = random_fp8(1, 1, 1, 8, 8, 128, seed=1, device=DEV)
+    o = torch.empty((1, 8, 1, 128), dtype=torch.bfloat16, device=DEV)
+    for bad in (0.0, -1.0, float("inf"), float("nan")):
+        with pytest.raises(ops.FaError) as e:
+            ops.fa_fwd_fp8(q8, k8, v8, o, None, False, 0.1, bad, dk, dv)
+        assert e.value.status == 1
+    q6, k6, v6, *_ = random_fp8(1, 1, 1, 8, 8, 64, seed=1, device=DEV)
+    with pytest.raises(ops.FaError) as e:
+        ops.fa_fwd_fp8(q6, k6, v6, torch.empty((1, 8, 1, 64), dtype=torch.bfloat16,
+                                                 device=DEV), None, False, 0.1, dq, dk, dv)
+    assert e.value.status == 2
+
+
+@pytest.mark.parametrize("name", list(FP8_WORKLOADS))
+def test_fp8_full_size_workload_sampled(ops, oracle, name):
+    w = FP8_WORKLOADS[name]
+    say(f"[fp8] full-size workload {name}")
+    q8, k8, v8, dq, dk, dv = make_fp8_inputs(w)
+    rng = np.random.default_rng(w.seed)
+    rows = {(b, h, i) for b in (0, w.B - 1) for h in (0, w.Hq - 1)
+            for i in (0, 1, 63, 64, 127, 128, w.Sq // 2, w.Sq - 1)}
+    for _ in range(160):
+        rows.add((int(rng.integers(w.B)), int(rng.integers(w.Hq)), int(rng.integers(w.Sq))))
+    qv = q8.float().abs().amax(dim=-1)            # hot rows: the x8 ones
+    hot = (qv > qv.median() * 4).nonzero().tolist()
+    for b, i, h in hot[:: max(1, len(hot) // 48)][:48]:
+        rows.add((b, h, i))
+    rows = np.array(sorted(rows), dtype=np.int64)
+    check_fp8(ops, oracle, q8, k8, v8, w.causal, w.scale, dq, dk, dv, out=w.o_dtype, rows=rows,
+              label=name)
