@@ -21,6 +21,10 @@ gather is pinned by hand-placed page contents with closed-form answers in
 codes with its own table, written from the format's definition and pinned
 code by code against it and against torch's float8_e4m3fn, then applies the
 same definition; planted decode and descale slips must fail its pins.
+``attn_bwd`` (dQ, dK, dV) is the gradient of the definition written out in
+numpy fp64; it is pinned against torch's fp64 autograd of the forward
+definition, central finite differences and closed forms, and five planted
+slips must fail those pins.
 """
 from __future__ import annotations
 
@@ -234,3 +238,54 @@ def attn_fwd_fp8(q8, k8, v8, causal: bool, scale: float, q_descale: float, k_des
                       float(scale) * float(q_descale) * float(k_descale), rows=rows,
                       nthreads=nthreads, _lib_override=_lib_override)
     return o * float(v_descale), lse
+
+
+def attn_bwd(q, k, v, do, causal: bool, scale: float):
+    """Gradients of the attention forward, in fp64, straight from its definition.
+
+    The pages list the backward pass only by the title of a page that is not
+    reproduced ("SM80 内核实现对比", navigation), so this follows the
+    mathematics of O = softmax(scale * Q K^T [+ causal mask]) V alone.  For one
+    (b, query head) with allowed-key mask, P = softmax(scale * Q K^T) row by
+    row, and for the upstream gradient dO:
+        dV = P^T dO
+        dP = dO V^T
+        dS = P * (dP - rowsum(dP * P))            (softmax Jacobian, per row)
+        dQ = scale * dS K,   dK = scale * dS^T Q
+    Query heads sharing a KV head (hq / (Hq / Hkv)) add their dK and dV.
+    Rows with no allowed key have P = 0 and contribute nothing.  Plain numpy
+    matrix products on float64 values of the bf16 inputs.
+
+    q, do: [B, Sq, Hq, D]; k, v: [B, Sk, Hkv, D] (bf16 torch tensors or raw
+    bf16 bits).  Returns (dq, dk, dv) float64 in the same layouts.
+    """
+    def f64(x):
+        bits = _bits(x).astype(np.uint32) << 16
+        return bits.view(np.float32).astype(np.float64)
+
+    Q, K, V, dO = f64(q), f64(k), f64(v), f64(do)
+    B, Sq, Hq, D = Q.shape
+    Sk, Hkv = K.shape[1], K.shape[2]
+    group = Hq // Hkv
+    dQ = np.zeros_like(Q)
+    dK = np.zeros_like(K)
+    dV = np.zeros_like(V)
+    i = np.arange(Sq)[:, None]
+    j = np.arange(Sk)[None, :]
+    allowed = (j <= i + (Sk - Sq)) if causal else np.ones((Sq, Sk), dtype=bool)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // group
+            s = scale * (Q[b, :, h, :] @ K[b, :, g, :].T)
+            s = np.where(allowed, s, -np.inf)
+            m = s.max(axis=1, keepdims=True)
+            live = np.isfinite(m)
+            e = np.where(allowed, np.exp(s - np.where(live, m, 0.0)), 0.0)
+            l = e.sum(axis=1, keepdims=True)
+            p = np.where(l > 0, e / np.where(l > 0, l, 1.0), 0.0)
+            dV[b, :, g, :] += p.T @ dO[b, :, h, :]
+            dp = dO[b, :, h, :] @ V[b, :, g, :].T
+            ds = p * (dp - (dp * p).sum(axis=1, keepdims=True))
+            dQ[b, :, h, :] = scale * (ds @ K[b, :, g, :])
+            dK[b, :, g, :] += scale * (ds.T @ Q[b, :, h, :])
+    return dQ, dK, dV

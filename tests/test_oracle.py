@@ -514,3 +514,87 @@ def test_fp8_equals_bf16_oracle_on_exact_values(oracle_mod):
                                  v8.float().to(torch.bfloat16), True, 0.3)
     np.testing.assert_array_equal(o1, o2)
     np.testing.assert_array_equal(l1, l2)
+
+
+# ----------------------------------------------------------------------------
+# backward: against torch autograd (fp64), finite differences, closed forms
+# ----------------------------------------------------------------------------
+def torch_grads(q, k, v, do, causal, scale):
+    """fp64 autograd of softmax(scale Q K^T [mask]) V: a different evaluation
+    of the same gradients (no hand-written backward formula)."""
+    Q, K, V, dO = (t.double().clone().requires_grad_(i < 3) for i, t in enumerate((q, k, v, do)))
+    B, Sq, Hq, D = Q.shape
+    Sk, Hkv = K.shape[1], K.shape[2]
+    Ke = K.repeat_interleave(Hq // Hkv, dim=2)
+    Ve = V.repeat_interleave(Hq // Hkv, dim=2)
+    s = torch.einsum("bihd,bjhd->bhij", Q, Ke) * scale
+    if causal:
+        i = torch.arange(Sq)[:, None]
+        j = torch.arange(Sk)[None, :]
+        s = s.masked_fill(~(j <= i + Sk - Sq), float("-inf"))
+    p = torch.softmax(s, dim=-1)
+    p = torch.nan_to_num(p, nan=0.0)
+    o = torch.einsum("bhij,bjhd->bihd", p, Ve)
+    (o * dO).sum().backward()
+    return Q.grad.numpy(), K.grad.numpy(), V.grad.numpy()
+
+
+@pytest.mark.parametrize("shape", [(1, 2, 2, 5, 7, 8, False), (2, 4, 2, 6, 6, 4, True),
+                                   (1, 3, 1, 7, 4, 8, True)])
+def test_bwd_matches_torch_autograd(oracle_mod, shape):
+    B, Hq, Hkv, Sq, Sk, D, causal = shape
+    q, k, v = random_qkv(B, Hq, Hkv, Sq, Sk, D, seed=51)
+    do = bf16(torch.randn(B, Sq, Hq, D, generator=torch.Generator().manual_seed(52)))
+    got = oracle_mod.attn_bwd(q, k, v, do, causal, 0.4)
+    ref = torch_grads(q.float(), k.float(), v.float(), do.float(), causal, 0.4)
+    for g, r, name in zip(got, ref, ("dq", "dk", "dv")):
+        np.testing.assert_allclose(g, r, rtol=1e-10, atol=1e-12, err_msg=name)
+
+
+def test_bwd_matches_finite_differences(oracle_mod):
+    # L = sum(O * dO); central differences of the fp64 forward definition
+    q, k, v = random_qkv(1, 2, 1, 4, 5, 4, seed=53)
+    do = bf16(torch.randn(1, 4, 2, 4, generator=torch.Generator().manual_seed(54)))
+    dq, dk, dv = oracle_mod.attn_bwd(q, k, v, do, True, 0.7)
+    Q, K, V, dO = (t.double().numpy() for t in (q.float(), k.float(), v.float(), do.float()))
+
+    def loss(Q, K, V):
+        total = 0.0
+        for h in range(2):
+            s = 0.7 * Q[0, :, h] @ K[0, :, 0].T
+            s = np.where(np.arange(5)[None, :] <= np.arange(4)[:, None] + 1, s, -np.inf)
+            p = np.exp(s - s.max(1, keepdims=True))
+            p /= p.sum(1, keepdims=True)
+            total += ((p @ V[0, :, 0]) * dO[0, :, h]).sum()
+        return total
+
+    eps = 1e-6
+    for X, G in ((Q, dq), (K, dk), (V, dv)):
+        for idx in [(0, 0, 0, 0), (0, 2, 0, 3), (0, 3, X.shape[2] - 1, 1)]:
+            Xp, Xm = X.copy(), X.copy()
+            Xp[idx] += eps
+            Xm[idx] -= eps
+            args_p = [Xp if Y is X else Y for Y in (Q, K, V)]
+            args_m = [Xm if Y is X else Y for Y in (Q, K, V)]
+            fd = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+            assert G[idx] == pytest.approx(fd, abs=1e-7), idx
+
+
+def test_bwd_single_key_closed_form(oracle_mod):
+    # one key: P = 1, so dV = sum over queries of dO, and dQ = dK = 0
+    q, k, v = random_qkv(1, 2, 1, 3, 1, 4, seed=55)
+    do = bf16(torch.randn(1, 3, 2, 4, generator=torch.Generator().manual_seed(56)))
+    dq, dk, dv = oracle_mod.attn_bwd(q, k, v, do, False, 0.5)
+    assert np.all(dq == 0.0) and np.all(dk == 0.0)
+    np.testing.assert_allclose(dv[0, 0, 0], do.double().numpy()[0].sum(axis=(0, 1)), rtol=1e-15)
+
+
+def test_bwd_uniform_scores_dv_is_column_mean(oracle_mod):
+    # K = 0: P = 1/Sk for every allowed key; dV_j = sum over queries of dO / Sk
+    q, _, v = random_qkv(1, 1, 1, 3, 4, 4, seed=57)
+    k = bf16(np.zeros((1, 4, 1, 4)))
+    do = bf16(torch.randn(1, 3, 1, 4, generator=torch.Generator().manual_seed(58)))
+    _, _, dv = oracle_mod.attn_bwd(q, k, v, do, False, 0.5)
+    expect = do.double().numpy()[0, :, 0, :].sum(axis=0) / 4.0
+    for j in range(4):
+        np.testing.assert_allclose(dv[0, j, 0], expect, rtol=1e-14)

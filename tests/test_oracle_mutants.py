@@ -153,3 +153,45 @@ def test_fp8_pins_reject_mutant(name):
         except (AssertionError, IndexError, ValueError):
             caught += 1
     assert caught > 0, f"no pin detects mutant {name}"
+
+
+# slips in the backward oracle (oracle/__init__.py)
+BWD_MUTANTS = {
+    "softmax_jacobian_without_rowsum": ("ds = p * (dp - (dp * p).sum(axis=1, keepdims=True))",
+                                        "ds = p * dp"),
+    "dv_from_unnormalised_p": ("dV[b, :, g, :] += p.T @ dO[b, :, h, :]",
+                               "dV[b, :, g, :] += e.T @ dO[b, :, h, :]"),
+    "dq_scale_dropped": ("dQ[b, :, h, :] = scale * (ds @ K[b, :, g, :])",
+                         "dQ[b, :, h, :] = ds @ K[b, :, g, :]"),
+    "dk_overwritten_not_summed": ("dK[b, :, g, :] += scale * (ds.T @ Q[b, :, h, :])",
+                                  "dK[b, :, g, :] = scale * (ds.T @ Q[b, :, h, :])"),
+    "causal_offset_top_left": ("allowed = (j <= i + (Sk - Sq)) if causal",
+                               "allowed = (j <= i) if causal"),
+}
+
+BWD_PIN_TESTS = [
+    lambda m: pins.test_bwd_matches_torch_autograd(m, (1, 2, 2, 5, 7, 8, False)),
+    lambda m: pins.test_bwd_matches_torch_autograd(m, (2, 4, 2, 6, 6, 4, True)),
+    lambda m: pins.test_bwd_matches_torch_autograd(m, (1, 3, 1, 7, 4, 8, True)),
+    pins.test_bwd_matches_finite_differences,
+    pins.test_bwd_single_key_closed_form,
+    pins.test_bwd_uniform_scores_dv_is_column_mean,
+]
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTANTS))
+def test_bwd_pins_reject_mutant(name):
+    import types
+    before, after = BWD_MUTANTS[name]
+    src = open(oracle_pkg.__file__).read()
+    assert src.count(before) == 1, f"mutation anchor for {name} not found exactly once"
+    mod = types.ModuleType("oracle_mutant")
+    mod.__file__ = oracle_pkg.__file__
+    exec(compile(src.replace(before, after), "oracle_mutant", "exec"), mod.__dict__)
+    caught = 0
+    for pin in BWD_PIN_TESTS:
+        try:
+            pin(mod)
+        except (AssertionError, IndexError, ValueError):
+            caught += 1
+    assert caught > 0, f"no pin detects mutant {name}"
