@@ -21,8 +21,8 @@ STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_INVALID_ARG", 2: "FA_ERR_UNSUPPORTED",
 
 # every symbol include/fa.h declares
 EXPORTS = ["fa_fwd", "fa_fwd_ex", "fa_workspace_size", "fa_plan", "fa_fwd_paged",
-           "fa_plan_paged", "fa_fwd_fp8", "fa_last_error", "fa_release_workspace",
-           "fa_version"]
+           "fa_plan_paged", "fa_fwd_fp8", "fa_bwd", "fa_bwd_workspace_size", "fa_last_error",
+           "fa_release_workspace", "fa_version"]
 
 
 class FaError(RuntimeError):
@@ -65,6 +65,10 @@ def _load():
     lib.fa_fwd_fp8.argtypes = ([c_void_p] * 5 + [c_int] * 7 + [c_float] * 4 +
                                [c_void_p, c_int])
     lib.fa_fwd_fp8.restype = c_int
+    lib.fa_bwd.argtypes = [c_void_p] * 9 + [c_int] * 7 + [c_float, c_void_p, c_void_p, c_size_t]
+    lib.fa_bwd.restype = c_int
+    lib.fa_bwd_workspace_size.argtypes = [c_int] * 6
+    lib.fa_bwd_workspace_size.restype = c_size_t
     lib.fa_last_error.argtypes = []
     lib.fa_last_error.restype = ctypes.c_char_p
     lib.fa_release_workspace.argtypes = []
@@ -247,3 +251,32 @@ def fa_fwd_fp8(q, k, v, o, lse, causal: bool, scale: float, q_descale: float, k_
                           B, Hq, Hkv, Sq, Sk, D, int(bool(causal)), float(scale),
                           float(q_descale), float(k_descale), float(v_descale),
                           _stream_handle(stream), odt))
+
+
+def fa_bwd_workspace_size(B, Hq, Hkv, Sq, Sk, D) -> int:
+    return int(lib.fa_bwd_workspace_size(B, Hq, Hkv, Sq, Sk, D))
+
+
+def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, causal: bool, scale: float, stream=None,
+           workspace=None) -> None:
+    """dq, dk, dv (bf16) of the attention forward that produced o and lse."""
+    import torch
+    B, Hq, Hkv, Sq, Sk, D = _shapes(q, k, v, o, lse)
+    for name, t in (("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bfloat16 tensor")
+    if tuple(dout.shape) != tuple(q.shape) or tuple(dq.shape) != tuple(q.shape):
+        raise ValueError("dout and dq must be [B, Sq, Hq, D]")
+    if tuple(dk.shape) != tuple(k.shape) or tuple(dv.shape) != tuple(k.shape):
+        raise ValueError("dk and dv must be [B, Sk, Hkv, D]")
+    if o.dtype != torch.bfloat16:
+        raise TypeError("o must be bfloat16")
+    if lse is None:
+        raise ValueError("the backward needs the forward's lse")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    _check(lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                      lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                      B, Hq, Hkv, Sq, Sk, D, int(bool(causal)), float(scale),
+                      _stream_handle(stream), ws_ptr, ws_bytes))

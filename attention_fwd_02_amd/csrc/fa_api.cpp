@@ -610,6 +610,84 @@ fa_status fa_fwd_fp8(const void *q, const void *k, const void *v, void *o, float
     return FA_OK;
 }
 
+size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int Sq, int Sk, int D)
+{
+    if (check_sizes(B, Hq, Hkv, Sq, Sk, D) != FA_OK) return 0;
+    return (size_t)B * Hq * Sq * sizeof(float);
+}
+
+fa_status fa_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
+                 const float *lse, void *dq, void *dk, void *dv, int B, int Hq, int Hkv, int Sq,
+                 int Sk, int D, int causal, float scale, hipStream_t stream, void *workspace,
+                 size_t workspace_bytes)
+{
+    g_last_error.clear();
+    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv)
+        return fail(FA_ERR_INVALID_ARG, "no pointer of fa_bwd may be NULL");
+    fa_status st = check_sizes(B, Hq, Hkv, Sq, Sk, D);
+    if (st != FA_OK) return st;
+    if (D != 64 && D != 128) return fail(FA_ERR_UNSUPPORTED, "the backward serves head dims 64 and 128");
+    // Q and dO tiles are addressed like K/V in the forward: 32-bit byte offsets per batch
+    if ((int64_t)Sq * Hq * D * 2 >= (int64_t(1) << 31))
+        return fail(FA_ERR_UNSUPPORTED, "one batch of q exceeds 2 GiB");
+    if (!isfinite(scale)) return fail(FA_ERR_INVALID_ARG, "scale must be finite");
+    if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "causal must be 0 or 1");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+        !aligned16(lse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
+        (workspace && !aligned16(workspace)))
+        return fail(FA_ERR_UNSUPPORTED, "every pointer of fa_bwd must be 16-byte aligned");
+    const size_t need = (size_t)B * Hq * Sq * sizeof(float);
+
+    int dev = 0;
+    DeviceInfo *info = nullptr;
+    st = device_info(&dev, &info);
+    if (st != FA_OK) return st;
+
+    fa::BwdLaunch L;
+    L.q = q; L.k = k; L.v = v; L.o = o; L.dout = dout; L.lse = lse;
+    L.dq = dq; L.dk = dk; L.dv = dv;
+    L.B = B; L.Hq = Hq; L.Hkv = Hkv; L.Sq = Sq; L.Sk = Sk; L.D = D; L.causal = causal;
+    L.scale = scale;
+    L.stream = stream;
+    // one workgroup per CU for both kernels (LDS rings of about 96 KiB)
+    const int64_t items_kv = (int64_t)B * Hkv * ((Sk + fa::kBwdKeysPerWG - 1) / fa::kBwdKeysPerWG);
+    const int64_t items_q = (int64_t)B * Hq * ((Sq + fa::kBwdRowsPerWG - 1) / fa::kBwdRowsPerWG);
+    if (items_kv >= (int64_t(1) << 31) || items_q >= (int64_t(1) << 31))
+        return fail(FA_ERR_UNSUPPORTED, "too many work items");
+    L.grid_dkdv = (int)std::min<int64_t>(items_kv, info->cus);
+    L.grid_dq = (int)std::min<int64_t>(items_q, info->cus);
+
+    std::unique_lock<std::mutex> lk(g_mu, std::defer_lock);
+    void *ws = workspace;
+    if (ws) {
+        if (workspace_bytes < need)
+            return fail(FA_ERR_INVALID_ARG, "workspace_bytes is smaller than fa_bwd_workspace_size()");
+    } else {
+        lk.lock();
+        if (info->ws_bytes < need) {
+            if (info->ws) {
+                (void)hipFree(info->ws);
+                info->ws = nullptr;
+                info->ws_bytes = 0;
+            }
+            void *pw = nullptr;
+            hipError_t e = hipMalloc(&pw, need);
+            if (e != hipSuccess || !pw)
+                return fail(FA_ERR_NOMEM, std::string("workspace hipMalloc: ") + hipGetErrorString(e));
+            info->ws = pw;
+            info->ws_bytes = need;
+        }
+        ws = info->ws;
+    }
+    L.delta = static_cast<float *>(ws);
+    if (log_enabled())
+        fprintf(stderr, "[fa] path=backward B=%d Hq=%d Hkv=%d Sq=%d Sk=%d D=%d causal=%d "
+                "grid_dkdv=%d grid_dq=%d\n", B, Hq, Hkv, Sq, Sk, D, causal, L.grid_dkdv, L.grid_dq);
+    hipError_t e = fa::launch_bwd(L);
+    if (e != hipSuccess) return fail(FA_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
+    return FA_OK;
+}
+
 fa_status fa_plan_paged(int B, int Hq, int Hkv, int Sq, int D, int num_pages, int page_size,
                         int max_pages, int num_splits, fa_plan_info *out)
 {

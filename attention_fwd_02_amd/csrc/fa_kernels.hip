@@ -603,29 +603,24 @@ __device__ __forceinline__ void flip_q(bf16x8_t (&qf)[D / 16], uint32_t qflip)
     for (int st = 0; st < D / 16; ++st) asm volatile("" ::"v"(qf[st]));
 }
 
-// Epilogue of one wave's 32 query columns: O = O / l_norm, and
-// LSE = ln 2 * (c*m + log2 l) from the exact row sum l.  l_norm (whole row)
-// is the sum of the rounded P that O accumulated; l_part is this lane
-// half's share of the exact sum.
+// Store a wave's 32 transposed rows (lane (col, half), register r of block db
+// = element 32 db + 8 (r / 4) + 4 half + r % 4 of row col) times `mult` at
+// out + obase, as bf16 (round to nearest even) or fp32.  All values first,
+// each store's data in registers of its own, then the stores back to back:
+// rewriting a store's data registers right behind it stalls the wave until
+// the store has read them.
 template <int D, bool OUT_F32>
-__device__ __forceinline__ void finish_rows(const f32x16_t (&o)[D / 32], float m_ref,
-                                            float l_part, float l_norm, float c, int half,
-                                            void *out, long obase, float *lse_out, bool write)
+__device__ __forceinline__ void store_rows(const f32x16_t (&o)[D / 32], float mult, int half,
+                                           void *out, long obase)
 {
-    const float l = add_halves(l_part);
-    const float inv = l_norm > 0.0f ? 1.0f / l_norm : 0.0f;
-    if (!write) return;
-    // all values first, each store's data in registers of its own, then the
-    // stores back to back: rewriting a store's data registers right behind
-    // it stalls the wave until the store has read them
     if (OUT_F32) {
         f32x4_t ov[D / 32][4];
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq)
-                ov[db][gq] = (f32x4_t){o[db][4 * gq] * inv, o[db][4 * gq + 1] * inv,
-                                       o[db][4 * gq + 2] * inv, o[db][4 * gq + 3] * inv};
+                ov[db][gq] = (f32x4_t){o[db][4 * gq] * mult, o[db][4 * gq + 1] * mult,
+                                       o[db][4 * gq + 2] * mult, o[db][4 * gq + 3] * mult};
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
@@ -639,8 +634,8 @@ __device__ __forceinline__ void finish_rows(const f32x16_t (&o)[D / 32], float m
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq)
-                ov[db][gq] = (u32x2_t){pack_bf16(o[db][4 * gq] * inv, o[db][4 * gq + 1] * inv),
-                                       pack_bf16(o[db][4 * gq + 2] * inv, o[db][4 * gq + 3] * inv)};
+                ov[db][gq] = (u32x2_t){pack_bf16(o[db][4 * gq] * mult, o[db][4 * gq + 1] * mult),
+                                       pack_bf16(o[db][4 * gq + 2] * mult, o[db][4 * gq + 3] * mult)};
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
@@ -649,6 +644,21 @@ __device__ __forceinline__ void finish_rows(const f32x16_t (&o)[D / 32], float m
                 *reinterpret_cast<u32x2_t *>(static_cast<uint16_t *>(out) + obase + db * 32 + 8 * gq +
                                              4 * half) = ov[db][gq];
     }
+}
+
+// Epilogue of one wave's 32 query columns: O = O / l_norm, and
+// LSE = ln 2 * (c*m + log2 l) from the exact row sum l.  l_norm (whole row)
+// is the sum of the rounded P that O accumulated; l_part is this lane
+// half's share of the exact sum.
+template <int D, bool OUT_F32>
+__device__ __forceinline__ void finish_rows(const f32x16_t (&o)[D / 32], float m_ref,
+                                            float l_part, float l_norm, float c, int half,
+                                            void *out, long obase, float *lse_out, bool write)
+{
+    const float l = add_halves(l_part);
+    const float inv = l_norm > 0.0f ? 1.0f / l_norm : 0.0f;
+    if (!write) return;
+    store_rows<D, OUT_F32>(o, inv, half, out, obase);
     if (lse_out && half == 0) {
         const float mc = (m_ref == kNegInf) ? 0.0f : m_ref * c;
         *lse_out = l > 0.0f ? (mc + __log2f(l)) * kLn2 : kNegInf;
@@ -1380,6 +1390,382 @@ fa_prefill_fp8_kernel(const Params p, const float v_descale)
                                 p.o, (((long)b * p.Sq + qi) * p.Hq + hq) * D,
                                 p.lse ? p.lse + ((long)b * p.Hq + hq) * p.Sq + qi : nullptr,
                                 qi < p.Sq);
+    }
+#endif
+}
+
+// ---------------------------------------------------------------------------
+// Backward: dQ, dK, dV from Q, K, V, O, dO and the forward's LSE.
+//   delta_i = sum_d dO_id O_id                                  (fa_bwd_delta_kernel)
+//   P = exp(scale Q K^T - LSE), dP = dO V^T, dS = P (dP - delta)
+//   dV = P^T dO, dK = scale dS^T Q                              (fa_bwd_dkdv_kernel)
+//   dQ = scale dS K                                             (fa_bwd_dq_kernel)
+// Two main kernels, each recomputing S and dP, so that every output element
+// is owned by one wave (no atomics: results are deterministic).  Both use the
+// forward's operand forms: one side of a product from registers (a row
+// fragment), the other read from an LDS tile, and the transposed operand of
+// the accumulating product read with the transposing LDS load in the key (or
+// query) grouping of the accumulator registers, so that those registers,
+// rounded to bf16, are its B operand directly.
+// ---------------------------------------------------------------------------
+struct BwdParams {
+    const uint16_t *q, *k, *v, *o, *dout;
+    const float *lse;
+    float *delta;
+    uint16_t *dq, *dk, *dv;
+    int B, Hq, Hkv, Sq, Sk, group, causal, off;
+    float c;          // |scale| * log2(e)
+    float scale;      // signed, for dQ and dK
+    uint32_t flip;    // 0x80008000 when scale < 0 (applied to the register fragment of S)
+    int n_blocks;     // dkdv: key blocks per KV head; dq: query blocks per head
+};
+
+// delta[b][h][i] = sum_d dO[b][i][h][d] * O[b][i][h][d], one row per thread.
+template <int D>
+__global__ void __launch_bounds__(256) fa_bwd_delta_kernel(const BwdParams p)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    const long row = (long)blockIdx.x * 256 + threadIdx.x;   // (b, i, h), h fastest
+    if (row >= (long)p.B * p.Sq * p.Hq) return;
+    const uint16_t *orow = p.o + row * D;
+    const uint16_t *drow = p.dout + row * D;
+    float acc = 0.0f;
+#pragma unroll
+    for (int c = 0; c < D; c += 8) {
+        const u32x4_t a = ld16(orow + c), g = ld16(drow + c);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            acc = fmaf(__uint_as_float(a[w] << 16), __uint_as_float(g[w] << 16), acc);
+            acc = fmaf(__uint_as_float(a[w] & 0xffff0000u), __uint_as_float(g[w] & 0xffff0000u),
+                       acc);
+        }
+    }
+    const int h = (int)(row % p.Hq);
+    const long bi = row / p.Hq;
+    const int i = (int)(bi % p.Sq);
+    const int b = (int)(bi / p.Sq);
+    p.delta[((long)b * p.Hq + h) * p.Sq + i] = acc;
+#endif
+}
+
+// One HBM -> LDS copy of 4 bytes per lane for two vectors (same offsets, two
+// descriptors, two LDS destinations): 64 floats each.
+__device__ __forceinline__ void lds_dma4_pair(char *lds_a, char *lds_b, int voff, u32x4_t da,
+                                              u32x4_t db)
+{
+    const uint32_t m0a = (uint32_t)reinterpret_cast<uintptr_t>((lds_void_t *)lds_a);
+    const uint32_t m0b = (uint32_t)reinterpret_cast<uintptr_t>((lds_void_t *)lds_b);
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dword %3, %4, 0 offen lds\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dword %3, %5, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(m0a), "s"(m0b), "v"(voff), "s"(da), "s"(db)
+        : "memory");
+}
+
+__device__ __forceinline__ u32x4_t raw_desc(const void *base, uint32_t nbytes)
+{
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    return (u32x4_t){(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, nbytes, (uint32_t)kBufferFlags};
+}
+
+// The accumulating product of both kernels: acc^T += X^T Y^T over a 32-row
+// block of an LDS tile (X rows at Xblk), Y^T the bf16 operand halves y0
+// (registers 0..7 of the 32x32 accumulator) and y1 (8..15).
+template <int D>
+__device__ __forceinline__ void bwd_accumulate(const char *Xblk, const OperandOffsets<D> &off,
+                                               bf16x8_t y0, bf16x8_t y1, f32x16_t (&acc)[D / 32])
+{
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+            const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4_t *)(Xblk + off.vofs(db, 0) + t2 * 16 * 2 * D));
+            const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4_t *)(Xblk + off.vofs(db, 1) + t2 * 16 * 2 * D));
+            const u32x2_t lw = __builtin_bit_cast(u32x2_t, lo);
+            const u32x2_t hw = __builtin_bit_cast(u32x2_t, hi);
+            const bf16x8_t a = __builtin_bit_cast(bf16x8_t, (u32x4_t){lw[0], lw[1], hw[0], hw[1]});
+            acc[db] = mfma32(a, t2 ? y1 : y0, acc[db]);
+        }
+    }
+}
+
+__device__ __forceinline__ void pack_halves(const float (&x)[16], bf16x8_t &y0, bf16x8_t &y1)
+{
+    u32x4_t w0, w1;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        w0[q] = pack_bf16(x[2 * q], x[2 * q + 1]);
+        w1[q] = pack_bf16(x[8 + 2 * q], x[8 + 2 * q + 1]);
+    }
+    y0 = __builtin_bit_cast(bf16x8_t, w0);
+    y1 = __builtin_bit_cast(bf16x8_t, w1);
+}
+
+// dQ: one workgroup = NW waves x 32 query rows of one (b, hq); K/V tiles of
+// 64 keys through the forward's three-stage ring.  Per 32-key block:
+// S^T = K Q^T and dP^T = V dO^T (lane = query column: LSE and delta are
+// lane-local), dS^T = P^T (dP^T - delta), dQ^T += K^T dS^T.
+template <int D, int NW>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 8 ? 2 : 1)))
+fa_bwd_dq_kernel(const BwdParams p)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    constexpr int BN = 64;
+    constexpr int BM = 32 * NW;
+    using TL = TileLoader<D, BN, NW>;
+    using BO = BlockOps<D>;
+    constexpr int TB = TL::TILE_BYTES;
+    constexpr int STAGE = 2 * TB;
+    __shared__ __attribute__((aligned(1024))) char lds[kPrefillStages * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 31;
+    const int half = lane >> 5;
+    OperandOffsets<D> off;
+    off.init(lane);
+
+    const int BH = p.B * p.Hq;
+    const int N = BH * p.n_blocks;
+    for (int it = 0; it * (int)gridDim.x < N; ++it) {
+        const int li = it * gridDim.x + ((it & 1) ? (gridDim.x - 1 - blockIdx.x) : blockIdx.x);
+        if (li >= N) continue;
+        // head by head, each head's longest (causal: last) query blocks first
+        const int bh = li / p.n_blocks;
+        const int rank = li % p.n_blocks;
+        const int mb = p.causal ? (p.n_blocks - 1 - rank) : rank;
+        const int b = bh / p.Hq;
+        const int hq = bh % p.Hq;
+        const int g = hq / p.group;
+        const int row0 = mb * BM;
+        const int wrow0 = row0 + wave * 32;
+        const int qi = wrow0 + col;
+        const bool valid = qi < p.Sq;
+        const int qc = min(qi, p.Sq - 1);
+        const int last_row = min(row0 + BM, p.Sq) - 1;
+        const int wlast = min(wrow0 + 31, p.Sq - 1);
+
+        int n_tiles = (p.Sk + BN - 1) / BN;
+        if (p.causal) {
+            const int hi = last_row + p.off;
+            n_tiles = hi < 0 ? 0 : min(n_tiles, hi / BN + 1);
+        }
+        const int NB = n_tiles * 2;
+        int NBw = NB;
+        if (wrow0 >= p.Sq)
+            NBw = 0;
+        else if (p.causal) {
+            const int wmax_lim = wlast + p.off;
+            NBw = wmax_lim < 0 ? 0 : min(NB, wmax_lim / 32 + 1);
+        }
+        const int lim_lane = p.causal ? qi + p.off : 0x7fffffff;
+        const int wmin_lim = p.causal ? wrow0 + p.off : 0x7fffffff;
+
+        TL ld;
+        ld.setup(p.k + ((long)b * p.Sk * p.Hkv + g) * D, p.v + ((long)b * p.Sk * p.Hkv + g) * D,
+                 p.Hkv * D * 2, p.Sk);
+        if (n_tiles > 0) ld.issue(lds, lds + TB, 0, wave, lane);
+        if (n_tiles > 1) ld.issue(lds + STAGE, lds + STAGE + TB, BN, wave, lane);
+
+        bf16x8_t qf[D / 16], dof[D / 16];
+        const long rowoff = (((long)b * p.Sq + qc) * p.Hq + hq) * D;
+        load_q<D>(qf, p.q + rowoff, half);
+        load_q<D>(dof, p.dout + rowoff, half);
+        const float lse = p.lse[((long)b * p.Hq + hq) * p.Sq + qc];
+        const float dlt = p.delta[((long)b * p.Hq + hq) * p.Sq + qc];
+        wait_vmem();
+        flip_q<D>(qf, p.flip);
+        flip_q<D>(dof, 0u);
+        // a row without keys has LSE = -inf: exp2(s c - inf) = 0 for every key
+        const float lse2 = lse == kNegInf ? __builtin_inff() : lse * 1.4426950408889634f;
+
+        f32x16_t dq[D / 32];
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) dq[db] = f32x16_t{};
+
+        int st = 0;
+        for (int t = 0; t < n_tiles; ++t) {
+            char *stage = lds + st * STAGE;
+            // tile t has landed (every wave's copies); tile t - 1's stage is free
+            wait_vmem();
+            __syncthreads();
+            if (t + 2 < n_tiles) {
+                const int s2 = st + 2 >= kPrefillStages ? st + 2 - kPrefillStages : st + 2;
+                ld.issue(lds + s2 * STAGE, lds + s2 * STAGE + TB, (t + 2) * BN, wave, lane);
+            }
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const int j = 2 * t + kb;
+                if (j >= NBw) continue;
+                const char *Kblk = stage + kb * 32 * 2 * D;
+                const char *Vblk = stage + TB + kb * 32 * 2 * D;
+                f32x16_t s = BO::qk(Kblk, off, qf);
+                const bool masked = (j * 32 + 32 > p.Sk) || (j * 32 + 31 > wmin_lim);
+                if (masked) BO::mask(s, j * 32, half, p.Sk, lim_lane);
+                const f32x16_t dp = BO::qk(Vblk, off, dof);
+                float ds[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float pr = fast_exp2(fmaf(s[r], p.c, -lse2));
+                    // masked keys score -inf: P = 0 also at scale 0 (-inf * 0 is NaN)
+                    if (masked) pr = (s[r] == kNegInf) ? 0.0f : pr;
+                    ds[r] = pr * (dp[r] - dlt);
+                }
+                bf16x8_t d0, d1;
+                pack_halves(ds, d0, d1);
+                bwd_accumulate<D>(Kblk, off, d0, d1, dq);
+            }
+            st = st + 1 == kPrefillStages ? 0 : st + 1;
+        }
+        __syncthreads();   // every wave is done with the LDS ring before the next item
+        if (valid)
+            store_rows<D, false>(dq, p.scale, half, p.dq, (((long)b * p.Sq + qi) * p.Hq + hq) * D);
+    }
+#endif
+}
+
+// dK, dV: one workgroup = NW waves x 32 keys of one (b, KV head); the Q and
+// dO tiles of every query head of the group stream through a three-stage
+// LDS ring (64 queries per tile, with their LSE and delta).  Per 32-query
+// block: S = Q K^T and dP = dO V^T (lane = key column, registers = queries),
+// P = exp(S - LSE), dS = P (dP - delta), dV^T += dO^T P, dK^T += Q^T dS.
+template <int D, int NW>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1)))
+fa_bwd_dkdv_kernel(const BwdParams p)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    constexpr int BQ = 64;
+    constexpr int BK = 32 * NW;
+    using TL = TileLoader<D, BQ, NW>;
+    using BO = BlockOps<D>;
+    constexpr int TB = TL::TILE_BYTES;
+    constexpr int STAGE = 2 * TB + 1024;   // Q tile, dO tile, LSE * log2e, delta
+    __shared__ __attribute__((aligned(1024))) char lds[kPrefillStages * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 31;
+    const int half = lane >> 5;
+    OperandOffsets<D> off;
+    off.init(lane);
+
+    const int BG = p.B * p.Hkv;
+    const int N = BG * p.n_blocks;
+    const int ntq_all = (p.Sq + BQ - 1) / BQ;
+    for (int it = 0; it * (int)gridDim.x < N; ++it) {
+        const int li = it * gridDim.x + ((it & 1) ? (gridDim.x - 1 - blockIdx.x) : blockIdx.x);
+        if (li >= N) continue;
+        // (b, g) by (b, g), each one's first (causal: longest) key blocks first
+        const int bg = li / p.n_blocks;
+        const int kblk = li % p.n_blocks;
+        const int b = bg / p.Hkv;
+        const int g = bg % p.Hkv;
+        const int k0 = kblk * BK;                 // first key of the workgroup
+        const int kj = k0 + wave * 32 + col;      // this lane's key
+        const bool kvalid = kj < p.Sk;
+        const int kc = min(kj, p.Sk - 1);
+        // causal: query i sees key j iff j <= i + off, i.e. i >= j - off
+        const int t0 = p.causal ? max(0, k0 - p.off) / BQ : 0;
+        const int ntq = max(0, ntq_all - t0);
+        const int n_units = ntq * p.group;        // (head, query tile) pairs
+
+        TL ld;
+        auto issue_unit = [&](int u, char *dst) {
+            const int hq = g * p.group + u / ntq;
+            const int t = t0 + u % ntq;
+            const long hbase = ((long)b * p.Sq * p.Hq + hq) * D;
+            ld.setup(p.q + hbase, p.dout + hbase, p.Hq * D * 2, p.Sq);
+            ld.issue(dst, dst + TB, t * BQ, wave, lane);
+            if (wave == 0) {
+                const long vb = ((long)b * p.Hq + hq) * p.Sq + (long)t * BQ;
+                const uint32_t nb = (uint32_t)((p.Sq - t * BQ) * 4);
+                lds_dma4_pair(dst + 2 * TB, dst + 2 * TB + 512, lane * 4,
+                              raw_desc(p.lse + vb, nb), raw_desc(p.delta + vb, nb));
+            }
+        };
+        if (n_units > 0) issue_unit(0, lds);
+        if (n_units > 1) issue_unit(1, lds + STAGE);
+
+        bf16x8_t kf[D / 16], vf[D / 16];
+        load_q<D>(kf, p.k + (((long)b * p.Sk + kc) * p.Hkv + g) * D, half);
+        load_q<D>(vf, p.v + (((long)b * p.Sk + kc) * p.Hkv + g) * D, half);
+        wait_vmem();
+        flip_q<D>(kf, p.flip);
+        flip_q<D>(vf, 0u);
+
+        f32x16_t dk[D / 32], dv[D / 32];
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+            dk[db] = f32x16_t{};
+            dv[db] = f32x16_t{};
+        }
+
+        int st = 0;
+        for (int u = 0; u < n_units; ++u) {
+            char *stage = lds + st * STAGE;
+            wait_vmem();
+            __syncthreads();
+            if (u + 2 < n_units) {
+                const int s2 = st + 2 >= kPrefillStages ? st + 2 - kPrefillStages : st + 2;
+                issue_unit(u + 2, lds + s2 * STAGE);
+            }
+            const int tq0 = (t0 + u % ntq) * BQ;   // first query of the tile
+            const float *lsev = reinterpret_cast<const float *>(stage + 2 * TB);
+            const float *dltv = reinterpret_cast<const float *>(stage + 2 * TB + 512);
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                const int q0 = tq0 + qb * 32;
+                if (q0 >= p.Sq) continue;
+                // causal: skip blocks whose last query sees none of the
+                // workgroup's keys
+                if (p.causal && q0 + 31 + p.off < k0) continue;
+                const char *Qblk = stage + qb * 32 * 2 * D;
+                const char *Oblk = stage + TB + qb * 32 * 2 * D;
+                const f32x16_t s = BO::qk(Qblk, off, kf);
+                const f32x16_t dp = BO::qk(Oblk, off, vf);
+                float pr[16], ds[16];
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int qo = qb * 32 + 8 * g4 + 4 * half;   // tile-relative query of register 4 g4
+                    const f32x4_t lv = *reinterpret_cast<const f32x4_t *>(lsev + qo);
+                    const f32x4_t dl = *reinterpret_cast<const f32x4_t *>(dltv + qo);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 4 * g4 + e;
+                        const int qi = tq0 + qo + e;
+                        const bool ok = kvalid && qi < p.Sq && (!p.causal || kj <= qi + p.off);
+                        const float l2 = lv[e] == kNegInf ? __builtin_inff() : lv[e] * 1.4426950408889634f;
+                        const float x = fast_exp2(fmaf(s[r], p.c, -l2));
+                        pr[r] = ok ? x : 0.0f;
+                        ds[r] = pr[r] * (dp[r] - dl[e]);
+                    }
+                }
+                bf16x8_t p0, p1, d0, d1;
+                pack_halves(pr, p0, p1);
+                pack_halves(ds, d0, d1);
+                bwd_accumulate<D>(Oblk, off, p0, p1, dv);
+                bwd_accumulate<D>(Qblk, off, d0, d1, dk);
+            }
+            st = st + 1 == kPrefillStages ? 0 : st + 1;
+        }
+        __syncthreads();
+        if (kvalid) {
+            const long kb_off = (((long)b * p.Sk + kj) * p.Hkv + g) * D;
+            store_rows<D, false>(dk, p.scale, half, p.dk, kb_off);
+            store_rows<D, false>(dv, 1.0f, half, p.dv, kb_off);
+        }
     }
 #endif
 }
@@ -2405,6 +2791,53 @@ hipError_t launch_prefill_fp8(const Launch &L, float v_descale)
         if (L.o_f32) go(std::integral_constant<int, 4>{}, std::true_type{});
         else go(std::integral_constant<int, 4>{}, std::false_type{});
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd(const BwdLaunch &L)
+{
+    if (L.D != 64 && L.D != 128) return hipErrorInvalidValue;
+    BwdParams p;
+    p.q = static_cast<const uint16_t *>(L.q);
+    p.k = static_cast<const uint16_t *>(L.k);
+    p.v = static_cast<const uint16_t *>(L.v);
+    p.o = static_cast<const uint16_t *>(L.o);
+    p.dout = static_cast<const uint16_t *>(L.dout);
+    p.lse = L.lse;
+    p.delta = L.delta;
+    p.dq = static_cast<uint16_t *>(L.dq);
+    p.dk = static_cast<uint16_t *>(L.dk);
+    p.dv = static_cast<uint16_t *>(L.dv);
+    p.B = L.B;
+    p.Hq = L.Hq;
+    p.Hkv = L.Hkv;
+    p.Sq = L.Sq;
+    p.Sk = L.Sk;
+    p.group = L.Hq / L.Hkv;
+    p.causal = L.causal;
+    p.off = L.Sk - L.Sq;
+    p.c = (L.scale < 0.0f ? -L.scale : L.scale) * 1.4426950408889634f;
+    p.scale = L.scale;
+    p.flip = L.scale < 0.0f ? 0x80008000u : 0u;
+
+    const long rows = (long)L.B * L.Sq * L.Hq;
+    dim3 gd((unsigned)((rows + 255) / 256)), bd(256);
+    auto by_d = [&](auto d) {
+        constexpr int D = decltype(d)::value;
+        hipLaunchKernelGGL((fa_bwd_delta_kernel<D>), gd, bd, 0, L.stream, p);
+        BwdParams pk = p;
+        pk.n_blocks = (L.Sk + kBwdKeysPerWG - 1) / kBwdKeysPerWG;
+        hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, kBwdKeysPerWG / 32>), dim3(L.grid_dkdv),
+                           dim3(64 * (kBwdKeysPerWG / 32)), 0, L.stream, pk);
+        BwdParams pq = p;
+        pq.n_blocks = (L.Sq + kBwdRowsPerWG - 1) / kBwdRowsPerWG;
+        hipLaunchKernelGGL((fa_bwd_dq_kernel<D, kBwdRowsPerWG / 32>), dim3(L.grid_dq),
+                           dim3(64 * (kBwdRowsPerWG / 32)), 0, L.stream, pq);
+    };
+    if (L.D == 128)
+        by_d(std::integral_constant<int, 128>{});
+    else
+        by_d(std::integral_constant<int, 64>{});
     return hipGetLastError();
 }
 

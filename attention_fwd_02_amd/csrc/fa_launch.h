@@ -67,4 +67,20 @@ constexpr int kFp8BN = 64;
 inline int fp8_lds_bytes(int D) { return kPrefillStages * 2 * kFp8BN * D; }
 hipError_t launch_prefill_fp8(const Launch &L, float v_descale);
 
+// Backward: delta pass, then dK/dV (workgroups of kBwdKeysPerWG keys of one
+// KV head) and dQ (kBwdRowsPerWG query rows of one head), all on L.stream.
+constexpr int kBwdKeysPerWG = 128;   // 4 waves x 32 keys
+constexpr int kBwdRowsPerWG = 256;   // 8 waves x 32 rows
+struct BwdLaunch {
+    const void *q, *k, *v, *o, *dout;   // bf16
+    const float *lse;                   // [B][Hq][Sq] from the forward
+    float *delta;                       // [B][Hq][Sq] workspace
+    void *dq, *dk, *dv;                 // bf16, layouts of q, k, v
+    int B, Hq, Hkv, Sq, Sk, D, causal;
+    float scale;
+    int grid_dkdv, grid_dq;
+    hipStream_t stream;
+};
+hipError_t launch_bwd(const BwdLaunch &L);
+
 }  // namespace fa

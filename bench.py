@@ -12,7 +12,9 @@ in HBM:
     (one fa_fwd_paged call each: paged split kernel and merge), and
   * head dim 256: a causal prefill, B=2, H=16, S=4096, and the decode shape
     (one fa_fwd call each), and
-  * the causal prefill's shape on FP8 E4M3 inputs (one fa_fwd_fp8 call).
+  * the causal prefill's shape on FP8 E4M3 inputs (one fa_fwd_fp8 call), and
+  * the backward of the causal prefill (one fa_bwd call: delta, dK/dV, dQ
+    kernels) on the prefill's own O and LSE and a seeded dO.
 Both go to the same stream; HIP events recorded on that stream around each
 call give the per-call durations.
 
@@ -21,7 +23,9 @@ flops per allowed query-key pair); `decode` holds the decode's algorithmic
 GB/s (Q, K, V read once, O and LSE written once), `paged_decode` and
 `paged_decode_ragged` the paged calls' (plus the block-table entries read),
 `d256_prefill` / `d256_decode` the head-dim-256 calls' TFLOP/s and GB/s,
-`fp8_prefill` the FP8 call's TFLOP/s against the dense FP8 MFMA peak.
+`fp8_prefill` the FP8 call's TFLOP/s against the dense FP8 MFMA peak,
+`backward` the backward's TFLOP/s (algorithmic: 5 products, 2.5x the
+forward's FLOPs) against the bf16 peak.
 `roofline` is the prefill kernel against the dense bf16 MFMA peak; the decode
 entries' `roofline` their call against HBM.  `cpu_baseline` times the fp64 oracle on a bounded sample of the
 prefill workload's rows and also compares those rows with the timed output.
@@ -162,6 +166,17 @@ def profile_one(args):
         lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=dev)
         fn = lambda: fa.fa_fwd_fp8(q, k, v, o, lse, w.causal, w.scale, dq, dk, dv)  # noqa: E731
         label = w.name
+    elif args.profile_kernel == "bwd":
+        w = WORKLOADS[PREFILL]
+        q, k, v = (t.to(dev) for t in make_inputs(w))
+        do = torch.randn(q.shape, generator=torch.Generator().manual_seed(65)).to(
+            torch.bfloat16).to(dev)
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=dev)
+        fa.fa_fwd(q, k, v, o, lse, w.causal, w.scale)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        fn = lambda: fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, w.causal, w.scale)  # noqa: E731
+        label = w.name + " backward"
     elif args.profile_kernel in ("prefill_d256", "decode_d256"):
         from attention_fwd_02_amd.inputs import HEADDIM_WORKLOADS
         w = HEADDIM_WORKLOADS[PREFILL_D256 if args.profile_kernel == "prefill_d256"
@@ -194,7 +209,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-kernel",
                     choices=["prefill", "decode", "paged", "paged_ragged", "prefill_d256",
-                             "decode_d256", "prefill_fp8", "copy"],
+                             "decode_d256", "prefill_fp8", "bwd", "copy"],
                     help="run only this call (warmup + steps) for counter collection; "
                          "'copy' is a plain 1 GiB device-to-device copy that calibrates "
                          "the HBM byte counters")
@@ -243,6 +258,10 @@ def main():
     of8 = torch.empty(qf8.shape, dtype=torch.bfloat16, device=dev)
     lf8 = torch.empty((wf.B, wf.Hq, wf.Sq), dtype=torch.float32, device=dev)
 
+    dop = torch.randn(qp.shape, generator=torch.Generator().manual_seed(65)).to(
+        torch.bfloat16).to(dev)
+    dqp, dkp, dvp = torch.empty_like(qp), torch.empty_like(kp), torch.empty_like(vp)
+
     stream = torch.cuda.current_stream()
 
     def prefill():
@@ -262,9 +281,13 @@ def main():
     def fp8_call():
         fa.fa_fwd_fp8(qf8, kf8, vf8, of8, lf8, wf.causal, wf.scale, dqf, dkf, dvf, stream=stream)
 
+    def bwd_call():
+        fa.fa_bwd(qp, kp, vp, op, dop, lp, dqp, dkp, dvp, wp.causal, wp.scale, stream=stream)
+
     def step(evs=None):
         calls = (prefill, decode, lambda: paged_call(PAGED), lambda: paged_call(PAGED_RAGGED),
-                 lambda: d256_call(PREFILL_D256), lambda: d256_call(DECODE_D256), fp8_call)
+                 lambda: d256_call(PREFILL_D256), lambda: d256_call(DECODE_D256), fp8_call,
+                 bwd_call)
         for i, call in enumerate(calls):
             if evs:
                 evs[i].record(stream)
@@ -277,7 +300,7 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(K)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(9)] for _ in range(K)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
@@ -346,6 +369,20 @@ def main():
                 "roofline": roofline(tf, PEAK_FP8_TFLOPS, "TFLOP/s", "mfma",
                                      measured_traffic("prefill_fp8"))}
 
+    def bwd_entry(i):
+        ms = sorted(e[i].elapsed_time(e[i + 1]) for e in evs)
+        avg = sum(ms) / K
+        fl = 5 * wp.flops() // 2
+        tf = fl / (avg * 1e-3) / 1e12
+        return {"workload": PREFILL + " backward", "value": round(tf, 3), "unit": "TFLOP/s",
+                "config": {"B": wp.B, "Hq": wp.Hq, "Hkv": wp.Hkv, "Sq": wp.Sq, "Sk": wp.Sk,
+                           "D": wp.D, "causal": wp.causal, "algorithmic_flops": fl,
+                           "flops_rule": "5 products (S, dP, dV, dK, dQ) of 2*D per allowed pair"},
+                "ms": {"avg": round(avg, 4), "median": round(ms[K // 2], 4),
+                       "min": round(ms[0], 4)},
+                "roofline": roofline(tf, PEAK_BF16_TFLOPS, "TFLOP/s", "mfma",
+                                     measured_traffic("bwd"))}
+
     flops = wp.flops()
     tflops = flops / (p_avg * 1e-3) / 1e12
     dbytes = wd.hbm_bytes()
@@ -374,7 +411,8 @@ def main():
                          f"{PAGED} and {PAGED_RAGGED} (the decode over 16-key pages; "
                          "8192 keys each, then lengths drawn from [1, 16384]) + "
                          f"{PREFILL_D256} and {DECODE_D256} (head dim 256) + "
-                         f"{PREFILL_FP8} (the causal prefill on FP8 E4M3 inputs)"),
+                         f"{PREFILL_FP8} (the causal prefill on FP8 E4M3 inputs) + "
+                         f"the backward of {PREFILL}"),
             "prefill": {"B": wp.B, "Hq": wp.Hq, "Hkv": wp.Hkv, "Sq": wp.Sq, "Sk": wp.Sk,
                         "D": wp.D, "causal": wp.causal, "algorithmic_flops": flops,
                         "plan": plan_p},
@@ -398,6 +436,7 @@ def main():
         "d256_prefill": d256_entry(PREFILL_D256, 4),
         "d256_decode": d256_entry(DECODE_D256, 5),
         "fp8_prefill": fp8_entry(6),
+        "backward": bwd_entry(7),
         "roofline": roofline(tflops, PEAK_BF16_TFLOPS, "TFLOP/s", "mfma",
                              measured_traffic("prefill")),
         "cpu_baseline": None,

@@ -201,6 +201,35 @@ fa_status fa_fwd_fp8(const void *q, const void *k, const void *v, void *o, float
                      float q_descale, float k_descale, float v_descale, hipStream_t stream,
                      fa_dtype o_dtype);
 
+/*
+ * fa_bwd -- gradients of the attention forward: dq, dk, dv from q, k, v, the
+ * forward's o and lse, and the upstream gradient dout.  The pages list the
+ * backward pass only by a page title, so it follows from the forward's
+ * mathematics: with P = softmax(scale q k^T [+ causal mask]) (recomputed from
+ * lse), delta_i = sum_d dout_id o_id,
+ *   dv = P^T dout,  dS = P (dout v^T - delta),  dq = scale dS k,
+ *   dk = scale dS^T q,
+ * with the query heads of a KV head adding their dk and dv.
+ *
+ *   q, o, dout, dq  [B][Sq][Hq][D] bf16     k, v, dk, dv  [B][Sk][Hkv][D] bf16
+ *   lse             [B][Hq][Sq] float32 (as fa_fwd wrote it)
+ *
+ * D = 64 or 128.  Every output element is written by one wave (no atomics):
+ * results are deterministic.  workspace: device memory of
+ * fa_bwd_workspace_size() bytes for delta, or NULL for the library-owned
+ * buffer (shared with fa_fwd_ex's split workspace, same rules).  Rows with no
+ * allowed key contribute nothing.  Asynchrony, alignment and errors as for
+ * fa_fwd.
+ */
+fa_status fa_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
+                 const float *lse, void *dq, void *dk, void *dv, int B, int Hq, int Hkv, int Sq,
+                 int Sk, int D, int causal, float scale, hipStream_t stream, void *workspace,
+                 size_t workspace_bytes);
+
+/* fa_bwd_workspace_size -- bytes of workspace fa_bwd needs (B * Hq * Sq
+ * floats); 0 for invalid sizes.  Pure host arithmetic. */
+size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int Sq, int Sk, int D);
+
 /* fa_last_error -- message for the last non-OK status of this host thread
  * ("" if none).  The pointer stays valid until the next call on this thread. */
 const char *fa_last_error(void);
