@@ -1536,13 +1536,19 @@ fa_bwd_dq_kernel(const BwdParams p)
     OperandOffsets<D> off;
     off.init(lane);
 
+    // (b, hq) pairs in 8 residue classes, one per XCD (workgroup index mod 8),
+    // when both counts allow: all blocks of a head then share one L2
     const int BH = p.B * p.Hq;
-    const int N = BH * p.n_blocks;
-    for (int it = 0; it * (int)gridDim.x < N; ++it) {
-        const int li = it * gridDim.x + ((it & 1) ? (gridDim.x - 1 - blockIdx.x) : blockIdx.x);
+    const int ND = (BH % 8 == 0 && gridDim.x % 8 == 0) ? 8 : 1;
+    const int x = blockIdx.x % ND;
+    const int jw = blockIdx.x / ND;
+    const int Gx = gridDim.x / ND;
+    const int N = (BH / ND) * p.n_blocks;
+    for (int it = 0; it * Gx < N; ++it) {
+        const int li = it * Gx + ((it & 1) ? (Gx - 1 - jw) : jw);
         if (li >= N) continue;
         // head by head, each head's longest (causal: last) query blocks first
-        const int bh = li / p.n_blocks;
+        const int bh = (li / p.n_blocks) * ND + x;
         const int rank = li % p.n_blocks;
         const int mb = p.causal ? (p.n_blocks - 1 - rank) : rank;
         const int b = bh / p.Hq;
@@ -1641,7 +1647,7 @@ fa_bwd_dq_kernel(const BwdParams p)
 // block: S = Q K^T and dP = dO V^T (lane = key column, registers = queries),
 // P = exp(S - LSE), dS = P (dP - delta), dV^T += dO^T P, dK^T += Q^T dS.
 template <int D, int NW>
-__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1)))
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 8 ? 2 : 1)))
 fa_bwd_dkdv_kernel(const BwdParams p)
 {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -1661,14 +1667,20 @@ fa_bwd_dkdv_kernel(const BwdParams p)
     OperandOffsets<D> off;
     off.init(lane);
 
+    // (b, g) pairs in 8 residue classes, one per XCD, as in fa_bwd_dq_kernel:
+    // the key blocks of a KV head stream the same Q and dO tiles through one L2
     const int BG = p.B * p.Hkv;
-    const int N = BG * p.n_blocks;
+    const int ND = (BG % 8 == 0 && gridDim.x % 8 == 0) ? 8 : 1;
+    const int x = blockIdx.x % ND;
+    const int jw = blockIdx.x / ND;
+    const int Gx = gridDim.x / ND;
+    const int N = (BG / ND) * p.n_blocks;
     const int ntq_all = (p.Sq + BQ - 1) / BQ;
-    for (int it = 0; it * (int)gridDim.x < N; ++it) {
-        const int li = it * gridDim.x + ((it & 1) ? (gridDim.x - 1 - blockIdx.x) : blockIdx.x);
+    for (int it = 0; it * Gx < N; ++it) {
+        const int li = it * Gx + ((it & 1) ? (Gx - 1 - jw) : jw);
         if (li >= N) continue;
         // (b, g) by (b, g), each one's first (causal: longest) key blocks first
-        const int bg = li / p.n_blocks;
+        const int bg = (li / p.n_blocks) * ND + x;
         const int kblk = li % p.n_blocks;
         const int b = bg / p.Hkv;
         const int g = bg % p.Hkv;

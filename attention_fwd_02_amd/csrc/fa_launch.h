@@ -69,7 +69,7 @@ hipError_t launch_prefill_fp8(const Launch &L, float v_descale);
 
 // Backward: delta pass, then dK/dV (workgroups of kBwdKeysPerWG keys of one
 // KV head) and dQ (kBwdRowsPerWG query rows of one head), all on L.stream.
-constexpr int kBwdKeysPerWG = 128;   // 4 waves x 32 keys
+constexpr int kBwdKeysPerWG = 128;   // 4 waves x 32 keys (8: 39 registers spilled at D = 128)
 constexpr int kBwdRowsPerWG = 256;   // 8 waves x 32 rows
 struct BwdLaunch {
     const void *q, *k, *v, *o, *dout;   // bf16
