@@ -613,7 +613,7 @@ fa_status fa_fwd_fp8(const void *q, const void *k, const void *v, void *o, float
 size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int Sq, int Sk, int D)
 {
     if (check_sizes(B, Hq, Hkv, Sq, Sk, D) != FA_OK) return 0;
-    return (size_t)B * Hq * Sq * sizeof(float);
+    return (size_t)2 * B * Hq * Sq * sizeof(float);
 }
 
 fa_status fa_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
@@ -636,7 +636,7 @@ fa_status fa_bwd(const void *q, const void *k, const void *v, const void *o, con
         !aligned16(lse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
         (workspace && !aligned16(workspace)))
         return fail(FA_ERR_UNSUPPORTED, "every pointer of fa_bwd must be 16-byte aligned");
-    const size_t need = (size_t)B * Hq * Sq * sizeof(float);
+    const size_t need = (size_t)2 * B * Hq * Sq * sizeof(float);   // delta, LSE * log2 e
 
     int dev = 0;
     DeviceInfo *info = nullptr;

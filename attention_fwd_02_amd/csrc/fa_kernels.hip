@@ -1411,7 +1411,8 @@ fa_prefill_fp8_kernel(const Params p, const float v_descale)
 struct BwdParams {
     const uint16_t *q, *k, *v, *o, *dout;
     const float *lse;
-    float *delta;
+    float *delta;            // [B][Hq][Sq]: rowsum(dO O)
+    float *lse2;             // [B][Hq][Sq]: LSE * log2(e), +inf for rows without keys
     uint16_t *dq, *dk, *dv;
     int B, Hq, Hkv, Sq, Sk, group, causal, off;
     float c;          // |scale| * log2(e)
@@ -1420,7 +1421,8 @@ struct BwdParams {
     int n_blocks;     // dkdv: key blocks per KV head; dq: query blocks per head
 };
 
-// delta[b][h][i] = sum_d dO[b][i][h][d] * O[b][i][h][d], one row per thread.
+// delta[b][h][i] = sum_d dO[b][i][h][d] * O[b][i][h][d] and lse2 = LSE log2 e,
+// one row per thread.
 template <int D>
 __global__ void __launch_bounds__(256) fa_bwd_delta_kernel(const BwdParams p)
 {
@@ -1444,7 +1446,12 @@ __global__ void __launch_bounds__(256) fa_bwd_delta_kernel(const BwdParams p)
     const long bi = row / p.Hq;
     const int i = (int)(bi % p.Sq);
     const int b = (int)(bi / p.Sq);
-    p.delta[((long)b * p.Hq + h) * p.Sq + i] = acc;
+    const long vi = ((long)b * p.Hq + h) * p.Sq + i;
+    p.delta[vi] = acc;
+    // exp(scale s - LSE) = exp2(c s - LSE log2 e); a row without keys has
+    // LSE = -inf and must give P = 0
+    const float l = p.lse[vi];
+    p.lse2[vi] = l == kNegInf ? __builtin_inff() : l * 1.4426950408889634f;
 #endif
 }
 
@@ -1588,13 +1595,11 @@ fa_bwd_dq_kernel(const BwdParams p)
         const long rowoff = (((long)b * p.Sq + qc) * p.Hq + hq) * D;
         load_q<D>(qf, p.q + rowoff, half);
         load_q<D>(dof, p.dout + rowoff, half);
-        const float lse = p.lse[((long)b * p.Hq + hq) * p.Sq + qc];
+        const float lse2 = p.lse2[((long)b * p.Hq + hq) * p.Sq + qc];
         const float dlt = p.delta[((long)b * p.Hq + hq) * p.Sq + qc];
         wait_vmem();
         flip_q<D>(qf, p.flip);
         flip_q<D>(dof, 0u);
-        // a row without keys has LSE = -inf: exp2(s c - inf) = 0 for every key
-        const float lse2 = lse == kNegInf ? __builtin_inff() : lse * 1.4426950408889634f;
 
         f32x16_t dq[D / 32];
 #pragma unroll
@@ -1704,7 +1709,7 @@ fa_bwd_dkdv_kernel(const BwdParams p)
                 const long vb = ((long)b * p.Hq + hq) * p.Sq + (long)t * BQ;
                 const uint32_t nb = (uint32_t)((p.Sq - t * BQ) * 4);
                 lds_dma4_pair(dst + 2 * TB, dst + 2 * TB + 512, lane * 4,
-                              raw_desc(p.lse + vb, nb), raw_desc(p.delta + vb, nb));
+                              raw_desc(p.lse2 + vb, nb), raw_desc(p.delta + vb, nb));
             }
         };
         if (n_units > 0) issue_unit(0, lds);
@@ -1747,6 +1752,11 @@ fa_bwd_dkdv_kernel(const BwdParams p)
                 const char *Oblk = stage + TB + qb * 32 * 2 * D;
                 const f32x16_t s = BO::qk(Qblk, off, kf);
                 const f32x16_t dp = BO::qk(Oblk, off, vf);
+                // this wave's keys kw0 .. kw0 + 31 against the block's queries:
+                // the per-element mask only where some pair is cut
+                const int kw0 = k0 + wave * 32;
+                const bool need_mask = kw0 + 31 >= p.Sk || q0 + 31 >= p.Sq ||
+                                       (p.causal && kw0 + 31 > q0 + p.off);
                 float pr[16], ds[16];
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4) {
@@ -1756,12 +1766,14 @@ fa_bwd_dkdv_kernel(const BwdParams p)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int r = 4 * g4 + e;
-                        const int qi = tq0 + qo + e;
-                        const bool ok = kvalid && qi < p.Sq && (!p.causal || kj <= qi + p.off);
-                        const float l2 = lv[e] == kNegInf ? __builtin_inff() : lv[e] * 1.4426950408889634f;
-                        const float x = fast_exp2(fmaf(s[r], p.c, -l2));
-                        pr[r] = ok ? x : 0.0f;
-                        ds[r] = pr[r] * (dp[r] - dl[e]);
+                        float x = fast_exp2(fmaf(s[r], p.c, -lv[e]));
+                        if (need_mask) {
+                            const int qi = tq0 + qo + e;
+                            const bool ok = kvalid && qi < p.Sq && (!p.causal || kj <= qi + p.off);
+                            x = ok ? x : 0.0f;
+                        }
+                        pr[r] = x;
+                        ds[r] = x * (dp[r] - dl[e]);
                     }
                 }
                 bf16x8_t p0, p1, d0, d1;
@@ -2817,6 +2829,7 @@ hipError_t launch_bwd(const BwdLaunch &L)
     p.dout = static_cast<const uint16_t *>(L.dout);
     p.lse = L.lse;
     p.delta = L.delta;
+    p.lse2 = L.delta + (long)L.B * L.Hq * L.Sq;
     p.dq = static_cast<uint16_t *>(L.dq);
     p.dk = static_cast<uint16_t *>(L.dk);
     p.dv = static_cast<uint16_t *>(L.dv);

@@ -74,7 +74,7 @@ constexpr int kBwdRowsPerWG = 256;   // 8 waves x 32 rows
 struct BwdLaunch {
     const void *q, *k, *v, *o, *dout;   // bf16
     const float *lse;                   // [B][Hq][Sq] from the forward
-    float *delta;                       // [B][Hq][Sq] workspace
+    float *delta;                       // workspace: delta, then LSE * log2 e, [B][Hq][Sq] each
     void *dq, *dk, *dv;                 // bf16, layouts of q, k, v
     int B, Hq, Hkv, Sq, Sk, D, causal;
     float scale;

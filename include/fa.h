@@ -216,7 +216,7 @@ fa_status fa_fwd_fp8(const void *q, const void *k, const void *v, void *o, float
  *
  * D = 64 or 128.  Every output element is written by one wave (no atomics):
  * results are deterministic.  workspace: device memory of
- * fa_bwd_workspace_size() bytes for delta, or NULL for the library-owned
+ * fa_bwd_workspace_size() bytes (delta and LSE * log2 e), or NULL for the library-owned
  * buffer (shared with fa_fwd_ex's split workspace, same rules).  Rows with no
  * allowed key contribute nothing.  Asynchrony, alignment and errors as for
  * fa_fwd.
@@ -226,8 +226,9 @@ fa_status fa_bwd(const void *q, const void *k, const void *v, const void *o, con
                  int Sk, int D, int causal, float scale, hipStream_t stream, void *workspace,
                  size_t workspace_bytes);
 
-/* fa_bwd_workspace_size -- bytes of workspace fa_bwd needs (B * Hq * Sq
- * floats); 0 for invalid sizes.  Pure host arithmetic. */
+/* fa_bwd_workspace_size -- bytes of workspace fa_bwd needs (2 * B * Hq * Sq
+ * floats: delta and the LSE in base 2); 0 for invalid sizes.  Pure host
+ * arithmetic. */
 size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int Sq, int Sk, int D);
 
 /* fa_last_error -- message for the last non-OK status of this host thread
