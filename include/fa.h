@@ -160,7 +160,8 @@ fa_status fa_plan(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal, int
  * each sequence's keys are cut into num_splits equal ranges (multiples of 32
  * keys); it is raised if needed so that one range spans at most 256 pages.
  * workspace / workspace_bytes: as for fa_fwd_ex, sized by fa_plan_paged's
- * workspace_bytes.  Only block-table entries of pages below Sk_b are read.
+ * workspace_bytes.  Only row b of the block table is read (entries within
+ * [0, max_pages)), and only the entries of pages below Sk_b are used.
  * An entry outside [0, num_pages) reads as zero keys and values: results for
  * that sequence are then meaningless, but no memory outside the caches is
  * touched.
