@@ -159,7 +159,6 @@ def scan_divergent_copies(asm: str) -> list:
                 continue
             if cf or op.startswith("s_and_saveexec"):
                 break           # a branch (no fall-through) or the region's start
-                break
             if op.startswith("s_"):
                 j -= 1
                 continue
