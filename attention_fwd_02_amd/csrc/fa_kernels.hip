@@ -1943,7 +1943,7 @@ __device__ __forceinline__ void keep(float a) { asm volatile("" ::"v"(a)); }
 // then P(j) becomes the pending P and S(j+1) the next S.
 template <int D, bool MASK>
 __device__ __forceinline__ void wide_settle(WideRows<D> &w, const f32x16_t (&sn)[2],
-                                            u32x4_t (&pw)[2][2], float (&la)[2])
+                                            u32x4_t (&pw)[2][2], float (&la)[2], int key0 = -1)
 {
     constexpr int DB = D / 32;
     // !(x <= T) is also true for inf and NaN
@@ -1951,6 +1951,8 @@ __device__ __forceinline__ void wide_settle(WideRows<D> &w, const f32x16_t (&sn)
     if (__any(big)) {
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
+            // a masked fast block masked only its P: mask S(j) for the redo
+            if (MASK && key0 >= 0) BlockOps<D>::mask(w.s[r], key0, w.half, w.key_end, w.lim[r]);
             float mx = kNegInf;
 #pragma unroll
             for (int e = 0; e < 16; ++e) mx = fmaxf(mx, w.s[r][e]);
@@ -1993,12 +1995,24 @@ __device__ __forceinline__ void wide_settle(WideRows<D> &w, const f32x16_t (&sn)
 // right behind a transcendental would stall the wave, and the next MFMA with
 // it).  The order is fixed with scheduling fences (the S MFMAs are inline
 // asm, which the scheduler's grouping does not recognise).
-template <int D>
+//
+// MASK: block j (keys from key0) may cross the causal diagonal or the key
+// end; masked keys get exponent -inf, so P is 0 there for any scale.
+template <int D, bool MASK = false>
 __device__ __forceinline__ void wide_block_fast(const char *Kn, const char *Vp,
-                                                const OperandOffsets<D> &off, WideRows<D> &w)
+                                                const OperandOffsets<D> &off, WideRows<D> &w,
+                                                int key0 = 0)
 {
     constexpr int QS = D / 16, DB = D / 32, PPS = 8 / QS;
     constexpr int PF = kWidePrefetch < QS ? kWidePrefetch : QS;
+    // largest allowed key offset from this lane half's first key (as in
+    // BlockOps::mask)
+    int last[2] = {0, 0};
+    if (MASK) {
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+            last[r] = min(w.lim[r], w.key_end - 1) - (key0 + 4 * w.half);
+    }
     f32x16_t sn[2];
     u32x4_t pw[2][2];
     float la[2] = {-0.0f, -0.0f};   // -0 + x is x: the first add folds away
@@ -2034,6 +2048,11 @@ __device__ __forceinline__ void wide_block_fast(const char *Kn, const char *Vp,
                 const int q = st * PPS + p;
                 xa[r][p][0] = fmaf(w.s[r][2 * q], w.c, -w.mc[r]);
                 xa[r][p][1] = fmaf(w.s[r][2 * q + 1], w.c, -w.mc[r]);
+                if (MASK) {
+                    const int e0 = 2 * q, e1 = 2 * q + 1;
+                    xa[r][p][0] = (8 * (e0 >> 2) + (e0 & 3) > last[r]) ? kNegInf : xa[r][p][0];
+                    xa[r][p][1] = (8 * (e1 >> 2) + (e1 & 3) > last[r]) ? kNegInf : xa[r][p][1];
+                }
             }
 #pragma unroll
         for (int p = 0; p < PPS; ++p) {
@@ -2087,7 +2106,7 @@ __device__ __forceinline__ void wide_block_fast(const char *Kn, const char *Vp,
         }
     }
     mfma_s_drain(sn[0], sn[1]);
-    wide_settle<D, false>(w, sn, pw, la);
+    wide_settle<D, MASK>(w, sn, pw, la, MASK ? key0 : -1);
 }
 
 // Block j in general: any of S(j+1), P V(j-1), P(j) may be absent for this
@@ -2138,7 +2157,7 @@ __device__ __forceinline__ void wide_block_general(const char *Kn, const char *V
 // tile's last block shows every wave is done with it.  Needs BN >= 64: the
 // P V of a tile's first block reads the last block of tile t - 1, which must
 // still be in place.
-template <int D, int BN, int NW, bool FAST>
+template <int D, int BN, int NW, bool FAST, bool MASK = false>
 __device__ __forceinline__ void wide_tile(int t, int n_tiles, char *stage, char *next, char *prev,
                                           const TileLoader<D, BN, NW> &ld, int wave, int lane,
                                           const OperandOffsets<D> &off, WideRows<D> &w)
@@ -2151,14 +2170,15 @@ __device__ __forceinline__ void wide_tile(int t, int n_tiles, char *stage, char 
         const char *Kn = (kb == KB - 1) ? next : stage + (kb + 1) * 32 * 2 * D;
         // V of the previous block; its offsets add the K-to-V distance
         const char *Vp = (kb == 0) ? prev + (KB - 1) * 32 * 2 * D : stage + (kb - 1) * 32 * 2 * D;
-        if (kb == KB - 1 && (FAST || t + 1 < n_tiles)) {
+        // (a fast tile that is not masked always has a next tile)
+        if (kb == KB - 1 && t + 1 < n_tiles) {
             wait_vmem();       // this wave's copies of tile t + 1 are in LDS
             __syncthreads();   // ... and every wave's; tile t - 1 is released
             if (t + 2 < n_tiles)
                 ld.issue(prev, prev + kPrefillStages * TB, (t + 2) * BN, wave, lane);
         }
         if (FAST)
-            wide_block_fast<D>(Kn, Vp, off, w);
+            wide_block_fast<D, MASK>(Kn, Vp, off, w, (t * KB + kb) * 32);
         else
             wide_block_general<D>(Kn, Vp, t * KB + kb, off, w);
     }
@@ -2175,6 +2195,16 @@ __device__ __forceinline__ bool wide_fast_ok(int t, int NBw, int key_end, int wm
 {
     const int jl = t * KB + KB - 1;   // the tile's last block
     return t >= 1 && jl + 1 < NBw && jl * 32 + 32 <= key_end && jl * 32 + 31 <= wmin_lim;
+}
+
+// The tile after the fast range takes the masked fast body when t >= 1 and
+// all its blocks are live for this wave (the diagonal or the key end cuts
+// it).  Its last block's S(j+1) is computed even when block j+1 is dead (from
+// whatever the next stage holds) and then never used.
+template <int KB>
+__device__ __forceinline__ bool wide_masked_ok(int t, int NBw)
+{
+    return t >= 1 && t * KB + KB - 1 < NBw;
 }
 
 // One work item of the 64-row kernel: 256 query rows of one (b, hq).
@@ -2345,7 +2375,8 @@ fa_prefill_wide_kernel(const Params p)
         // tile t lives in stage t % 3.  Tile 0 takes the general body; the
         // fast tiles [1, t_end) run with compile-time stage addresses, three
         // per trip from stage 1, then the one or two left (stages 1 and 2);
-        // the tiles from t_end on take the general body (runtime stages).
+        // tile t_end may take the masked fast body; the tiles after it take
+        // the general body (runtime stages).
         int t_end = 1;
         while (t_end < n_tiles && wide_fast_ok<KB>(t_end, w.NBw, w.key_end, w.wmin_lim)) ++t_end;
         int t = 0;
@@ -2371,6 +2402,14 @@ fa_prefill_wide_kernel(const Params p)
         if (t < t_end) {
             wide_tile<D, BN, NW, true>(t, n_tiles, lds + 2 * TB, lds, lds + TB, ld, wave, lane,
                                        off, w);
+            ++t;
+        }
+        if (t < n_tiles && wide_masked_ok<KB>(t, w.NBw)) {
+            const int sc = t % kPrefillStages;
+            const int sn = sc == kPrefillStages - 1 ? 0 : sc + 1;
+            const int sp = sc == 0 ? kPrefillStages - 1 : sc - 1;
+            wide_tile<D, BN, NW, true, true>(t, n_tiles, lds + sc * TB, lds + sn * TB, lds + sp * TB,
+                                             ld, wave, lane, off, w);
             ++t;
         }
         for (; t < n_tiles; ++t) {

@@ -155,6 +155,16 @@ def test_rows64_config_scales_and_overflow_redo(ops, oracle, env_vars, scale):
     full_check(ops, oracle, q, k, v, True, scale, out="f32", label=f"rows64 scale={scale}")
 
 
+def test_rows64_overflow_redo_in_diagonal_tile(ops, oracle, env_vars):
+    # keys from 512 on are 6x larger: the rows 512..575 first meet them in
+    # their diagonal tile (keys 512..575), so that tile's masked fast body
+    # redoes its blocks, and the keys it masks are the largest ones
+    env_vars(CONFIGS["rows64_bn64_w4"])
+    q, k, v = random_qkv(1, 2, 1, 640, 640, 128, seed=31)
+    k[:, 512:] *= 6.0
+    full_check(ops, oracle, q, k, v, True, 0.5, out="f32", label="redo in the diagonal tile")
+
+
 def test_item_order_does_not_change_results(ops, env_vars):
     # head-major and rank-major walks run the same per-item arithmetic
     q, k, v = random_qkv(2, 8, 8, 1000, 1000, 128, seed=30)
