@@ -216,6 +216,34 @@ __device__ __forceinline__ void lds_dma16_pair(char *lds_k, char *lds_v, int vof
             : "memory");
 }
 
+// One copy of lds_dma16_pair's kind into one destination.
+template <bool STREAM = false>
+__device__ __forceinline__ void lds_dma16(char *lds, int voff, u32x4_t d)
+{
+    const uint32_t m0 = (uint32_t)reinterpret_cast<uintptr_t>((lds_void_t *)lds);
+    uint32_t saved;
+    if (STREAM)
+        asm volatile(
+            "s_mov_b32 %0, m0\n\t"
+            "s_mov_b32 m0, %1\n\t"
+            "s_nop 0\n\t"
+            "buffer_load_dwordx4 %2, %3, 0 offen nt lds\n\t"
+            "s_mov_b32 m0, %0"
+            : "=&s"(saved)
+            : "s"(m0), "v"(voff), "s"(d)
+            : "memory");
+    else
+        asm volatile(
+            "s_mov_b32 %0, m0\n\t"
+            "s_mov_b32 m0, %1\n\t"
+            "s_nop 0\n\t"
+            "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+            "s_mov_b32 m0, %0"
+            : "=&s"(saved)
+            : "s"(m0), "v"(voff), "s"(d)
+            : "memory");
+}
+
 // HBM -> LDS copy of one K and one V tile of BN keys by NW waves.  One
 // buffer_load_dwordx4 ... lds instruction writes 1 KiB: 64 lanes x 16 bytes at
 // consecutive LDS addresses.  Lane l of instruction q fills tile row
@@ -263,6 +291,20 @@ struct TileLoader {
             const int row = q * RPI + lane / CPR;          // tile-relative row
             const int voff = toff + row * kstride_bytes + (((lane % CPR) ^ swz<D>(row)) * 16);
             lds_dma16_pair<STREAM>(lds_k + q * 1024, lds_v + q * 1024, voff, kdesc, vdesc);
+        }
+    }
+
+    // The copies of one tensor only (V if IS_V, else K).
+    template <bool IS_V>
+    __device__ __forceinline__ void issue_one(char *dst, int key0, int wave, int lane) const
+    {
+        const int toff = key0 * kstride_bytes;
+#pragma unroll
+        for (int i = 0; i < PER_WAVE; ++i) {
+            const int q = i * NW + wave;
+            const int row = q * RPI + lane / CPR;
+            const int voff = toff + row * kstride_bytes + (((lane % CPR) ^ swz<D>(row)) * 16);
+            lds_dma16<STREAM>(dst + q * 1024, voff, IS_V ? vdesc : kdesc);
         }
     }
 };
@@ -2471,7 +2513,10 @@ fa_decode_split_kernel(const Params p)
     constexpr int STAGE = 2 * TB;
 
     constexpr int S = kDecodeStages;
-    __shared__ __attribute__((aligned(1024))) char lds[S * STAGE];
+    // D >= 256: K tile n in K stage n % KS, V tile n in V stage n % VS
+    constexpr int KS = kDecodeKStages256, VS = kDecodeVStages256;
+    constexpr int LDS_BYTES = D >= 256 ? (KS + VS) * TB : S * STAGE;
+    __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
 
     const int lane = threadIdx.x;
     const int col = lane & 31;
@@ -2509,11 +2554,22 @@ fa_decode_split_kernel(const Params p)
     const int lim_lane = p.causal ? qi + p.off : 0x7fffffff;
     const int wmin_lim = p.causal ? p.off : 0x7fffffff;   // row 0 has the smallest limit
 
-    // the first S - 1 tiles' copies go out together, then Q (padding columns
-    // load a real row: they are never written)
+    // the first tiles' copies go out together, then Q (padding columns load
+    // a real row: they are never written).  D >= 256: K(0), V(0), K(1);
+    // otherwise the first S - 1 tiles.
+    char *const kring = lds, *const vring = lds + KS * TB;
+    if constexpr (D >= 256) {
+        if (n_tiles > 0) {
+            ld.template issue_one<false>(kring, k_begin, 0, lane);
+            ld.template issue_one<true>(vring, k_begin, 0, lane);
+        }
+        if (n_tiles > 1) ld.template issue_one<false>(kring + TB, k_begin + BN, 0, lane);
+    } else {
 #pragma unroll
-    for (int u = 0; u < S - 1; ++u)
-        if (u < n_tiles) ld.issue(lds + u * STAGE, lds + u * STAGE + TB, k_begin + u * BN, 0, lane);
+        for (int u = 0; u < S - 1; ++u)
+            if (u < n_tiles)
+                ld.issue(lds + u * STAGE, lds + u * STAGE + TB, k_begin + u * BN, 0, lane);
+    }
     load_q<D>(qf, p.q + (((long)b * p.Sq + qi) * p.Hq + hq) * D, half);
     flip_q<D>(qf, p.qflip);
     // Q has landed, and with it every copy issued before it.  Saying so
@@ -2522,13 +2578,36 @@ fa_decode_split_kernel(const Params p)
     // top of the key loop, draining the ring once per trip.
     wait_vmem();
     if constexpr (D >= 256) {
-        // one tile per trip, stage offsets at run time: the S-way unrolled
-        // trip below does not fit the register file at D = 256
-        int st = 0;
+        // one tile per trip, stage offsets at run time (an unrolled trip does
+        // not fit the register file at D = 256).  A 32-key tile is 16 copies
+        // per tensor, so vmcnt (at most 63) could cover only one whole tile
+        // ahead with a common ring; with separate rings the copies in flight
+        // are V(n + 1), K(n + 1) and K(n + 2), 48 KiB, in 80 KiB of LDS:
+        // two workgroups per CU.  Copies go out in the order V(n), K(n + 1),
+        // so tile n has landed once at most K(n + 1)'s 16 are outstanding.
+        constexpr int LPT = TL::PER_WAVE;
+        int ks = 0, vs = 0;
         for (int n = 0; n < n_tiles; ++n) {
-            decode_step<D, BN, S, TL>(n, n_tiles, k_begin, lds, st, ld, lane, k_end, wmin_lim,
-                                      off, qf, o, m_ref, l_run, l_rnd, p.c, half, lim_lane);
-            st = st + 1 == S ? 0 : st + 1;
+            if (n + 1 < n_tiles)
+                __builtin_amdgcn_s_waitcnt((LPT & 15) | ((LPT >> 4) << 14) | 0x0F70);
+            else
+                wait_vmem();
+            // one wave: orders its LDS reads of tile n - 1 before the copies
+            // below overwrite its stages
+            __syncthreads();
+            if (n + 1 < n_tiles)
+                ld.template issue_one<true>(vring + (vs ^ 1) * TB, k_begin + (n + 1) * BN, 0,
+                                            lane);
+            if (n + 2 < n_tiles) {
+                const int k2 = ks + 2 >= KS ? ks + 2 - KS : ks + 2;
+                ld.template issue_one<false>(kring + k2 * TB, k_begin + (n + 2) * BN, 0, lane);
+            }
+            const int key0 = k_begin + n * BN;
+            WaveTile<D, BN>::template step<true>(kring + ks * TB, vring + vs * TB, off, qf, o,
+                                                 m_ref, l_run, l_rnd, p.c, half, key0, k_end,
+                                                 lim_lane);
+            ks = ks + 1 == KS ? 0 : ks + 1;
+            vs ^= 1;
         }
     } else {
         // S tiles per trip keep every stage offset a compile-time constant
