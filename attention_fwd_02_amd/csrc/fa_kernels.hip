@@ -2306,7 +2306,14 @@ __device__ __forceinline__ void wide_item_issue(const Params &p, const WideItem 
     ld.setup(p.k + ((long)I.b * p.Sk * p.Hkv + I.g) * D, p.v + ((long)I.b * p.Sk * p.Hkv + I.g) * D,
              p.Hkv * D * 2, p.Sk);
     if (I.n_tiles > 0) ld.issue(lds, lds + VOFF, 0, wave, lane);
-    if (I.n_tiles > 1) ld.issue(lds + TB, lds + TB + VOFF, BN, wave, lane);
+    // D = 128: tile 1's first key behind an opaque value, so that its
+    // offsets are formed here from the per-lane parts tile 0 uses instead of
+    // being precomputed for the whole kernel (the register allocator spilled
+    // those, and each reload between copies waited for every copy before it;
+    // D = 64 has registers to spare and measured faster without this)
+    int k1 = BN;
+    if constexpr (D >= 128) asm volatile("" : "+s"(k1));
+    if (I.n_tiles > 1) ld.issue(lds + TB, lds + TB + VOFF, k1, wave, lane);
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
         const int qi = min(I.wrow0 + 32 * r + col, p.Sq - 1);
