@@ -671,20 +671,34 @@ __device__ __forceinline__ void store_rows(const f32x16_t (&o)[D / 32], float mu
                 *reinterpret_cast<f32x4_t *>(static_cast<float *>(out) + obase + db * 32 + 8 * gq +
                                              4 * half) = ov[db][gq];
     } else {
-        u32x2_t ov[D / 32][4];
+        // bf16: a lane holds 4 consecutive elements per (db, gq) and its
+        // partner in the other lane half the next 4.  One lane-half swap per
+        // register pair gives the lower half 8 consecutive elements of gq
+        // 2m and the upper half those of gq 2m + 1: half as many stores,
+        // 16 bytes each.
+        u32x4_t ov[D / 32][2];
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-            for (int gq = 0; gq < 4; ++gq)
-                ov[db][gq] = (u32x2_t){pack_bf16(o[db][4 * gq] * mult, o[db][4 * gq + 1] * mult),
-                                       pack_bf16(o[db][4 * gq + 2] * mult, o[db][4 * gq + 3] * mult)};
+            for (int m = 0; m < 2; ++m) {
+                const int ga = 2 * m, gb = 2 * m + 1;
+                const uint32_t a0 = pack_bf16(o[db][4 * ga] * mult, o[db][4 * ga + 1] * mult);
+                const uint32_t a1 = pack_bf16(o[db][4 * ga + 2] * mult, o[db][4 * ga + 3] * mult);
+                const uint32_t b0 = pack_bf16(o[db][4 * gb] * mult, o[db][4 * gb + 1] * mult);
+                const uint32_t b1 = pack_bf16(o[db][4 * gb + 2] * mult, o[db][4 * gb + 3] * mult);
+                // lower lanes: (own a, upper partner's a); upper lanes: (lower
+                // partner's b, own b)
+                const auto s0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
+                const auto s1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
+                ov[db][m] = (u32x4_t){s0[0], s1[0], s0[1], s1[1]};
+            }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-            for (int gq = 0; gq < 4; ++gq)
-                *reinterpret_cast<u32x2_t *>(static_cast<uint16_t *>(out) + obase + db * 32 + 8 * gq +
-                                             4 * half) = ov[db][gq];
+            for (int m = 0; m < 2; ++m)
+                *reinterpret_cast<u32x4_t *>(static_cast<uint16_t *>(out) + obase + db * 32 +
+                                             16 * m + 8 * half) = ov[db][m];
     }
 }
 
