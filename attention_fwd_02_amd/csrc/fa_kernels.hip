@@ -1400,8 +1400,13 @@ fa_prefill_fp8_kernel(const Params p, const float v_descale)
                  reinterpret_cast<const uint16_t *>(v8 + ((long)b * p.Sk * p.Hkv + g) * D),
                  p.Hkv * D, p.Sk);
 
-        if (n_tiles > 0) ld.issue(lds, lds + TB, 0, wave, lane);
-        if (n_tiles > 1) ld.issue(lds + STAGE, lds + STAGE + TB, BN, wave, lane);
+        // the first keys of tiles 0 and 1 behind opaque values: their copy
+        // offsets are formed here, not precomputed for the kernel and spilled
+        // (each reload waits, vmcnt(0), for every copy and store before it)
+        int k0 = 0, k1 = BN;
+        asm volatile("" : "+s"(k0), "+s"(k1));
+        if (n_tiles > 0) ld.issue(lds, lds + TB, k0, wave, lane);
+        if (n_tiles > 1) ld.issue(lds + STAGE, lds + STAGE + TB, k1, wave, lane);
         {
             // this lane's Q bytes: k-step st, dims 64 st + 32 half .. + 31
             const uint8_t *qrow = q8 + (((long)b * p.Sq + min(qi, p.Sq - 1)) * p.Hq + hq) * D;
