@@ -303,7 +303,7 @@ fa_status make_paged_plan(int B, int Hkv, int page_size, int max_pages, int D, i
         ns = env_int("FA_NUM_SPLITS", 0);
         if (ns <= 0) {
             const int64_t bg = (int64_t)B * Hkv;
-            int per_cu = std::min(8, (160 * 1024) / fa::paged_lds_bytes(D));
+            int per_cu = std::min(8, (160 * 1024) / fa::decode_lds_bytes(D));
             per_cu = std::max(1, env_int("FA_DECODE_WAVES_PER_CU", per_cu));
             const int64_t want = ((int64_t)cus * per_cu + bg - 1) / bg;
             const int64_t by_len = std::max<int64_t>(1, cap / (4 * fa::kDecodeBN));

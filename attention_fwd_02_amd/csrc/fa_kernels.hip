@@ -367,6 +367,18 @@ struct PagedTileLoader {
     // copy instructions split evenly), based at that page.
     __device__ __forceinline__ void issue(char *lds_k, char *lds_v, int key0, int, int lane) const
     {
+        issue_sel<0>(lds_k, lds_v, key0, lane);
+    }
+    // The copies of one tensor only (V if IS_V, else K) into dst.
+    template <bool IS_V>
+    __device__ __forceinline__ void issue_one(char *dst, int key0, int, int lane) const
+    {
+        issue_sel<IS_V ? 2 : 1>(dst, dst, key0, lane);
+    }
+    // WHICH: 0 both tensors, 1 K only (into lds_k), 2 V only (into lds_v)
+    template <int WHICH>
+    __device__ __forceinline__ void issue_sel(char *lds_k, char *lds_v, int key0, int lane) const
+    {
         constexpr int QPP = NQ / PPT;                       // instructions per page
 #pragma unroll
         for (int c = 0; c < PPT; ++c) {
@@ -399,7 +411,12 @@ struct PagedTileLoader {
                 const int row = q * RPI + lane / CPR;       // tile-relative row
                 const int voff = base + q * RPI * kstride_bytes +
                                  (((lane % CPR) ^ swz<D>(row)) * 16);
-                lds_dma16_pair<true>(lds_k + q * 1024, lds_v + q * 1024, voff, kd, vd);
+                if (WHICH == 0)
+                    lds_dma16_pair<true>(lds_k + q * 1024, lds_v + q * 1024, voff, kd, vd);
+                else if (WHICH == 1)
+                    lds_dma16<true>(lds_k + q * 1024, voff, kd);
+                else
+                    lds_dma16<true>(lds_v + q * 1024, voff, vd);
             }
         }
     }
@@ -2686,7 +2703,10 @@ fa_decode_paged_kernel(const Params p, const PagedParams pp)
     constexpr int STAGE = 2 * TB;
 
     constexpr int S = kDecodeStages;
-    __shared__ __attribute__((aligned(1024))) char lds[S * STAGE];
+    // D >= 256: separate K and V rings, as in fa_decode_split_kernel
+    constexpr int KS = kDecodeKStages256, VS = kDecodeVStages256;
+    constexpr int LDS_BYTES = D >= 256 ? (KS + VS) * TB : S * STAGE;
+    __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
 
     const int lane = threadIdx.x;
     const int col = lane & 31;
@@ -2727,20 +2747,46 @@ fa_decode_paged_kernel(const Params p, const PagedParams pp)
     const int lim_lane = p.causal ? qi + offk : 0x7fffffff;
     const int wmin_lim = p.causal ? offk : 0x7fffffff;
 
+    char *const kring = lds, *const vring = lds + KS * TB;
+    if constexpr (D >= 256) {
+        if (n_tiles > 0) {
+            ld.template issue_one<false>(kring, k_begin, 0, lane);
+            ld.template issue_one<true>(vring, k_begin, 0, lane);
+        }
+        if (n_tiles > 1) ld.template issue_one<false>(kring + TB, k_begin + BN, 0, lane);
+    } else {
 #pragma unroll
-    for (int u = 0; u < S - 1; ++u)
-        if (u < n_tiles) ld.issue(lds + u * STAGE, lds + u * STAGE + TB, k_begin + u * BN, 0, lane);
+        for (int u = 0; u < S - 1; ++u)
+            if (u < n_tiles)
+                ld.issue(lds + u * STAGE, lds + u * STAGE + TB, k_begin + u * BN, 0, lane);
+    }
     load_q<D>(qf, p.q + (((long)b * p.Sq + qi) * p.Hq + hq) * D, half);
     flip_q<D>(qf, p.qflip);
     wait_vmem();   // as in fa_decode_split_kernel: no ring drain per trip
     if constexpr (D >= 256) {
-        // one tile per trip, stage offsets at run time: the S-way unrolled
-        // trip below does not fit the register file at D = 256
-        int st = 0;
+        // one tile per trip over separate K and V rings; the waits and the
+        // copy order are those of fa_decode_split_kernel at D = 256
+        constexpr int LPT = TL::PER_WAVE;
+        int ks = 0, vs = 0;
         for (int n = 0; n < n_tiles; ++n) {
-            decode_step<D, BN, S, TL>(n, n_tiles, k_begin, lds, st, ld, lane, k_end, wmin_lim,
-                                      off, qf, o, m_ref, l_run, l_rnd, p.c, half, lim_lane);
-            st = st + 1 == S ? 0 : st + 1;
+            if (n + 1 < n_tiles)
+                __builtin_amdgcn_s_waitcnt((LPT & 15) | ((LPT >> 4) << 14) | 0x0F70);
+            else
+                wait_vmem();
+            __syncthreads();
+            if (n + 1 < n_tiles)
+                ld.template issue_one<true>(vring + (vs ^ 1) * TB, k_begin + (n + 1) * BN, 0,
+                                            lane);
+            if (n + 2 < n_tiles) {
+                const int k2 = ks + 2 >= KS ? ks + 2 - KS : ks + 2;
+                ld.template issue_one<false>(kring + k2 * TB, k_begin + (n + 2) * BN, 0, lane);
+            }
+            const int key0 = k_begin + n * BN;
+            WaveTile<D, BN>::template step<true>(kring + ks * TB, vring + vs * TB, off, qf, o,
+                                                 m_ref, l_run, l_rnd, p.c, half, key0, k_end,
+                                                 lim_lane);
+            ks = ks + 1 == KS ? 0 : ks + 1;
+            vs ^= 1;
         }
     } else {
         // S tiles per trip keep every stage offset a compile-time constant

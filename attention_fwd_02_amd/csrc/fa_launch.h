@@ -22,9 +22,8 @@ constexpr int kDecodeRows = 32;
 #define FA_DECODE_STAGES 3
 #endif
 constexpr int kDecodeStages = FA_DECODE_STAGES;
-// At D = 256 the split kernel keeps K and V in rings of their own, three K
-// tiles and two V tiles (80 KiB: two workgroups per CU); the paged kernel
-// keeps the common ring.
+// At D = 256 the decode kernels keep K and V in rings of their own, three K
+// tiles and two V tiles (80 KiB: two workgroups per CU).
 constexpr int kDecodeKStages256 = 3;
 constexpr int kDecodeVStages256 = 2;
 inline int decode_lds_bytes(int D)
@@ -32,7 +31,6 @@ inline int decode_lds_bytes(int D)
     return D >= 256 ? (kDecodeKStages256 + kDecodeVStages256) * kDecodeBN * D * 2
                     : kDecodeStages * 2 * kDecodeBN * D * 2;
 }
-inline int paged_lds_bytes(int D) { return kDecodeStages * 2 * kDecodeBN * D * 2; }
 // Paged decode: a wave keeps the page ids of its key range in this many
 // VGPRs (64 pages each), which bounds the pages one split may touch.
 constexpr int kPagedIdRegs = 4;
