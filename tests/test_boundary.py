@@ -176,6 +176,22 @@ def test_paged_bad_arguments_rejected_before_any_hip_call(b, kw, status):
     assert msg
 
 
+def test_head_dim_256_decode_plans(b):
+    # D = 256: separate K and V rings of 3 + 2 32-key tiles (80 KiB of LDS)
+    # leave two single-wave workgroups per CU, so the 256 (b, g) pairs of the
+    # decode workload take 2 splits (a 256-CU part filled once)
+    p = b.fa_plan(32, 32, 8, 1, 8192, 256, False, 0)
+    assert p["path"] == 1 and p["num_splits"] == 2 and p["grid"] == 32 * 8 * 2
+    assert p["workspace_bytes"] == 2 * 32 * 32 * 257 * 4
+    assert b.fa_workspace_size(32, 32, 8, 1, 8192, 256, 0) == 2 * 32 * 32 * 257 * 4
+    # the paged kernel uses the same rings (at least 2 splits; here the
+    # 256-page bound per split, 512 16-key pages, asks for one more)
+    q = b.fa_plan_paged(32, 32, 8, 1, 256, 16384, 16, 512, 0)
+    assert q["path"] == 2 and q["num_splits"] == 3
+    q = b.fa_plan_paged(32, 32, 8, 1, 256, 16384, 64, 128, 0)
+    assert q["num_splits"] == 2 and q["grid"] == 32 * 8 * 2
+
+
 def test_paged_plan_host_arithmetic(b):
     # the paged decode workload: 256 (b, g) pairs x 3 splits, like the
     # contiguous decode; partials [splits][B][Hq][Sq][D+1] fp32
