@@ -26,6 +26,13 @@ end of a divergent region (see there).
 Wait states are counted conservatively: one per instruction, ``N + 1`` for
 ``s_nop N``.  Other inline-assembly instructions count but are not reported
 (the MFMA chains and the drain are written to respect the rules).
+
+An inline-asm MFMA whose text carries the comment ``accumulate-only`` (the
+ping-pong prefill's P V and row-sum MFMAs) promises that its accumulator is
+read only by later MFMAs of the same chain (which the hardware orders) or
+after an explicit drain.  For it a branch within the window is no finding:
+the scan instead runs on through the branch in program order, so that an
+access on the fall-through path is still reported.
 """
 from __future__ import annotations
 
@@ -55,8 +62,12 @@ def _operands(text: str) -> list:
     return out
 
 
-def _instructions(asm: str):
-    """(line number, text, inside inline asm, is control flow) per instruction."""
+ACCUMULATE_ONLY = "accumulate-only"
+
+
+def _instructions(asm: str, with_marks: bool = False):
+    """(line number, text, inside inline asm, is control flow) per instruction;
+    with_marks adds whether the line carried the accumulate-only marker."""
     out = []
     in_asm = False
     for no, line in enumerate(asm.splitlines(), 1):
@@ -69,14 +80,16 @@ def _instructions(asm: str):
             continue
         if not t or t.startswith(";") or t.startswith("."):
             continue
+        mark = ACCUMULATE_ONLY in t
         if re.match(r"^[\w.$]+:", t):
-            out.append((no, t, in_asm, True))
+            out.append((no, t, in_asm, True, mark) if with_marks else (no, t, in_asm, True))
             continue
         t = t.split(";")[0].strip()
         if not t:
             continue
         op = t.split()[0]
-        out.append((no, t, in_asm, op.startswith(("s_branch", "s_cbranch", "s_setpc", "s_endpgm"))))
+        cf = op.startswith(("s_branch", "s_cbranch", "s_setpc", "s_endpgm"))
+        out.append((no, t, in_asm, cf, mark) if with_marks else (no, t, in_asm, cf))
     return out
 
 
@@ -89,17 +102,22 @@ def _wait_states(text: str) -> int:
 
 def scan(asm: str, result_wait: int = 18, operand_wait: int = 2) -> list:
     """Findings (one string each) for every inline-asm MFMA in ``asm``."""
-    ins = _instructions(asm)
+    marked = _instructions(asm, with_marks=True)
+    ins = [m[:4] for m in marked]
     findings = []
     for k, (no, text, in_asm, _) in enumerate(ins):
         if not (in_asm and text.startswith("v_mfma")):
             continue
+        acc_only = marked[k][4]
         ops = _operands(text)
         dst, srcs = ops[0], set().union(*ops[1:]) if len(ops) > 1 else set()
         # after: nothing emitted by the compiler touches dst until the wait is over
         ws, j = 0, k + 1
         while j < len(ins) and ws < result_wait:
             no2, t2, a2, cf = ins[j]
+            if cf and acc_only:
+                j += 1          # follow the fall-through path
+                continue
             if cf:
                 findings.append(f"line {no}: {text}: control flow {ws} wait states later "
                                 f"(line {no2}: {t2})")

@@ -46,31 +46,58 @@ struct DeviceInfo {
     size_t ws_bytes = 0;
 };
 
+// One record per device index, at a fixed address for the life of the
+// process: pointers handed out by device_info() stay valid whatever other
+// threads probe later.
+constexpr int kMaxDevices = 64;
 std::mutex g_mu;
-std::vector<DeviceInfo> g_dev;
+DeviceInfo g_dev[kMaxDevices];
+
+// Fills in d (under g_mu) from the device's properties: no launch, no allocation.
+hipError_t probe_locked(int dev, DeviceInfo &d)
+{
+    if (d.probed) return hipSuccess;
+    hipDeviceProp_t prop;
+    hipError_t e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return e;
+    d.arch = prop.gcnArchName;
+    d.cus = prop.multiProcessorCount;
+    d.supported = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    d.probed = true;
+    return hipSuccess;
+}
 
 fa_status device_info(int *dev_out, DeviceInfo **info_out)
 {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return fail(FA_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(FA_ERR_UNSUPPORTED, "device index beyond the library's table of 64");
     std::lock_guard<std::mutex> lk(g_mu);
-    if ((int)g_dev.size() <= dev) g_dev.resize(dev + 1);
     DeviceInfo &d = g_dev[dev];
-    if (!d.probed) {
-        hipDeviceProp_t prop;
-        e = hipGetDeviceProperties(&prop, dev);
-        if (e != hipSuccess)
-            return fail(FA_ERR_HIP, std::string("hipGetDeviceProperties: ") + hipGetErrorString(e));
-        d.arch = prop.gcnArchName;
-        d.cus = prop.multiProcessorCount;
-        d.supported = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
-        d.probed = true;
-    }
+    e = probe_locked(dev, d);
+    if (e != hipSuccess)
+        return fail(FA_ERR_HIP, std::string("hipGetDeviceProperties: ") + hipGetErrorString(e));
     if (!d.supported) return fail(FA_ERR_UNSUPPORTED, "device architecture " + d.arch + " is not gfx950");
     *dev_out = dev;
     *info_out = &d;
     return FA_OK;
+}
+
+// The current device's compute-unit count for the pure size queries
+// (fa_workspace_size, fa_plan, fa_plan_paged): the device property, read
+// without launching anything, so that a size asked for before the first
+// call equals what that call plans.  0 when no device is usable (the
+// planner then assumes the MI355X's 256).
+int query_cus()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    std::lock_guard<std::mutex> lk(g_mu);
+    DeviceInfo &d = g_dev[dev];
+    if (probe_locked(dev, d) != hipSuccess) return 0;
+    return d.cus;
 }
 
 bool log_enabled()
@@ -113,6 +140,7 @@ struct Plan {
     int block_m = 0, block_n = 0;
     int grid = 0, items = 0;
     int prefill_bn = 0, prefill_nw = 0, prefill_nr = 1;
+    int prefill_pp = 0;  // ring depth of the ping-pong kernel, 0 = not used
     int head_major = 0;
     size_t ws_bytes = 0;
 };
@@ -197,18 +225,32 @@ fa_status make_plan(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal, i
             nw = enw;
             nr = enr;
         }
+        // the ping-pong kernel (8 waves x 32 rows, two per SIMD in opposite
+        // MFMA / softmax phases, D = 64 or 128) only on request:
+        // FA_PREFILL_PP = 4 / 5 (its ring depth)
+        int pp = 0;
+        const int epp = env_int("FA_PREFILL_PP", -1);
+        if (epp == 0 || (epp > 0 && fa::prefill_pp_ok(D, epp))) pp = epp;
+        if (ebn > 0 && enw > 0 && fa::prefill_cfg_ok(D, ebn, enw, enr)) pp = 0;
+        if (pp) {
+            bn = fa::kPrefillPPBN;
+            nw = fa::kPrefillPPWaves;
+            nr = 1;
+        }
         const int bm = 32 * nw * nr;
         pl.block_m = bm;
         pl.block_n = bn;
         pl.prefill_bn = bn;
         pl.prefill_nw = nw;
         pl.prefill_nr = nr;
+        pl.prefill_pp = pp;
         const int64_t items = (int64_t)B * Hq * ((Sq + bm - 1) / bm);
         if (items >= (int64_t(1) << 31)) return fail(FA_ERR_UNSUPPORTED, "too many work items");
         // workgroups a CU holds at once: LDS (160 KiB) and the waves per SIMD
         // the configuration's register budget allows (4 SIMDs per CU)
-        int wg_per_cu = std::min((160 * 1024) / fa::prefill_lds_bytes(D, bn),
-                                 4 * fa::prefill_waves_per_simd(nr) / nw);
+        int wg_per_cu = pp ? std::min((160 * 1024) / fa::prefill_pp_lds_bytes(D, pp), 1)
+                           : std::min((160 * 1024) / fa::prefill_lds_bytes(D, bn),
+                                      4 * fa::prefill_waves_per_simd(nr) / nw);
         wg_per_cu = std::max(1, std::min(wg_per_cu, env_int("FA_WG_PER_CU", wg_per_cu)));
         int64_t grid = std::min<int64_t>(items, (int64_t)cus * wg_per_cu);
         if (env_int("FA_PERSISTENT", 1) == 0) grid = items;
@@ -334,15 +376,6 @@ fa_status make_paged_plan(int B, int Hkv, int page_size, int max_pages, int D, i
     return FA_OK;
 }
 
-int probed_cus()
-{
-    std::lock_guard<std::mutex> lk(g_mu);
-    int dev = 0;
-    if (hipGetDevice(&dev) == hipSuccess && dev < (int)g_dev.size() && g_dev[dev].probed)
-        return g_dev[dev].cus;
-    return 0;
-}
-
 }  // namespace
 
 extern "C" {
@@ -395,6 +428,7 @@ fa_status fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float 
     L.prefill_bn = pl.prefill_bn;
     L.prefill_nw = pl.prefill_nw;
     L.prefill_nr = pl.prefill_nr;
+    L.prefill_pp = pl.prefill_pp;
     L.head_major = pl.head_major;
     L.stream = stream;
 
@@ -432,13 +466,7 @@ fa_status fa_fwd(const void *q, const void *k, const void *v, void *o, float *ls
 size_t fa_workspace_size(int B, int Hq, int Hkv, int Sq, int Sk, int D, int num_splits)
 {
     if (check_sizes(B, Hq, Hkv, Sq, Sk, D) != FA_OK) return 0;
-    int cus = 0;
-    {
-        std::lock_guard<std::mutex> lk(g_mu);
-        int dev = 0;
-        if (hipGetDevice(&dev) == hipSuccess && dev < (int)g_dev.size() && g_dev[dev].probed)
-            cus = g_dev[dev].cus;
-    }
+    const int cus = query_cus();
     Plan pl;
     // the workspace depends on the split plan only, which ignores causality
     if (make_plan(B, Hq, Hkv, Sq, Sk, D, 0, num_splits, cus, &pl) != FA_OK) return 0;
@@ -452,13 +480,7 @@ fa_status fa_plan(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal, int
     if (!out) return fail(FA_ERR_INVALID_ARG, "out must not be NULL");
     fa_status st = check_sizes(B, Hq, Hkv, Sq, Sk, D);
     if (st != FA_OK) return st;
-    int cus = 0;
-    {
-        std::lock_guard<std::mutex> lk(g_mu);
-        int dev = 0;
-        if (hipGetDevice(&dev) == hipSuccess && dev < (int)g_dev.size() && g_dev[dev].probed)
-            cus = g_dev[dev].cus;
-    }
+    const int cus = query_cus();
     Plan pl;
     st = make_plan(B, Hq, Hkv, Sq, Sk, D, causal, num_splits, cus, &pl);
     if (st != FA_OK) return st;
@@ -522,6 +544,7 @@ fa_status fa_fwd_paged(const void *q, const void *k_cache, const void *v_cache,
     L.split_len = 0;
     L.grid = pl.grid;
     L.prefill_bn = L.prefill_nw = L.prefill_nr = 0;
+    L.prefill_pp = 0;
     L.head_major = 0;
     L.stream = stream;
     fa::PagedLaunch P;
@@ -599,6 +622,7 @@ fa_status fa_fwd_fp8(const void *q, const void *k, const void *v, void *o, float
     L.prefill_bn = fa::kFp8BN;
     L.prefill_nw = nw;
     L.prefill_nr = 1;
+    L.prefill_pp = 0;
     L.head_major = env_int("FA_HEAD_MAJOR", causal ? 1 : 0) != 0;
     L.stream = stream;
     if (log_enabled())
@@ -696,7 +720,7 @@ fa_status fa_plan_paged(int B, int Hq, int Hkv, int Sq, int D, int num_pages, in
     fa_status st = check_paged(B, Hq, Hkv, Sq, D, num_pages, page_size, max_pages);
     if (st != FA_OK) return st;
     Plan pl;
-    st = make_paged_plan(B, Hkv, page_size, max_pages, D, num_splits, probed_cus(), Hq, Sq, &pl);
+    st = make_paged_plan(B, Hkv, page_size, max_pages, D, num_splits, query_cus(), Hq, Sq, &pl);
     if (st != FA_OK) return st;
     out->path = 2;
     out->num_splits = pl.num_splits;
@@ -717,9 +741,9 @@ fa_status fa_release_workspace(void)
     std::lock_guard<std::mutex> lk(g_mu);
     int cur = 0;
     if (hipGetDevice(&cur) != hipSuccess) cur = -1;
-    for (size_t d = 0; d < g_dev.size(); ++d) {
+    for (int d = 0; d < kMaxDevices; ++d) {
         if (!g_dev[d].ws) continue;
-        if (hipSetDevice((int)d) == hipSuccess) (void)hipFree(g_dev[d].ws);
+        if (hipSetDevice(d) == hipSuccess) (void)hipFree(g_dev[d].ws);
         g_dev[d].ws = nullptr;
         g_dev[d].ws_bytes = 0;
     }

@@ -2540,6 +2540,524 @@ fa_prefill_wide_kernel(const Params p)
 }
 
 // ---------------------------------------------------------------------------
+// Ping-pong prefill: 8 waves x 32 query rows = 256 rows of one (b, hq) per
+// item, two waves per SIMD.  Waves 0-3 (group A) and 4-7 (group B) share the
+// SIMDs pairwise and run the same two-phase loop half a period apart:
+//
+//   M(t): S(t) = K(t) Q^T (2 key blocks x D/16 MFMAs) and O += V(t-1)^T P(t-1)^T
+//         (4 x D/32 MFMAs), plus the row sums of the rounded P(t-1);
+//   V(t): the online softmax that turns S(t) into P(t) (VALU only).
+//
+//   phase:   0     1     2     3     4   ...   2T   2T+1
+//   group A  M(0)  V(0)  M(1)  V(1)  M(2)      M(T)  -
+//   group B  -     M(0)  V(0)  M(1)  V(1)      V(T-1) M(T)
+//
+// A workgroup barrier closes every phase, so on each SIMD one wave issues
+// MFMAs while the other runs its softmax: measured on gfx950, an MFMA-only
+// wave keeps its 32-cycle issue rate beside a VALU-only wave, whereas one
+// wave interleaving both loses about 12 cycles of VALU issue per MFMA.  This
+// is the SIMD-level form of the overlap the FlashAttention page describes for
+// SM90 (softmax of one tile under the matrix work of another, "SM80 内核实现对比",
+// section 5.2), without its warp specialisation: every wave does both kinds
+// of work, in alternation.
+//
+// K/V: 64-key tiles in an NS-stage LDS ring (K tiles, then V tiles).  Tile t
+// is read in M(t) (K) and M(t+1) (V), i.e. in phases 2t .. 2t+3, so its stage
+// is free from phase 2t+4 on.  Every wave copies its share of each tile at
+// the start of one of its V phases, into a stage that is already free then:
+// group A (V(t) in phase 2t+1) tile t + NS - 2, into the stage of tile t - 2;
+// group B (V(t) in phase 2t+2) tile t + NS - 1, into the stage of tile t - 1.
+// Tile t + 1 is read from phase 2t+2 on, so both groups wait for their copies
+// of it in phase 2t+1 (A at the end of V(t), B at the end of M(t)), before the
+// barrier; the copies have 2 NS - 6 (A) and 2 NS - 5 (B) phases to land.
+//
+// Softmax: V(0) (and any tile that is masked or partly dead for the wave)
+// uses the exact running max; the other tiles use the lazy reference max of
+// the wide kernel above: P = exp2(c s - c m_ref) without a max, redone against
+// the exact max when a lane's P sum exceeds kWideOverflow (also inf / NaN).
+// ---------------------------------------------------------------------------
+constexpr int kPPWaves = 8;
+constexpr int kPPBN = 64;
+
+// Workgroup barrier between phases, without the memory fence of
+// __syncthreads (which would wait for the K/V copies still in flight).  The
+// empty asm statements keep the compiler from moving LDS accesses across it,
+// the scheduling fences any other instruction: without them the scheduler
+// hoisted a V phase's register-only softmax work above the barrier into the
+// M phase, where it defeats the alternation.
+__device__ __forceinline__ void pp_barrier()
+{
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int D>
+struct PPRows {
+    static constexpr int QS = D / 16, DB = D / 32;
+    bf16x8_t qf[QS];
+    f32x16_t o[DB];
+    f32x16_t s[2];         // S^T of the current tile, key blocks 0 and 1
+    bf16x8_t p[4];         // P of the previous tile, 16-key steps 0..3
+    f32x4_t l_acc;         // element 0: row sum of the rounded P (whole row)
+    float m_ref, l_run;    // reference max (score units), exact row sum (lane half)
+    bf16x8_t sel;
+};
+
+// LDS reads at a 32-bit LDS byte address (the constant part of the address
+// folds into the instruction's offset field).
+__device__ __forceinline__ bf16x8_t lds_read16(uint32_t addr)
+{
+    return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t *>((uintptr_t)addr);
+}
+// A operand V^T of a 16-key P V step: two transposing reads (keys k0 + 4 h
+// + 0..3 and k0 + 8 + 4 h + 0..3 of 4 head dims), from the lane addresses of
+// OperandOffsets::v.
+__device__ __forceinline__ bf16x8_t lds_read_vt(uint32_t a0, uint32_t a1)
+{
+    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        reinterpret_cast<lds_i16x4_t *>((uintptr_t)a0));
+    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        reinterpret_cast<lds_i16x4_t *>((uintptr_t)a1));
+    const u32x2_t lw = __builtin_bit_cast(u32x2_t, lo);
+    const u32x2_t hw = __builtin_bit_cast(u32x2_t, hi);
+    return __builtin_bit_cast(bf16x8_t, (u32x4_t){lw[0], lw[1], hw[0], hw[1]});
+}
+
+// Per-lane LDS addresses of one phase's operand reads: the tile's base plus
+// the lane's offsets, formed once per phase behind an opaque value, so that
+// the compiler does not keep a register for every (stage, step) combination.
+template <int D>
+struct PPAddr {
+    uint32_t k[D / 16];      // K fragment of k-step st (key block 0; block 1 is +32 rows)
+    uint32_t v[D / 32][2];   // V^T halves of d block db (16-key step 0; step t2 is +16 t2 rows)
+    __device__ __forceinline__ void set(uint32_t kbase, uint32_t vbase, const OperandOffsets<D> &off)
+    {
+#pragma unroll
+        for (int st = 0; st < D / 16; ++st) {
+            k[st] = kbase + (uint32_t)off.kofs(st);
+            asm volatile("" : "+v"(k[st]));
+        }
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int sec = 0; sec < 2; ++sec) {
+                v[db][sec] = vbase + (uint32_t)off.vofs(db, sec);
+                asm volatile("" : "+v"(v[db][sec]));
+            }
+    }
+};
+
+// The M phase's MFMAs as inline asm with tied accumulators, so that O, S and
+// the row sums keep their registers through the phase (with the builtins the
+// register allocator moved O between register sets, copying it every phase).
+// The compiler's hazard recognizer does not see inside, so:
+//  * S is complete before the V phase reads it: the S MFMAs are issued in
+//    the first part of the M phase, and about half the phase's P V MFMAs
+//    follow the last of them;
+//  * pp_drain_o precedes every VALU access to O and the row sums (the
+//    rescale after an overflow, the epilogue);
+//  * an M phase starts with two wait states (s_nop 1) after the VALU writes
+//    of P and O of the phase before it;
+//  * operand registers are rewritten by the rolling reads at least three
+//    steps after the MFMA that read them.
+__device__ __forceinline__ void pp_mfma_first(f32x16_t &d, bf16x8_t a, bf16x8_t q)
+{
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(q));
+}
+__device__ __forceinline__ void pp_mfma_next(f32x16_t &d, bf16x8_t a, bf16x8_t q)
+{
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(q));
+}
+// O and the row sums are read only by the next MFMAs of their chains or after
+// pp_drain_o / the fenced wait of the rescale path: the build's device-code
+// scan lets a branch follow these MFMAs closely (the "accumulate-only" mark)
+// and checks the fall-through code instead.
+__device__ __forceinline__ void pp_mfma_pv(f32x16_t &o, bf16x8_t v, bf16x8_t p)
+{
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0 ; accumulate-only"
+                 : "+v"(o)
+                 : "v"(v), "v"(p));
+}
+__device__ __forceinline__ void pp_mfma_rowsum(f32x4_t &l, bf16x8_t sel, bf16x8_t p)
+{
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0 ; accumulate-only"
+                 : "+v"(l)
+                 : "v"(sel), "v"(p));
+}
+
+// Wait for the P V and row-sum MFMAs before the VALU reads O or the row
+// sums (24 wait states; an 8-pass MFMA needs about half): the accumulators
+// are operands, so nothing the compiler emits can touch them before it.
+template <int D>
+__device__ __forceinline__ void pp_drain_o(PPRows<D> &w)
+{
+    if constexpr (D / 32 == 4)
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                     : "+v"(w.o[0]), "+v"(w.o[1]), "+v"(w.o[2]), "+v"(w.o[3]),
+                       "+v"(w.l_acc)::"memory");
+    else
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                     : "+v"(w.o[0]), "+v"(w.o[1]), "+v"(w.l_acc)::"memory");
+}
+
+// The same wait for S, after an M phase that ends with S MFMAs.
+template <int D>
+__device__ __forceinline__ void pp_drain_s(PPRows<D> &w)
+{
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(w.s[0]), "+v"(w.s[1])::"memory");
+}
+
+// M phase.  DO_S: S(t) of both key blocks of tile t; DO_PV: O += V^T P^T for
+// both blocks of tile t - 1, and the row sums of the rounded P; operand
+// addresses from `ad` (formed during the V phase before).  Blocks dead for
+// this wave are computed too (their K and V rows are in range) and get P = 0
+// in the V phase: no conditional writes, so the compiler keeps S and P in
+// place.  Operand reads run two steps ahead of their MFMAs.  The S MFMAs go
+// first, two per P V MFMA, so that S is complete long before the V phase
+// reads it (the last S MFMA is followed by about half the P V MFMAs); O and
+// the row sums are waited for only where the VALU reads them (pp_drain_o).
+template <int D, bool DO_S, bool DO_PV>
+__device__ __forceinline__ void pp_mphase(const PPAddr<D> &ad, PPRows<D> &w)
+{
+    constexpr int QS = D / 16, DB = D / 32;
+    constexpr int NSM = DO_S ? 2 * QS : 0;    // S MFMAs
+    constexpr int NPV = DO_PV ? 4 * DB : 0;   // P V MFMAs (4 steps of 16 keys x DB)
+    // step order: S steps at twice the rate of P V steps while both remain
+    constexpr int N = NSM + NPV;
+    auto is_s = [&](int j) {   // step j is an S step, and which one
+        if (!DO_PV) return true;
+        if (!DO_S) return false;
+        return j < 3 * (NSM / 2) ? (j % 3) != 2 : false;
+    };
+    auto idx = [&](int j) {    // index of step j among its kind
+        if (!DO_PV) return j;
+        if (!DO_S) return j;
+        if (j < 3 * (NSM / 2)) return (j % 3) != 2 ? 2 * (j / 3) + (j % 3) : j / 3;
+        return j - NSM;
+    };
+    auto ldk = [&](int i) {   // S step i: kb = i % 2, st = i / 2
+        return lds_read16(ad.k[i >> 1] + (i & 1) * 32 * 2 * D);
+    };
+    auto ldv = [&](int i) {   // P V step i: t2 = i / DB, db = i % DB
+        const int t2 = i / DB, db = i % DB;
+        return lds_read_vt(ad.v[db][0] + t2 * 16 * 2 * D, ad.v[db][1] + t2 * 16 * 2 * D);
+    };
+    set_prio<1>();
+    asm volatile("s_nop 1" ::: "memory");
+    bf16x8_t op[3];   // operand reads two steps ahead (rolling)
+#pragma unroll
+    for (int j = 0; j < 2 && j < N; ++j) op[j] = is_s(j) ? ldk(idx(j)) : ldv(idx(j));
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+        if (j + 2 < N) op[(j + 2) % 3] = is_s(j + 2) ? ldk(idx(j + 2)) : ldv(idx(j + 2));
+        const int i = idx(j);
+        if (is_s(j)) {
+            const int kb = i & 1, st = i >> 1;
+            if (st == 0)
+                pp_mfma_first(w.s[kb], op[j % 3], w.qf[st]);
+            else
+                pp_mfma_next(w.s[kb], op[j % 3], w.qf[st]);
+        } else {
+            const int t2 = i / DB, db = i % DB;
+            pp_mfma_pv(w.o[db], op[j % 3], w.p[t2]);
+            if (db == DB - 1) pp_mfma_rowsum(w.l_acc, w.sel, w.p[t2]);
+        }
+    }
+    set_prio<0>();
+}
+
+// P of one key block from its S (16 registers) against c * m_ref = mc,
+// packed to bf16 as the B operands of two 16-key P V steps; la adds the
+// exact values.  MASK: keys past `last` (offset from this lane half's first
+// key of the block) get exponent -inf, i.e. P = 0 for any scale.
+template <bool MASK>
+__device__ __forceinline__ void pp_probs(const f32x16_t &s, float c, float mc, int last,
+                                         bf16x8_t &p0, bf16x8_t &p1, float &la)
+{
+    u32x4_t w0, w1;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        float x0 = fmaf(s[2 * q], c, -mc);
+        float x1 = fmaf(s[2 * q + 1], c, -mc);
+        if (MASK) {
+            const int e0 = 2 * q, e1 = 2 * q + 1;
+            x0 = (8 * (e0 >> 2) + (e0 & 3) > last) ? kNegInf : x0;
+            x1 = (8 * (e1 >> 2) + (e1 & 3) > last) ? kNegInf : x1;
+        }
+        const float a = fast_exp2(x0), b = fast_exp2(x1);
+        if (q < 4)
+            w0[q] = pack_bf16(a, b);
+        else
+            w1[q - 4] = pack_bf16(a, b);
+        la += a + b;
+    }
+    p0 = __builtin_bit_cast(bf16x8_t, w0);
+    p1 = __builtin_bit_cast(bf16x8_t, w1);
+}
+
+// V phase with the exact running max: blocks at or past `live` are dead
+// (P = 0), keys past the lane's limit are masked.  key0: the tile's first
+// key.  Returns the factor the caller applies to O and the row sums.
+template <int D>
+__device__ __forceinline__ float pp_vphase_exact(PPRows<D> &w, int live, int key0, int half,
+                                                 int lim, float c)
+{
+    int last[2];
+    float mx = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        // largest allowed key offset from this lane half's first key of the block
+        last[kb] = kb < live ? lim - (key0 + kb * 32 + 4 * half) : -1;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const bool ok = 8 * (r >> 2) + (r & 3) <= last[kb];
+            mx = fmaxf(mx, ok ? w.s[kb][r] : kNegInf);
+        }
+    }
+    mx = max_halves(mx);
+    const float m_new = fmaxf(w.m_ref, mx);
+    // nothing accumulated yet (m_ref = -inf): O and the sums are zero
+    float alpha = 1.0f;
+    if (w.m_ref == kNegInf)
+        alpha = 0.0f;
+    else if (m_new > w.m_ref)
+        alpha = fast_exp2((w.m_ref - m_new) * c);
+    w.m_ref = m_new;
+    const float mc = (m_new == kNegInf) ? 0.0f : m_new * c;
+    float la = 0.0f;
+    pp_probs<true>(w.s[0], c, mc, last[0], w.p[0], w.p[1], la);
+    pp_probs<true>(w.s[1], c, mc, last[1], w.p[2], w.p[3], la);
+    w.l_run = w.l_run * alpha + la;
+    return alpha;
+}
+
+// V phase: P(t) from S(t).  Tiles whose two blocks are live and unmasked for
+// the wave, after the reference max is set (FAST), skip the max and redo the
+// tile against the exact max only when a lane's P sum overflows; O and the
+// rounded-P row sum are rescaled on that path only.
+template <int D>
+__device__ __forceinline__ void pp_vphase(PPRows<D> &w, bool fast, int live, int key0, int half,
+                                          int lim, float c)
+{
+    constexpr int DB = D / 32;
+    bool redo = !fast;
+    if (fast) {
+        const float mc = w.m_ref * c;
+        float la = -0.0f;
+        pp_probs<false>(w.s[0], c, mc, 0, w.p[0], w.p[1], la);
+        pp_probs<false>(w.s[1], c, mc, 0, w.p[2], w.p[3], la);
+        // !(x <= T) is also true for inf and NaN
+        redo = __any(!(la <= kWideOverflow));
+        if (!redo) w.l_run += la;
+    }
+    float alpha = 1.0f;
+    if (redo) {
+        // the wait for the last P V and row-sum MFMAs before O and the row
+        // sums are read; fenced rather than tied to O (tying O to an asm
+        // statement in this branch costs the copies described below)
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        alpha = pp_vphase_exact<D>(w, live, key0, half, lim, c);
+    }
+    // written after the branch on purpose: the compiler folds it away on the
+    // common path (alpha = 1 there), whereas a rescale written inside the
+    // branch made the register allocator keep two homes for O and copy it
+    // every phase
+    w.l_acc[0] *= alpha;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) w.o[db][e] *= alpha;
+}
+
+template <int D, int NS, bool OUT_F32>
+__global__ void __launch_bounds__(kPPWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
+fa_prefill_pp_kernel(const Params p)
+{
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
+    constexpr int NW = kPPWaves, BN = kPPBN, BM = 32 * NW;
+    using TL = TileLoader<D, BN, NW>;
+    constexpr int TB = TL::TILE_BYTES;
+    constexpr int VOFF = NS * TB;   // V tile s sits at K tile s + VOFF
+    constexpr int CPW = 2 * TL::PER_WAVE;   // copy instructions per wave and tile
+    static_assert(NS >= 4 && NS <= 5, "ring depth");
+
+    __shared__ __attribute__((aligned(1024))) char lds[2 * NS * TB];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2;          // 0: group A, 1: group B
+    const int col = lane & 31;
+    const int half = lane >> 5;
+
+    OperandOffsets<D> off;
+    off.init(lane);
+#pragma unroll
+    for (int db = 0; db < OperandOffsets<D>::NV; ++db)
+#pragma unroll
+        for (int sec = 0; sec < 2; ++sec) off.v[db][sec] += VOFF;
+    const uint32_t lds_base = (uint32_t)reinterpret_cast<uintptr_t>((lds_void_t *)lds);
+
+    const int BH = p.B * p.Hq;
+    const int ND = p.domains;
+    const int x = blockIdx.x % ND;
+    const int jw = blockIdx.x / ND;
+    const int Gx = gridDim.x / ND;
+    const int BHx = BH / ND;
+    const int Nx = BHx * p.n_mblocks;
+
+    // item `it` of this workgroup: (b, hq, query block), snake order
+    auto item = [&](int it, int &b, int &hq, int &row0, int &T) {
+        if (it * Gx >= Nx) return false;
+        const int li = it * Gx + ((it & 1) ? (Gx - 1 - jw) : jw);
+        if (li >= Nx) return false;
+        const int rank = p.head_major ? li % p.n_mblocks : li / BHx;
+        const int bh = (p.head_major ? li / p.n_mblocks : li % BHx) * ND + x;
+        const int mb = p.causal ? (p.n_mblocks - 1 - rank) : rank;
+        b = bh / p.Hq;
+        hq = bh % p.Hq;
+        row0 = mb * BM;
+        const int last_row = min(row0 + BM, p.Sq) - 1;
+        int n = (p.Sk + BN - 1) / BN;
+        if (p.causal) {
+            const int hi = last_row + p.off;
+            n = hi < 0 ? 0 : min(n, hi / BN + 1);
+        }
+        T = n;
+        return true;
+    };
+    // each of the 8 waves copies an eighth of every tile
+    TL ld;
+    auto issue_item = [&](int b, int hq, int row0, int T, PPRows<D> &w) {
+        const int g = hq / p.group;
+        ld.setup(p.k + ((long)b * p.Sk * p.Hkv + g) * D, p.v + ((long)b * p.Sk * p.Hkv + g) * D,
+                 p.Hkv * D * 2, p.Sk);
+        if (T > 0) ld.issue(lds, lds + VOFF, 0, wave, lane);
+        const int qi = min(row0 + 32 * wave + col, p.Sq - 1);
+        load_q<D>(w.qf, p.q + (((long)b * p.Sq + qi) * p.Hq + hq) * D, half);
+#pragma unroll
+        for (int u = 1; u < NS; ++u)
+            if (u < T) ld.issue(lds + u * TB, lds + VOFF + u * TB, u * BN, wave, lane);
+    };
+
+    PPRows<D> w;
+    int b = 0, hq = 0, row0 = 0, T = 0;
+    bool have = item(0, b, hq, row0, T);
+    if (have) issue_item(b, hq, row0, T, w);
+
+    for (int it = 0; have; ++it) {
+        const int wrow0 = row0 + 32 * wave;
+        const int qi = wrow0 + col;
+        const int wlast = min(wrow0 + 31, p.Sq - 1);
+        // key blocks this wave has work on (a prefix), and the smallest and
+        // this lane's causal limits
+        int NBw;
+        if (wrow0 >= p.Sq)
+            NBw = 0;
+        else if (p.causal) {
+            const int wmax_lim = wlast + p.off;
+            NBw = wmax_lim < 0 ? 0 : min(2 * T, wmax_lim / 32 + 1);
+        } else
+            NBw = 2 * T;
+        const int wmin_lim = p.causal ? wrow0 + p.off : 0x7fffffff;
+        const int lim = min(p.causal ? qi + p.off : 0x7fffffff, p.Sk - 1);
+        const int key_end = p.Sk;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) w.o[db] = f32x16_t{};
+        w.l_acc = f32x4_t{};
+        w.m_ref = kNegInf;
+        w.l_run = 0.0f;
+        w.sel = rowsum_selector(lane);
+
+        // Q and tile 0 landed; later tiles may be in flight
+        wait_tiles_ahead<CPW, 4>(min(NS - 1, T - 1));
+        flip_q<D>(w.qf, p.qflip);
+        pp_barrier();
+
+        // a tile's blocks: live count for this wave, and whether any key of
+        // a live block is cut by the causal limit or the key end
+        auto live_of = [&](int t) { return max(0, min(2, NBw - 2 * t)); };
+        auto clean = [&](int t) {
+            return (2 * t + 1) * 32 + 31 <= wmin_lim && (2 * t + 2) * 32 <= key_end;
+        };
+        auto kbase = [&](int k) { return lds_base + (k % NS) * TB; };
+        // every V phase writes all of P (0 for dead blocks and masked keys)
+        auto vphase = [&](int k) {
+            const int live = live_of(k);
+            pp_vphase<D>(w, k >= 1 && live == 2 && clean(k), live, k * BN, half, lim, p.c);
+        };
+        // operand addresses of M(k): K tile k, V tile k - 1
+        PPAddr<D> ad;
+        auto addr = [&](int k) { ad.set(kbase(k), kbase(k + NS - 1), off); };
+        // tile k + 1 is read from phase 2k+2 on: this wave's copies of it
+        // have landed (later tiles may still be in flight) ...
+        auto wait_next = [&](int k) {
+            if (k + 1 < T) {
+                const int issued_last = min(T - 1, max(NS - 1, k + NS - 2));
+                wait_tiles_ahead<CPW, 4>(issued_last - (k + 1));
+            }
+        };
+        // ... and every wave's after the barrier that follows.  This wave's
+        // share of the next tile its V(k) may fill (see above).
+        auto refill = [&](int k) {
+            const int u = k + NS - 2 + grp;
+            if (u >= NS && u < T)
+                ld.issue(lds + (u % NS) * TB, lds + VOFF + (u % NS) * TB, u * BN, wave, lane);
+        };
+        // Both groups run the same sequence M(0) V(0) M(1) V(1) ... M(T),
+        // one barrier after every phase; group B starts one barrier late and
+        // group A ends one barrier late, so that their phases alternate.
+        if (T > 0) {
+            addr(0);
+            if (grp == 1) pp_barrier();
+            pp_mphase<D, true, false>(ad, w);
+            pp_drain_s<D>(w);
+            if (grp == 1) wait_next(0);
+            pp_barrier();
+            vphase(0);
+            addr(1);
+            if (grp == 0) wait_next(0);
+            pp_barrier();
+            for (int k = 1; k < T; ++k) {
+                pp_mphase<D, true, true>(ad, w);
+                if (grp == 1) wait_next(k);
+                pp_barrier();
+                refill(k);
+                vphase(k);
+                addr(k + 1);
+                if (grp == 0) wait_next(k);
+                pp_barrier();
+            }
+            pp_mphase<D, false, true>(ad, w);
+            pp_barrier();
+            if (grp == 0) pp_barrier();
+        }
+        pp_drain_o<D>(w);
+
+        // this item's stores, then (the ring is free) the next item's copies
+        // and Q: the item start waits for the stores, Q and the first tile
+        // only, since vector-memory operations complete in issue order
+        finish_rows<D, OUT_F32>(w.o, w.m_ref, w.l_run, w.l_acc[0], p.c, half, p.o,
+                                (((long)b * p.Sq + qi) * p.Hq + hq) * D,
+                                p.lse ? p.lse + ((long)b * p.Hq + hq) * p.Sq + qi : nullptr,
+                                qi < p.Sq);
+        int nb = 0, nhq = 0, nrow0 = 0, nT = 0;
+        have = item(it + 1, nb, nhq, nrow0, nT);
+        if (have) issue_item(nb, nhq, nrow0, nT, w);
+        b = nb;
+        hq = nhq;
+        row0 = nrow0;
+        T = nT;
+    }
+#endif
+}
+
+// ---------------------------------------------------------------------------
 // Split-key decode: one wave per (b, KV head g, split).  Its 32 MFMA columns
 // are the (query row, head-in-group) pairs of KV head g: column j is query
 // j / group, head g * group + j % group; columns >= Sq * group are padding.
@@ -2922,6 +3440,16 @@ static void launch_prefill_cfg(const Launch &L, const Params &p)
     }
 }
 
+template <int D, int NS>
+static void launch_prefill_pp(const Launch &L, const Params &p)
+{
+    dim3 g(L.grid), blk(kPPWaves * 64);
+    if (L.o_f32)
+        hipLaunchKernelGGL((fa_prefill_pp_kernel<D, NS, true>), g, blk, 0, L.stream, p);
+    else
+        hipLaunchKernelGGL((fa_prefill_pp_kernel<D, NS, false>), g, blk, 0, L.stream, p);
+}
+
 // The compiled prefill tile configurations: head dim, keys per tile, waves
 // per workgroup, 32-row column blocks per wave.
 struct PrefillCfg {
@@ -2950,8 +3478,27 @@ static const PrefillCfg *find_prefill_cfg(int D, int bn, int nw, int nr)
 
 bool prefill_cfg_ok(int D, int bn, int nw, int nr) { return find_prefill_cfg(D, bn, nw, nr); }
 
+bool prefill_pp_ok(int D, int stages) { return (D == 64 || D == 128) && (stages == 4 || stages == 5); }
+
 hipError_t launch_prefill(const Launch &L)
 {
+    if (L.prefill_pp) {
+        if (!prefill_pp_ok(L.D, L.prefill_pp)) return hipErrorInvalidValue;
+        Params p = make_params(L);
+        const int BH = L.B * L.Hq;
+        const int bm = 32 * kPPWaves;
+        p.n_mblocks = (L.Sq + bm - 1) / bm;
+        p.domains = (BH % 8 == 0 && L.grid % 8 == 0) ? 8 : 1;
+        p.head_major = L.head_major;
+        if (L.D == 128) {
+            if (L.prefill_pp == 5) launch_prefill_pp<128, 5>(L, p);
+            else launch_prefill_pp<128, 4>(L, p);
+        } else {
+            if (L.prefill_pp == 5) launch_prefill_pp<64, 5>(L, p);
+            else launch_prefill_pp<64, 4>(L, p);
+        }
+        return hipGetLastError();
+    }
     const PrefillCfg *cfg = find_prefill_cfg(L.D, L.prefill_bn, L.prefill_nw, L.prefill_nr);
     if (!cfg) return hipErrorInvalidValue;
     Params p = make_params(L);

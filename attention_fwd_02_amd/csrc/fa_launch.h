@@ -14,6 +14,12 @@ constexpr int kPrefillStages = 3;
 inline int prefill_lds_bytes(int D, int bn) { return kPrefillStages * 2 * bn * D * 2; }
 inline int prefill_waves_per_simd(int nr) { return nr == 1 ? 2 : 1; }
 bool prefill_cfg_ok(int D, int bn, int nw, int nr);   // is this configuration compiled?
+// Ping-pong prefill: 8 waves x 32 rows, 64-key tiles, two waves per SIMD in
+// alternating MFMA and softmax phases; `stages` K/V tiles in the LDS ring.
+constexpr int kPrefillPPWaves = 8;
+constexpr int kPrefillPPBN = 64;
+inline int prefill_pp_lds_bytes(int D, int stages) { return stages * 2 * kPrefillPPBN * D * 2; }
+bool prefill_pp_ok(int D, int stages);
 // Keys per tile of the split-key decode kernel; query rows it serves per KV
 // head; depth of its LDS ring (tiles: one being read, the rest in flight).
 constexpr int kDecodeBN = 32;
@@ -53,6 +59,7 @@ struct Launch {
     int prefill_nw;      // prefill: waves per workgroup
     int prefill_nr;      // prefill: 32-row column blocks per wave
     int head_major;      // prefill: item order (1: head by head, 0: rank by rank)
+    int prefill_pp;      // prefill: 0, or the ring depth (4 or 5) of the ping-pong kernel
     hipStream_t stream;
 };
 

@@ -106,13 +106,18 @@ fa_status fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float 
 /*
  * fa_workspace_size -- bytes of split workspace the call with these sizes and
  * this num_splits (0 = automatic) needs; 0 when it takes the single-pass path.
- * Pure host arithmetic, no device access.  Returns 0 for invalid sizes.
+ * Hkv is an argument because the automatic split count depends on the number
+ * of (batch, KV head) pairs.  Host arithmetic plus a one-time query of the
+ * current device's compute-unit count (a device property: nothing is
+ * launched or allocated), so the size asked for before any call equals what
+ * fa_fwd_ex then needs on that device; with no usable device it plans for
+ * 256 compute units.  Returns 0 for invalid sizes.
  */
 size_t fa_workspace_size(int B, int Hq, int Hkv, int Sq, int Sk, int D, int num_splits);
 
 /*
- * fa_plan -- which kernels a call with these sizes would launch.  Pure host
- * arithmetic except the one-time device query (CU count, architecture).
+ * fa_plan -- which kernels a call with these sizes would launch.  Host
+ * arithmetic plus the one-time device property query of fa_workspace_size.
  * Fills *out; returns FA_ERR_INVALID_ARG / FA_ERR_UNSUPPORTED as fa_fwd_ex would.
  */
 typedef struct {
@@ -174,7 +179,7 @@ fa_status fa_fwd_paged(const void *q, const void *k_cache, const void *v_cache,
 
 /*
  * fa_plan_paged -- the launch fa_fwd_paged would make (path 2): splits per
- * sequence, grid, workspace bytes.  Pure host arithmetic, like fa_plan.
+ * sequence, grid, workspace bytes.  Host arithmetic, like fa_plan.
  */
 fa_status fa_plan_paged(int B, int Hq, int Hkv, int Sq, int D, int num_pages, int page_size,
                         int max_pages, int num_splits, fa_plan_info *out);

@@ -90,7 +90,20 @@ def _bits(x) -> np.ndarray:
 
 
 def default_threads() -> int:
-    n = os.cpu_count() or 1
+    """The host cores this process may run on: its CPU affinity set, capped
+    by a cgroup CPU quota when one is set (a container's share of a larger
+    host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    try:
+        with open("/sys/fs/cgroup/cpu.max") as f:
+            quota, period = f.read().split()[:2]
+        if quota != "max":
+            n = min(n, max(1, -(-int(quota) // int(period))))
+    except (OSError, ValueError):
+        pass
     return max(1, n)
 
 

@@ -207,3 +207,12 @@ def test_paged_plan_host_arithmetic(b):
     assert b.fa_plan_paged(1, 8, 2, 1, 128, 1024, 256, 64, 1)["num_splits"] == 1
     assert b.fa_plan_paged(1, 8, 2, 1, 128, 1024, 256, 64, 7)["num_splits"] == 7
     assert b.fa_plan_paged(1, 8, 2, 1, 128, 1024, 16, 2, 64)["num_splits"] == 1
+
+
+def test_workspace_size_matches_the_plan_before_any_call(b):
+    # a pure size query (no call made yet in this process on a device) plans
+    # for the same compute-unit count as the call itself, so the two agree
+    for shape in ((32, 32, 8, 1, 8192, 128, 0), (2, 8, 2, 1, 3000, 128, 6), (4, 16, 4, 2, 700, 64, 0)):
+        B, Hq, Hkv, Sq, Sk, D, ns = shape
+        plan = b.fa_plan(B, Hq, Hkv, Sq, Sk, D, 0, ns)
+        assert b.fa_workspace_size(B, Hq, Hkv, Sq, Sk, D, ns) == plan["workspace_bytes"] > 0

@@ -58,6 +58,21 @@ def test_branch_before_wait_is_found():
     assert "control flow" in asm_check.scan(asm)[0]
 
 
+ACC = "v_mfma_f32_32x32x16_bf16 v[32:47], v[0:3], v[4:7], v[32:47] ; accumulate-only"
+
+
+def test_accumulate_only_mfma_may_precede_a_branch():
+    asm = listing(ACC, "s_cbranch_scc1 .LBB0_3", "v_exp_f32_e32 v8, v9", ".LBB0_3:",
+                  "s_barrier", asm_idx=(0,))
+    assert asm_check.scan(asm) == []
+
+
+def test_accumulate_only_result_read_past_the_branch_is_found():
+    asm = listing(ACC, "s_cbranch_scc1 .LBB0_3", "v_mul_f32_e32 v40, v40, v9", asm_idx=(0,))
+    found = asm_check.scan(asm)
+    assert len(found) == 1 and "accessed" in found[0]
+
+
 def test_operand_written_just_before_is_found():
     asm = listing("v_accvgpr_write_b32 a2, v7", MFMA, "s_nop 7\n\ts_nop 7\n\ts_nop 7",
                   asm_idx=(1, 2))
