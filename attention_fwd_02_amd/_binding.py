@@ -20,7 +20,7 @@ STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_INVALID_ARG", 2: "FA_ERR_UNSUPPORTED",
                 3: "FA_ERR_NOMEM", 4: "FA_ERR_HIP"}
 
 # every symbol include/fa.h declares
-EXPORTS = ["fa_fwd", "fa_fwd_ex", "fa_workspace_size", "fa_plan", "fa_fwd_paged",
+EXPORTS = ["fa_fwd", "fa_fwd_ex", "fa_fwd_noalloc", "fa_workspace_size", "fa_plan", "fa_fwd_paged",
            "fa_plan_paged", "fa_fwd_fp8", "fa_bwd", "fa_bwd_workspace_size", "fa_last_error",
            "fa_release_workspace", "fa_version"]
 
@@ -53,6 +53,8 @@ def _load():
     lib.fa_fwd.restype = c_int
     lib.fa_fwd_ex.argtypes = fwd_args + [c_int, c_int, c_void_p, c_size_t]
     lib.fa_fwd_ex.restype = c_int
+    lib.fa_fwd_noalloc.argtypes = fwd_args + [c_int, c_int]
+    lib.fa_fwd_noalloc.restype = c_int
     lib.fa_workspace_size.argtypes = [c_int] * 7
     lib.fa_workspace_size.restype = c_size_t
     lib.fa_plan.argtypes = [c_int] * 8 + [ctypes.POINTER(FaPlanInfo)]
@@ -167,6 +169,24 @@ def fa_fwd_ex(q, k, v, o, lse, causal: bool, scale: float, stream=None, num_spli
                          lse.data_ptr() if lse is not None else None,
                          B, Hq, Hkv, Sq, Sk, D, int(bool(causal)), float(scale),
                          _stream_handle(stream), odt, int(num_splits), ws_ptr, ws_bytes))
+
+
+def fa_fwd_noalloc(q, k, v, o, lse, causal: bool, scale: float, stream=None,
+                   num_splits: int = 0) -> None:
+    """As fa_fwd_ex, with the split partials in the library's static device
+    array (the call allocates nothing)."""
+    import torch
+    if o.dtype == torch.bfloat16:
+        odt = FA_DTYPE_BF16
+    elif o.dtype == torch.float32:
+        odt = FA_DTYPE_F32
+    else:
+        raise TypeError("o must be bfloat16 or float32")
+    B, Hq, Hkv, Sq, Sk, D = _shapes(q, k, v, o, lse)
+    _check(lib.fa_fwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                              lse.data_ptr() if lse is not None else None,
+                              B, Hq, Hkv, Sq, Sk, D, int(bool(causal)), float(scale),
+                              _stream_handle(stream), odt, int(num_splits)))
 
 
 def fa_plan_paged(B, Hq, Hkv, Sq, D, num_pages, page_size, max_pages, num_splits=0) -> dict:

@@ -376,14 +376,13 @@ fa_status make_paged_plan(int B, int Hkv, int page_size, int max_pages, int D, i
     return FA_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-fa_status fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse, int B,
-                    int Hq, int Hkv, int Sq, int Sk, int D, int causal, float scale,
-                    hipStream_t stream, fa_dtype o_dtype, int num_splits, void *workspace,
-                    size_t workspace_bytes)
+// The forward of fa_fwd_ex and fa_fwd_noalloc.  `static_ws`: the split
+// partials go to this device's static scratch array instead of a caller or
+// library-owned workspace, and nothing is allocated.
+fa_status fwd_impl(const void *q, const void *k, const void *v, void *o, float *lse, int B, int Hq,
+                   int Hkv, int Sq, int Sk, int D, int causal, float scale, hipStream_t stream,
+                   fa_dtype o_dtype, int num_splits, void *workspace, size_t workspace_bytes,
+                   bool static_ws)
 {
     g_last_error.clear();
     if (!q || !k || !v || !o) return fail(FA_ERR_INVALID_ARG, "q, k, v and o must not be NULL");
@@ -414,6 +413,12 @@ fa_status fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float 
     Plan pl;
     st = make_plan(B, Hq, Hkv, Sq, Sk, D, causal, num_splits, info->cus, &pl);
     if (st != FA_OK) return st;
+    if (static_ws && pl.ws_bytes > fa::kStaticScratchBytes)
+        return fail(FA_ERR_UNSUPPORTED,
+                    "the split plan needs " + std::to_string(pl.ws_bytes) +
+                        " bytes of scratch; the static buffer of fa_fwd_noalloc holds " +
+                        std::to_string(fa::kStaticScratchBytes) +
+                        " (call fa_fwd_ex with a workspace instead)");
 
     fa::Launch L;
     L.q = q; L.k = k; L.v = v; L.o = o; L.lse = lse;
@@ -443,6 +448,17 @@ fa_status fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float 
     hipError_t e;
     if (pl.path == 0) {
         e = fa::launch_prefill(L);
+    } else if (static_ws) {
+        if (pl.ws_bytes > 0) {
+            void *ws = nullptr;
+            e = fa::static_scratch_ptr(dev, &ws);
+            if (e != hipSuccess)
+                return fail(FA_ERR_HIP, std::string("hipGetSymbolAddress: ") + hipGetErrorString(e));
+            const size_t n_rows = (size_t)B * Hq * Sq;
+            L.part_o = static_cast<float *>(ws);
+            L.part_lse = L.part_o + (size_t)pl.num_splits * n_rows * D;
+        }
+        e = fa::launch_decode(L);
     } else {
         std::unique_lock<std::mutex> lk(g_mu, std::defer_lock);
         if (pl.ws_bytes > 0) {
@@ -454,6 +470,27 @@ fa_status fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float 
     }
     if (e != hipSuccess) return fail(FA_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
     return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse, int B,
+                    int Hq, int Hkv, int Sq, int Sk, int D, int causal, float scale,
+                    hipStream_t stream, fa_dtype o_dtype, int num_splits, void *workspace,
+                    size_t workspace_bytes)
+{
+    return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, causal, scale, stream, o_dtype,
+                    num_splits, workspace, workspace_bytes, false);
+}
+
+fa_status fa_fwd_noalloc(const void *q, const void *k, const void *v, void *o, float *lse,
+                         int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal, float scale,
+                         hipStream_t stream, fa_dtype o_dtype, int num_splits)
+{
+    return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, causal, scale, stream, o_dtype,
+                    num_splits, nullptr, 0, true);
 }
 
 fa_status fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int Hq,

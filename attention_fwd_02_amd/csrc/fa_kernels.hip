@@ -49,6 +49,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "fa_launch.h"
@@ -3601,6 +3602,36 @@ hipError_t launch_bwd(const BwdLaunch &L)
     else
         by_d(std::integral_constant<int, 64>{});
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Split partials of the allocation-free entry point (fa_fwd_noalloc): one
+// array per GPU the library runs on, held until the process ends.  In host
+// code `scratch` only names the symbol; its device address, different on
+// every GPU, comes from hipGetSymbolAddress with that GPU current, looked up
+// once per device and kept.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxScratchDevices];
+}  // namespace
+
+hipError_t static_scratch_ptr(int dev, void **out)
+{
+    if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        // the caller has made `dev` the current device
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!ptr) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 static hipError_t launch_merge(const Launch &L, const Params &p)

@@ -63,6 +63,12 @@ struct Launch {
     hipStream_t stream;
 };
 
+// Static scratch of the allocation-free entry point: kStaticScratchBytes per
+// device (the split partials of one call), address per device.
+constexpr size_t kStaticScratchBytes = size_t(16) << 20;
+constexpr int kMaxScratchDevices = 64;
+hipError_t static_scratch_ptr(int dev, void **out);   // `dev` must be current
+
 hipError_t launch_prefill(const Launch &L);
 hipError_t launch_decode(const Launch &L);  // split kernel, then the merge pass if splits > 1
 

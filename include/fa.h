@@ -104,6 +104,25 @@ fa_status fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float 
                     size_t workspace_bytes);
 
 /*
+ * fa_fwd_noalloc -- fa_fwd_ex for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same computation and arguments, without a workspace.  The
+ * split partials go to a static device array of 16 MiB that the library
+ * holds on every GPU it runs on until the process ends; a plan that needs
+ * more than that (fa_workspace_size of the same problem) returns
+ * FA_ERR_UNSUPPORTED, and the prefill path needs none.  The call allocates
+ * nothing (no hipMalloc, no library allocation); its first call on a device
+ * looks up that device's array address once.  Every call on one GPU shares
+ * that GPU's array and leaves its contents behind (no call needs them
+ * cleared): calls on one GPU whose kernels may overlap in time, i.e. on
+ * different streams without ordering, race and must not be made.  Other
+ * arguments, statuses and asynchrony as for fa_fwd_ex.
+ */
+fa_status fa_fwd_noalloc(const void *q, const void *k, const void *v, void *o, float *lse,
+                         int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal, float scale,
+                         hipStream_t stream, fa_dtype o_dtype, int num_splits);
+
+/*
  * fa_workspace_size -- bytes of split workspace the call with these sizes and
  * this num_splits (0 = automatic) needs; 0 when it takes the single-pass path.
  * Hkv is an argument because the automatic split count depends on the number
