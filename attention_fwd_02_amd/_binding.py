@@ -8,6 +8,7 @@ module fails loudly: there is no fallback path.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -40,12 +41,12 @@ class FaPlanInfo(ctypes.Structure):
                 ("rows_per_wave", ctypes.c_int)]
 
 
-def _load():
-    if not os.path.exists(LIB_PATH):
+def _load(path=LIB_PATH):
+    if not os.path.exists(path):
         raise ImportError(
-            f"{LIB_PATH} is not built; run `python -m attention_fwd_02_amd.build` "
+            f"{path} is not built; run `python -m attention_fwd_02_amd.build` "
             "(or __graft_entry__.build()) first")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     c_int, c_float, c_void_p, c_size_t = ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
     fwd_args = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                 c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_float, c_void_p]
@@ -81,6 +82,22 @@ def _load():
 
 
 lib = _load()
+_other_builds = {}
+
+
+@contextlib.contextmanager
+def using_library(path):
+    """Inside the block, this module's functions call another build of the
+    same library at `path` (the LDS race-check debug builds), then libfa.so
+    again.  Not thread-safe; for tests."""
+    global lib
+    if path not in _other_builds:
+        _other_builds[path] = _load(path)
+    saved, lib = lib, _other_builds[path]
+    try:
+        yield
+    finally:
+        lib = saved
 
 
 def _check(status: int):

@@ -33,8 +33,23 @@ FLAGS = [
 ]
 
 
-def check_device_code() -> None:
-    """Generate the kernels' gfx950 assembly and scan it; raise on findings."""
+# sha256 of the kernels' generated gfx950 assembly, written next to libfa.so:
+# it names the device code a measurement was taken on (the HBM traffic
+# counters record it), unchanged by edits that do not change that code.
+DEVICE_SHA = LIB + ".device-sha256"
+
+
+def device_code_sha256(asm: str) -> str:
+    """sha256 of the assembly without its compilation-unit id symbol (a name
+    hipcc derives per compile, not code)."""
+    import hashlib
+    text = "\n".join(l for l in asm.splitlines() if "__hip_cuid_" not in l)
+    return hashlib.sha256(text.encode()).hexdigest()
+
+
+def check_device_code() -> str:
+    """Generate the kernels' gfx950 assembly and scan it; raise on findings.
+    Returns the assembly's sha256."""
     asm = asm_check.device_asm(HIPCC, FLAGS, INCLUDE, os.path.join(CSRC, "fa_kernels.hip"))
     found = asm_check.scan(asm)
     if found:
@@ -44,6 +59,54 @@ def check_device_code() -> None:
     if found:
         raise RuntimeError("register copies at the end of divergent regions:\n  "
                            + "\n  ".join(found[:20]))
+    return device_code_sha256(asm)
+
+
+# Debug builds of the same sources with the LDS ring race checks on (see
+# FA_LDS_CHECK in fa_kernels.hip): copies waited for at issue, or each copy's
+# destination poisoned first.  Tests compare them bit for bit with libfa.so.
+CHECK_VARIANTS = {"sync": 1, "poison": 2}
+
+
+def check_lib_path(name: str) -> str:
+    return os.path.join(HERE, f"libfa_check_{name}.so")
+
+
+def build_check_variants(verbose: bool = False) -> list:
+    """Compile every debug build in CHECK_VARIANTS (in parallel)."""
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    procs = []
+    for name, level in CHECK_VARIANTS.items():
+        out = check_lib_path(name)
+        cmd = [HIPCC, *FLAGS, f"-DFA_LDS_CHECK={level}", "-I", INCLUDE, "-o", out + ".tmp", *srcs]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((out, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE,
+                                            text=True)))
+    built = []
+    for out, p in procs:
+        _, err = p.communicate()
+        if p.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {out} ({p.returncode}):\n{err[-4000:]}")
+        os.replace(out + ".tmp", out)
+        built.append(out)
+    return built
+
+
+CEIL_LIB = os.path.join(HERE, "libfa_ceilings.so")
+
+
+def build_ceilings(verbose: bool = False) -> str:
+    """Compile the ceiling loops (fa_ceilings.hip) into libfa_ceilings.so."""
+    tmp = CEIL_LIB + ".tmp"
+    cmd = [HIPCC, *FLAGS, "-I", INCLUDE, "-o", tmp, os.path.join(CSRC, "fa_ceilings.hip")]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stderr[-4000:]}")
+    os.replace(tmp, CEIL_LIB)
+    return CEIL_LIB
 
 
 def build_lib(verbose: bool = False) -> str:
@@ -54,11 +117,11 @@ def build_lib(verbose: bool = False) -> str:
     cmd = [HIPCC, *FLAGS, "-I", INCLUDE, "-o", tmp, *srcs]
     if verbose:
         print(" ".join(cmd), flush=True)
-    check_err = []
+    check_err, sha = [], []
 
     def _check():
         try:
-            check_device_code()
+            sha.append(check_device_code())
         except Exception as e:  # reported after the library build
             check_err.append(e)
 
@@ -78,8 +141,12 @@ def build_lib(verbose: bool = False) -> str:
     if verbose and err.strip():
         print(err, file=sys.stderr)
     os.replace(tmp, LIB)
+    with open(DEVICE_SHA, "w") as f:
+        f.write(sha[0] + "\n")
     return LIB
 
 
 if __name__ == "__main__":
     print(build_lib(verbose=True))
+    print(build_ceilings(verbose=True))
+    print(build_check_variants(verbose=True))

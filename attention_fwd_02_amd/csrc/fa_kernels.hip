@@ -168,6 +168,49 @@ __device__ __forceinline__ int swz(int r)
     return (r1 << 2) | ((r0 ^ r2) << 1) | (r0 ^ r3);
 }
 
+// Race checks of the LDS rings, in debug builds of the library only
+// (FA_LDS_CHECK = 0 in the product build).  A ring stage must be ready (its
+// copies landed and every wave past the barrier that follows the wait) before
+// it is read, and reusable (every wave done reading it) before the copies of
+// a later tile go into it ("理解 H100：从硬件数据路径到 Nsight Compute 瓶颈分析",
+// section 6, the asynchronous pipeline's stage states).
+//  * FA_LDS_CHECK = 1 (synchronous copies): each copy is waited for
+//    (vmcnt(0)) right after it is issued, so every stage is ready long
+//    before the kernel's own wait and barrier would make it so.  A missing or
+//    too-short wait in the normal build then shows as a bitwise difference.
+//  * FA_LDS_CHECK = 2 (poison): before each copy, the issuing lane writes
+//    all-ones -- NaN as bf16, fp32 and E4M3 -- into the LDS bytes that copy
+//    will fill, and waits for the write.  A wave still reading the stage
+//    (not reusable), or reading it before the copy lands (not ready), takes
+//    the poison instead of data it could have silently got away with.
+#ifndef FA_LDS_CHECK
+#define FA_LDS_CHECK 0
+#endif
+
+template <int BYTES>
+__device__ __forceinline__ void lds_check_before_copy(char *dst)
+{
+#if FA_LDS_CHECK == 2
+    const uint32_t lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    char __attribute__((address_space(3))) *d =
+        (char __attribute__((address_space(3))) *)(lds_void_t *)dst + lane * BYTES;
+    if constexpr (BYTES == 16)
+        *(u32x4_t __attribute__((address_space(3))) *)d = (u32x4_t){~0u, ~0u, ~0u, ~0u};
+    else
+        *(uint32_t __attribute__((address_space(3))) *)d = ~0u;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#else
+    (void)dst;
+#endif
+}
+
+__device__ __forceinline__ void lds_check_after_copy()
+{
+#if FA_LDS_CHECK == 1
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#endif
+}
+
 // One HBM -> LDS copy instruction: buffer_load_dwordx4 ... lds writes the 64
 // lanes' 16 bytes at consecutive LDS addresses from M0 on.  It is issued as
 // inline asm on purpose: the compiler tracks its own LDS-DMA loads and, unable
@@ -189,6 +232,8 @@ __device__ __forceinline__ void lds_dma16_pair(char *lds_k, char *lds_v, int vof
     const uint32_t m0k = (uint32_t)reinterpret_cast<uintptr_t>((lds_void_t *)lds_k);
     const uint32_t m0v = (uint32_t)reinterpret_cast<uintptr_t>((lds_void_t *)lds_v);
     uint32_t saved;
+    lds_check_before_copy<16>(lds_k);
+    lds_check_before_copy<16>(lds_v);
     if (STREAM)
         asm volatile(
             "s_mov_b32 %0, m0\n\t"
@@ -215,6 +260,7 @@ __device__ __forceinline__ void lds_dma16_pair(char *lds_k, char *lds_v, int vof
             : "=&s"(saved)
             : "s"(m0k), "s"(m0v), "v"(voff), "s"(kd), "s"(vd)
             : "memory");
+    lds_check_after_copy();
 }
 
 // One copy of lds_dma16_pair's kind into one destination.
@@ -223,6 +269,7 @@ __device__ __forceinline__ void lds_dma16(char *lds, int voff, u32x4_t d)
 {
     const uint32_t m0 = (uint32_t)reinterpret_cast<uintptr_t>((lds_void_t *)lds);
     uint32_t saved;
+    lds_check_before_copy<16>(lds);
     if (STREAM)
         asm volatile(
             "s_mov_b32 %0, m0\n\t"
@@ -243,6 +290,7 @@ __device__ __forceinline__ void lds_dma16(char *lds, int voff, u32x4_t d)
             : "=&s"(saved)
             : "s"(m0), "v"(voff), "s"(d)
             : "memory");
+    lds_check_after_copy();
 }
 
 // HBM -> LDS copy of one K and one V tile of BN keys by NW waves.  One
@@ -1542,6 +1590,8 @@ __device__ __forceinline__ void lds_dma4_pair(char *lds_a, char *lds_b, int voff
     const uint32_t m0a = (uint32_t)reinterpret_cast<uintptr_t>((lds_void_t *)lds_a);
     const uint32_t m0b = (uint32_t)reinterpret_cast<uintptr_t>((lds_void_t *)lds_b);
     uint32_t saved;
+    lds_check_before_copy<4>(lds_a);
+    lds_check_before_copy<4>(lds_b);
     asm volatile(
         "s_mov_b32 %0, m0\n\t"
         "s_mov_b32 m0, %1\n\t"
@@ -1554,6 +1604,7 @@ __device__ __forceinline__ void lds_dma4_pair(char *lds_a, char *lds_b, int voff
         : "=&s"(saved)
         : "s"(m0a), "s"(m0b), "v"(voff), "s"(da), "s"(db)
         : "memory");
+    lds_check_after_copy();
 }
 
 __device__ __forceinline__ u32x4_t raw_desc(const void *base, uint32_t nbytes)

@@ -14,8 +14,12 @@ in HBM:
     (one fa_fwd call each), and
   * the causal prefill's shape on FP8 E4M3 inputs (one fa_fwd_fp8 call), and
   * the backward of the causal prefill (one fa_bwd call: delta, dK/dV, dQ
-    kernels) on the prefill's own O and LSE and a seeded dO.
-Both go to the same stream; HIP events recorded on that stream around each
+    kernels) on the prefill's own O and LSE and a seeded dO, and
+  * the other three shapes of the suite, one fa_fwd call each: the
+    single-head B=1 H=1 S=128 D=64 (fp32 O), the small causal prefill
+    B=2 H=8 S=1024 D=64 and the long non-causal GQA prefill B=1 Hq=32 Hkv=8
+    S=16384 D=128.
+All go to the same stream; HIP events recorded on that stream around each
 call give the per-call durations.
 
 Printed: one JSON line.  `value` is the prefill's algorithmic TFLOP/s (4*D
@@ -25,7 +29,12 @@ GB/s (Q, K, V read once, O and LSE written once), `paged_decode` and
 `d256_prefill` / `d256_decode` the head-dim-256 calls' TFLOP/s and GB/s,
 `fp8_prefill` the FP8 call's TFLOP/s against the dense FP8 MFMA peak,
 `backward` the backward's TFLOP/s (algorithmic: 5 products, 2.5x the
-forward's FLOPs) against the bf16 peak.
+forward's FLOPs) against the bf16 peak, `single_head`, `causal_small` and
+`gqa_long` the other shapes' TFLOP/s.  `ceilings` are same-machine loops (HBM
+streaming read, MFMA issue and the clock it runs at, LDS and VALU rates) that
+the datasheet peaks are read against; `conditions` the GPU, ROCm, power cap
+and the shader/memory clocks sampled while the step ran without pause;
+`host` the CPU the baseline ran on.
 `roofline` is the prefill kernel against the dense bf16 MFMA peak; the decode
 entries' `roofline` their call against HBM.  `cpu_baseline` times the fp64 oracle on a bounded sample of the
 prefill workload's rows and also compares those rows with the timed output.
@@ -39,10 +48,10 @@ timed before that run up to 30 % slower.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -61,8 +70,16 @@ PAGED_RAGGED = "paged_decode_b32_hq32_hkv8_ragged16384_ps16_d128"
 PREFILL_D256 = "causal_b2_h16_s4096_d256"
 DECODE_D256 = "decode_b32_hq32_hkv8_sk8192_d256"
 PREFILL_FP8 = "causal_b4_h16_s4096_d128_fp8"
+SINGLE = "single_head_s128_d64"
+SMALL = "causal_b2_h8_s1024_d64"
+GQA = "gqa_b1_hq32_hkv8_s16384_d128"
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
-KERNEL_SRC = os.path.join(ROOT, "attention_fwd_02_amd", "csrc", "fa_kernels.hip")
+DEVICE_SHA = os.path.join(ROOT, "attention_fwd_02_amd", "libfa.so.device-sha256")
+
+
+def log(msg):
+    """Progress on stderr (stdout carries only the JSON line)."""
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
 
 
 def roofline(achieved, peak, unit, bound, traffic=None):
@@ -70,20 +87,25 @@ def roofline(achieved, peak, unit, bound, traffic=None):
             "frac": round(achieved / peak, 4), "traffic": traffic}
 
 
-def kernel_source_hash():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def device_code_hash():
+    """sha256 of the built kernels' gfx950 assembly (written by the build)."""
+    try:
+        with open(DEVICE_SHA) as f:
+            return f.read().strip()
+    except OSError:
+        return None
 
 
 def measured_traffic(key):
     """HBM bytes per launch from the committed rocprofv3 counter runs, or None
-    when the kernel source changed since they were taken."""
+    when the kernels' device code changed since they were taken."""
     try:
         with open(COUNTERS) as f:
             c = json.load(f)[key]
     except (OSError, KeyError, ValueError):
         return None
-    if c.get("source_sha256") != kernel_source_hash():
+    h = device_code_hash()
+    if h is None or c.get("device_code_sha256") != h:
         return None
     return int(c["hbm_bytes_per_launch"])
 
@@ -97,7 +119,7 @@ def cpu_baseline_leg(w, q, k, v, o_gpu, lse_gpu, seconds):
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     from tests.helpers import check
 
-    threads = max(1, min(os.cpu_count() or 1, 16))
+    threads = oracle.default_threads()
     rng = np.random.default_rng(1234)
 
     def rows_of(n):
@@ -128,14 +150,105 @@ def cpu_baseline_leg(w, q, k, v, o_gpu, lse_gpu, seconds):
     o_s = np.stack([og[b, i, h] for b, h, i in rows])
     l_s = np.array([lg[b, h, i] for b, h, i in rows])
     eo, el = check(o_s, l_s, o_ref, lse_ref, w.o_dtype, "timed output")
+    err = np.abs(o_s - o_ref)
+    over = err > 1e-2
     return {
         "value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
         "kind": "oracle",
         "sample": (f"{n} random query rows of the {PREFILL} workload "
                    f"({fl / 1e9:.1f} GFLOP algorithmic, {dt:.1f} s, fp64, "
                    f"{threads} threads)"),
-        "parity_on_timed_output": {"rows": n, "max_abs_dO": eo, "max_abs_dLSE": el},
+        "parity_on_timed_output": {
+            "rows": n, "max_abs_dO": eo, "max_abs_dLSE": el,
+            "elements": int(err.size),
+            "elements_over_flat_1e-2": int(over.sum()),
+            "abs_O_range_of_those": ([float(np.abs(o_ref[over]).min()),
+                                      float(np.abs(o_ref[over]).max())] if over.any() else None),
+            "rule": ("|dO| <= 1e-2 + half a bf16 ulp of the oracle's value (the output's own "
+                     "rounding), |dLSE| <= 1e-3"),
+        },
     }
+
+
+def host_facts():
+    """The CPU the baseline ran on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        aff = None
+    quota = None
+    try:
+        with open("/sys/fs/cgroup/cpu.max") as f:
+            quota = f.read().strip()
+    except OSError:
+        pass
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "affinity_cpus": aff,
+            "cgroup_cpu_max": quota}
+
+
+def _smi(args, timeout=20):
+    """Output of rocm-smi with `args` (JSON), or None."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", *args, "--json"], capture_output=True, text=True,
+                           timeout=timeout)
+        return json.loads(r.stdout) if r.returncode == 0 and r.stdout.strip() else None
+    except (OSError, ValueError, subprocess.SubprocessError):
+        return None
+
+
+def _pick(d, words):
+    """Values of `d` (card entries of a rocm-smi JSON) whose key holds all of `words`."""
+    out = {}
+    if isinstance(d, dict):
+        for card, ent in d.items():
+            if isinstance(ent, dict):
+                for k, v in ent.items():
+                    if all(w in k.lower() for w in words):
+                        out[k] = v
+    return out
+
+
+def sustained_clocks(run_for, seconds):
+    """Keep the step running back to back for `seconds` while a thread samples
+    rocm-smi's current clocks; returns the samples and the steps' own pace."""
+    import threading
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            c = _smi(["--showclocks"])
+            if c is not None:
+                samples.append({**_pick(c, ["sclk"]), **_pick(c, ["mclk"])})
+
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    ms = run_for(seconds)
+    stop.set()
+    th.join(timeout=30)
+
+    def mhz(word):
+        vals = []
+        for smp in samples:
+            for k, v in smp.items():
+                m = re.search(r"(\d+)\s*mhz", str(v).lower())
+                if word in k.lower() and "speed" in k.lower() and m:
+                    vals.append(int(m.group(1)))
+        vals.sort()
+        return ({"min": vals[0], "median": vals[len(vals) // 2], "max": vals[-1], "n": len(vals)}
+                if vals else None)
+
+    return {"seconds": seconds, "ms_per_step": ms, "sclk_MHz": mhz("sclk"),
+            "mclk_MHz": mhz("mclk"), "source": "rocm-smi --showclocks, sampled back to back"}
 
 
 def profile_one(args):
@@ -187,11 +300,13 @@ def profile_one(args):
         fn = lambda: fa.fa_fwd(q, k, v, o, lse, w.causal, w.scale)  # noqa: E731
         label = w.name
     else:
-        w = WORKLOADS[PREFILL if args.profile_kernel == "prefill" else DECODE]
+        w = WORKLOADS[{"prefill": PREFILL, "decode": DECODE, "single_head": SINGLE,
+                       "causal_small": SMALL, "gqa_long": GQA}[args.profile_kernel]]
         q, k, v = (t.to(dev) for t in make_inputs(w))
-        o = torch.empty_like(q)
+        o = torch.empty(q.shape, dtype=torch.float32 if w.o_dtype == "f32" else torch.bfloat16,
+                        device=dev)
         lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=dev)
-        fn = lambda: fa.fa_fwd(q, k, v, o, lse, w.causal, w.scale)  # noqa: E731
+        fn = lambda: fa.fa_fwd_ex(q, k, v, o, lse, w.causal, w.scale)  # noqa: E731
         label = w.name
     for _ in range(args.warmup + args.steps):
         fn()
@@ -207,9 +322,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--cpu-seconds", type=float, default=25.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true")
+    ap.add_argument("--settle-seconds", type=float, default=2.0,
+                    help="back-to-back steps after the warm-up while the clocks are sampled")
     ap.add_argument("--profile-kernel",
                     choices=["prefill", "decode", "paged", "paged_ragged", "prefill_d256",
-                             "decode_d256", "prefill_fp8", "bwd", "copy"],
+                             "decode_d256", "prefill_fp8", "bwd", "single_head", "causal_small",
+                             "gqa_long", "copy"],
                     help="run only this call (warmup + steps) for counter collection; "
                          "'copy' is a plain 1 GiB device-to-device copy that calibrates "
                          "the HBM byte counters")
@@ -262,6 +381,15 @@ def main():
         torch.bfloat16).to(dev)
     dqp, dkp, dvp = torch.empty_like(qp), torch.empty_like(kp), torch.empty_like(vp)
 
+    suite = {}
+    for key in (SINGLE, SMALL, GQA):
+        w = WORKLOADS[key]
+        q, k, v = (t.to(dev) for t in make_inputs(w))
+        o = torch.empty(q.shape, dtype=torch.float32 if w.o_dtype == "f32" else torch.bfloat16,
+                        device=dev)
+        suite[key] = (w, q, k, v, o,
+                      torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=dev))
+
     stream = torch.cuda.current_stream()
 
     def prefill():
@@ -284,10 +412,16 @@ def main():
     def bwd_call():
         fa.fa_bwd(qp, kp, vp, op, dop, lp, dqp, dkp, dvp, wp.causal, wp.scale, stream=stream)
 
+    def suite_call(key):
+        w, q, k, v, o, lse = suite[key]
+        fa.fa_fwd_ex(q, k, v, o, lse, w.causal, w.scale, stream=stream)
+
+    calls = (prefill, decode, lambda: paged_call(PAGED), lambda: paged_call(PAGED_RAGGED),
+             lambda: d256_call(PREFILL_D256), lambda: d256_call(DECODE_D256), fp8_call,
+             bwd_call, lambda: suite_call(SINGLE), lambda: suite_call(SMALL),
+             lambda: suite_call(GQA))
+
     def step(evs=None):
-        calls = (prefill, decode, lambda: paged_call(PAGED), lambda: paged_call(PAGED_RAGGED),
-                 lambda: d256_call(PREFILL_D256), lambda: d256_call(DECODE_D256), fp8_call,
-                 bwd_call)
         for i, call in enumerate(calls):
             if evs:
                 evs[i].record(stream)
@@ -295,12 +429,27 @@ def main():
         if evs:
             evs[len(calls)].record(stream)
 
+    log("inputs resident; warm-up")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    log(f"{args.warmup} warm-up steps done")
 
+    def run_for(seconds):
+        t0, n = time.perf_counter(), 0
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(10):
+                step()
+            torch.cuda.synchronize()
+            n += 10
+        return round((time.perf_counter() - t0) * 1e3 / max(n, 1), 4)
+
+    clocks = sustained_clocks(run_for, args.settle_seconds) if args.settle_seconds > 0 else None
+
+    log("clocks sampled; timed steps")
     K = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(9)] for _ in range(K)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+           for _ in range(K)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
@@ -369,6 +518,22 @@ def main():
                 "roofline": roofline(tf, PEAK_FP8_TFLOPS, "TFLOP/s", "mfma",
                                      measured_traffic("prefill_fp8"))}
 
+    def suite_entry(key, i):
+        w = suite[key][0]
+        ms = sorted(e[i].elapsed_time(e[i + 1]) for e in evs)
+        avg = sum(ms) / K
+        tf = w.flops() / (avg * 1e-3) / 1e12
+        return {"workload": key, "value": round(tf, 3), "unit": "TFLOP/s",
+                "config": {"B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Sq": w.Sq, "Sk": w.Sk,
+                           "D": w.D, "causal": w.causal, "o_dtype": w.o_dtype,
+                           "algorithmic_flops": w.flops(),
+                           "plan": fa.fa_plan(w.B, w.Hq, w.Hkv, w.Sq, w.Sk, w.D, w.causal, 0)},
+                "ms": {"avg": round(avg, 4), "median": round(ms[K // 2], 4),
+                       "min": round(ms[0], 4)},
+                "roofline": roofline(tf, PEAK_BF16_TFLOPS, "TFLOP/s", "mfma",
+                                     measured_traffic({SINGLE: "single_head", SMALL: "causal_small",
+                                                       GQA: "gqa_long"}[key]))}
+
     def bwd_entry(i):
         ms = sorted(e[i].elapsed_time(e[i + 1]) for e in evs)
         avg = sum(ms) / K
@@ -412,7 +577,7 @@ def main():
                          "8192 keys each, then lengths drawn from [1, 16384]) + "
                          f"{PREFILL_D256} and {DECODE_D256} (head dim 256) + "
                          f"{PREFILL_FP8} (the causal prefill on FP8 E4M3 inputs) + "
-                         f"the backward of {PREFILL}"),
+                         f"the backward of {PREFILL} + {SINGLE}, {SMALL} and {GQA}"),
             "prefill": {"B": wp.B, "Hq": wp.Hq, "Hkv": wp.Hkv, "Sq": wp.Sq, "Sk": wp.Sk,
                         "D": wp.D, "causal": wp.causal, "algorithmic_flops": flops,
                         "plan": plan_p},
@@ -437,11 +602,37 @@ def main():
         "d256_decode": d256_entry(DECODE_D256, 5),
         "fp8_prefill": fp8_entry(6),
         "backward": bwd_entry(7),
+        "single_head": suite_entry(SINGLE, 8),
+        "causal_small": suite_entry(SMALL, 9),
+        "gqa_long": suite_entry(GQA, 10),
         "roofline": roofline(tflops, PEAK_BF16_TFLOPS, "TFLOP/s", "mfma",
                              measured_traffic("prefill")),
         "cpu_baseline": None,
+        "conditions": None,
+        "ceilings": None,
+        "host": host_facts(),
     }
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            rocm = f.read().strip()
+    except OSError:
+        rocm = None
+    power = _smi(["--showmaxpower"])
+    out["conditions"] = {
+        "gcn_arch": getattr(props, "gcnArchName", None), "rocm": rocm,
+        "torch": torch.__version__, "hip": torch.version.hip,
+        "power_cap": _pick(power, ["power"]) or None,
+        "clocks_while_stepping": clocks,
+    }
+    if not args.no_ceilings:
+        log("timed steps done; ceilings")
+        from attention_fwd_02_amd import ceilings
+        c = ceilings.measure_all(torch, dev)
+        c["prefill_frac_of_mfma_loop"] = round(tflops / c["mfma_bf16_TFLOPs"], 4)
+        c["decode_frac_of_read_loop"] = round(gbps / c["hbm_read_GBps"], 4)
+        out["ceilings"] = c
     if not args.no_cpu_baseline:
+        log("cpu baseline (the oracle on a sample of the prefill's rows)")
         out["cpu_baseline"] = cpu_baseline_leg(wp, qp_h, kp_h, vp_h, op, lp, args.cpu_seconds)
     print(json.dumps(out), flush=True)
     return 0

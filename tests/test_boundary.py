@@ -20,8 +20,8 @@ def b():
     return _binding
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
 
@@ -37,6 +37,20 @@ def test_library_exports_every_declared_symbol(b):
     for name in declared_functions():
         assert name in exported, f"{name} declared in fa.h but not exported"
         assert hasattr(b.lib, name)
+
+
+def test_ceilings_library_exports_its_header():
+    """The measuring loops' library (libfa_ceilings.so) loads and exports
+    every function include/fa_ceilings.h declares."""
+    from attention_fwd_02_amd import ceilings
+    names = declared_functions(os.path.join(ROOT, "include", "fa_ceilings.h"))
+    assert names == sorted(ceilings.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", ceilings.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s(\w+)", out))
+    lib = ceilings.load()
+    for name in names:
+        assert name in exported and hasattr(lib, name)
 
 
 def test_version(b):
