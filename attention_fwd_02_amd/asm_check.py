@@ -147,6 +147,46 @@ def scan(asm: str, result_wait: int = 18, operand_wait: int = 2) -> list:
     return findings
 
 
+def scan_inline_dot(asm: str, result_wait: int = 3) -> list:
+    """Findings for every inline-asm dot-product instruction (``v_dot*``).
+
+    On CDNA3/CDNA4 a VALU dot instruction's result is not interlocked: a
+    different VALU instruction (or a same-opcode dot reading it as an A/B
+    operand) must wait 3 wait states before reading the VGPR a dot wrote;
+    only the same dot opcode taking it as its accumulator may follow at
+    once.  The compiler inserts those wait states for dots it emits itself,
+    but not for one written as inline assembly, which it cannot see into.
+    The kernels write no dot instruction today (this LLVM cannot select the
+    gfx950 v_dot2c_f32_bf16 intrinsic, so one could only come as inline asm);
+    this keeps one from coming back without its wait states.  A branch within
+    the window is reported too.
+    """
+    ins = _instructions(asm)
+    findings = []
+    for k, (no, text, in_asm, _) in enumerate(ins):
+        if not (in_asm and text.startswith("v_dot")):
+            continue
+        op = text.split()[0]
+        dst = _operands(text)[0]
+        ws, j = 0, k + 1
+        while j < len(ins) and ws < result_wait:
+            no2, t2, _, cf = ins[j]
+            if cf:
+                findings.append(f"line {no}: {text}: control flow {ws} wait states later "
+                                f"(line {no2}: {t2})")
+                break
+            ops2 = _operands(t2)
+            reads = set().union(*ops2[1:]) if len(ops2) > 1 else set()
+            chained = t2.split()[0] == op and ops2[0] == dst and not (reads & dst)
+            if not chained and (reads | (ops2[0] if ops2 else set())) & dst:
+                findings.append(f"line {no}: {text}: its result is accessed {ws} wait "
+                                f"states later (line {no2}: {t2})")
+                break
+            ws += _wait_states(t2)
+            j += 1
+    return findings
+
+
 _COPIES = ("v_mov_b32", "v_mov_b64", "v_accvgpr_write_b32", "v_accvgpr_read_b32",
            "v_accvgpr_mov_b32")
 

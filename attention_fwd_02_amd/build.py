@@ -55,6 +55,10 @@ def check_device_code() -> str:
     if found:
         raise RuntimeError("inline-asm MFMA hazards in the generated code:\n  "
                            + "\n  ".join(found[:20]))
+    found = asm_check.scan_inline_dot(asm)
+    if found:
+        raise RuntimeError("inline-asm dot results read without their wait states:\n  "
+                           + "\n  ".join(found[:20]))
     found = asm_check.scan_divergent_copies(asm)
     if found:
         raise RuntimeError("register copies at the end of divergent regions:\n  "

@@ -114,3 +114,35 @@ def test_kernels_have_no_inline_mfma_hazards():
     assert n > 0, "no inline-asm MFMA found: the scan would be vacuous"
     assert asm_check.scan(asm) == []
     assert asm_check.scan_divergent_copies(asm) == []
+    assert asm_check.scan_inline_dot(asm) == []
+
+
+DOT = "v_dot2c_f32_bf16 v10, v2, v3"
+
+
+def test_inline_dot_read_by_another_valu_is_found():
+    # the row-sum pattern: a dot accumulates, a lane swap reads the sum next
+    asm = listing(DOT, "v_permlane32_swap_b32 v10, v11", asm_idx=(0,))
+    found = asm_check.scan_inline_dot(asm)
+    assert len(found) == 1 and "accessed 0 wait states later" in found[0]
+    asm = listing(DOT, "v_exp_f32_e32 v8, v9", "v_add_f32_e32 v12, v10, v12", asm_idx=(0,))
+    assert "accessed 1 wait states later" in asm_check.scan_inline_dot(asm)[0]
+
+
+def test_inline_dot_chain_and_waited_read_pass():
+    # the same dot accumulating into the same register follows at once; a
+    # different VALU reads after 3 wait states
+    asm = listing(DOT, "v_dot2c_f32_bf16 v10, v4, v3", "s_nop 2",
+                  "v_add_f32_e32 v12, v10, v12", asm_idx=(0, 1, 2))
+    assert asm_check.scan_inline_dot(asm) == []
+
+
+def test_inline_dot_result_as_a_b_operand_is_found():
+    asm = listing(DOT, "v_dot2c_f32_bf16 v11, v10, v3", asm_idx=(0, 1))
+    assert asm_check.scan_inline_dot(asm)
+
+
+def test_inline_dot_overwritten_or_branch_is_found():
+    assert asm_check.scan_inline_dot(listing(DOT, "v_mov_b32_e32 v10, 0", asm_idx=(0,)))
+    assert "control flow" in asm_check.scan_inline_dot(
+        listing(DOT, "s_cbranch_execz .LBB0_2", asm_idx=(0,)))[0]
