@@ -143,6 +143,10 @@ struct Plan {
     int prefill_pp = 0;  // ring depth of the ping-pong kernel, 0 = not used
     int head_major = 0;
     size_t ws_bytes = 0;
+    size_t part_rows = 0;   // split partial rows in the workspace
+    // paged decode with length-balanced ranges (see make_paged_plan)
+    int balanced = 0;
+    int slots = 0, range_cap = 0, len_min = 0, len_max = 0;
 };
 
 size_t split_ws_bytes(int B, int Hq, int Sq, int D, int ns)
@@ -193,6 +197,7 @@ fa_status make_plan(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal, i
         pl.items = B * Hkv * ns;
         pl.grid = pl.items;
         pl.ws_bytes = split_ws_bytes(B, Hq, Sq, D, ns);
+        pl.part_rows = ns > 1 ? (size_t)ns * B * Hq * Sq : 0;
     } else {
         pl.path = 0;
         // tile configuration: 8 waves x 32 rows x 64 keys (two waves per
@@ -271,7 +276,7 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 // `need`) or at the device's library-owned buffer, grown on demand.  `lk`
 // (on g_mu) stays locked while the launch uses the library buffer.
 fa_status attach_workspace(DeviceInfo *info, void *workspace, size_t workspace_bytes, size_t need,
-                           int num_splits, std::unique_lock<std::mutex> &lk, fa::Launch *L)
+                           size_t part_rows, std::unique_lock<std::mutex> &lk, fa::Launch *L)
 {
     void *ws = workspace;
     if (ws) {
@@ -299,9 +304,8 @@ fa_status attach_workspace(DeviceInfo *info, void *workspace, size_t workspace_b
         }
         ws = info->ws;
     }
-    const size_t n_rows = (size_t)L->B * L->Hq * L->Sq;
     L->part_o = static_cast<float *>(ws);
-    L->part_lse = L->part_o + (size_t)num_splits * n_rows * L->D;
+    L->part_lse = L->part_o + part_rows * L->D;
     return FA_OK;
 }
 
@@ -328,10 +332,22 @@ fa_status check_paged(int B, int Hq, int Hkv, int Sq, int D, int num_pages, int 
     return FA_OK;
 }
 
-// Splits per sequence: each sequence's keys are cut into num_splits equal
-// ranges (multiples of the tile).  The lengths live on the device, so the
-// automatic count is sized for the table's capacity like the contiguous
-// decode, then raised until one range touches at most
+// Two ways to cut the keys of the paged decode.
+//
+// Length-balanced ranges (the automatic choice, num_splits = 0): every
+// sequence's keys are cut into ranges of one common length L that the
+// kernels derive on the device from the lengths: the shortest (at least 4
+// tiles) for which the (range, KV head) items fit the CUs' resident slots in
+// one round, at most len_max, the longest range whose pages fit the kernel's
+// page-id registers.  A long sequence gets more ranges than a short one.  The
+// host only bounds the count: range_cap = max(slots / Hkv, B * ceil(capacity /
+// len_max)) ranges (grid and workspace) always suffice.  The merge always runs.
+//
+// Equal splits (num_splits >= 1, or FA_NUM_SPLITS, or FA_PAGED_BALANCED=0,
+// or more than kPagedBalancedMaxSeqs sequences):
+// each sequence's keys are cut into num_splits equal ranges (multiples of
+// the tile).  The automatic count is sized for the table's capacity like the
+// contiguous decode, then raised until one range touches at most
 // kPagedMaxPagesPerSplit pages.
 fa_status make_paged_plan(int B, int Hkv, int page_size, int max_pages, int D, int num_splits,
                           int cus, int Hq, int Sq, Plan *out)
@@ -340,13 +356,46 @@ fa_status make_paged_plan(int B, int Hkv, int page_size, int max_pages, int D, i
     if (cus <= 0) cus = 256;
     const int64_t cap = (int64_t)max_pages * page_size;
     const int max_splits = (int)((cap + fa::kDecodeBN - 1) / fa::kDecodeBN);
+    int per_cu = std::min(8, (160 * 1024) / fa::decode_lds_bytes(D));
+    per_cu = std::max(1, env_int("FA_DECODE_WAVES_PER_CU", per_cu));
     int ns = num_splits;
+    // (range counts are 32-bit on the device: ranges are at least 4 tiles)
+    const bool count_fits =
+        (int64_t)B * ((cap + 4 * fa::kDecodeBN - 1) / (4 * fa::kDecodeBN)) < (int64_t(1) << 31);
+    if (ns == 0 && env_int("FA_NUM_SPLITS", 0) <= 0 && env_int("FA_PAGED_BALANCED", 1) != 0 &&
+        B <= fa::kPagedBalancedMaxSeqs && count_fits) {
+        const int64_t slots = (int64_t)cus * per_cu;
+        const int64_t len_min = 4 * fa::kDecodeBN;
+        const int64_t len_max =
+            std::max<int64_t>(len_min, (int64_t)(fa::kPagedMaxPagesPerSplit - 1) * page_size /
+                                           fa::kDecodeBN * fa::kDecodeBN);
+        const int64_t range_cap = std::max<int64_t>(std::max<int64_t>(1, slots / Hkv),
+                                                    (int64_t)B * ((cap + len_max - 1) / len_max));
+        if (range_cap * Hkv >= (int64_t(1) << 31) || slots >= (int64_t(1) << 31))
+            return fail(FA_ERR_UNSUPPORTED, "too many work items");
+        Plan pl;
+        pl.path = 1;
+        pl.num_splits = 0;   // per sequence, on the device
+        pl.split_len = 0;
+        pl.block_m = fa::kDecodeRows;
+        pl.block_n = fa::kDecodeBN;
+        pl.items = (int)(range_cap * Hkv);
+        pl.grid = pl.items;
+        pl.part_rows = (size_t)range_cap * Hq * Sq;
+        // partials, then each sequence's (first range, range count)
+        pl.ws_bytes = pl.part_rows * (size_t)(D + 1) * sizeof(float) + (size_t)2 * B * sizeof(int);
+        pl.balanced = 1;
+        pl.slots = (int)slots;
+        pl.range_cap = (int)range_cap;
+        pl.len_min = (int)len_min;
+        pl.len_max = (int)len_max;
+        *out = pl;
+        return FA_OK;
+    }
     if (ns == 0) {
         ns = env_int("FA_NUM_SPLITS", 0);
         if (ns <= 0) {
             const int64_t bg = (int64_t)B * Hkv;
-            int per_cu = std::min(8, (160 * 1024) / fa::decode_lds_bytes(D));
-            per_cu = std::max(1, env_int("FA_DECODE_WAVES_PER_CU", per_cu));
             const int64_t want = ((int64_t)cus * per_cu + bg - 1) / bg;
             const int64_t by_len = std::max<int64_t>(1, cap / (4 * fa::kDecodeBN));
             ns = (int)std::max<int64_t>(1, std::min<int64_t>(want, by_len));
@@ -372,6 +421,7 @@ fa_status make_paged_plan(int B, int Hkv, int page_size, int max_pages, int D, i
     pl.items = (int)items;
     pl.grid = pl.items;
     pl.ws_bytes = split_ws_bytes(B, Hq, Sq, D, ns);
+    pl.part_rows = ns > 1 ? (size_t)ns * B * Hq * Sq : 0;
     *out = pl;
     return FA_OK;
 }
@@ -454,15 +504,14 @@ fa_status fwd_impl(const void *q, const void *k, const void *v, void *o, float *
             e = fa::static_scratch_ptr(dev, &ws);
             if (e != hipSuccess)
                 return fail(FA_ERR_HIP, std::string("hipGetSymbolAddress: ") + hipGetErrorString(e));
-            const size_t n_rows = (size_t)B * Hq * Sq;
             L.part_o = static_cast<float *>(ws);
-            L.part_lse = L.part_o + (size_t)pl.num_splits * n_rows * D;
+            L.part_lse = L.part_o + pl.part_rows * D;
         }
         e = fa::launch_decode(L);
     } else {
         std::unique_lock<std::mutex> lk(g_mu, std::defer_lock);
         if (pl.ws_bytes > 0) {
-            st = attach_workspace(info, workspace, workspace_bytes, pl.ws_bytes, pl.num_splits,
+            st = attach_workspace(info, workspace, workspace_bytes, pl.ws_bytes, pl.part_rows,
                                   lk, &L);
             if (st != FA_OK) return st;
         }
@@ -590,6 +639,11 @@ fa_status fa_fwd_paged(const void *q, const void *k_cache, const void *v_cache,
     P.num_pages = num_pages;
     P.page_size = page_size;
     P.max_pages = max_pages;
+    P.balanced = pl.balanced;
+    P.slots = pl.slots;
+    P.range_cap = pl.range_cap;
+    P.len_min = pl.len_min;
+    P.len_max = pl.len_max;
 
     if (log_enabled())
         fprintf(stderr,
@@ -600,7 +654,7 @@ fa_status fa_fwd_paged(const void *q, const void *k_cache, const void *v_cache,
 
     std::unique_lock<std::mutex> lk(g_mu, std::defer_lock);
     if (pl.ws_bytes > 0) {
-        st = attach_workspace(info, workspace, workspace_bytes, pl.ws_bytes, pl.num_splits, lk, &L);
+        st = attach_workspace(info, workspace, workspace_bytes, pl.ws_bytes, pl.part_rows, lk, &L);
         if (st != FA_OK) return st;
     }
     hipError_t e = fa::launch_decode_paged(L, P);

@@ -3260,7 +3260,160 @@ struct PagedParams {
     const int *table;        // [B][max_pages]
     const int *seq_lens;     // [B]
     int max_pages, num_pages, lg_page;
+    // length-balanced ranges (balanced != 0): see paged_range_tiles
+    int balanced;
+    int slots;               // resident (range, KV head) waves the CUs hold at once
+    int range_cap;           // ranges the grid and the workspace provide for
+    int len_min, len_max;    // bounds of the common range length (multiples of kDecodeBN)
+    int *range_info;         // [B][2]: each sequence's first range and range count
 };
+
+// ---- length-balanced key ranges of the paged decode ---------------------------
+// Every sequence's keys are cut into ranges of one common length L: the
+// shortest multiple of the tile in [len_min, len_max] for which the (range,
+// KV head) items fit the CUs' resident slots in one round.  A long sequence
+// then gets more ranges than a short one, no item streams more than L keys,
+// and no slot waits for a second round (waves and tail: "理解 H100：从硬件数据
+// 路径到 Nsight Compute 瓶颈分析", section 2).  When even len_max needs more
+// items than slots, L = len_max.  The lengths live on the device, so every
+// wave derives L (a binary search over the range count, which falls as L
+// grows), and the range its item stands for, from seq_lens itself: no
+// planning pass and no host synchronisation.  Ranges are numbered sequence by
+// sequence: sequence b owns ranges [first_b, first_b + n_b), n_b = ceil(Sk_b /
+// L).  The host sizes range_cap >= max(slots / Hkv, B ceil(capacity /
+// len_max)), which the count never exceeds.
+__device__ __forceinline__ int paged_seq_len(const PagedParams &pp, int b)
+{
+    return min(max(pp.seq_lens[b], 0), pp.max_pages << pp.lg_page);
+}
+
+// Wave-wide integer sum and inclusive prefix sum on DPP moves within rows of
+// 16 lanes and four v_readlane of the row totals: a few dozen cycles, where
+// the same through the LDS crossbar (ds_bpermute) costs a round trip per step.
+// The sum comes back as a scalar (uniform).
+#define FA_DPP(x, ctrl) __builtin_amdgcn_update_dpp(0, (x), (ctrl), 0xf, 0xf, true)
+
+__device__ __forceinline__ int wave_sum_i32(int x)
+{
+    x += FA_DPP(x, 0xB1);    // quad_perm [1,0,3,2]
+    x += FA_DPP(x, 0x4E);    // quad_perm [2,3,0,1]: every lane holds its quad's sum
+    x += FA_DPP(x, 0x124);   // row_ror:4
+    x += FA_DPP(x, 0x128);   // row_ror:8: every lane holds its row's sum
+    return __builtin_amdgcn_readlane(x, 0) + __builtin_amdgcn_readlane(x, 16) +
+           __builtin_amdgcn_readlane(x, 32) + __builtin_amdgcn_readlane(x, 48);
+}
+
+__device__ __forceinline__ int wave_incl_scan(int x, int lane)
+{
+    x += FA_DPP(x, 0x111);   // row_shr:1 (lanes shifted in from outside the row read 0)
+    x += FA_DPP(x, 0x112);   // row_shr:2
+    x += FA_DPP(x, 0x114);   // row_shr:4
+    x += FA_DPP(x, 0x118);   // row_shr:8: inclusive prefix within each row of 16
+    const int r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31),
+              r2 = __builtin_amdgcn_readlane(x, 47);
+    const int row = lane >> 4;
+    return x + (row > 0 ? r0 : 0) + (row > 1 ? r1 : 0) + (row > 2 ? r2 : 0);
+}
+#undef FA_DPP
+
+// The tiles (kDecodeBN keys) of sequences 64 r + lane, r < 4, 0 past B: the
+// balanced cut serves at most kPagedBalancedMaxSeqs = 256 sequences, whose
+// lengths each wave then keeps in four registers (one memory round trip,
+// however many times the search below counts ranges).
+static_assert(kPagedBalancedMaxSeqs == 4 * 64, "four registers of 64 lanes");
+struct PagedTiles {
+    int t[4];
+    int nreg;   // registers in use: ceil(B / 64), uniform
+};
+
+__device__ __forceinline__ PagedTiles paged_tiles(const PagedParams &pp, int B, int lane)
+{
+    PagedTiles pt;
+    pt.nreg = (B + 63) / 64;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        // a clamped load and a select: no divergent region
+        const int b = 64 * r + lane;
+        const int v = r < pt.nreg ? paged_seq_len(pp, min(b, B - 1)) : 0;
+        pt.t[r] = b < B ? (v + kDecodeBN - 1) / kDecodeBN : 0;
+    }
+    return pt;
+}
+
+// Sequence b's tiles (b uniform), as a scalar.
+__device__ __forceinline__ int paged_tiles_of(const PagedTiles &pt, int b)
+{
+    const int r = b >> 6;
+    const int v = r == 0 ? pt.t[0] : r == 1 ? pt.t[1] : r == 2 ? pt.t[2] : pt.t[3];
+    return __builtin_amdgcn_readlane(v, b & 63);
+}
+
+// The number of ranges of lt tiles each (all 64 lanes of the wave call this).
+__device__ __forceinline__ int paged_range_count(const PagedTiles &pt, int lt)
+{
+    int n = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+        if (r < pt.nreg) n += (pt.t[r] + lt - 1) / lt;   // a uniform branch
+    return wave_sum_i32(n);
+}
+
+// The common range length, in tiles (all 64 lanes of the wave call this).
+__device__ __forceinline__ int paged_range_tiles(const PagedParams &pp, const PagedTiles &pt,
+                                                 int Hkv)
+{
+    const int target = max(1, pp.slots / Hkv);
+    int lo = pp.len_min / kDecodeBN, hi = pp.len_max / kDecodeBN;
+    if (paged_range_count(pt, hi) > target) return hi;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (paged_range_count(pt, mid) <= target)
+            hi = mid;
+        else
+            lo = mid + 1;
+    }
+    return lo;
+}
+
+// Range c's sequence b and that sequence's first range, or b = -1 when c is
+// past the last range.
+__device__ __forceinline__ void paged_find_range(const PagedTiles &pt, int lt, int c, int lane,
+                                                 int &b, int &first)
+{
+    b = -1;
+    first = 0;
+    int base = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        if (r >= pt.nreg) break;
+        const int n = (pt.t[r] + lt - 1) / lt;
+        const int incl = wave_incl_scan(n, lane);
+        const unsigned long long hit = __ballot(base + incl > c);
+        if (hit) {
+            const int ln = __ffsll((long long)hit) - 1;
+            b = 64 * r + ln;
+            first = base + __builtin_amdgcn_readlane(incl - n, ln);
+            return;
+        }
+        base += __builtin_amdgcn_readlane(incl, 63);
+    }
+}
+
+// Sequence b's first range and range count.
+__device__ __forceinline__ void paged_ranges_of(const PagedTiles &pt, int b, int lt, int lane,
+                                                int &first, int &count)
+{
+    int before = 0, mine = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        if (r >= pt.nreg) break;
+        const int n = (pt.t[r] + lt - 1) / lt;
+        before += 64 * r + lane < b ? n : 0;
+        mine += 64 * r + lane == b ? n : 0;
+    }
+    first = wave_sum_i32(before);
+    count = wave_sum_i32(mine);
+}
 
 template <int D, bool OUT_F32, int PPT>
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1 : 2)))
@@ -3286,21 +3439,54 @@ fa_decode_paged_kernel(const Params p, const PagedParams pp)
     off.init(lane);
 
     const int item = blockIdx.x;
-    const int s = item % p.num_splits;
-    const int bg = item / p.num_splits;
-    const int b = bg / p.Hkv;
-    const int g = bg % p.Hkv;
+    int b, g, s, k_begin, k_end;
+    if (pp.balanced) {
+        // item = (range s, KV head g); the ranges of all sequences in a row
+        // Sequence b owns items [first_b Hkv, (first_b + n_b) Hkv): its n_b
+        // ranges for each KV head in turn (KV head major, the equal splits'
+        // order).  With each KV head's items on other XCDs than in this
+        // order, the same ranges streamed 4-8 % slower.
+        const PagedTiles pt = paged_tiles(pp, p.B, lane);
+        const int lt = paged_range_tiles(pp, pt, p.Hkv);
+        if (item < p.B) {
+            // the merge's table: sequence `item`'s first range and range count
+            int f, n;
+            paged_ranges_of(pt, item, lt, lane, f, n);
+            if (lane == 0) {
+                pp.range_info[2 * item] = f;
+                pp.range_info[2 * item + 1] = n;
+            }
+        }
+        int first;
+        paged_find_range(pt, lt, item / p.Hkv, lane, b, first);
+        if (b < 0) return;                      // past the last range: the whole wave
+        const int n_b = max(1, (paged_tiles_of(pt, b) + lt - 1) / lt);
+        const int local = item - first * p.Hkv;
+        g = local / n_b;
+        s = first + local % n_b;                // the range, numbered over all sequences
+        // (first <= s by construction; the clamps keep every key index in
+        // [0, Sk_b] whatever the range table says)
+        const int sk_b = paged_seq_len(pp, b);
+        k_begin = min(max(s - first, 0) * lt * BN, sk_b);
+        k_end = min(k_begin + lt * BN, sk_b);
+    } else {
+        s = item % p.num_splits;
+        const int bg = item / p.num_splits;
+        b = bg / p.Hkv;
+        g = bg % p.Hkv;
+        const int sk_b = paged_seq_len(pp, b);
+        int len = (sk_b + p.num_splits - 1) / p.num_splits;
+        len = (len + BN - 1) / BN * BN;
+        k_begin = min(s * len, sk_b);
+        k_end = min(k_begin + len, sk_b);
+    }
 
     const int rows = p.Sq * p.group;
     const bool valid = col < rows;
     const int qi = valid ? col / p.group : 0;
     const int hq = g * p.group + (valid ? col % p.group : 0);
 
-    const int sk = min(max(pp.seq_lens[b], 0), pp.max_pages << pp.lg_page);
-    int len = (sk + p.num_splits - 1) / p.num_splits;
-    len = (len + BN - 1) / BN * BN;
-    const int k_begin = min(s * len, sk);
-    const int k_end = min(k_begin + len, sk);
+    const int sk = paged_seq_len(pp, b);
     const int n_tiles = (k_end - k_begin + BN - 1) / BN;
 
     TL ld;
@@ -3371,12 +3557,14 @@ fa_decode_paged_kernel(const Params p, const PagedParams pp)
     }
 
     const float l_norm = add_halves(l_rnd);
-    if (p.num_splits == 1) {
+    if (!pp.balanced && p.num_splits == 1) {
         finish_rows<D, OUT_F32>(o, m_ref, l_run, l_norm, p.c, half, p.o,
                                 (((long)b * p.Sq + qi) * p.Hq + hq) * D,
                                 p.lse ? p.lse + ((long)b * p.Hq + hq) * p.Sq + qi : nullptr, valid);
     } else {
-        const long prow = (((long)s * p.B + b) * p.Hq + hq) * p.Sq + qi;
+        // partial rows: [split][B][Hq][Sq], or [range][Hq][Sq] when balanced
+        const long prow = pp.balanced ? ((long)s * p.Hq + hq) * p.Sq + qi
+                                      : (((long)s * p.B + b) * p.Hq + hq) * p.Sq + qi;
         finish_rows<D, true>(o, m_ref, l_run, l_norm, p.c, half, p.part_o, prow * D,
                              p.part_lse + prow, valid);
     }
@@ -3389,17 +3577,13 @@ fa_decode_paged_kernel(const Params p, const PagedParams pp)
 //   O = sum_s w_s O_s / sum_s w_s; splits with LSE_s = -inf weigh 0, and a row
 //   whose splits are all -inf gets O = 0, LSE = -inf.
 // ---------------------------------------------------------------------------
+// Output row `row` from the partials at first, first + stride, ... (ns of them).
 template <int D, bool OUT_F32>
-__global__ void __launch_bounds__(64) fa_merge_kernel(const Params p)
+__device__ __forceinline__ void merge_row(const Params &p, long row, long first, long stride,
+                                          int ns, int lane)
 {
-#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
-    const int lane = threadIdx.x;
-    const long row = blockIdx.x;                 // (b, hq, i) with i fastest
-    const long n_rows = (long)p.B * p.Hq * p.Sq;
-    const int ns = p.num_splits;
-
     float M = kNegInf;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, p.part_lse[s * n_rows + row]);
+    for (int s = 0; s < ns; ++s) M = fmaxf(M, p.part_lse[first + s * stride]);
     const float Mu = (M == kNegInf) ? 0.0f : M;
 
     constexpr int PER = D / 64;                  // head dims per lane
@@ -3408,10 +3592,10 @@ __global__ void __launch_bounds__(64) fa_merge_kernel(const Params p)
     for (int e = 0; e < PER; ++e) acc[e] = 0.0f;
     float wsum = 0.0f;
     for (int s = 0; s < ns; ++s) {
-        const float ls = p.part_lse[s * n_rows + row];
+        const float ls = p.part_lse[first + s * stride];
         const float w = (ls == kNegInf) ? 0.0f : __expf(ls - Mu);
         wsum += w;
-        const float *po = p.part_o + (s * n_rows + row) * D + lane * PER;
+        const float *po = p.part_o + (first + s * stride) * D + lane * PER;
 #pragma unroll
         for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, po[e], acc[e]);
     }
@@ -3438,6 +3622,37 @@ __global__ void __launch_bounds__(64) fa_merge_kernel(const Params p)
     }
     if (p.lse && lane == 0)
         p.lse[row] = wsum > 0.0f ? Mu + __logf(wsum) : kNegInf;
+}
+
+template <int D, bool OUT_F32>
+__global__ void __launch_bounds__(64) fa_merge_kernel(const Params p)
+{
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
+    const long row = blockIdx.x;                 // (b, hq, i) with i fastest
+    const long n_rows = (long)p.B * p.Hq * p.Sq;
+    merge_row<D, OUT_F32>(p, row, row, n_rows, p.num_splits, threadIdx.x);
+#endif
+}
+
+// The merge of the length-balanced paged decode: row (b, hq, i) combines the
+// partials of sequence b's ranges, [range][Hq][Sq], which the split kernel
+// listed in range_info; a sequence without keys has no range and gets O = 0,
+// LSE = -inf.
+template <int D, bool OUT_F32>
+__global__ void __launch_bounds__(64) fa_merge_paged_kernel(const Params p, const PagedParams pp)
+{
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
+    const int lane = threadIdx.x;
+    const long row = blockIdx.x;
+    const int i = (int)(row % p.Sq);
+    const int hq = (int)((row / p.Sq) % p.Hq);
+    const int b = (int)(row / ((long)p.Sq * p.Hq));
+    // written by the split kernel's first B items; clamped to the partials
+    // the workspace holds
+    const int first = min(max(pp.range_info[2 * b], 0), pp.range_cap);
+    const int count = min(max(pp.range_info[2 * b + 1], 0), pp.range_cap - first);
+    merge_row<D, OUT_F32>(p, row, ((long)first * p.Hq + hq) * p.Sq + i, (long)p.Hq * p.Sq, count,
+                          lane);
 #endif
 }
 
@@ -3728,14 +3943,30 @@ hipError_t launch_decode_paged(const Launch &L, const PagedLaunch &P)
     pp.num_pages = P.num_pages;
     pp.lg_page = 0;
     while ((1 << pp.lg_page) < P.page_size) ++pp.lg_page;
-    dim3 g(L.B * L.Hkv * L.num_splits);
+    pp.balanced = P.balanced;
+    pp.slots = P.slots;
+    pp.range_cap = P.range_cap;
+    pp.len_min = P.len_min;
+    pp.len_max = P.len_max;
+    pp.range_info = P.balanced ? reinterpret_cast<int *>(L.part_lse + (size_t)P.range_cap * L.Hq * L.Sq)
+                               : nullptr;
+    dim3 g(P.balanced ? L.Hkv * P.range_cap : L.B * L.Hkv * L.num_splits);
     // pages per 32-key tile: 1, or 2 for 16-key pages
     if (P.page_size >= kDecodeBN)
         launch_paged_cfg<1>(L, p, pp, g);
     else
         launch_paged_cfg<kDecodeBN / 16>(L, p, pp, g);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || L.num_splits == 1) return e;
+    if (e != hipSuccess) return e;
+    if (P.balanced) {
+        dim3 gm((unsigned)((long)L.B * L.Hq * L.Sq)), blk(64);
+        with_head_dim(L, [&](auto d, auto of) {
+            hipLaunchKernelGGL((fa_merge_paged_kernel<decltype(d)::value, decltype(of)::value>),
+                               gm, blk, 0, L.stream, p, pp);
+        });
+        return hipGetLastError();
+    }
+    if (L.num_splits == 1) return e;
     return launch_merge(L, p);
 }
 

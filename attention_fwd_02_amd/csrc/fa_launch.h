@@ -41,6 +41,9 @@ inline int decode_lds_bytes(int D)
 // VGPRs (64 pages each), which bounds the pages one split may touch.
 constexpr int kPagedIdRegs = 4;
 constexpr int kPagedMaxPagesPerSplit = 64 * kPagedIdRegs;
+// The length-balanced paged cut keeps the sequences' lengths in four
+// registers per wave: at most this many sequences (beyond: equal splits).
+constexpr int kPagedBalancedMaxSeqs = 256;
 
 struct Launch {
     const void *q, *k, *v;
@@ -78,6 +81,13 @@ struct PagedLaunch {
     const int *table;     // [B][max_pages] device
     const int *seq_lens;  // [B] device
     int num_pages, page_size, max_pages;
+    // length-balanced ranges: one common range length, chosen on the device
+    // within [len_min, len_max] so that the (range, KV head) items about fill
+    // `slots`; grid and workspace provide for range_cap ranges.  The
+    // workspace holds the partials, then [B][2] ints (each sequence's first
+    // range and range count, for the merge)
+    int balanced;
+    int slots, range_cap, len_min, len_max;
 };
 hipError_t launch_decode_paged(const Launch &L, const PagedLaunch &P);
 

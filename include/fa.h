@@ -180,9 +180,17 @@ fa_status fa_plan(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal, int
  * (Sk_b = 0, say) gets O = 0 and LSE = -inf.
  *
  * page_size: a power of two >= 16.  Sq * Hq / Hkv <= 32 (the split-key
- * decode's tile), else FA_ERR_UNSUPPORTED.  num_splits: 0 = automatic, else
- * each sequence's keys are cut into num_splits equal ranges (multiples of 32
- * keys); it is raised if needed so that one range spans at most 256 pages.
+ * decode's tile), else FA_ERR_UNSUPPORTED.
+ * num_splits: 0 = automatic.  For B <= 256 the automatic cut is length
+ * balanced: every sequence's keys are cut into ranges of one common length,
+ * chosen on the device from seq_lens (the shortest multiple of 32 keys, at
+ * least 128, for which the (range, KV head) work items fit the GPU's resident
+ * decode waves in one round), so that a long sequence gets more ranges than a
+ * short one.  Otherwise (num_splits >= 1, or B > 256) each sequence's keys
+ * are cut into num_splits equal ranges (multiples of 32 keys); it is raised if
+ * needed so that one range spans at most 256 pages.  The result depends on
+ * the cut only through rounding (the partial results are merged by their
+ * log-sum-exp).
  * workspace / workspace_bytes: as for fa_fwd_ex, sized by fa_plan_paged's
  * workspace_bytes.  Only row b of the block table is read (entries within
  * [0, max_pages)), and only the entries of pages below Sk_b are used.
@@ -198,7 +206,8 @@ fa_status fa_fwd_paged(const void *q, const void *k_cache, const void *v_cache,
 
 /*
  * fa_plan_paged -- the launch fa_fwd_paged would make (path 2): splits per
- * sequence, grid, workspace bytes.  Host arithmetic, like fa_plan.
+ * sequence (0 for the length-balanced cut, decided on the device), grid,
+ * workspace bytes.  Host arithmetic, like fa_plan.
  */
 fa_status fa_plan_paged(int B, int Hq, int Hkv, int Sq, int D, int num_pages, int page_size,
                         int max_pages, int num_splits, fa_plan_info *out);

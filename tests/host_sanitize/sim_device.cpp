@@ -190,6 +190,23 @@ hipError_t launch_decode(const Launch &L)
 
 hipError_t launch_decode_paged(const Launch &L, const PagedLaunch &P)
 {
+    if (P.balanced) {
+        // length-balanced ranges: range_cap of them, each with its KV heads
+        if (L.grid != L.Hkv * P.range_cap || P.len_min < kDecodeBN || P.len_max < P.len_min ||
+            P.len_min % kDecodeBN || P.len_max % kDecodeBN || P.slots < 1)
+            die("balanced paged plan");
+        if (P.range_cap < 1 || (long)P.range_cap * L.Hkv >= (1L << 31))
+            die("range capacity");
+        const size_t prow = (size_t)P.range_cap * L.Hq * L.Sq;
+        if (!L.part_o || L.part_lse != L.part_o + prow * L.D) die("balanced partials");
+        read_bytes(P.table, (size_t)L.B * P.max_pages * sizeof(int));
+        read_bytes(P.seq_lens, (size_t)L.B * sizeof(int));
+        write_bytes(L.part_o, prow * L.D * sizeof(float));
+        write_bytes(L.part_lse, prow * sizeof(float));
+        write_bytes(L.part_lse + prow, (size_t)2 * L.B * sizeof(int));   // range table
+        write_o_lse(L);
+        return hipSuccess;
+    }
     if (L.num_splits < 1 || L.grid != L.B * L.Hkv * L.num_splits) die("paged grid");
     read_bytes(P.table, (size_t)L.B * P.max_pages * sizeof(int));
     read_bytes(P.seq_lens, (size_t)L.B * sizeof(int));

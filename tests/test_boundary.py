@@ -190,7 +190,7 @@ def test_paged_bad_arguments_rejected_before_any_hip_call(b, kw, status):
     assert msg
 
 
-def test_head_dim_256_decode_plans(b):
+def test_head_dim_256_decode_plans(b, monkeypatch):
     # D = 256: separate K and V rings of 3 + 2 32-key tiles (80 KiB of LDS)
     # leave two single-wave workgroups per CU, so the 256 (b, g) pairs of the
     # decode workload take 2 splits (a 256-CU part filled once)
@@ -199,15 +199,18 @@ def test_head_dim_256_decode_plans(b):
     assert p["workspace_bytes"] == 2 * 32 * 32 * 257 * 4
     assert b.fa_workspace_size(32, 32, 8, 1, 8192, 256, 0) == 2 * 32 * 32 * 257 * 4
     # the paged kernel uses the same rings (at least 2 splits; here the
-    # 256-page bound per split, 512 16-key pages, asks for one more)
+    # 256-page bound per split, 512 16-key pages, asks for one more) when
+    # its keys are cut into equal splits
+    monkeypatch.setenv("FA_PAGED_BALANCED", "0")
     q = b.fa_plan_paged(32, 32, 8, 1, 256, 16384, 16, 512, 0)
     assert q["path"] == 2 and q["num_splits"] == 3
     q = b.fa_plan_paged(32, 32, 8, 1, 256, 16384, 64, 128, 0)
     assert q["num_splits"] == 2 and q["grid"] == 32 * 8 * 2
 
 
-def test_paged_plan_host_arithmetic(b):
-    # the paged decode workload: 256 (b, g) pairs x 3 splits, like the
+def test_paged_plan_host_arithmetic(b, monkeypatch):
+    monkeypatch.setenv("FA_PAGED_BALANCED", "0")
+    # equal splits: the paged decode workload: 256 (b, g) pairs x 3 splits, like the
     # contiguous decode; partials [splits][B][Hq][Sq][D+1] fp32
     p = b.fa_plan_paged(32, 32, 8, 1, 128, 16384, 16, 512, 0)
     assert p["path"] == 2 and p["num_splits"] == 3 and p["grid"] == 32 * 8 * 3
@@ -230,3 +233,58 @@ def test_workspace_size_matches_the_plan_before_any_call(b):
         B, Hq, Hkv, Sq, Sk, D, ns = shape
         plan = b.fa_plan(B, Hq, Hkv, Sq, Sk, D, 0, ns)
         assert b.fa_workspace_size(B, Hq, Hkv, Sq, Sk, D, ns) == plan["workspace_bytes"] > 0
+
+
+def range_count(lens, Hkv, slots, range_cap, len_min, len_max, cap):
+    """The length-balanced ranges for these lengths, by the rule the paged
+    kernels apply on the device, restated as a linear search: L is the
+    shortest multiple of 32 in [len_min, len_max] whose range count fits
+    slots / Hkv, else len_max.  Returns (L, count)."""
+    lens = [min(max(x, 0), cap) for x in lens]
+    count = lambda L: sum(-(-x // L) for x in lens)  # noqa: E731
+    for L in range(len_min, len_max + 1, 32):
+        if count(L) <= max(1, slots // Hkv):
+            return L, count(L)
+    return len_max, count(len_max)
+
+
+def test_balanced_paged_plan_host_arithmetic(b):
+    # automatic cut: length-balanced ranges; 768 resident slots (3 decode
+    # waves per CU x 256 CUs), ranges of at most 254 16-key pages (4064 keys)
+    # and at least 128 keys; range_cap = max(slots / Hkv, B * ceil(cap / 4064))
+    p = b.fa_plan_paged(32, 32, 8, 1, 128, 16384, 16, 512, 0)       # capacity 8192
+    assert p["path"] == 2 and p["num_splits"] == 0
+    assert p["grid"] == p["work_items"] == 96 * 8
+    assert p["workspace_bytes"] == 96 * 32 * 1 * 129 * 4 + 2 * 32 * 4
+    p = b.fa_plan_paged(32, 32, 8, 1, 128, 16384, 16, 1024, 0)      # capacity 16384
+    assert p["grid"] == 160 * 8
+    p = b.fa_plan_paged(32, 32, 8, 1, 256, 16384, 16, 512, 0)       # D = 256: 512 slots
+    assert p["grid"] == 96 * 8
+    # a forced split count keeps the equal splits, and so do more than 256
+    # sequences (the kernels keep the lengths in four registers of 64 lanes)
+    assert b.fa_plan_paged(32, 32, 8, 1, 128, 16384, 16, 512, 3)["num_splits"] == 3
+    assert b.fa_plan_paged(257, 32, 8, 1, 128, 16384, 16, 512, 0)["num_splits"] >= 1
+
+
+@pytest.mark.parametrize("B,Hkv,ps,max_pages", [(32, 8, 16, 512), (32, 8, 16, 1024), (3, 2, 16, 20),
+                                                (7, 1, 256, 64), (256, 8, 16, 4096), (1, 8, 64, 4)])
+def test_balanced_ranges_never_exceed_the_capacity(b, B, Hkv, ps, max_pages):
+    # for any lengths the range count stays within range_cap (grid and
+    # workspace), every range spans at most 256 pages, and the lengths of
+    # the bench's two paged workloads give one range per resident slot or so
+    import random
+    p = b.fa_plan_paged(B, 8 * Hkv, Hkv, 1, 128, 1 << 16, ps, max_pages, 0)
+    cap, slots = max_pages * ps, 768
+    range_cap = p["grid"] // Hkv
+    len_min, len_max = 128, max(128, (255 * ps) // 32 * 32)
+    assert (len_max + ps - 1) // ps + 1 <= 256
+    rng = random.Random(B * 131 + max_pages)
+    draws = [[cap] * B, [0] * B, [1] * B, [cap] + [0] * (B - 1), [cap - 1] * B]
+    draws += [[rng.randint(0, cap) for _ in range(B)] for _ in range(50)]
+    for lens in draws:
+        L, n = range_count(lens, Hkv, slots, range_cap, len_min, len_max, cap)
+        assert n <= range_cap, (lens[:4], L, n, range_cap)
+        assert len_min <= L <= len_max and L % 32 == 0
+    if (B, Hkv, ps, max_pages) == (32, 8, 16, 512):
+        L, n = range_count([8192] * 32, Hkv, slots, range_cap, len_min, len_max, cap)
+        assert (L, n * Hkv) == (2752, 768)          # the equal-length workload: one round
