@@ -14,9 +14,13 @@ intermittently, with no fault.
 reports, for every inline-assembly MFMA:
 
 * any compiler-emitted instruction that reads or writes the MFMA's
-  destination registers, or a branch or label, before ``result_wait`` wait
-  states have passed (an 8-pass XDL result needs about 12 on gfx950 before a
-  VALU or memory instruction may read it; 18 covers a 16-pass one);
+  destination registers, or a branch or label, before its result wait has
+  passed: an XDL MFMA of N passes needs N + 4 wait states on gfx950 before a
+  VALU or memory instruction may read or overwrite its result (the rule
+  LLVM's hazard recognizer applies to the MFMAs it emits itself); the scan
+  asks N + 5, one more, for the two inline-asm forms here, 8-pass
+  v_mfma_f32_32x32x16_bf16 (13) and 4-pass v_mfma_f32_16x16x32_bf16 (9), and
+  ``result_wait`` (18) for any other;
 * any compiler-emitted VALU instruction that writes one of the MFMA's source
   registers fewer than ``operand_wait`` wait states before it (2 are needed).
 
@@ -100,6 +104,10 @@ def _wait_states(text: str) -> int:
     return 1
 
 
+# inline-asm MFMA opcode -> wait states before its result may be accessed
+RESULT_WAIT = {"v_mfma_f32_32x32x16_bf16": 8 + 5, "v_mfma_f32_16x16x32_bf16": 4 + 5}
+
+
 def scan(asm: str, result_wait: int = 18, operand_wait: int = 2) -> list:
     """Findings (one string each) for every inline-asm MFMA in ``asm``."""
     marked = _instructions(asm, with_marks=True)
@@ -111,9 +119,10 @@ def scan(asm: str, result_wait: int = 18, operand_wait: int = 2) -> list:
         acc_only = marked[k][4]
         ops = _operands(text)
         dst, srcs = ops[0], set().union(*ops[1:]) if len(ops) > 1 else set()
+        need = RESULT_WAIT.get(text.split()[0], result_wait)
         # after: nothing emitted by the compiler touches dst until the wait is over
         ws, j = 0, k + 1
-        while j < len(ins) and ws < result_wait:
+        while j < len(ins) and ws < need:
             no2, t2, a2, cf = ins[j]
             if cf and acc_only:
                 j += 1          # follow the fall-through path

@@ -82,6 +82,7 @@ def measure_all(torch, device="cuda:0") -> dict:
         "valu_fma_cycles_per_instr": round(valu_cycles(False), 2),
         "valu_exp_cycles_per_instr": round(valu_cycles(True), 2),
         "mfma32_cycles_with_k_fma": {str(k): round(coissue_cycles(k), 2) for k in (0, 4, 6, 8)},
+        "mfma32_cycles_with_k_exp": {str(k): round(coissue_cycles(-k), 2) for k in (1, 2, 4)},
         "loops": ("HBM: 2 GiB streaming read x10, 16 B per lane, 8 workgroups per CU; MFMA: "
                   "one wave per SIMD, four independent 32x32 accumulators; LDS: 8 waves per "
                   "CU, conflict-free reads; VALU: one wave per SIMD, independent streams"),

@@ -125,8 +125,8 @@ __global__ void __launch_bounds__(256) ceil_mfma_kernel(int iters, float *out, l
 }
 
 // ---- MFMA + VALU co-issue ------------------------------------------------------
-// 8 MFMAs per trip, K independent v_fma_f32 after each.
-template <int K>
+// 8 MFMAs per trip, K independent v_fma_f32 (or v_exp_f32 when EXP) after each.
+template <int K, bool EXP = false>
 __global__ void __launch_bounds__(256) ceil_coissue_kernel(int iters, float *out, long long *cyc)
 {
     const int l = threadIdx.x;
@@ -147,9 +147,12 @@ __global__ void __launch_bounds__(256) ceil_coissue_kernel(int iters, float *out
 #pragma unroll
             for (int k = 0; k < K; ++k) {
                 float &y = x[(m * K + k) & 7];
-                asm volatile("v_fma_f32 %0, %0, %1, %2"
-                             : "+v"(y)
-                             : "v"(x[(m * K + k + 3) & 7]), "v"(x[(m * K + k + 5) & 7]));
+                if constexpr (EXP)
+                    asm volatile("v_exp_f32 %0, %1" : "=v"(y) : "v"(x[(m * K + k + 3) & 7]));
+                else
+                    asm volatile("v_fma_f32 %0, %0, %1, %2"
+                                 : "+v"(y)
+                                 : "v"(x[(m * K + k + 3) & 7]), "v"(x[(m * K + k + 5) & 7]));
             }
         }
     }
@@ -412,7 +415,10 @@ int fa_ceil_coissue(int k_valu, int iters, double *cycles_per_mfma)
     case 5: hipLaunchKernelGGL((ceil_coissue_kernel<5>), dim3(grid), dim3(256), 0, 0, iters, o, cy); break;
     case 6: hipLaunchKernelGGL((ceil_coissue_kernel<6>), dim3(grid), dim3(256), 0, 0, iters, o, cy); break;
     case 8: hipLaunchKernelGGL((ceil_coissue_kernel<8>), dim3(grid), dim3(256), 0, 0, iters, o, cy); break;
-    default: snprintf(g_err, sizeof(g_err), "k_valu must be 0, 2, 4, 5, 6 or 8"); return 1;
+    case -1: hipLaunchKernelGGL((ceil_coissue_kernel<1, true>), dim3(grid), dim3(256), 0, 0, iters, o, cy); break;
+    case -2: hipLaunchKernelGGL((ceil_coissue_kernel<2, true>), dim3(grid), dim3(256), 0, 0, iters, o, cy); break;
+    case -4: hipLaunchKernelGGL((ceil_coissue_kernel<4, true>), dim3(grid), dim3(256), 0, 0, iters, o, cy); break;
+    default: snprintf(g_err, sizeof(g_err), "k_valu must be 0, 2, 4, 5, 6, 8, -1, -2 or -4"); return 1;
     }
     CEIL_CK(hipGetLastError());
     CEIL_CK(hipDeviceSynchronize());

@@ -2022,6 +2022,18 @@ __device__ __forceinline__ void mfma_s_drain(f32x16_t &a, f32x16_t &b)
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a), "+v"(b)::"memory");
 }
 
+// The same fence without the wait, for the end of the hand-ordered fast
+// block: there the last S MFMAs are followed by the block's last P V and
+// row-sum MFMAs and a quarter step of softmax work (16 or more instructions,
+// in an order fixed by scheduling fences), which already cover the 8-pass
+// MFMA's result latency.  The build's scan of the generated code checks that
+// enough wait states pass before any access to S (asm_check.py); the drain
+// cost about 90 cycles per 32-key block.
+__device__ __forceinline__ void mfma_s_fence(f32x16_t &a, f32x16_t &b)
+{
+    asm volatile("" : "+v"(a), "+v"(b)::"memory");
+}
+
 // S^T of one 32-key block (K rows at Kblk) for both column blocks.  All K
 // fragments are read first: the MFMAs are volatile asm, which the compiler
 // does not move loads across, so a read inside the loop would cost one LDS
@@ -2235,7 +2247,7 @@ __device__ __forceinline__ void wide_block_fast(const char *Kn, const char *Vp,
             w.l_acc[1] = mfma16(w.sel, w.pp[1][1], w.l_acc[1]);
         }
     }
-    mfma_s_drain(sn[0], sn[1]);
+    mfma_s_fence(sn[0], sn[1]);
     wide_settle<D, MASK>(w, sn, pw, la, MASK ? key0 : -1);
 }
 

@@ -32,8 +32,9 @@ int fa_ceil_hbm_read(const void *buf, size_t bytes, int reps, double *gbps);
  * waves' cycle counters against the constant-rate real-time counter). */
 int fa_ceil_mfma(int fp8, int iters, double *tflops, double *clock_mhz);
 
-/* Cycles per MFMA when k_valu (0, 2, 4, 5, 6 or 8) independent v_fma_f32
- * sit between consecutive MFMAs of one wave, one wave per SIMD. */
+/* Cycles per MFMA when k_valu (0, 2, 4, 5, 6 or 8) independent v_fma_f32, or
+ * -k_valu (1, 2 or 4) independent v_exp_f32, sit between consecutive MFMAs
+ * of one wave, one wave per SIMD. */
 int fa_ceil_coissue(int k_valu, int iters, double *cycles_per_mfma);
 
 /* Conflict-free LDS read stream, 8 waves per CU: ds_read_b128
