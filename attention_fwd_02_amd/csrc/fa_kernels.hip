@@ -168,6 +168,18 @@ __device__ __forceinline__ int swz(int r)
     return (r1 << 2) | ((r0 ^ r2) << 1) | (r0 ^ r3);
 }
 
+// The swizzle of the FP8 tiles (rows of 128 bytes, eight 16-byte chunks).
+// Their V^T read (ds_read_b64_tr_b8) takes 8 bytes per lane from the rows
+// {a..a+3, a+8..a+11}, a = 0 or 4 mod 16, 32 bytes per row; with 64 banks
+// (32 lanes of 8 bytes per cycle) the even rows of that set, and the odd
+// ones, need distinct 32-byte positions: distinct swz >> 1.  swz<64> above
+// maps rows a and a+8 to the same position (a 2-way conflict the SQ counters
+// showed, 8.5 M conflict cycles per call); this one keeps that apart, the
+// K reads' conditions (distinct over 8 consecutive rows, and over the even
+// and the odd rows of 16) and the 32-bank ones, checked by simulation of
+// every read of the FP8 kernel.
+__device__ __forceinline__ int swz_fp8(int r) { return (r & 7) ^ (5 * ((r >> 3) & 1)); }
+
 // Race checks of the LDS rings, in debug builds of the library only
 // (FA_LDS_CHECK = 0 in the product build).  A ring stage must be ready (its
 // copies landed and every wave past the barrier that follows the wait) before
@@ -298,7 +310,7 @@ __device__ __forceinline__ void lds_dma16(char *lds, int voff, u32x4_t d)
 // consecutive LDS addresses.  Lane l of instruction q fills tile row
 // q * RPI + l / CPR at physical chunk l % CPR, i.e. it loads the logical chunk
 // (l % CPR) ^ swz(row) of that key's row.
-template <int D, int BN, int NW, bool STREAM = false>
+template <int D, int BN, int NW, bool STREAM = false, bool FP8SWZ = false>
 struct TileLoader {
     static constexpr int CPR = D / 8;                 // 16-byte chunks per row
     static constexpr int RPI = 64 / CPR;              // rows per instruction
@@ -308,6 +320,11 @@ struct TileLoader {
     static_assert(NQ % NW == 0, "instructions must split evenly over the waves");
 
     u32x4_t kdesc, vdesc;   // K and V rows [0, key_end) of one (batch, KV head)
+
+    __device__ __forceinline__ static int row_swz(int row)
+    {
+        return FP8SWZ ? swz_fp8(row) : swz<D>(row);
+    }
     int kstride_bytes;      // bytes between consecutive keys in HBM
 
     // Descriptors whose byte range ends with row key_end - 1, so that rows
@@ -338,7 +355,7 @@ struct TileLoader {
         for (int i = 0; i < PER_WAVE; ++i) {
             const int q = i * NW + wave;
             const int row = q * RPI + lane / CPR;          // tile-relative row
-            const int voff = toff + row * kstride_bytes + (((lane % CPR) ^ swz<D>(row)) * 16);
+            const int voff = toff + row * kstride_bytes + (((lane % CPR) ^ row_swz(row)) * 16);
             lds_dma16_pair<STREAM>(lds_k + q * 1024, lds_v + q * 1024, voff, kdesc, vdesc);
         }
     }
@@ -352,7 +369,7 @@ struct TileLoader {
         for (int i = 0; i < PER_WAVE; ++i) {
             const int q = i * NW + wave;
             const int row = q * RPI + lane / CPR;
-            const int voff = toff + row * kstride_bytes + (((lane % CPR) ^ swz<D>(row)) * 16);
+            const int voff = toff + row * kstride_bytes + (((lane % CPR) ^ row_swz(row)) * 16);
             lds_dma16<STREAM>(dst + q * 1024, voff, IS_V ? vdesc : kdesc);
         }
     }
@@ -1191,7 +1208,7 @@ struct Fp8Offsets {
 #pragma unroll
             for (int c2 = 0; c2 < 2; ++c2) {
                 const int chunk = 4 * st + 2 * half + c2;
-                k[st][c2] = col * RB + ((chunk ^ swz<D / 2>(col)) * 16);
+                k[st][c2] = col * RB + ((chunk ^ swz_fp8(col)) * 16);
             }
         const int sl = lane & 15, grp = lane >> 4;
         static_assert(D == 128, "vofs assumes 8 chunks per row (4 dim blocks)");
@@ -1200,7 +1217,7 @@ struct Fp8Offsets {
             const int i = 8 * t4 + (sl >> 1);
             const int r = i & 15;
             const int key = (i >> 4) * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-            const int sw = swz<D / 2>(key);
+            const int sw = swz_fp8(key);
             vb[t4] = key * RB + 16 * ((grp ^ sw) & 1) + 8 * (sl & 1);
             vs[t4] = sw >> 1;
         }
@@ -1348,11 +1365,12 @@ struct Fp8RowState {
 template <int D, int NW>
 __device__ __forceinline__ void prefill_tile_fp8(int t, int n_tiles, char *stage, char *next,
                                                  char *after,
-                                                 const TileLoader<D / 2, 64, NW> &ld, int wave,
+                                                 const TileLoader<D / 2, 64, NW, false, true> &ld,
+                                                 int wave,
                                                  int lane, const Fp8Offsets<D> &off,
                                                  Fp8RowState<D> &rs)
 {
-    constexpr int TB = TileLoader<D / 2, 64, NW>::TILE_BYTES;
+    constexpr int TB = TileLoader<D / 2, 64, NW, false, true>::TILE_BYTES;
     using FO = Fp8Ops<D>;
     const bool live = t < rs.NBw;
     const bool live_next = t + 1 < rs.NBw;
@@ -1389,7 +1407,7 @@ fa_prefill_fp8_kernel(const Params p, const float v_descale)
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
     constexpr int BN = 64;
     constexpr int BM = 32 * NW;
-    using TL = TileLoader<D / 2, BN, NW>;
+    using TL = TileLoader<D / 2, BN, NW, false, true>;
     using FO = Fp8Ops<D>;
     constexpr int TB = TL::TILE_BYTES;
     constexpr int STAGE = 2 * TB;
