@@ -86,6 +86,15 @@ CASES = [
     (dict(B=1, max_len=4096, page_size=16), [4096], 1),        # 1 split raised to 2 (<= 256 pages each)
     (dict(D=256, Hq=8, Hkv=2), [300, 17, 0], 0),               # head dim 256
     (dict(D=256, page_size=32, Sq=2, causal=True), [100, 1, 64], 2),
+    # the automatic cut is length-balanced (ranges of one common length,
+    # chosen on the device from the lengths): its edges
+    (dict(), [0, 0, 0], 0),                                    # no keys anywhere: no range
+    (dict(Hq=8, Hkv=1), [300, 50, 0], 0),                      # MQA
+    (dict(B=70, max_len=300, lengths="ragged"), None, 0),      # lengths in two registers
+    (dict(B=200, Hq=4, Hkv=4, max_len=64, lengths="ragged"), None, 0),   # in four
+    (dict(B=257, Hq=4, Hkv=2, max_len=48, lengths="ragged"), None, 0),   # over 256: equal splits
+    (dict(B=1, max_len=16384, page_size=16), [16384], 0),      # one long sequence, many ranges
+    (dict(B=4, Hq=32, Hkv=8, max_len=8192, page_size=16), [8192, 1, 8191, 33], 0),
 ]
 
 
