@@ -138,10 +138,10 @@ __device__ __forceinline__ u32x4_t ld16(const uint16_t *p)
 // Wave issue priority (s_setprio): a wave raises it while it issues an MFMA
 // chain, so that with two waves on a SIMD the matrix pipe is fed first and the
 // other wave's VALU work fills the cycles in between.
-template <int P>
+template <int P, bool ON = true>
 __device__ __forceinline__ void set_prio()
 {
-    if (kUsePrio) __builtin_amdgcn_s_setprio(P);
+    if (kUsePrio && ON) __builtin_amdgcn_s_setprio(P);
 }
 
 // Wait until this wave's outstanding vector-memory operations (including the
@@ -832,19 +832,23 @@ template <int D>
 struct BlockOps {
     static constexpr int QS = D / 16;
     static constexpr int DB = D / 32;
+    // At D = 256 a wave has its SIMD to itself (one workgroup per CU), so a
+    // priority has nothing to order; left out there, the compiler may
+    // schedule the softmax's VALU work between the MFMAs (+1.4 % measured).
+    static constexpr bool kPrio = D < 256;
 
     // S^T of one 32-key block whose K rows start at Kblk (LDS).
     __device__ __forceinline__ static f32x16_t qk(const char *Kblk, const OperandOffsets<D> &off,
                                                   const bf16x8_t (&qf)[QS])
     {
         f32x16_t s = f32x16_t{};
-        set_prio<1>();
+        set_prio<1, kPrio>();
 #pragma unroll
         for (int st = 0; st < QS; ++st) {
             const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(Kblk + off.kofs(st));
             s = mfma32(a, qf[st], s);
         }
-        set_prio<0>();
+        set_prio<0, kPrio>();
         return s;
     }
 
@@ -932,7 +936,7 @@ struct BlockOps {
                                               bf16x8_t sel, bf16x8_t p0, bf16x8_t p1,
                                               f32x16_t (&o)[DB], f32x4_t &l_acc)
     {
-        set_prio<1>();
+        set_prio<1, kPrio>();
         l_acc = mfma16(sel, p0, l_acc);
         l_acc = mfma16(sel, p1, l_acc);
 #pragma unroll
@@ -950,7 +954,7 @@ struct BlockOps {
                 o[db] = mfma32(a, t2 ? p1 : p0, o[db]);
             }
         }
-        set_prio<0>();
+        set_prio<0, kPrio>();
     }
 };
 
