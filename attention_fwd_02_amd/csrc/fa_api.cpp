@@ -216,6 +216,9 @@ fa_status make_plan(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal, i
         } else if ((int64_t)B * Hq * m8 < cus) {
             nw = 4;
             bn = 32;
+            // still fewer 128-row items than CUs: 64-row items (two waves),
+            // so that every CU's LDS and L1 serve the same waves
+            if ((int64_t)B * Hq * ((Sq + 127) / 128) < cus) nw = 2;
         } else if (!causal || Sq >= 2048) {
             // 64 rows per wave: faster wherever most tiles take its pipelined
             // body (non-causal, or causal rows of 2048 and more); shorter

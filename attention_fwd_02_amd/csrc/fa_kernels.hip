@@ -3766,6 +3766,8 @@ static const PrefillCfg kPrefillCfgs[] = {
     {64, 64, 8, 1, launch_prefill_cfg<64, 64, 8, 1>},
     {64, 64, 4, 1, launch_prefill_cfg<64, 64, 4, 1>},
     {64, 32, 4, 1, launch_prefill_cfg<64, 32, 4, 1>},
+    {64, 32, 2, 1, launch_prefill_cfg<64, 32, 2, 1>},
+    {128, 32, 2, 1, launch_prefill_cfg<128, 32, 2, 1>},
     {64, 64, 4, 2, launch_prefill_cfg<64, 64, 4, 2>},
     {256, 32, 4, 1, launch_prefill_cfg<256, 32, 4, 1>},
 };

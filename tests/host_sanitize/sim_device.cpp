@@ -145,7 +145,7 @@ bool prefill_cfg_ok(int D, int bn, int nw, int nr)
     static const int cfgs[][4] = {{128, 64, 8, 1}, {128, 64, 4, 1}, {128, 32, 4, 1},
                                   {128, 32, 8, 1}, {128, 64, 4, 2}, {64, 64, 8, 1},
                                   {64, 64, 4, 1},  {64, 32, 4, 1},  {64, 64, 4, 2},
-                                  {256, 32, 4, 1}};
+                                  {256, 32, 4, 1}, {64, 32, 2, 1},  {128, 32, 2, 1}};
     for (const auto &c : cfgs)
         if (c[0] == D && c[1] == bn && c[2] == nw && c[3] == nr) return true;
     return false;

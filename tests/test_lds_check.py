@@ -96,6 +96,8 @@ CASES = {
                                  lambda: _dense(1, 8, 2, 1200, 1200, 128, False)),
     "prefill_bn32_w8": ({"FA_PREFILL_BN": "32", "FA_PREFILL_NW": "8", "FA_PREFILL_NR": "1"},
                         lambda: _dense(2, 3, 3, 513, 513, 128, True)),
+    "prefill_bn32_w2": ({"FA_PREFILL_BN": "32", "FA_PREFILL_NW": "2", "FA_PREFILL_NR": "1"},
+                        lambda: _dense(1, 4, 2, 300, 333, 64, True)),
     "prefill_pingpong_ring4": ({"FA_PREFILL_PP": "4"},
                                lambda: _dense(1, 4, 4, 1100, 1300, 128, True)),
     "prefill_pingpong_ring5": ({"FA_PREFILL_PP": "5"},

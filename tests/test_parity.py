@@ -103,6 +103,7 @@ CONFIGS = {
     "rows64_bn64_w4": {"FA_PREFILL_BN": "64", "FA_PREFILL_NW": "4", "FA_PREFILL_NR": "2"},
     "bn32_w8": {"FA_PREFILL_BN": "32", "FA_PREFILL_NW": "8", "FA_PREFILL_NR": "1"},
     "bn64_w4": {"FA_PREFILL_BN": "64", "FA_PREFILL_NW": "4", "FA_PREFILL_NR": "1"},
+    "bn32_w2": {"FA_PREFILL_BN": "32", "FA_PREFILL_NW": "2", "FA_PREFILL_NR": "1"},
     # ping-pong kernel (8 waves, alternating MFMA and softmax phases), 4- and 5-tile rings
     "pingpong_ring4": {"FA_PREFILL_PP": "4"},
     "pingpong_ring5": {"FA_PREFILL_PP": "5"},
