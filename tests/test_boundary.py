@@ -121,9 +121,9 @@ def test_workspace_size_and_plan_host_arithmetic(b):
         assert p["block_m"] == 256 and p["block_n"] == 64 and p["grid"] == 256
         assert p["waves"] == 4 and p["rows_per_wave"] == 64
     # too few 256-row items to cover the CUs: 4-wave workgroups, 32-key tiles
-    p = b.fa_plan(4, 16, 16, 1024, 1024, 64, True, 0)
-    assert p["block_m"] == 128 and p["block_n"] == 32 and p["work_items"] == 4 * 16 * 8
-    assert p["grid"] == 4 * 16 * 8 and p["waves"] == 4
+    p = b.fa_plan(4, 8, 8, 1024, 1024, 64, True, 0)
+    assert p["block_m"] == 128 and p["block_n"] == 32 and p["work_items"] == 4 * 8 * 8
+    assert p["grid"] == 4 * 8 * 8 and p["waves"] == 4
     # ... and too few 128-row items as well: 2-wave workgroups (64 rows)
     p = b.fa_plan(2, 8, 8, 1024, 1024, 64, True, 0)
     assert p["block_m"] == 64 and p["block_n"] == 32 and p["work_items"] == 2 * 8 * 16
