@@ -103,6 +103,44 @@ __device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c)
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// S^T MFMAs of the hand-ordered loops (the 64-row prefill's fast block, the
+// dK/dV pipeline), with the accumulator in VGPRs.  The VALU reads S next,
+// and the compiler keeps every accumulator of those kernels in AGPRs (moving
+// S out would cost 32 v_accvgpr_read per block), so these two are written
+// out; the B operand (Q, or the K / V rows) comes straight from AGPRs.  The compiler does not see
+// the MFMA inside, so it would also not wait for its result: the chain of
+// one accumulator ends in mfma_s_drain, which takes the accumulators as
+// operands, so nothing the compiler emits can touch them before the wait.
+// (It could still copy or spill one between the MFMA and the drain; the
+// build scans the generated code for any such access and rejects it.)
+__device__ __forceinline__ void mfma_s_first(f32x16_t &d, bf16x8_t a, bf16x8_t b)
+{
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_s_next(f32x16_t &d, bf16x8_t a, bf16x8_t b)
+{
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+}
+
+// The wait after the last S MFMAs of a block (24 wait states; the 8-pass
+// MFMA needs about half of that), before anything may read or move S.
+__device__ __forceinline__ void mfma_s_drain(f32x16_t &a, f32x16_t &b)
+{
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a), "+v"(b)::"memory");
+}
+
+// The same fence without the wait, for the end of the hand-ordered fast
+// block: there the last S MFMAs are followed by the block's last P V and
+// row-sum MFMAs and a quarter step of softmax work (16 or more instructions,
+// in an order fixed by scheduling fences), which already cover the 8-pass
+// MFMA's result latency.  The build's scan of the generated code checks that
+// enough wait states pass before any access to S (asm_check.py); the drain
+// cost about 90 cycles per 32-key block.
+__device__ __forceinline__ void mfma_s_fence(f32x16_t &a, f32x16_t &b)
+{
+    asm volatile("" : "+v"(a), "+v"(b)::"memory");
+}
+
 // Combine a value with the one held by lane ^ 32 through a symmetric op.
 __device__ __forceinline__ float max_halves(float x)
 {
@@ -147,6 +185,27 @@ __device__ __forceinline__ void set_prio()
 // Wait until this wave's outstanding vector-memory operations (including the
 // HBM -> LDS copies) are done.  gfx9 s_waitcnt: vmcnt(0), expcnt(7), lgkmcnt(15).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Pins the computation of a VGPR value before this point (an empty volatile
+// asm that reads it), so that a software-pipelined step keeps its share of
+// the VALU work between its own MFMAs.
+__device__ __forceinline__ void keep(uint32_t a) { asm volatile("" ::"v"(a)); }
+__device__ __forceinline__ void keep(float a) { asm volatile("" ::"v"(a)); }
+
+// Workgroup barrier between phases, without the memory fence of
+// __syncthreads (which would wait for the K/V copies still in flight).  The
+// empty asm statements keep the compiler from moving LDS accesses across it,
+// the scheduling fences any other instruction: without them the scheduler
+// hoisted a V phase's register-only softmax work above the barrier into the
+// M phase, where it defeats the alternation.
+__device__ __forceinline__ void pp_barrier()
+{
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
 
 // ---------------------------------------------------------------------------
 // LDS tile layout, K and V alike: [rows][D] bf16, rows of 2*D bytes; the
@@ -1545,7 +1604,7 @@ fa_prefill_fp8_kernel(const Params p, const float v_descale)
 
 // ---------------------------------------------------------------------------
 // Backward: dQ, dK, dV from Q, K, V, O, dO and the forward's LSE.
-//   delta_i = sum_d dO_id O_id                                  (fa_bwd_delta_kernel)
+//   delta_i = sum_d dO_id O_id, kept negated                   (fa_bwd_delta_kernel)
 //   P = exp(scale Q K^T - LSE), dP = dO V^T, dS = P (dP - delta)
 //   dV = P^T dO, dK = scale dS^T Q                              (fa_bwd_dkdv_kernel)
 //   dQ = scale dS K                                             (fa_bwd_dq_kernel)
@@ -1560,7 +1619,7 @@ fa_prefill_fp8_kernel(const Params p, const float v_descale)
 struct BwdParams {
     const uint16_t *q, *k, *v, *o, *dout;
     const float *lse;
-    float *delta;            // [B][Hq][Sq]: rowsum(dO O)
+    float *ndelta;           // [B][Hq][Sq]: -rowsum(dO O)
     float *lse2;             // [B][Hq][Sq]: LSE * log2(e), +inf for rows without keys
     uint16_t *dq, *dk, *dv;
     int B, Hq, Hkv, Sq, Sk, group, causal, off;
@@ -1570,7 +1629,7 @@ struct BwdParams {
     int n_blocks;     // dkdv: key blocks per KV head; dq: query blocks per head
 };
 
-// delta[b][h][i] = sum_d dO[b][i][h][d] * O[b][i][h][d] and lse2 = LSE log2 e,
+// ndelta[b][h][i] = -sum_d dO[b][i][h][d] * O[b][i][h][d] and lse2 = LSE log2 e,
 // one row per thread.
 template <int D>
 __global__ void __launch_bounds__(256) fa_bwd_delta_kernel(const BwdParams p)
@@ -1596,7 +1655,7 @@ __global__ void __launch_bounds__(256) fa_bwd_delta_kernel(const BwdParams p)
     const int i = (int)(bi % p.Sq);
     const int b = (int)(bi / p.Sq);
     const long vi = ((long)b * p.Hq + h) * p.Sq + i;
-    p.delta[vi] = acc;
+    p.ndelta[vi] = -acc;
     // exp(scale s - LSE) = exp2(c s - LSE log2 e); a row without keys has
     // LSE = -inf and must give P = 0
     const float l = p.lse[vi];
@@ -1748,7 +1807,7 @@ fa_bwd_dq_kernel(const BwdParams p)
         load_q<D>(qf, p.q + rowoff, half);
         load_q<D>(dof, p.dout + rowoff, half);
         const float lse2 = p.lse2[((long)b * p.Hq + hq) * p.Sq + qc];
-        const float dlt = p.delta[((long)b * p.Hq + hq) * p.Sq + qc];
+        const float ndl = p.ndelta[((long)b * p.Hq + hq) * p.Sq + qc];
         wait_vmem();
         flip_q<D>(qf, p.flip);
         flip_q<D>(dof, 0u);
@@ -1783,7 +1842,7 @@ fa_bwd_dq_kernel(const BwdParams p)
                     float pr = fast_exp2(fmaf(s[r], p.c, -lse2));
                     // masked keys score -inf: P = 0 also at scale 0 (-inf * 0 is NaN)
                     if (masked) pr = (s[r] == kNegInf) ? 0.0f : pr;
-                    ds[r] = pr * (dp[r] - dlt);
+                    ds[r] = pr * (dp[r] + ndl);
                 }
                 bf16x8_t d0, d1;
                 pack_halves(ds, d0, d1);
@@ -1799,22 +1858,198 @@ fa_bwd_dq_kernel(const BwdParams p)
 }
 
 // dK, dV: one workgroup = NW waves x 32 keys of one (b, KV head); the Q and
-// dO tiles of every query head of the group stream through a three-stage
-// LDS ring (64 queries per tile, with their LSE and delta).  Per 32-query
-// block: S = Q K^T and dP = dO V^T (lane = key column, registers = queries),
+// dO tiles of every query head of the group stream through a four-stage LDS
+// ring (64 queries per tile, with their LSE and delta).  Per 32-query block
+// n: S = Q K^T and dP = dO V^T (lane = key column, registers = queries),
 // P = exp(S - LSE), dS = P (dP - delta), dV^T += dO^T P, dK^T += Q^T dS.
+// With one wave per SIMD nothing else fills the matrix unit's idle cycles,
+// so the block loop is software-pipelined: step n issues the S and dP MFMAs
+// of block n + 1 and the accumulating MFMAs of block n - 1, and computes
+// block n's P and dS on the VALU between them.  The three parts share no
+// registers, so no MFMA waits for the softmax terms.  Tile u holds blocks 2u
+// and 2u + 1.  Step 2u + 1 begins with the barrier that makes tile u + 1
+// ready and tile u - 1's stage reusable (its last reader is the accumulation
+// of block 2u - 1, in step 2u), then starts the copies of tile u + 3 into
+// that stage.
+// ---------------------------------------------------------------------------
+constexpr int kBwdStages = 4;
+
+template <int D>
+struct BwdKeys {
+    bf16x8_t kf[D / 16], vf[D / 16];   // this lane's key row of K and of V (B operands)
+    f32x16_t dk[D / 32], dv[D / 32];   // dK^T and dV^T (lane = key column)
+};
+
+// One 32-query block in the ring: its Q rows and dO rows, and this lane's
+// LSE * log2 e and -delta values (16 bytes at +32 g4: registers 4 g4 .. 4 g4 + 3).
+struct BwdBlock {
+    const char *q, *o;
+    const char *lse, *ndl;
+};
+
+// -delta of a block's 16 rows of this lane in accumulator order: the initial
+// value of its dP chain, which then yields dP - delta.
+__device__ __forceinline__ f32x16_t bwd_ld_ndelta(const BwdBlock &b)
+{
+    f32x16_t d;
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4_t v = *reinterpret_cast<const f32x4_t *>(b.ndl + 32 * g4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) d[4 * g4 + e] = v[e];
+    }
+    return d;
+}
+
+// An S or dP MFMA chain's first step from a given accumulator (see mfma_s_first).
+__device__ __forceinline__ void mfma_s_from(f32x16_t &d, bf16x8_t a, bf16x8_t b, f32x16_t c)
+{
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(d) : "v"(a), "a"(b), "v"(c));
+}
+
+// The transposed operand of accumulating MFMA st of a block (see bwd_accumulate).
+template <int D>
+__device__ __forceinline__ bf16x8_t bwd_ld_tr(const char *X, const OperandOffsets<D> &off, int st)
+{
+    constexpr int DB = D / 32;
+    const int t2 = st / DB, db = st % DB;
+    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4_t *)(X + off.vofs(db, 0) + t2 * 16 * 2 * D));
+    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4_t *)(X + off.vofs(db, 1) + t2 * 16 * 2 * D));
+    const u32x2_t lw = __builtin_bit_cast(u32x2_t, lo);
+    const u32x2_t hw = __builtin_bit_cast(u32x2_t, hi);
+    return __builtin_bit_cast(bf16x8_t, (u32x4_t){lw[0], lw[1], hw[0], hw[1]});
+}
+
+// Step n of the dK/dV pipeline.  nx: block n + 1 (S and dP into sn, dpn);
+// cu: block n (P and dS from s, dp into pn, dn); pv: block n - 1 (its P and
+// dS in pp, dd accumulate into dV and dK; ACC = false: no such block).
+// Slot st issues S k-step st, dV MFMA st, dP k-step st and dK MFMA st, with
+// the slot's 16 / QS elements of P(n) and dS(n) spread between them, and
+// copy(st), the slot's share of a later tile's HBM -> LDS copies; the
+// operand reads run kBwdPrefetch slots ahead.  S and dP are inline-asm MFMAs
+// with VGPR accumulators (the VALU reads them in the next step) and the K and
+// V rows in AGPRs; the s_nop at the end of the step, with the slots after the
+// last ones of each chain, covers their result latency before the next step
+// (or a branch) may touch them, which the build's scan of the generated code
+// checks.
+constexpr int kBwdPrefetch = 2;
+
+template <int D, bool ACC, class CP>
+__device__ __forceinline__ void bwd_kv_step(BwdKeys<D> &w, const OperandOffsets<D> &off,
+                                            const BwdBlock &nx, const BwdBlock &cu,
+                                            const BwdBlock &pv, float c,
+                                            const f32x16_t &s, const f32x16_t &dp,
+                                            f32x16_t &sn, f32x16_t &dpn, const bf16x8_t (&pp)[2],
+                                            const bf16x8_t (&dd)[2], bf16x8_t (&pn)[2],
+                                            bf16x8_t (&dn)[2], CP &&copy)
+{
+    constexpr int QS = D / 16, DB = D / 32, EPS = 16 / QS;
+    constexpr int PF = kBwdPrefetch < QS ? kBwdPrefetch : QS;
+    bf16x8_t qa[QS], oa[QS], va[QS], ka[QS];
+    f32x4_t lv[4];
+    u32x4_t pw[2], dw[2];
+    // the reads of slot i, in the order the slots consume them (LDS reads
+    // complete in order); the LSE of a group of 4 rows comes with the slot
+    // that first needs it, block n + 1's -delta (the dP chain's start) with
+    // slot 0
+    f32x16_t nd;
+    auto rd = [&](int i) {
+        qa[i] = *reinterpret_cast<const bf16x8_t *>(nx.q + off.kofs(i));
+        if (i == 0) nd = bwd_ld_ndelta(nx);
+        if ((i * EPS) % 4 == 0) {
+            const int g4 = i * EPS / 4;
+            lv[g4] = *reinterpret_cast<const f32x4_t *>(cu.lse + 32 * g4);
+        }
+        if (ACC) va[i] = bwd_ld_tr<D>(pv.o, off, i);
+        oa[i] = *reinterpret_cast<const bf16x8_t *>(nx.o + off.kofs(i));
+        if (ACC) ka[i] = bwd_ld_tr<D>(pv.q, off, i);
+    };
+#pragma unroll
+    for (int i = 0; i < PF; ++i) rd(i);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int st = 0; st < QS; ++st) {
+        const int t2 = st / DB, db = st % DB;
+        float x[EPS], y[EPS];
+        if (st == 0) mfma_s_first(sn, qa[st], w.kf[st]);
+        else mfma_s_next(sn, qa[st], w.kf[st]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (st + PF < QS) rd(st + PF);
+#pragma unroll
+        for (int i = 0; i < EPS; ++i) {
+            const int r = st * EPS + i, g4 = r / 4, e = r % 4;
+            x[i] = fmaf(s[r], c, -lv[g4][e]);
+        }
+#pragma unroll
+        for (int i = 0; i < EPS / 2; ++i) {
+            y[i] = fast_exp2(x[i]);
+            keep(y[i]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (ACC) w.dv[db] = mfma32(va[st], pp[t2], w.dv[db]);
+        __builtin_amdgcn_sched_barrier(0);
+        copy(st);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = EPS / 2; i < EPS; ++i) {
+            y[i] = fast_exp2(x[i]);
+            keep(y[i]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (st == 0) mfma_s_from(dpn, oa[st], w.vf[st], nd);
+        else mfma_s_next(dpn, oa[st], w.vf[st]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < EPS; i += 2) {
+            const int r = st * EPS + i;
+            const float d0 = y[i] * dp[r];       // dp: dP - delta
+            const float d1 = y[i + 1] * dp[r + 1];
+            const int wi = r / 2;   // bf16 pair: word wi % 4 of half wi / 4
+            pw[wi / 4][wi % 4] = pack_bf16(y[i], y[i + 1]);
+            dw[wi / 4][wi % 4] = pack_bf16(d0, d1);
+            keep(pw[wi / 4][wi % 4]);
+            keep(dw[wi / 4][wi % 4]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (ACC) w.dk[db] = mfma32(ka[st], dd[t2], w.dk[db]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    asm volatile("s_nop 7" : "+v"(sn), "+v"(dpn)::"memory");
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        pn[h] = __builtin_bit_cast(bf16x8_t, pw[h]);
+        dn[h] = __builtin_bit_cast(bf16x8_t, dw[h]);
+    }
+}
+
+// Causal blocks that cross the diagonal, between steps: element r of the
+// lane (query base + 8 (r / 4) + r % 4) is allowed only if that offset is at
+// least lo; the others score -inf, so that P = 0 there (c > 0).  Rows past
+// the last query need no mask: their Q and dO rows, LSE and delta read as
+// zero, so that P = 1 and dS = 0 there, and both accumulating products add
+// exact zeros.  Keys past the last key need none either: a lane's values
+// only reach its own columns of dK and dV, which are not stored.
+__device__ __forceinline__ void bwd_mask_rows(f32x16_t &s, int lo)
+{
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = (8 * (r >> 2) + (r & 3) < lo) ? kNegInf : s[r];
+}
+
 template <int D, int NW>
-__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 8 ? 2 : 1)))
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1)))
 fa_bwd_dkdv_kernel(const BwdParams p)
 {
 #if defined(__HIP_DEVICE_COMPILE__)
     constexpr int BQ = 64;
     constexpr int BK = 32 * NW;
     using TL = TileLoader<D, BQ, NW>;
-    using BO = BlockOps<D>;
     constexpr int TB = TL::TILE_BYTES;
     constexpr int STAGE = 2 * TB + 1024;   // Q tile, dO tile, LSE * log2e, delta
-    __shared__ __attribute__((aligned(1024))) char lds[kPrefillStages * STAGE];
+    constexpr int LPU = 2 * TL::PER_WAVE;  // Q and dO row copies per wave and tile
+    static_assert(LPU + 2 <= 15, "vmcnt immediate");
+    __shared__ __attribute__((aligned(1024))) char lds[kBwdStages * STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -1833,6 +2068,19 @@ fa_bwd_dkdv_kernel(const BwdParams p)
     const int Gx = gridDim.x / ND;
     const int N = (BG / ND) * p.n_blocks;
     const int ntq_all = (p.Sq + BQ - 1) / BQ;
+    // byte offset of each of this lane's Q / dO row copies within a tile
+    // (row stride Hq * D * 2, 16-byte chunks placed by the tile swizzle)
+    const int qstride = p.Hq * D * 2;
+    int loff[TL::PER_WAVE];
+#pragma unroll
+    for (int i = 0; i < TL::PER_WAVE; ++i) {
+        const int row = (i * NW + wave) * TL::RPI + lane / TL::CPR;
+        loff[i] = row * qstride + (((lane % TL::CPR) ^ swz<D>(row)) * 16);
+    }
+    // scale 0: S is 0 for every pair, which zero K rows give exactly; with
+    // c = 1 the diagonal mask's -inf then still gives P = 0
+    const bool zero_scale = p.c == 0.0f;
+    const float c = zero_scale ? 1.0f : p.c;
     for (int it = 0; it * Gx < N; ++it) {
         const int li = it * Gx + ((it & 1) ? (Gx - 1 - jw) : jw);
         if (li >= N) continue;
@@ -1842,7 +2090,8 @@ fa_bwd_dkdv_kernel(const BwdParams p)
         const int b = bg / p.Hkv;
         const int g = bg % p.Hkv;
         const int k0 = kblk * BK;                 // first key of the workgroup
-        const int kj = k0 + wave * 32 + col;      // this lane's key
+        const int kw0 = k0 + wave * 32;           // first key of the wave
+        const int kj = kw0 + col;                 // this lane's key
         const bool kvalid = kj < p.Sk;
         const int kc = min(kj, p.Sk - 1);
         // causal: query i sees key j iff j <= i + off, i.e. i >= j - off
@@ -1850,102 +2099,151 @@ fa_bwd_dkdv_kernel(const BwdParams p)
         const int ntq = max(0, ntq_all - t0);
         const int n_units = ntq * p.group;        // (head, query tile) pairs
 
-        TL ld;
-        auto issue_unit = [&](int u, char *dst) {
-            const int hq = g * p.group + u / ntq;
-            const int t = t0 + u % ntq;
+        // copies of tile u (query head g * group + u / ntq, query tile
+        // t0 + u % ntq), in LPU + 2 copy instructions per wave: the Q and dO
+        // rows in PER_WAVE pairs, then the LSE and delta vectors (wave 0; the
+        // other waves copy an empty range into the stage's spare bytes, so
+        // that every wave counts as many copies per tile).  Tiles past the
+        // last one are copied the same way from empty ranges: they fill a
+        // free stage with zeros and keep the count per tile fixed.
+        int cp_h = 0, cp_t = 0;   // head within the group and tile of the next tile to copy
+        u32x4_t cq, co, cl, cd;
+        int ctoff = 0, cstage = 0;
+        auto copy_begin = [&]() {
+            const bool real = cp_h < p.group;
+            const int hq = g * p.group + (real ? cp_h : 0);
+            const int t = t0 + cp_t;
             const long hbase = ((long)b * p.Sq * p.Hq + hq) * D;
-            ld.setup(p.q + hbase, p.dout + hbase, p.Hq * D * 2, p.Sq);
-            ld.issue(dst, dst + TB, t * BQ, wave, lane);
-            if (wave == 0) {
-                const long vb = ((long)b * p.Hq + hq) * p.Sq + (long)t * BQ;
-                const uint32_t nb = (uint32_t)((p.Sq - t * BQ) * 4);
-                lds_dma4_pair(dst + 2 * TB, dst + 2 * TB + 512, lane * 4,
-                              raw_desc(p.lse2 + vb, nb), raw_desc(p.delta + vb, nb));
+            const uint32_t nbytes = real ? (uint32_t)((p.Sq - 1) * qstride + D * 2) : 0u;
+            cq = raw_desc(p.q + hbase, nbytes);
+            co = raw_desc(p.dout + hbase, nbytes);
+            const long vb = ((long)b * p.Hq + hq) * p.Sq + (long)t * BQ;
+            const uint32_t nb = (real && wave == 0) ? (uint32_t)((p.Sq - t * BQ) * 4) : 0u;
+            cl = raw_desc(p.lse2 + vb, nb);
+            cd = raw_desc(p.ndelta + vb, nb);
+            ctoff = t * BQ * qstride;
+            if (++cp_t == ntq) {
+                cp_t = 0;
+                ++cp_h;
             }
         };
-        if (n_units > 0) issue_unit(0, lds);
-        if (n_units > 1) issue_unit(1, lds + STAGE);
+        auto copy_part = [&](int i) {
+            char *dst = lds + cstage * STAGE;
+            if (i < TL::PER_WAVE) {
+                const int q = i * NW + wave;
+                lds_dma16_pair(dst + q * 1024, dst + TB + q * 1024, ctoff + loff[i], cq, co);
+            } else if (i == TL::PER_WAVE) {
+                const int spare = wave == 0 ? 0 : 256;
+                lds_dma4_pair(dst + 2 * TB + spare, dst + 2 * TB + 512 + spare, lane * 4, cl, cd);
+            }
+        };
+        auto copy_tile = [&](int u) {
+            cstage = u % kBwdStages;
+            copy_begin();
+#pragma unroll
+            for (int i = 0; i <= TL::PER_WAVE; ++i) copy_part(i);
+        };
+        auto no_copy = [](int) {};
+        auto block_of = [&](int u, int qb) {
+            const char *stg = lds + (u % kBwdStages) * STAGE;
+            return BwdBlock{stg + qb * 32 * 2 * D, stg + TB + qb * 32 * 2 * D,
+                            stg + 2 * TB + qb * 128 + 16 * half,
+                            stg + 2 * TB + 512 + qb * 128 + 16 * half};
+        };
+        // whether block qb of tile u crosses the causal diagonal for this
+        // wave, and the lane's smallest allowed row offset there
+        auto mask_of = [&](int u, int qb, int &lo) {
+            const int q0 = (t0 + u % ntq) * BQ + qb * 32;
+            lo = kj - p.off - (q0 + 4 * half);
+            return p.causal && kw0 + 31 > q0 + p.off;
+        };
 
-        bf16x8_t kf[D / 16], vf[D / 16];
-        load_q<D>(kf, p.k + (((long)b * p.Sk + kc) * p.Hkv + g) * D, half);
-        load_q<D>(vf, p.v + (((long)b * p.Sk + kc) * p.Hkv + g) * D, half);
+        if (n_units > 0) copy_tile(0);
+        BwdKeys<D> w;
+        load_q<D>(w.kf, p.k + (((long)b * p.Sk + kc) * p.Hkv + g) * D, half);
+        load_q<D>(w.vf, p.v + (((long)b * p.Sk + kc) * p.Hkv + g) * D, half);
         wait_vmem();
-        flip_q<D>(kf, p.flip);
-        flip_q<D>(vf, 0u);
-
-        f32x16_t dk[D / 32], dv[D / 32];
+        if (zero_scale) {
+#pragma unroll
+            for (int st = 0; st < D / 16; ++st) w.kf[st] = bf16x8_t{};
+        }
+        flip_q<D>(w.kf, p.flip);
+        flip_q<D>(w.vf, 0u);
+        // the K and V rows are only ever B operands of inline-asm MFMAs:
+        // moved to AGPRs here, once, not before each MFMA
+#pragma unroll
+        for (int st = 0; st < D / 16; ++st) asm volatile("" : "+a"(w.kf[st]), "+a"(w.vf[st]));
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-            dk[db] = f32x16_t{};
-            dv[db] = f32x16_t{};
+            w.dk[db] = f32x16_t{};
+            w.dv[db] = f32x16_t{};
         }
+        __syncthreads();   // tile 0 is in LDS (every wave's copies)
 
-        int st = 0;
-        for (int u = 0; u < n_units; ++u) {
-            char *stage = lds + st * STAGE;
-            wait_vmem();
-            __syncthreads();
-            if (u + 2 < n_units) {
-                const int s2 = st + 2 >= kPrefillStages ? st + 2 - kPrefillStages : st + 2;
-                issue_unit(u + 2, lds + s2 * STAGE);
-            }
-            const int tq0 = (t0 + u % ntq) * BQ;   // first query of the tile
-            const float *lsev = reinterpret_cast<const float *>(stage + 2 * TB);
-            const float *dltv = reinterpret_cast<const float *>(stage + 2 * TB + 512);
+        if (n_units > 0) {
+            copy_tile(1);
+            copy_tile(2);
+            copy_begin();   // tile 3's descriptors, for step 1
+            f32x16_t sx, dpx, sy, dpy;             // S, dP of the even / odd block
+            bf16x8_t px[2], dx[2], py[2], dy[2];   // their P and dS (B operands)
+            int lo;
+            {
+                // S(0), dP(0); step 0: S(1), P(0)
+                const BwdBlock c0 = block_of(0, 0), c1 = block_of(0, 1);
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                const int q0 = tq0 + qb * 32;
-                if (q0 >= p.Sq) continue;
-                // causal: skip blocks whose last query sees none of the
-                // workgroup's keys
-                if (p.causal && q0 + 31 + p.off < k0) continue;
-                const char *Qblk = stage + qb * 32 * 2 * D;
-                const char *Oblk = stage + TB + qb * 32 * 2 * D;
-                const f32x16_t s = BO::qk(Qblk, off, kf);
-                const f32x16_t dp = BO::qk(Oblk, off, vf);
-                // this wave's keys kw0 .. kw0 + 31 against the block's queries:
-                // the per-element mask only where some pair is cut
-                const int kw0 = k0 + wave * 32;
-                const bool need_mask = kw0 + 31 >= p.Sk || q0 + 31 >= p.Sq ||
-                                       (p.causal && kw0 + 31 > q0 + p.off);
-                float pr[16], ds[16];
-#pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) {
-                    const int qo = qb * 32 + 8 * g4 + 4 * half;   // tile-relative query of register 4 g4
-                    const f32x4_t lv = *reinterpret_cast<const f32x4_t *>(lsev + qo);
-                    const f32x4_t dl = *reinterpret_cast<const f32x4_t *>(dltv + qo);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int r = 4 * g4 + e;
-                        float x = fast_exp2(fmaf(s[r], p.c, -lv[e]));
-                        if (need_mask) {
-                            const int qi = tq0 + qo + e;
-                            const bool ok = kvalid && qi < p.Sq && (!p.causal || kj <= qi + p.off);
-                            x = ok ? x : 0.0f;
-                        }
-                        pr[r] = x;
-                        ds[r] = x * (dp[r] - dl[e]);
+                for (int st = 0; st < D / 16; ++st) {
+                    const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(c0.q + off.kofs(st));
+                    const bf16x8_t o = *reinterpret_cast<const bf16x8_t *>(c0.o + off.kofs(st));
+                    if (st == 0) {
+                        mfma_s_first(sx, a, w.kf[st]);
+                        mfma_s_from(dpx, o, w.vf[st], bwd_ld_ndelta(c0));
+                    } else {
+                        mfma_s_next(sx, a, w.kf[st]);
+                        mfma_s_next(dpx, o, w.vf[st]);
                     }
                 }
-                bf16x8_t p0, p1, d0, d1;
-                pack_halves(pr, p0, p1);
-                pack_halves(ds, d0, d1);
-                bwd_accumulate<D>(Oblk, off, p0, p1, dv);
-                bwd_accumulate<D>(Qblk, off, d0, d1, dk);
+                mfma_s_drain(sx, dpx);
+                if (mask_of(0, 0, lo)) bwd_mask_rows(sx, lo);
+                bwd_kv_step<D, false>(w, off, c1, c0, c0, c, sx, dpx, sy, dpy, py, dy, px, dx,
+                                      no_copy);
             }
-            st = st + 1 == kPrefillStages ? 0 : st + 1;
+            for (int u = 0; u < n_units; ++u) {
+                const BwdBlock c0 = block_of(u, 0), c1 = block_of(u, 1);
+                // step 2u + 1: S(2u + 2) from tile u + 1 (zeros past the last
+                // tile: a dead S), P(2u + 1), accumulation of block 2u, and
+                // the copies of tile u + 3 into tile u - 1's stage.  Tile
+                // u + 2's copies may stay in flight.
+                __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_s_waitcnt(0x0F70 | (LPU + 2));
+                pp_barrier();
+                cstage = (u + 3) % kBwdStages;
+                if (mask_of(u, 1, lo)) bwd_mask_rows(sy, lo);
+                bwd_kv_step<D, true>(w, off, block_of(u + 1, 0), c1, c0, c, sy, dpy, sx, dpx, px,
+                                     dx, py, dy, copy_part);
+                if (u + 1 < n_units) {
+                    // step 2u + 2: S(2u + 3), P(2u + 2), accumulation of block
+                    // 2u + 1, and the descriptors of tile u + 4's copies
+                    const BwdBlock n0 = block_of(u + 1, 0), n1 = block_of(u + 1, 1);
+                    if (mask_of(u + 1, 0, lo)) bwd_mask_rows(sx, lo);
+                    bwd_kv_step<D, true>(w, off, n1, n0, c1, c, sx, dpx, sy, dpy, py, dy, px, dx,
+                                         [&](int st) {
+                                             if (st == 1) copy_begin();
+                                         });
+                }
+            }
+            const BwdBlock last = block_of(n_units - 1, 1);
+            bwd_accumulate<D>(last.o, off, py[0], py[1], w.dv);
+            bwd_accumulate<D>(last.q, off, dy[0], dy[1], w.dk);
         }
-        __syncthreads();
+        __syncthreads();   // every wave is done with the ring before the next item
         if (kvalid) {
             const long kb_off = (((long)b * p.Sk + kj) * p.Hkv + g) * D;
-            store_rows<D, false>(dk, p.scale, half, p.dk, kb_off);
-            store_rows<D, false>(dv, 1.0f, half, p.dv, kb_off);
+            store_rows<D, false>(w.dk, p.scale, half, p.dk, kb_off);
+            store_rows<D, false>(w.dv, 1.0f, half, p.dv, kb_off);
         }
     }
 #endif
 }
-
 // ---------------------------------------------------------------------------
 // Wide prefill: one wave per SIMD, 64 query rows per wave (column blocks
 // r = 0, 1 of 32 rows), so that each K and V operand read from LDS feeds two
@@ -2019,43 +2317,6 @@ __device__ __forceinline__ bf16x8_t wide_ld_v(const char *Vblk, const OperandOff
     return __builtin_bit_cast(bf16x8_t, (u32x4_t){lw[0], lw[1], hw[0], hw[1]});
 }
 
-// S^T MFMAs of the fast block, with the accumulator in VGPRs.  The VALU
-// reads S next, and the compiler keeps every accumulator of this kernel in
-// AGPRs (moving S out would cost 32 v_accvgpr_read per block), so these two
-// are written out; Q comes straight from AGPRs.  The compiler does not see
-// the MFMA inside, so it would also not wait for its result: the chain of
-// one accumulator ends in mfma_s_drain, which takes the accumulators as
-// operands, so nothing the compiler emits can touch them before the wait.
-// (It could still copy or spill one between the MFMA and the drain; the
-// build scans the generated code for any such access and rejects it.)
-__device__ __forceinline__ void mfma_s_first(f32x16_t &d, bf16x8_t a, bf16x8_t b)
-{
-    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
-}
-__device__ __forceinline__ void mfma_s_next(f32x16_t &d, bf16x8_t a, bf16x8_t b)
-{
-    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
-}
-
-// The wait after the last S MFMAs of a block (24 wait states; the 8-pass
-// MFMA needs about half of that), before anything may read or move S.
-__device__ __forceinline__ void mfma_s_drain(f32x16_t &a, f32x16_t &b)
-{
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a), "+v"(b)::"memory");
-}
-
-// The same fence without the wait, for the end of the hand-ordered fast
-// block: there the last S MFMAs are followed by the block's last P V and
-// row-sum MFMAs and a quarter step of softmax work (16 or more instructions,
-// in an order fixed by scheduling fences), which already cover the 8-pass
-// MFMA's result latency.  The build's scan of the generated code checks that
-// enough wait states pass before any access to S (asm_check.py); the drain
-// cost about 90 cycles per 32-key block.
-__device__ __forceinline__ void mfma_s_fence(f32x16_t &a, f32x16_t &b)
-{
-    asm volatile("" : "+v"(a), "+v"(b)::"memory");
-}
-
 // S^T of one 32-key block (K rows at Kblk) for both column blocks.  All K
 // fragments are read first: the MFMAs are volatile asm, which the compiler
 // does not move loads across, so a read inside the loop would cost one LDS
@@ -2097,11 +2358,6 @@ __device__ __forceinline__ void wide_pair(const f32x16_t &s, int q, float c, flo
     la += a + b;
 }
 
-// Pins the computation of a VGPR value before this point (an empty volatile
-// asm that reads it), so that a software-pipelined step keeps its share of
-// the VALU work between its own MFMAs.
-__device__ __forceinline__ void keep(uint32_t a) { asm volatile("" ::"v"(a)); }
-__device__ __forceinline__ void keep(float a) { asm volatile("" ::"v"(a)); }
 
 // End of block j: where P(j) overflowed, redo it against the exact row max;
 // then P(j) becomes the pending P and S(j+1) the next S.
@@ -2664,21 +2920,6 @@ fa_prefill_wide_kernel(const Params p)
 // ---------------------------------------------------------------------------
 constexpr int kPPWaves = 8;
 constexpr int kPPBN = 64;
-
-// Workgroup barrier between phases, without the memory fence of
-// __syncthreads (which would wait for the K/V copies still in flight).  The
-// empty asm statements keep the compiler from moving LDS accesses across it,
-// the scheduling fences any other instruction: without them the scheduler
-// hoisted a V phase's register-only softmax work above the barrier into the
-// M phase, where it defeats the alternation.
-__device__ __forceinline__ void pp_barrier()
-{
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-}
 
 template <int D>
 struct PPRows {
@@ -3868,7 +4109,7 @@ hipError_t launch_bwd(const BwdLaunch &L)
     p.o = static_cast<const uint16_t *>(L.o);
     p.dout = static_cast<const uint16_t *>(L.dout);
     p.lse = L.lse;
-    p.delta = L.delta;
+    p.ndelta = L.delta;
     p.lse2 = L.delta + (long)L.B * L.Hq * L.Sq;
     p.dq = static_cast<uint16_t *>(L.dq);
     p.dk = static_cast<uint16_t *>(L.dk);
