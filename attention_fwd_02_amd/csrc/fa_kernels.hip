@@ -128,6 +128,10 @@ __device__ __forceinline__ void mfma_s_drain(f32x16_t &a, f32x16_t &b)
 {
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a), "+v"(b)::"memory");
 }
+__device__ __forceinline__ void mfma_s_drain(f32x16_t &a)
+{
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a)::"memory");
+}
 
 // The same fence without the wait, for the end of the hand-ordered fast
 // block: there the last S MFMAs are followed by the block's last P V and
@@ -2882,6 +2886,339 @@ fa_prefill_wide_kernel(const Params p)
 }
 
 // ---------------------------------------------------------------------------
+// Pipelined prefill for head dim 256: NW waves x 32 query rows of one (b, hq)
+// per item, one wave per SIMD (Q and O alone take 192 registers per lane).
+// 32-key blocks; step j issues the S^T MFMAs of block j + 1 and the P V
+// MFMAs (and rounded-P row sums) of block j - 1, and computes P(j) on the
+// VALU between them, so that no MFMA waits for the softmax.  Softmax: the
+// lazy reference max of the 64-row kernel -- the exact row max of block 0,
+// moved only when a block's exact P sum exceeds kWideOverflow in some lane
+// (also inf / NaN), which then redoes that block against its exact max.
+// K and V tiles (32 keys) have rings of their own, three stages each:
+// block j's K is read in step j - 1 and its V in step j + 1.  Step j first
+// waits for K(j + 1) and V(j - 1); its barrier then releases the stages of
+// K(j) and V(j - 2), and the step copies K(j + 3) and V(j + 1) into them,
+// each two steps before it is read.  Every wave issues 2 PER_WAVE copies per
+// step; past the last block the copies read an empty range (zeros into a
+// free stage), which keeps that count fixed.
+// ---------------------------------------------------------------------------
+template <int D>
+struct PipeRows {
+    bf16x8_t qf[D / 16];   // Q fragment: B operand of the S^T MFMAs (AGPRs)
+    f32x16_t o[D / 32];    // O^T
+    f32x4_t l_acc;         // element 0: row sum of the rounded P (whole row)
+    bf16x8_t sel;          // row-sum selector operand
+    float m_ref;           // reference max (score units)
+    float mc;              // c * m_ref, 0 while m_ref = -inf
+    float l_run;           // exact row sum (this lane half)
+    float c;
+};
+
+// Step j.  Kn: K rows of block j + 1 (S^T into sn); Vp: V rows of block
+// j - 1 (P V with pp, its P; ACC = false: no such block); s: S^T(j),
+// masked, turned into pw (P(j) as bf16 words) and la (its exact sum over
+// this lane half) against the reference max.  Slot st issues S k-step st
+// and P V step st with P(j)'s elements st * 16 / QS .. between them, and
+// copy(st); the operand reads run kWidePrefetch slots ahead.
+template <int D, bool ACC, class CP>
+__device__ __forceinline__ void pipe_step(PipeRows<D> &w, const OperandOffsets<D> &off,
+                                          const char *Kn, const char *Vp, const f32x16_t &s,
+                                          f32x16_t &sn, const bf16x8_t (&pp)[2],
+                                          u32x4_t (&pw)[2], float &la, CP &&copy)
+{
+    constexpr int QS = D / 16, DB = D / 32, EPS = 16 / QS;
+    constexpr int PF = kWidePrefetch < QS ? kWidePrefetch : QS;
+    bf16x8_t ka[QS], va[QS];
+    float y[16];
+    auto rd = [&](int i) __attribute__((always_inline)) {
+        ka[i] = wide_ld_k<D>(Kn, off, i);
+        if (ACC) va[i] = wide_ld_v<D>(Vp, off, i);
+    };
+#pragma unroll
+    for (int i = 0; i < PF; ++i) rd(i);
+    __builtin_amdgcn_sched_barrier(0);
+    la = -0.0f;   // -0 + x is x: the first add folds away
+#pragma unroll
+    for (int st = 0; st < QS; ++st) {
+        const int t2 = st / DB, db = st % DB;
+        if (st == 0) mfma_s_first(sn, ka[st], w.qf[st]);
+        else mfma_s_next(sn, ka[st], w.qf[st]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (st + PF < QS) rd(st + PF);
+#pragma unroll
+        for (int i = 0; i < EPS; ++i) {
+            const int r = st * EPS + i;
+            y[r] = fast_exp2(fmaf(s[r], w.c, -w.mc));
+            keep(y[r]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (ACC) w.o[db] = mfma32(va[st], pp[t2], w.o[db]);
+        __builtin_amdgcn_sched_barrier(0);
+        copy(st);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < EPS; ++i) {
+            const int r = st * EPS + i;
+            la += y[r];
+            if (r & 1) {
+                pw[r >> 3][(r >> 1) & 3] = pack_bf16(y[r - 1], y[r]);
+                keep(pw[r >> 3][(r >> 1) & 3]);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (ACC && st == QS - 1) {
+            w.l_acc = mfma16(w.sel, pp[0], w.l_acc);
+            w.l_acc = mfma16(w.sel, pp[1], w.l_acc);
+        }
+    }
+    asm volatile("s_nop 7" : "+v"(sn)::"memory");
+}
+
+// After step j: where P(j) overflowed, redo it against the exact row max
+// (s is block j's masked S^T); then add its exact sum.
+template <int D>
+__device__ __forceinline__ void pipe_settle(PipeRows<D> &w, const f32x16_t &s, u32x4_t (&pw)[2],
+                                            float &la)
+{
+    const bool big = !(la <= kWideOverflow);   // also true for inf and NaN
+    if (__any(big)) {
+        const float mx = BlockOps<D>::rowmax(s);
+        const float m_new = fmaxf(w.m_ref, mx);
+        const float alpha = (w.m_ref == kNegInf) ? 0.0f : fast_exp2((w.m_ref - m_new) * w.c);
+        w.l_run *= alpha;
+        w.l_acc[0] *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) w.o[db][e] *= alpha;
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        w.m_ref = m_new;
+        w.mc = (m_new == kNegInf) ? 0.0f : m_new * w.c;
+        la = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) wide_pair<false>(s, q, w.c, w.mc, pw, la);
+    }
+    w.l_run += la;
+}
+
+template <int D, int NW, bool OUT_F32>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1)))
+fa_prefill_pipe_kernel(const Params p)
+{
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
+    constexpr int BN = 32;
+    constexpr int BM = 32 * NW;
+    constexpr int QS = D / 16;
+    using TL = TileLoader<D, BN, NW>;
+    using BO = BlockOps<D>;
+    constexpr int TB = TL::TILE_BYTES;
+    constexpr int NSK = 3;                 // K ring stages, then as many V stages
+    constexpr int VOFF = NSK * TB;         // V stage s sits at K stage s + VOFF
+    constexpr int LPS = 2 * TL::PER_WAVE;  // copies per wave and step
+    static_assert(LPS <= 15, "vmcnt immediate");
+    __shared__ __attribute__((aligned(1024))) char lds[2 * NSK * TB];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 31;
+    const int half = lane >> 5;
+    OperandOffsets<D> off;
+    off.init(lane);
+#pragma unroll
+    for (int db = 0; db < OperandOffsets<D>::NV; ++db)
+#pragma unroll
+        for (int sec = 0; sec < 2; ++sec) {
+            off.v[db][sec] += VOFF;
+            // keep the bias inside the register: folded back into the
+            // immediates it would overflow their 16 bits
+            asm volatile("" : "+v"(off.v[db][sec]));
+        }
+
+    // byte offset of each of this lane's K / V row copies within a tile
+    const int kstride = p.Hkv * D * 2;
+    int loff[TL::PER_WAVE];
+#pragma unroll
+    for (int i = 0; i < TL::PER_WAVE; ++i) {
+        const int row = (i * NW + wave) * TL::RPI + lane / TL::CPR;
+        loff[i] = row * kstride + (((lane % TL::CPR) ^ swz<D>(row)) * 16);
+    }
+    // scale 0: S is 0 for every pair, which a zero Q gives exactly; with
+    // c = 1 the mask's -inf then still gives P = 0
+    const bool zero_scale = p.c == 0.0f;
+    const float c = zero_scale ? 1.0f : p.c;
+
+    const int BH = p.B * p.Hq;
+    const int ND = p.domains;
+    const int x = blockIdx.x % ND;
+    const int jw = blockIdx.x / ND;
+    const int Gx = gridDim.x / ND;
+    const int BHx = BH / ND;
+    const int Nx = BHx * p.n_mblocks;
+
+    for (int it = 0; it * Gx < Nx; ++it) {
+        const int li = it * Gx + ((it & 1) ? (Gx - 1 - jw) : jw);
+        if (li >= Nx) continue;
+        const int rank = p.head_major ? li % p.n_mblocks : li / BHx;
+        const int bh = (p.head_major ? li / p.n_mblocks : li % BHx) * ND + x;
+        const int mb = p.causal ? (p.n_mblocks - 1 - rank) : rank;
+        const int b = bh / p.Hq;
+        const int hq = bh % p.Hq;
+        const int g = hq / p.group;
+        const int row0 = mb * BM;
+        const int wrow0 = row0 + wave * 32;
+        const int qi = wrow0 + col;
+        const int last_row = min(row0 + BM, p.Sq) - 1;
+        int NB = (p.Sk + BN - 1) / BN;   // blocks (= tiles) the workgroup walks
+        if (p.causal) {
+            const int hi = last_row + p.off;
+            NB = hi < 0 ? 0 : min(NB, hi / BN + 1);
+        }
+        const int lim = p.causal ? qi + p.off : 0x7fffffff;
+        const int wmin_lim = p.causal ? wrow0 + p.off : 0x7fffffff;
+        auto needs_mask = [&](int j) __attribute__((always_inline)) { return j * 32 + 32 > p.Sk || j * 32 + 31 > wmin_lim; };
+
+        const uint32_t kv_bytes = p.Sk > 0 ? (uint32_t)((p.Sk - 1) * kstride + D * 2) : 0u;
+        const u32x4_t kd = raw_desc(p.k + ((long)b * p.Sk * p.Hkv + g) * D, kv_bytes);
+        const u32x4_t vd = raw_desc(p.v + ((long)b * p.Sk * p.Hkv + g) * D, kv_bytes);
+        // copy i of this wave's share of K(t) / V(t); past the last key the
+        // byte range makes it zeros (offsets in unsigned arithmetic: the
+        // tiles past the end may lie beyond 2 GiB)
+        auto toff = [&](int t, int i) __attribute__((always_inline)) {
+            return (int)((uint32_t)t * (uint32_t)(BN * kstride) + (uint32_t)loff[i]);
+        };
+        auto copy_k = [&](int t, int i) __attribute__((always_inline)) {
+            lds_dma16(lds + (t % NSK) * TB + (i * NW + wave) * 1024, toff(t, i), kd);
+        };
+        auto copy_v = [&](int t, int i) __attribute__((always_inline)) {
+            lds_dma16(lds + VOFF + (t % NSK) * TB + (i * NW + wave) * 1024, toff(t, i), vd);
+        };
+
+        PipeRows<D> w;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) w.o[db] = f32x16_t{};
+        w.l_acc = f32x4_t{};
+        w.sel = rowsum_selector(lane);
+        w.m_ref = kNegInf;
+        w.mc = 0.0f;
+        w.l_run = 0.0f;
+        w.c = c;
+
+        if (NB > 0) {
+#pragma unroll
+            for (int i = 0; i < TL::PER_WAVE; ++i) copy_k(0, i);
+        }
+        load_q<D>(w.qf, p.q + (((long)b * p.Sq + min(qi, p.Sq - 1)) * p.Hq + hq) * D, half);
+        wait_vmem();
+        if (zero_scale) {
+#pragma unroll
+            for (int st = 0; st < QS; ++st) w.qf[st] = bf16x8_t{};
+        }
+        flip_q<D>(w.qf, p.qflip);
+        // Q fragments are only ever B operands of inline-asm MFMAs: AGPRs
+#pragma unroll
+        for (int st = 0; st < QS; ++st) asm volatile("" : "+a"(w.qf[st]));
+        __syncthreads();   // K(0) is in LDS (every wave's copies)
+
+        if (NB > 0) {
+            // the copies steps -2 and -1 would have issued: K(1) and V(-1)
+            // (nothing: an empty range into V(2)'s stage), then K(2) and V(0)
+            const u32x4_t none = raw_desc(p.v, 0u);
+#pragma unroll
+            for (int i = 0; i < TL::PER_WAVE; ++i) copy_k(1, i);
+#pragma unroll
+            for (int i = 0; i < TL::PER_WAVE; ++i)
+                lds_dma16(lds + VOFF + 2 * TB + (i * NW + wave) * 1024, loff[i], none);
+#pragma unroll
+            for (int i = 0; i < TL::PER_WAVE; ++i) copy_k(2, i);
+#pragma unroll
+            for (int i = 0; i < TL::PER_WAVE; ++i) copy_v(0, i);
+
+            f32x16_t sx, sy;                 // S^T of the even / odd block
+            bf16x8_t px[2], py[2];           // P of the even / odd block
+            u32x4_t pw[2];
+            float la;
+            // S(0) and the reference max from its exact (masked) row max
+            {
+                bf16x8_t ka[QS];
+#pragma unroll
+                for (int st = 0; st < QS; ++st) ka[st] = wide_ld_k<D>(lds, off, st);
+#pragma unroll
+                for (int st = 0; st < QS; ++st) {
+                    if (st == 0) mfma_s_first(sx, ka[st], w.qf[st]);
+                    else mfma_s_next(sx, ka[st], w.qf[st]);
+                }
+                mfma_s_drain(sx);
+                if (needs_mask(0)) BO::mask(sx, 0, half, p.Sk, lim);
+                const float mx = BO::rowmax(sx);
+                w.m_ref = mx;
+                w.mc = (mx == kNegInf) ? 0.0f : mx * c;
+            }
+            // step j: wait for K(j + 1) and V(j - 1) (the copies of step
+            // j - 1 may stay in flight), barrier, then the step with the
+            // copies of K(j + 3) and V(j + 1) in its first slots
+            auto sync = [&]() __attribute__((always_inline)) {
+                __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_s_waitcnt(0x0F70 | LPS);
+                pp_barrier();
+            };
+            auto copies = [&](int j) __attribute__((always_inline)) {
+                return [&, j](int st) __attribute__((always_inline)) {
+                    if (st < TL::PER_WAVE) copy_k(j + 3, st);
+                    else if (st < 2 * TL::PER_WAVE) copy_v(j + 1, st - TL::PER_WAVE);
+                };
+            };
+            sync();
+            pipe_step<D, false>(w, off, lds + TB, lds, sx, sy, py, pw, la, copies(0));
+            pipe_settle<D>(w, sx, pw, la);
+            px[0] = __builtin_bit_cast(bf16x8_t, pw[0]);
+            px[1] = __builtin_bit_cast(bf16x8_t, pw[1]);
+            // step j >= 1: the register sets of block j (even: sx / px, odd:
+            // sy / py) are fixed by the parity, which the loop unrolls
+            auto step = [&](auto odd, int j) __attribute__((always_inline)) {
+                constexpr bool ODD = decltype(odd)::value;
+                const char *Kn = lds + ((j + 1) % NSK) * TB;
+                const char *Vp = lds + ((j + 2) % NSK) * TB;   // + VOFF in the offsets
+                f32x16_t &s = ODD ? sy : sx;
+                f32x16_t &sn = ODD ? sx : sy;
+                bf16x8_t(&pp)[2] = ODD ? px : py;
+                bf16x8_t(&pn)[2] = ODD ? py : px;
+                if (needs_mask(j)) BO::mask(s, j * 32, half, p.Sk, lim);
+                sync();
+                pipe_step<D, true>(w, off, Kn, Vp, s, sn, pp, pw, la, copies(j));
+                pipe_settle<D>(w, s, pw, la);
+                pn[0] = __builtin_bit_cast(bf16x8_t, pw[0]);
+                pn[1] = __builtin_bit_cast(bf16x8_t, pw[1]);
+            };
+            for (int j = 1; j < NB; j += 2) {
+                step(std::true_type{}, j);
+                if (j + 1 < NB) step(std::false_type{}, j + 1);
+            }
+            // the last block's P V, once V(NB - 1) is in (the last step's
+            // copies may stay in flight)
+            sync();
+            const bf16x8_t(&pl)[2] = (NB & 1) ? px : py;
+            const char *Vl = lds + ((NB - 1) % NSK) * TB;
+#pragma unroll
+            for (int ps = 0; ps < QS; ++ps) {
+                const int t2 = ps / (D / 32), db = ps % (D / 32);
+                w.o[db] = mfma32(wide_ld_v<D>(Vl, off, ps), pl[t2], w.o[db]);
+            }
+            w.l_acc = mfma16(w.sel, pl[0], w.l_acc);
+            w.l_acc = mfma16(w.sel, pl[1], w.l_acc);
+        }
+        __syncthreads();   // every wave is done with the rings before the next item
+
+        finish_rows<D, OUT_F32>(w.o, w.m_ref, w.l_run, w.l_acc[0], c, half, p.o,
+                                (((long)b * p.Sq + qi) * p.Hq + hq) * D,
+                                p.lse ? p.lse + ((long)b * p.Hq + hq) * p.Sq + qi : nullptr,
+                                qi < p.Sq);
+    }
+#endif
+}
+
+// ---------------------------------------------------------------------------
 // Ping-pong prefill: 8 waves x 32 query rows = 256 rows of one (b, hq) per
 // item, two waves per SIMD.  Waves 0-3 (group A) and 4-7 (group B) share the
 // SIMDs pairwise and run the same two-phase loop half a period apart:
@@ -3968,7 +4305,13 @@ template <int D, int BN, int NW, int NR>
 static void launch_prefill_cfg(const Launch &L, const Params &p)
 {
     dim3 g(L.grid), blk(NW * 64);
-    if constexpr (NR == 1) {
+    if constexpr (D == 256) {
+        static_assert(BN == 32 && NR == 1, "head dim 256: the pipelined 32-key kernel");
+        if (L.o_f32)
+            hipLaunchKernelGGL((fa_prefill_pipe_kernel<D, NW, true>), g, blk, 0, L.stream, p);
+        else
+            hipLaunchKernelGGL((fa_prefill_pipe_kernel<D, NW, false>), g, blk, 0, L.stream, p);
+    } else if constexpr (NR == 1) {
         if (L.o_f32)
             hipLaunchKernelGGL((fa_prefill_kernel<D, BN, NW, true>), g, blk, 0, L.stream, p);
         else
