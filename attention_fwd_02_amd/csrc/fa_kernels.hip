@@ -3175,11 +3175,14 @@ fa_prefill_pipe_kernel(const Params p)
             px[0] = __builtin_bit_cast(bf16x8_t, pw[0]);
             px[1] = __builtin_bit_cast(bf16x8_t, pw[1]);
             // step j >= 1: the register sets of block j (even: sx / px, odd:
-            // sy / py) are fixed by the parity, which the loop unrolls
-            auto step = [&](auto odd, int j) __attribute__((always_inline)) {
+            // sy / py) follow from its parity, and its ring stage j % 3 is a
+            // compile-time constant (STAGE), so that every LDS address of
+            // the step is a lane offset plus an immediate
+            auto step = [&](auto odd, auto stage, int j) __attribute__((always_inline)) {
                 constexpr bool ODD = decltype(odd)::value;
-                const char *Kn = lds + ((j + 1) % NSK) * TB;
-                const char *Vp = lds + ((j + 2) % NSK) * TB;   // + VOFF in the offsets
+                constexpr int ST = decltype(stage)::value;
+                const char *Kn = lds + ((ST + 1) % NSK) * TB;
+                const char *Vp = lds + ((ST + NSK - 1) % NSK) * TB;   // + VOFF in the offsets
                 f32x16_t &s = ODD ? sy : sx;
                 f32x16_t &sn = ODD ? sx : sy;
                 bf16x8_t(&pp)[2] = ODD ? px : py;
@@ -3191,10 +3194,24 @@ fa_prefill_pipe_kernel(const Params p)
                 pn[0] = __builtin_bit_cast(bf16x8_t, pw[0]);
                 pn[1] = __builtin_bit_cast(bf16x8_t, pw[1]);
             };
-            for (int j = 1; j < NB; j += 2) {
-                step(std::true_type{}, j);
-                if (j + 1 < NB) step(std::false_type{}, j + 1);
+            using T = std::true_type;
+            using F = std::false_type;
+            int j = 1;
+            // six steps per trip (j = 1 mod 6), then the rest
+            for (; j + 5 < NB; j += 6) {
+                step(T{}, std::integral_constant<int, 1>{}, j);
+                step(F{}, std::integral_constant<int, 2>{}, j + 1);
+                step(T{}, std::integral_constant<int, 0>{}, j + 2);
+                step(F{}, std::integral_constant<int, 1>{}, j + 3);
+                step(T{}, std::integral_constant<int, 2>{}, j + 4);
+                step(F{}, std::integral_constant<int, 0>{}, j + 5);
             }
+            // the rest: at most five steps, from j = 1 mod 6
+            if (j < NB) step(T{}, std::integral_constant<int, 1>{}, j);
+            if (j + 1 < NB) step(F{}, std::integral_constant<int, 2>{}, j + 1);
+            if (j + 2 < NB) step(T{}, std::integral_constant<int, 0>{}, j + 2);
+            if (j + 3 < NB) step(F{}, std::integral_constant<int, 1>{}, j + 3);
+            if (j + 4 < NB) step(T{}, std::integral_constant<int, 2>{}, j + 4);
             // the last block's P V, once V(NB - 1) is in (the last step's
             // copies may stay in flight)
             sync();
