@@ -170,6 +170,24 @@ def test_rows64_overflow_redo_in_diagonal_tile(ops, oracle, env_vars):
     full_check(ops, oracle, q, k, v, True, 0.5, out="f32", label="redo in the diagonal tile")
 
 
+@pytest.mark.parametrize("scale", [-0.3, 0.0, 2.5])
+def test_d256_scales_and_overflow_redo(ops, oracle, scale):
+    # head dim 256 (the pipelined 32-row kernel): hot rows and a large |scale|
+    # make P pass the block-sum bound, which redoes the block against its
+    # exact row max; scale 0 runs as a zero Q with c = 1
+    q, k, v = random_qkv(1, 4, 2, 700, 900, 256, seed=37)
+    q[:, ::7] *= 8.0
+    full_check(ops, oracle, q, k, v, True, scale, out="f32", label=f"d256 scale={scale}")
+
+
+def test_d256_overflow_redo_in_diagonal_block(ops, oracle):
+    # keys from 512 on are 6x larger: rows 512.. first meet them in their
+    # diagonal block, which is masked and redone
+    q, k, v = random_qkv(1, 2, 1, 640, 640, 256, seed=41)
+    k[:, 512:] *= 6.0
+    full_check(ops, oracle, q, k, v, True, 0.5, out="f32", label="d256 redo in the diagonal block")
+
+
 def test_item_order_does_not_change_results(ops, env_vars):
     # head-major and rank-major walks run the same per-item arithmetic
     q, k, v = random_qkv(2, 8, 8, 1000, 1000, 128, seed=30)
