@@ -18,8 +18,9 @@ reports, for every inline-assembly MFMA:
   passed: an XDL MFMA of N passes needs N + 4 wait states on gfx950 before a
   VALU or memory instruction may read or overwrite its result (the rule
   LLVM's hazard recognizer applies to the MFMAs it emits itself); the scan
-  asks N + 5, one more, for the two inline-asm forms here, 8-pass
-  v_mfma_f32_32x32x16_bf16 (13) and 4-pass v_mfma_f32_16x16x32_bf16 (9), and
+  asks N + 5, one more, for the inline-asm forms here, 8-pass
+  v_mfma_f32_32x32x16_bf16 (13), 4-pass v_mfma_f32_16x16x32_bf16 (9) and
+  16-pass v_mfma_f32_32x32x64_f8f6f4 on FP8 operands (21), and
   ``result_wait`` (18) for any other;
 * any compiler-emitted VALU instruction that writes one of the MFMA's source
   registers fewer than ``operand_wait`` wait states before it (2 are needed).
@@ -105,7 +106,8 @@ def _wait_states(text: str) -> int:
 
 
 # inline-asm MFMA opcode -> wait states before its result may be accessed
-RESULT_WAIT = {"v_mfma_f32_32x32x16_bf16": 8 + 5, "v_mfma_f32_16x16x32_bf16": 4 + 5}
+RESULT_WAIT = {"v_mfma_f32_32x32x16_bf16": 8 + 5, "v_mfma_f32_16x16x32_bf16": 4 + 5,
+               "v_mfma_f32_32x32x64_f8f6f4": 16 + 5}
 
 
 def scan(asm: str, result_wait: int = 18, operand_wait: int = 2) -> list:

@@ -694,9 +694,12 @@ fa_status fa_fwd_fp8(const void *q, const void *k, const void *v, void *o, float
     if (st != FA_OK) return st;
 
     // 32 rows per wave, 64-key tiles, 8 waves (two per SIMD, 256 registers
-    // each); FA_FP8_NW=4 selects one wave per SIMD (measured 1.7x slower on
-    // the causal S=4096 shape: no second wave fills the first's stalls)
+    // each): the pipelined kernel.  FA_FP8_PIPE=0 selects the earlier
+    // unpipelined one, and FA_FP8_NW=4 its one-wave-per-SIMD form (measured
+    // 1.7x slower on the causal S=4096 shape: no second wave fills the first's
+    // stalls).
     const int nw = env_int("FA_FP8_NW", 8) == 4 ? 4 : 8;
+    const int pipe = (nw == 8 && env_int("FA_FP8_PIPE", 1) != 0) ? 1 : 0;
     const int bm = 32 * nw;
     const int64_t items = (int64_t)B * Hq * ((Sq + bm - 1) / bm);
     if (items >= (int64_t(1) << 31)) return fail(FA_ERR_UNSUPPORTED, "too many work items");
@@ -717,12 +720,13 @@ fa_status fa_fwd_fp8(const void *q, const void *k, const void *v, void *o, float
     L.prefill_nw = nw;
     L.prefill_nr = 1;
     L.prefill_pp = 0;
+    L.fp8_pipe = pipe;
     L.head_major = env_int("FA_HEAD_MAJOR", causal ? 1 : 0) != 0;
     L.stream = stream;
     if (log_enabled())
         fprintf(stderr, "[fa] path=fp8-prefill B=%d Hq=%d Hkv=%d Sq=%d Sk=%d D=%d causal=%d "
-                "waves=%d grid=%lld items=%lld\n", B, Hq, Hkv, Sq, Sk, D, causal, nw,
-                (long long)grid, (long long)items);
+                "waves=%d pipe=%d grid=%lld items=%lld\n", B, Hq, Hkv, Sq, Sk, D, causal, nw,
+                pipe, (long long)grid, (long long)items);
     hipError_t e = fa::launch_prefill_fp8(L, v_descale);
     if (e != hipSuccess) return fail(FA_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
     return FA_OK;

@@ -3236,6 +3236,484 @@ fa_prefill_pipe_kernel(const Params p)
 }
 
 // ---------------------------------------------------------------------------
+// Pipelined FP8 prefill (D = 128): 8 waves x 32 query rows = 256 rows of one
+// (b, hq) per item, two waves per SIMD.  The operands are those of
+// fa_prefill_fp8_kernel: E4M3 tiles with rows of D bytes, the 32x32x64 FP8
+// MFMA, P rounded to E4M3, V^T through the 8-bit transposing read.  The steps
+// are those of fa_prefill_pipe_kernel, on blocks of 64 keys (one FP8 MFMA per
+// 32 head dims of P V): step j issues the four S^T MFMAs of block j + 1 and
+// the four P V MFMAs of block j - 1 (then its rounded-P row sum) and computes
+// P(j) on the VALU between them, a quarter per MFMA pair, so that neither
+// unit waits for the other's results.
+// Softmax: the lazy reference max -- the exact row max of block 0, moved only
+// when a block's exact P sum passes kFp8PipeOverflow = 2^8 in some lane (also
+// inf / NaN), which redoes that block against its exact row max.  Each P is
+// then below 2^8, inside E4M3's largest value 448.
+// K and V have three-stage rings of their own (8 KiB per stage): step j waits
+// for K(j + 1) and V(j - 1), and after its barrier copies K(j + 3) and
+// V(j + 1) into the stages of K(j) and V(j - 2) from inside its first slots;
+// past the last block the copies read an empty range, which keeps the count
+// of copies per step fixed for vmcnt.
+// Registers: two waves per SIMD leave 256 per lane, which the compiler splits
+// evenly between VGPRs and AGPRs as soon as a kernel uses AGPRs at all, and
+// 128 VGPRs do not hold S, P and the operands.  So every MFMA here is inline
+// asm with VGPR operands and accumulators, and the kernel uses no AGPR.  The
+// S^T accumulators are fenced at the end of each step (the VALU reads them in
+// the next one); O and the row sums are read only by the later MFMAs of their
+// chains, which the hardware orders, or after fp8_drain_o.  The build's scan
+// of the generated code checks the wait states around each of them.
+// ---------------------------------------------------------------------------
+constexpr float kFp8PipeOverflow = 256.0f;
+constexpr int kFp8PipeWaves = 8;
+
+// The FP8 MFMA (16 passes): S^T with a VGPR accumulator ...
+__device__ __forceinline__ void mfma_s8_first(f32x16_t &d, i32x8_t a, i32x8_t b)
+{
+    asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_s8_next(f32x16_t &d, i32x8_t a, i32x8_t b)
+{
+    asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+// ... O^T += V^T P^T ("accumulate-only": the build's scan follows a branch
+// past it instead of reporting it) ...
+__device__ __forceinline__ void mfma_o8(f32x16_t &o, i32x8_t a, i32x8_t b)
+{
+    asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0 ; accumulate-only"
+                 : "+v"(o)
+                 : "v"(a), "v"(b));
+}
+// ... and the row sums of the rounded P against the all-ones A operand,
+// which the compiler may rematerialise right before it: two wait states lead
+// (a VALU write of an MFMA source needs two).
+__device__ __forceinline__ void mfma_rowsum8(f32x16_t &l, i32x8_t ones, i32x8_t p)
+{
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0 ; accumulate-only"
+                 : "+v"(l)
+                 : "v"(ones), "v"(p));
+}
+
+__device__ __forceinline__ i32x8_t fp8_ones()
+{
+    constexpr int kOnes = 0x38383838;   // E4M3 1.0 in every byte
+    return (i32x8_t){kOnes, kOnes, kOnes, kOnes, kOnes, kOnes, kOnes, kOnes};
+}
+
+template <int D>
+struct Fp8PipeRows {
+    i32x8_t qf[D / 64];   // Q fragments: B operands of the S^T MFMAs
+    f32x16_t o[D / 32];   // O^T
+    f32x16_t l_acc;       // element 0: row sum of the rounded P (whole row)
+    float m_ref;          // reference max (score units)
+    float mc;             // c * m_ref, 0 while m_ref = -inf
+    float l_run;          // exact row sum (this lane half)
+    float c;
+    i32x8_t ones;         // E4M3 1.0 in every byte: A operand of the row sums
+};
+
+// The wait for the P V and row-sum MFMAs before the VALU reads O or the row
+// sums: 24 wait states (the 16-pass MFMA needs 21), with the accumulators as
+// operands, so that nothing the compiler emits can touch them before it.
+template <int D>
+__device__ __forceinline__ void fp8_drain_o(Fp8PipeRows<D> &w)
+{
+    static_assert(D / 32 == 4, "four O accumulators");
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+v"(w.o[0]), "+v"(w.o[1]), "+v"(w.o[2]), "+v"(w.o[3]), "+v"(w.l_acc)::"memory");
+}
+
+// A operand of S^T MFMA m of a 64-key block (K rows at Kblk): key half
+// m / KS, k-step m % KS.
+template <int D>
+__device__ __forceinline__ i32x8_t fp8_ld_k(const char *Kblk, const Fp8Offsets<D> &off, int m)
+{
+    constexpr int KS = D / 64;
+    const int kb = m / KS, st = m % KS;
+    const u32x4_t lo = *reinterpret_cast<const u32x4_t *>(Kblk + kb * 32 * D + off.k[st][0]);
+    const u32x4_t hi = *reinterpret_cast<const u32x4_t *>(Kblk + kb * 32 * D + off.k[st][1]);
+    return (i32x8_t){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                     (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+
+// A operand V^T of P V MFMA db (head dims 32 db .. 32 db + 31, the block's
+// 64 keys in the byte order of P): four 8-bit transposing reads.
+template <int D>
+__device__ __forceinline__ i32x8_t fp8_ld_v(const char *Vblk, const Fp8Offsets<D> &off, int db)
+{
+    i32x8_t a;
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4) {
+        const i32x2_t w =
+            __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t *)(Vblk + off.vofs(db, t4)));
+        a[2 * t4] = w[0];
+        a[2 * t4 + 1] = w[1];
+    }
+    return a;
+}
+
+// y[0..3] as E4M3 bytes (round to nearest even), byte order of the P V
+// MFMA's B operand.  Both halves of the word are written, so the register
+// the first conversion merges into needs no value: an empty asm statement
+// hands one over, which spares the compiler a move that zeroes or copies it.
+__device__ __forceinline__ int fp8_word(const float *y)
+{
+    int old;
+    asm volatile("" : "=v"(old));
+    const int word = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], old, false);
+    return __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], word, true);
+}
+
+// Step j.  Kn: K rows of block j + 1 (S^T into sn); Vp: V rows of block
+// j - 1 (P V with pp, its P; ACC = false: no such block); s: S^T(j), masked,
+// turned into pw (P(j) as E4M3 bytes, byte 16 kb + r of the B operand) and la
+// (its exact sum over this lane half) against the reference max.  Slot m
+// issues S MFMA m and P V MFMA m with P(j)'s elements 8m .. 8m + 7 between
+// them, and copy(m); each slot's operands are read one slot ahead.
+template <int D, bool ACC, class CP>
+__device__ __forceinline__ void fp8_pipe_step(Fp8PipeRows<D> &w, const Fp8Offsets<D> &off,
+                                              const char *Kn, const char *Vp,
+                                              const f32x16_t (&s)[2], f32x16_t (&sn)[2],
+                                              const i32x8_t &pp, i32x8_t &pw, float &la, CP &&copy)
+{
+    constexpr int KS = D / 64, DB = D / 32, NM = 2 * KS;
+    static_assert(NM == DB, "one S^T and one P V MFMA per slot");
+    i32x8_t ka[NM], va[DB];
+    float y[32];
+    auto rd = [&](int i) __attribute__((always_inline)) {
+        ka[i] = fp8_ld_k<D>(Kn, off, i);
+        if (ACC) va[i] = fp8_ld_v<D>(Vp, off, i);
+    };
+    rd(0);
+    __builtin_amdgcn_sched_barrier(0);
+    la = -0.0f;   // -0 + x is x: the first add folds away
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+        const int kb = m / KS, st = m % KS;
+        if (st == 0) mfma_s8_first(sn[kb], ka[m], w.qf[st]);
+        else mfma_s8_next(sn[kb], ka[m], w.qf[st]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (m + 1 < NM) rd(m + 1);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int e = 8 * m + i;
+            y[e] = fast_exp2(fmaf(s[e >> 4][e & 15], w.c, -w.mc));
+            keep(y[e]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (ACC) mfma_o8(w.o[m], va[m], pp);
+        __builtin_amdgcn_sched_barrier(0);
+        copy(m);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int e = 8 * m + 4 * h;
+            pw[2 * m + h] = fp8_word(&y[e]);
+            keep((uint32_t)pw[2 * m + h]);
+            la += (y[e] + y[e + 1]) + (y[e + 2] + y[e + 3]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if (ACC) mfma_rowsum8(w.l_acc, w.ones, pp);
+    asm volatile("s_nop 7" : "+v"(sn[0]), "+v"(sn[1])::"memory");
+}
+
+// After step j: where P(j) overflowed, redo it against the exact row max
+// (s is block j's masked S^T); then add its exact sum.
+template <int D>
+__device__ __forceinline__ void fp8_pipe_settle(Fp8PipeRows<D> &w, const f32x16_t (&s)[2],
+                                                i32x8_t &pw, float &la)
+{
+    const bool big = !(la <= kFp8PipeOverflow);   // also true for inf and NaN
+    if (__any(big)) {
+        fp8_drain_o(w);
+        float mx = kNegInf;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][e]);
+        mx = max_halves(mx);
+        const float m_new = fmaxf(w.m_ref, mx);
+        const float alpha = (w.m_ref == kNegInf) ? 0.0f : fast_exp2((w.m_ref - m_new) * w.c);
+        w.l_run *= alpha;
+        w.l_acc[0] *= alpha;   // only element 0 of the row-sum accumulator is read
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) w.o[db][e] *= alpha;
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        w.m_ref = m_new;
+        w.mc = (m_new == kNegInf) ? 0.0f : m_new * w.c;
+        float y[32];
+#pragma unroll
+        for (int e = 0; e < 32; ++e) y[e] = fast_exp2(fmaf(s[e >> 4][e & 15], w.c, -w.mc));
+        la = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            pw[q] = fp8_word(&y[4 * q]);
+            la += (y[4 * q] + y[4 * q + 1]) + (y[4 * q + 2] + y[4 * q + 3]);
+        }
+    }
+    w.l_run += la;
+}
+
+template <int D, bool OUT_F32>
+__global__ void __launch_bounds__(kFp8PipeWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
+fa_prefill_fp8_pipe_kernel(const Params p, const float v_descale)
+{
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
+    static_assert(D == 128, "the FP8 operand offsets assume head dim 128");
+    constexpr int NW = kFp8PipeWaves;
+    constexpr int BN = 64;
+    constexpr int BM = 32 * NW;
+    constexpr int KS = D / 64;
+    constexpr int RB = D;                   // bytes per tile row
+    constexpr int CPR = RB / 16;            // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;           // rows per copy instruction
+    constexpr int PER_WAVE = BN / RPI / NW; // copies per wave, tensor and tile
+    static_assert(PER_WAVE >= 1 && PER_WAVE * RPI * NW == BN, "copies split evenly");
+    constexpr int TB = BN * RB;             // 8 KiB per tile
+    constexpr int NSK = 3;                  // K ring stages, then as many V stages
+    constexpr int VOFF = NSK * TB;          // V stage s sits at K stage s + VOFF
+    constexpr int LPS = 2 * PER_WAVE;       // copies per wave and step
+    static_assert(LPS <= 2 * KS, "the copies go out in the step's first slots");
+    __shared__ __attribute__((aligned(1024))) char lds[2 * NSK * TB];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 31;
+    const int half = lane >> 5;
+    Fp8Offsets<D> off;
+    off.init(lane);
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4) off.vb[t4] += VOFF;
+
+    const uint8_t *q8 = reinterpret_cast<const uint8_t *>(p.q);
+    const uint8_t *k8 = reinterpret_cast<const uint8_t *>(p.k);
+    const uint8_t *v8 = reinterpret_cast<const uint8_t *>(p.v);
+
+    // byte offset of each of this lane's K / V row copies within a tile
+    const int kstride = p.Hkv * D;
+    int loff[PER_WAVE];
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+        const int row = (i * NW + wave) * RPI + lane / CPR;
+        loff[i] = row * kstride + (((lane % CPR) ^ swz_fp8(row)) * 16);
+    }
+    // scale 0: S is 0 for every pair, which a zero Q gives exactly; with
+    // c = 1 the mask's -inf then still gives P = 0
+    const bool zero_scale = p.c == 0.0f;
+    const float c = zero_scale ? 1.0f : p.c;
+
+    const int BH = p.B * p.Hq;
+    const int ND = p.domains;
+    const int x = blockIdx.x % ND;
+    const int jw = blockIdx.x / ND;
+    const int Gx = gridDim.x / ND;
+    const int BHx = BH / ND;
+    const int Nx = BHx * p.n_mblocks;
+
+    for (int it = 0; it * Gx < Nx; ++it) {
+        const int li = it * Gx + ((it & 1) ? (Gx - 1 - jw) : jw);
+        if (li >= Nx) continue;
+        const int rank = p.head_major ? li % p.n_mblocks : li / BHx;
+        const int bh = (p.head_major ? li / p.n_mblocks : li % BHx) * ND + x;
+        const int mb = p.causal ? (p.n_mblocks - 1 - rank) : rank;
+        const int b = bh / p.Hq;
+        const int hq = bh % p.Hq;
+        const int g = hq / p.group;
+        const int row0 = mb * BM;
+        const int wrow0 = row0 + wave * 32;
+        const int qi = wrow0 + col;
+        const int last_row = min(row0 + BM, p.Sq) - 1;
+        int NB = (p.Sk + BN - 1) / BN;   // blocks (= tiles) the workgroup walks
+        if (p.causal) {
+            const int hi = last_row + p.off;
+            NB = hi < 0 ? 0 : min(NB, hi / BN + 1);
+        }
+        const int lim = p.causal ? qi + p.off : 0x7fffffff;
+        const int wmin_lim = p.causal ? wrow0 + p.off : 0x7fffffff;
+        auto needs_mask = [&](int j) __attribute__((always_inline)) {
+            return j * BN + BN > p.Sk || j * BN + BN - 1 > wmin_lim;
+        };
+        auto mask = [&](f32x16_t (&s)[2], int j) __attribute__((always_inline)) {
+            BlockOps<64>::mask(s[0], j * BN, half, p.Sk, lim);
+            BlockOps<64>::mask(s[1], j * BN + 32, half, p.Sk, lim);
+        };
+
+        const uint32_t kv_bytes = p.Sk > 0 ? (uint32_t)((p.Sk - 1) * kstride + D) : 0u;
+        const u32x4_t kd = raw_desc(k8 + ((long)b * p.Sk * p.Hkv + g) * D, kv_bytes);
+        const u32x4_t vd = raw_desc(v8 + ((long)b * p.Sk * p.Hkv + g) * D, kv_bytes);
+        // copy i of this wave's share of K(t) / V(t); past the last key the
+        // byte range makes it zeros (offsets in unsigned arithmetic: the
+        // tiles past the end may lie beyond 2 GiB)
+        auto toff = [&](int t, int i) __attribute__((always_inline)) {
+            return (int)((uint32_t)t * (uint32_t)(BN * kstride) + (uint32_t)loff[i]);
+        };
+        auto copy_k = [&](int t, int i) __attribute__((always_inline)) {
+            lds_dma16(lds + (t % NSK) * TB + (i * NW + wave) * 1024, toff(t, i), kd);
+        };
+        auto copy_v = [&](int t, int i) __attribute__((always_inline)) {
+            lds_dma16(lds + VOFF + (t % NSK) * TB + (i * NW + wave) * 1024, toff(t, i), vd);
+        };
+
+        Fp8PipeRows<D> w;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) w.o[db] = f32x16_t{};
+        w.l_acc = f32x16_t{};
+        w.m_ref = kNegInf;
+        w.mc = 0.0f;
+        w.l_run = 0.0f;
+        w.c = c;
+        w.ones = fp8_ones();
+
+        if (NB > 0) {
+#pragma unroll
+            for (int i = 0; i < PER_WAVE; ++i) copy_k(0, i);
+        }
+        {
+            // this lane's Q bytes: k-step st, dims 64 st + 32 half .. + 31
+            const uint8_t *qrow = q8 + (((long)b * p.Sq + min(qi, p.Sq - 1)) * p.Hq + hq) * D;
+#pragma unroll
+            for (int st = 0; st < KS; ++st) {
+                const u32x4_t lo =
+                    ld16(reinterpret_cast<const uint16_t *>(qrow + 64 * st + 32 * half));
+                const u32x4_t hi =
+                    ld16(reinterpret_cast<const uint16_t *>(qrow + 64 * st + 32 * half + 16));
+                w.qf[st] = (i32x8_t){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                     (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+            }
+        }
+        wait_vmem();
+#pragma unroll
+        for (int st = 0; st < KS; ++st) {
+            if (zero_scale) w.qf[st] = i32x8_t{};
+            // a negative scale negates Q exactly (E4M3 sign bits)
+            if (p.qflip) w.qf[st] ^= (int)0x80808080u;
+            asm volatile("" : "+v"(w.qf[st]));
+        }
+        __syncthreads();   // K(0) is in LDS (every wave's copies)
+
+        if (NB > 0) {
+            // the copies steps -2 and -1 would have issued: K(1) and V(-1)
+            // (nothing: an empty range into V(2)'s stage), then K(2) and V(0)
+            const u32x4_t none = raw_desc(v8, 0u);
+#pragma unroll
+            for (int i = 0; i < PER_WAVE; ++i) copy_k(1, i);
+#pragma unroll
+            for (int i = 0; i < PER_WAVE; ++i)
+                lds_dma16(lds + VOFF + 2 * TB + (i * NW + wave) * 1024, loff[i], none);
+#pragma unroll
+            for (int i = 0; i < PER_WAVE; ++i) copy_k(2, i);
+#pragma unroll
+            for (int i = 0; i < PER_WAVE; ++i) copy_v(0, i);
+
+            f32x16_t sx[2], sy[2];   // S^T of the even / odd block
+            i32x8_t px, py;          // P of the even / odd block
+            i32x8_t pw;
+            float la;
+            // S(0) and the reference max from its exact (masked) row max
+            {
+                i32x8_t ka[2 * KS];
+#pragma unroll
+                for (int m = 0; m < 2 * KS; ++m) ka[m] = fp8_ld_k<D>(lds, off, m);
+#pragma unroll
+                for (int m = 0; m < 2 * KS; ++m) {
+                    const int kb = m / KS, st = m % KS;
+                    if (st == 0) mfma_s8_first(sx[kb], ka[m], w.qf[st]);
+                    else mfma_s8_next(sx[kb], ka[m], w.qf[st]);
+                }
+                mfma_s_drain(sx[0], sx[1]);
+                if (needs_mask(0)) mask(sx, 0);
+                float mx = kNegInf;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sx[kb][e]);
+                mx = max_halves(mx);
+                w.m_ref = mx;
+                w.mc = (mx == kNegInf) ? 0.0f : mx * c;
+            }
+            // step j: wait for K(j + 1) and V(j - 1) (the copies of step
+            // j - 1 may stay in flight), barrier, then the step with the
+            // copies of K(j + 3) and V(j + 1) in its first slots
+            auto sync = [&]() __attribute__((always_inline)) {
+                __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_s_waitcnt(0x0F70 | LPS);
+                pp_barrier();
+            };
+            auto copies = [&](int j) __attribute__((always_inline)) {
+                return [&, j](int m) __attribute__((always_inline)) {
+                    if (m < PER_WAVE) copy_k(j + 3, m);
+                    else if (m < 2 * PER_WAVE) copy_v(j + 1, m - PER_WAVE);
+                };
+            };
+            sync();
+            fp8_pipe_step<D, false>(w, off, lds + TB, lds, sx, sy, py, pw, la, copies(0));
+            fp8_pipe_settle<D>(w, sx, pw, la);
+            px = pw;
+            // step j >= 1: the register sets of block j (even: sx / px, odd:
+            // sy / py) follow from its parity, and its ring stage j % 3 is a
+            // compile-time constant, so that every LDS address of the step
+            // is a lane offset plus an immediate
+            auto step = [&](auto odd, auto stage, int j) __attribute__((always_inline)) {
+                constexpr bool ODD = decltype(odd)::value;
+                constexpr int ST = decltype(stage)::value;
+                const char *Kn = lds + ((ST + 1) % NSK) * TB;
+                const char *Vp = lds + ((ST + NSK - 1) % NSK) * TB;   // + VOFF in the offsets
+                f32x16_t(&s)[2] = ODD ? sy : sx;
+                f32x16_t(&sn)[2] = ODD ? sx : sy;
+                i32x8_t &pp = ODD ? px : py;
+                i32x8_t &pn = ODD ? py : px;
+                if (needs_mask(j)) mask(s, j);
+                sync();
+                fp8_pipe_step<D, true>(w, off, Kn, Vp, s, sn, pp, pw, la, copies(j));
+                fp8_pipe_settle<D>(w, s, pw, la);
+                pn = pw;
+            };
+            using T = std::true_type;
+            using F = std::false_type;
+            int j = 1;
+            // six steps per trip (j = 1 mod 6), then the rest
+            for (; j + 5 < NB; j += 6) {
+                step(T{}, std::integral_constant<int, 1>{}, j);
+                step(F{}, std::integral_constant<int, 2>{}, j + 1);
+                step(T{}, std::integral_constant<int, 0>{}, j + 2);
+                step(F{}, std::integral_constant<int, 1>{}, j + 3);
+                step(T{}, std::integral_constant<int, 2>{}, j + 4);
+                step(F{}, std::integral_constant<int, 0>{}, j + 5);
+            }
+            // the rest: at most five steps, from j = 1 mod 6
+            if (j < NB) step(T{}, std::integral_constant<int, 1>{}, j);
+            if (j + 1 < NB) step(F{}, std::integral_constant<int, 2>{}, j + 1);
+            if (j + 2 < NB) step(T{}, std::integral_constant<int, 0>{}, j + 2);
+            if (j + 3 < NB) step(F{}, std::integral_constant<int, 1>{}, j + 3);
+            if (j + 4 < NB) step(T{}, std::integral_constant<int, 2>{}, j + 4);
+            // the last block's P V, once V(NB - 1) is in (the last step's
+            // copies may stay in flight)
+            sync();
+            i32x8_t pl = (NB & 1) ? px : py;
+            // the select is a VALU write of an MFMA operand: two wait states
+            asm volatile("s_nop 1" : "+v"(pl));
+            const char *Vl = lds + ((NB - 1) % NSK) * TB;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) mfma_o8(w.o[db], fp8_ld_v<D>(Vl, off, db), pl);
+            mfma_rowsum8(w.l_acc, w.ones, pl);
+        }
+        fp8_drain_o(w);
+        __syncthreads();   // every wave is done with the rings before the next item
+
+        // O = v_descale * O / l: the descale folds into the normaliser
+        finish_rows<D, OUT_F32>(w.o, w.m_ref, w.l_run, w.l_acc[0] / v_descale, c, half, p.o,
+                                (((long)b * p.Sq + qi) * p.Hq + hq) * D,
+                                p.lse ? p.lse + ((long)b * p.Hq + hq) * p.Sq + qi : nullptr,
+                                qi < p.Sq);
+    }
+#endif
+}
+
+// ---------------------------------------------------------------------------
 // Ping-pong prefill: 8 waves x 32 query rows = 256 rows of one (b, hq) per
 // item, two waves per SIMD.  Waves 0-3 (group A) and 4-7 (group B) share the
 // SIMDs pairwise and run the same two-phase loop half a period apart:
@@ -4449,6 +4927,17 @@ hipError_t launch_prefill_fp8(const Launch &L, float v_descale)
         hipLaunchKernelGGL((fa_prefill_fp8_kernel<128, decltype(nw)::value, decltype(of)::value>),
                            g, blk, 0, L.stream, p, v_descale);
     };
+    if (L.fp8_pipe) {
+        // the pipelined kernel: 8 waves x 32 rows, two waves per SIMD
+        if (L.prefill_nw != kFp8PipeWaves) return hipErrorInvalidValue;
+        if (L.o_f32)
+            hipLaunchKernelGGL((fa_prefill_fp8_pipe_kernel<128, true>), g, blk, 0, L.stream, p,
+                               v_descale);
+        else
+            hipLaunchKernelGGL((fa_prefill_fp8_pipe_kernel<128, false>), g, blk, 0, L.stream, p,
+                               v_descale);
+        return hipGetLastError();
+    }
     if (L.prefill_nw == 8) {
         if (L.o_f32) go(std::integral_constant<int, 8>{}, std::true_type{});
         else go(std::integral_constant<int, 8>{}, std::false_type{});

@@ -63,6 +63,7 @@ struct Launch {
     int prefill_nr;      // prefill: 32-row column blocks per wave
     int head_major;      // prefill: item order (1: head by head, 0: rank by rank)
     int prefill_pp;      // prefill: 0, or the ring depth (4 or 5) of the ping-pong kernel
+    int fp8_pipe = 0;    // FP8 prefill: 1 = the pipelined kernel (8 waves)
     hipStream_t stream;
 };
 
@@ -93,7 +94,9 @@ hipError_t launch_decode_paged(const Launch &L, const PagedLaunch &P);
 
 // FP8 E4M3 prefill: L.q/k/v hold E4M3 codes, L.scale already includes the
 // q and k descales; O is multiplied by v_descale.  64-key tiles, 32 rows per
-// wave, L.prefill_nw waves (4 or 8) per workgroup, L.grid workgroups.
+// wave, L.prefill_nw waves (4 or 8) per workgroup, L.grid workgroups.  With
+// L.fp8_pipe the pipelined kernel runs instead: 8 waves (two per SIMD) x 32
+// rows, separate K and V rings (48 KiB).
 constexpr int kFp8BN = 64;
 inline int fp8_lds_bytes(int D) { return kPrefillStages * 2 * kFp8BN * D; }
 hipError_t launch_prefill_fp8(const Launch &L, float v_descale);

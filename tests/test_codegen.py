@@ -53,6 +53,16 @@ def test_access_after_the_wait_passes():
     assert asm_check.scan(asm) == []
 
 
+def test_fp8_mfma_needs_21_wait_states():
+    # the 16-pass FP8 MFMA: 20 wait states are too few, 21 are enough
+    fp8 = "v_mfma_f32_32x32x64_f8f6f4 v[32:47], v[0:7], v[8:15], v[32:47]"
+    early = listing(fp8, "s_nop 7\n\ts_nop 7\n\ts_nop 3", "v_mov_b32_e32 v0, v40",
+                    asm_idx=(0,))
+    assert "accessed 20 wait states later" in asm_check.scan(early)[0]
+    ok = listing(fp8, "s_nop 7\n\ts_nop 7\n\ts_nop 4", "v_mov_b32_e32 v0, v40", asm_idx=(0,))
+    assert asm_check.scan(ok) == []
+
+
 def test_branch_before_wait_is_found():
     asm = listing(MFMA, "s_cbranch_scc1 .LBB0_3", asm_idx=(0,))
     assert "control flow" in asm_check.scan(asm)[0]

@@ -142,6 +142,17 @@ def test_fp8_scale_sign_and_zero(ops, oracle, scale):
               label=f"scale={scale}")
 
 
+@pytest.mark.parametrize("shape", [SHAPES[1], SHAPES[3], SHAPES[4]],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_fp8_unpipelined_kernel(ops, oracle, monkeypatch, shape):
+    # the earlier, unpipelined 8-wave kernel (selected by FA_FP8_PIPE=0)
+    monkeypatch.setenv("FA_FP8_PIPE", "0")
+    B, Hq, Hkv, Sq, Sk, causal, out = shape
+    q8, k8, v8, dq, dk, dv = random_fp8(B, Hq, Hkv, Sq, Sk, 128, seed=Sq * 5 + Sk)
+    check_fp8(ops, oracle, q8, k8, v8, causal, 1.0 / math.sqrt(128), dq, dk, dv, out=out,
+              label=f"unpipelined {shape}")
+
+
 def test_fp8_waves4_config(ops, oracle, monkeypatch):
     # the 4-wave configuration (one wave per SIMD), forced
     monkeypatch.setenv("FA_FP8_NW", "4")

@@ -107,6 +107,7 @@ CASES = {
     "decode_split_d256": ({}, lambda: _dense(4, 8, 2, 1, 3000, 256, False, splits=2)),
     "decode_paged_ragged": ({}, _paged),
     "fp8_prefill_causal": ({}, lambda: _fp8(True)),
+    "fp8_prefill_unpipelined": ({"FA_FP8_PIPE": "0"}, lambda: _fp8(True)),
     "backward": ({}, _bwd),
 }
 
