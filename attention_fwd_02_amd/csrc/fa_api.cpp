@@ -141,6 +141,7 @@ struct Plan {
     int grid = 0, items = 0;
     int prefill_bn = 0, prefill_nw = 0, prefill_nr = 1;
     int prefill_pp = 0;  // ring depth of the ping-pong kernel, 0 = not used
+    int prefill_pipe = 0;  // the pipelined 32-key kernel at head dim 128 (8 waves)
     int head_major = 0;
     size_t ws_bytes = 0;
     size_t part_rows = 0;   // split partial rows in the workspace
@@ -206,6 +207,7 @@ fa_status make_plan(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal, i
         // leave CUs idle.  FA_PREFILL_BN / FA_PREFILL_NW / FA_PREFILL_NR
         // override (for measurements).
         int bn = 64, nw = 8, nr = 1;
+        int pipe = 0;
         const int64_t m8 = (Sq + 255) / 256;
         if (D == 256) {
             // 32-key tiles (16 KiB per tile at D = 256: the three-stage ring
@@ -219,6 +221,14 @@ fa_status make_plan(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal, i
             // still fewer 128-row items than CUs: 64-row items (two waves),
             // so that every CU's LDS and L1 serve the same waves
             if ((int64_t)B * Hq * ((Sq + 127) / 128) < cus) nw = 2;
+        } else if (D == 128 && env_int("FA_PREFILL_PIPE", 1) != 0) {
+            // head dim 128: the pipelined 32-key kernel, 8 waves x 32 rows
+            // (two waves per SIMD).  Measured against the 64-row kernel
+            // (median of 30 interleaved calls): causal S = 1024 -10 %, 2048
+            // -9 %, 4096 -4 %, 8192 -2 %, non-causal S = 4096 -4 %, GQA
+            // S = 16384 equal.  FA_PREFILL_PIPE=0 restores the choice below.
+            pipe = 1;
+            bn = 32;
         } else if (!causal || Sq >= 2048) {
             // 64 rows per wave: faster wherever most tiles take its pipelined
             // body (non-causal, or causal rows of 2048 and more); shorter
@@ -232,6 +242,7 @@ fa_status make_plan(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal, i
             bn = ebn;
             nw = enw;
             nr = enr;
+            pipe = 0;
         }
         // the ping-pong kernel (8 waves x 32 rows, two per SIMD in opposite
         // MFMA / softmax phases, D = 64 or 128) only on request:
@@ -244,7 +255,9 @@ fa_status make_plan(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal, i
             bn = fa::kPrefillPPBN;
             nw = fa::kPrefillPPWaves;
             nr = 1;
+            pipe = 0;
         }
+        pl.prefill_pipe = pipe;
         const int bm = 32 * nw * nr;
         pl.block_m = bm;
         pl.block_n = bn;
@@ -487,6 +500,7 @@ fa_status fwd_impl(const void *q, const void *k, const void *v, void *o, float *
     L.prefill_nw = pl.prefill_nw;
     L.prefill_nr = pl.prefill_nr;
     L.prefill_pp = pl.prefill_pp;
+    L.prefill_pipe = pl.prefill_pipe;
     L.head_major = pl.head_major;
     L.stream = stream;
 

@@ -2273,6 +2273,9 @@ fa_bwd_dkdv_kernel(const BwdParams p)
 constexpr float kWideOverflow = 18446744073709551616.0f;   // 2^64
 // Operand reads of the fast block run this many steps ahead of their MFMAs.
 constexpr int kWidePrefetch = 2;
+// Slots of a pipelined step whose operands are read ahead (the first ones
+// at the end of the step before).
+constexpr int kPipePF = 2;
 
 template <int D>
 struct WideRows {
@@ -2914,20 +2917,56 @@ struct PipeRows {
     float c;
 };
 
+// With two waves per SIMD (8 waves, VG) a lane has 256 registers, which the
+// compiler splits evenly between VGPRs and AGPRs once a kernel uses any
+// AGPR; 128 VGPRs spill S, P and the operands.  There every MFMA is inline
+// asm with VGPR operands (the ping-pong kernel's forms, declared below): the
+// P V and row-sum accumulators are read only by the later MFMAs of their
+// chains or after pipe_drain_o, which the build's scan of the generated code
+// checks.  The row sum's selector operand may be rematerialised right before
+// its MFMA, so two wait states lead that one.
+__device__ __forceinline__ void pp_mfma_first(f32x16_t &d, bf16x8_t a, bf16x8_t q);
+__device__ __forceinline__ void pp_mfma_next(f32x16_t &d, bf16x8_t a, bf16x8_t q);
+__device__ __forceinline__ void pp_mfma_pv(f32x16_t &o, bf16x8_t v, bf16x8_t p);
+__device__ __forceinline__ void pipe_mfma_rowsum(f32x4_t &l, bf16x8_t sel, bf16x8_t p)
+{
+    asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0 ; accumulate-only"
+                 : "+v"(l)
+                 : "v"(sel), "v"(p));
+}
+// the wait for those MFMAs before the VALU reads O or the row sums (24 wait
+// states; the 8-pass MFMA needs 13), with the accumulators as operands
+template <int D>
+__device__ __forceinline__ void pipe_drain_o(PipeRows<D> &w)
+{
+    static_assert(D / 32 == 4, "four O accumulators");
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+v"(w.o[0]), "+v"(w.o[1]), "+v"(w.o[2]), "+v"(w.o[3]), "+v"(w.l_acc)::"memory");
+}
+
 // Step j.  Kn: K rows of block j + 1 (S^T into sn); Vp: V rows of block
 // j - 1 (P V with pp, its P; ACC = false: no such block); s: S^T(j),
 // masked, turned into pw (P(j) as bf16 words) and la (its exact sum over
 // this lane half) against the reference max.  Slot st issues S k-step st
 // and P V step st with P(j)'s elements st * 16 / QS .. between them, and
-// copy(st); the operand reads run kWidePrefetch slots ahead.
-template <int D, bool ACC, class CP>
+// copy(st); the operand reads run kPipePF slots ahead.  kpre / vpre hold the
+// operands of the step's first kPipePF slots on entry, and those of the next
+// step (K rows at Kn2, V rows at Vn2) on return: before its last slot the
+// step waits for its own reads, then takes the next step's barrier
+// (sync_next) and reads them, so that the next step starts without waiting
+// for LDS.
+template <int D, bool VG, bool ACC, class CP, class SY>
 __device__ __forceinline__ void pipe_step(PipeRows<D> &w, const OperandOffsets<D> &off,
                                           const char *Kn, const char *Vp, const f32x16_t &s,
                                           f32x16_t &sn, const bf16x8_t (&pp)[2],
-                                          u32x4_t (&pw)[2], float &la, CP &&copy)
+                                          u32x4_t (&pw)[2], float &la, CP &&copy,
+                                          const char *Kn2, const char *Vn2,
+                                          bf16x8_t (&kpre)[kPipePF], bf16x8_t (&vpre)[kPipePF],
+                                          SY &&sync_next)
 {
     constexpr int QS = D / 16, DB = D / 32, EPS = 16 / QS;
-    constexpr int PF = kWidePrefetch < QS ? kWidePrefetch : QS;
+    constexpr int PF = kPipePF;
+    static_assert(PF < QS, "the prefetched slots are a prefix of the step");
     bf16x8_t ka[QS], va[QS];
     float y[16];
     auto rd = [&](int i) __attribute__((always_inline)) {
@@ -2935,14 +2974,34 @@ __device__ __forceinline__ void pipe_step(PipeRows<D> &w, const OperandOffsets<D
         if (ACC) va[i] = wide_ld_v<D>(Vp, off, i);
     };
 #pragma unroll
-    for (int i = 0; i < PF; ++i) rd(i);
-    __builtin_amdgcn_sched_barrier(0);
+    for (int i = 0; i < PF; ++i) {
+        ka[i] = kpre[i];
+        va[i] = vpre[i];
+    }
     la = -0.0f;   // -0 + x is x: the first add folds away
 #pragma unroll
     for (int st = 0; st < QS; ++st) {
         const int t2 = st / DB, db = st % DB;
-        if (st == 0) mfma_s_first(sn, ka[st], w.qf[st]);
-        else mfma_s_next(sn, ka[st], w.qf[st]);
+        if (st == QS - 1) {
+            // every read of this step has been issued: wait for them, take
+            // the next step's barrier and read its first operands
+            __builtin_amdgcn_sched_barrier(0);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            sync_next();
+#pragma unroll
+            for (int i = 0; i < PF; ++i) {
+                kpre[i] = wide_ld_k<D>(Kn2, off, i);
+                vpre[i] = wide_ld_v<D>(Vn2, off, i);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (VG) {
+            if (st == 0) pp_mfma_first(sn, ka[st], w.qf[st]);
+            else pp_mfma_next(sn, ka[st], w.qf[st]);
+        } else {
+            if (st == 0) mfma_s_first(sn, ka[st], w.qf[st]);
+            else mfma_s_next(sn, ka[st], w.qf[st]);
+        }
         __builtin_amdgcn_sched_barrier(0);
         if (st + PF < QS) rd(st + PF);
 #pragma unroll
@@ -2952,7 +3011,10 @@ __device__ __forceinline__ void pipe_step(PipeRows<D> &w, const OperandOffsets<D
             keep(y[r]);
         }
         __builtin_amdgcn_sched_barrier(0);
-        if (ACC) w.o[db] = mfma32(va[st], pp[t2], w.o[db]);
+        if constexpr (ACC) {
+            if constexpr (VG) pp_mfma_pv(w.o[db], va[st], pp[t2]);
+            else w.o[db] = mfma32(va[st], pp[t2], w.o[db]);
+        }
         __builtin_amdgcn_sched_barrier(0);
         copy(st);
         __builtin_amdgcn_sched_barrier(0);
@@ -2967,8 +3029,13 @@ __device__ __forceinline__ void pipe_step(PipeRows<D> &w, const OperandOffsets<D
         }
         __builtin_amdgcn_sched_barrier(0);
         if (ACC && st == QS - 1) {
-            w.l_acc = mfma16(w.sel, pp[0], w.l_acc);
-            w.l_acc = mfma16(w.sel, pp[1], w.l_acc);
+            if constexpr (VG) {
+                pipe_mfma_rowsum(w.l_acc, w.sel, pp[0]);
+                pipe_mfma_rowsum(w.l_acc, w.sel, pp[1]);
+            } else {
+                w.l_acc = mfma16(w.sel, pp[0], w.l_acc);
+                w.l_acc = mfma16(w.sel, pp[1], w.l_acc);
+            }
         }
     }
     asm volatile("s_nop 7" : "+v"(sn)::"memory");
@@ -2976,12 +3043,13 @@ __device__ __forceinline__ void pipe_step(PipeRows<D> &w, const OperandOffsets<D
 
 // After step j: where P(j) overflowed, redo it against the exact row max
 // (s is block j's masked S^T); then add its exact sum.
-template <int D>
+template <int D, bool VG>
 __device__ __forceinline__ void pipe_settle(PipeRows<D> &w, const f32x16_t &s, u32x4_t (&pw)[2],
                                             float &la)
 {
     const bool big = !(la <= kWideOverflow);   // also true for inf and NaN
     if (__any(big)) {
+        if constexpr (VG) pipe_drain_o(w);
         const float mx = BlockOps<D>::rowmax(s);
         const float m_new = fmaxf(w.m_ref, mx);
         const float alpha = (w.m_ref == kNegInf) ? 0.0f : fast_exp2((w.m_ref - m_new) * w.c);
@@ -3003,12 +3071,14 @@ __device__ __forceinline__ void pipe_settle(PipeRows<D> &w, const f32x16_t &s, u
 }
 
 template <int D, int NW, bool OUT_F32>
-__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1)))
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 8 ? 2 : 1)))
 fa_prefill_pipe_kernel(const Params p)
 {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
     constexpr int BN = 32;
     constexpr int BM = 32 * NW;
+    // two waves per SIMD (8 waves): all MFMAs inline asm with VGPR operands
+    constexpr bool VG = NW == 8;
     constexpr int QS = D / 16;
     using TL = TileLoader<D, BN, NW>;
     using BO = BlockOps<D>;
@@ -3117,8 +3187,12 @@ fa_prefill_pipe_kernel(const Params p)
         }
         flip_q<D>(w.qf, p.qflip);
         // Q fragments are only ever B operands of inline-asm MFMAs: AGPRs
+        // (one wave per SIMD), VGPRs (two)
 #pragma unroll
-        for (int st = 0; st < QS; ++st) asm volatile("" : "+a"(w.qf[st]));
+        for (int st = 0; st < QS; ++st) {
+            if constexpr (VG) asm volatile("" : "+v"(w.qf[st]));
+            else asm volatile("" : "+a"(w.qf[st]));
+        }
         __syncthreads();   // K(0) is in LDS (every wave's copies)
 
         if (NB > 0) {
@@ -3146,8 +3220,13 @@ fa_prefill_pipe_kernel(const Params p)
                 for (int st = 0; st < QS; ++st) ka[st] = wide_ld_k<D>(lds, off, st);
 #pragma unroll
                 for (int st = 0; st < QS; ++st) {
-                    if (st == 0) mfma_s_first(sx, ka[st], w.qf[st]);
-                    else mfma_s_next(sx, ka[st], w.qf[st]);
+                    if constexpr (VG) {
+                        if (st == 0) pp_mfma_first(sx, ka[st], w.qf[st]);
+                        else pp_mfma_next(sx, ka[st], w.qf[st]);
+                    } else {
+                        if (st == 0) mfma_s_first(sx, ka[st], w.qf[st]);
+                        else mfma_s_next(sx, ka[st], w.qf[st]);
+                    }
                 }
                 mfma_s_drain(sx);
                 if (needs_mask(0)) BO::mask(sx, 0, half, p.Sk, lim);
@@ -3155,9 +3234,24 @@ fa_prefill_pipe_kernel(const Params p)
                 w.m_ref = mx;
                 w.mc = (mx == kNegInf) ? 0.0f : mx * c;
             }
-            // step j: wait for K(j + 1) and V(j - 1) (the copies of step
-            // j - 1 may stay in flight), barrier, then the step with the
-            // copies of K(j + 3) and V(j + 1) in its first slots
+            // the wave's last key block with an allowed key (-1: none).  Its
+            // later blocks are masked out entirely, so the steps past them
+            // are skipped: with two waves per SIMD that gives the SIMD to the
+            // other wave, whose rows reach further
+            int Lw = NB - 1;
+            {
+                const int wlast = min(wrow0 + 31, p.Sq - 1);
+                if (wlast < wrow0)
+                    Lw = -1;
+                else if (p.causal)
+                    Lw = wlast + p.off < 0 ? -1 : min(NB - 1, (wlast + p.off) / 32);
+            }
+            // the barrier before step j: wait for K(j + 1) and V(j - 1) (the
+            // copies of step j - 1 may stay in flight), then every wave's;
+            // step j copies K(j + 3) and V(j + 1) in its first slots.  Step
+            // j - 1 takes it before its last slot, once all its reads (of
+            // K(j) and V(j - 2), whose stages step j refills) are in
+            static_assert(LPS <= D / 16 - 1, "a step's copies go out before its last slot");
             auto sync = [&]() __attribute__((always_inline)) {
                 __builtin_amdgcn_sched_barrier(0);
                 __builtin_amdgcn_s_waitcnt(0x0F70 | LPS);
@@ -3169,9 +3263,19 @@ fa_prefill_pipe_kernel(const Params p)
                     else if (st < 2 * TL::PER_WAVE) copy_v(j + 1, st - TL::PER_WAVE);
                 };
             };
+            // the operands of each step's first slots, read at the end of the
+            // step before (step 0's here: K(1); it has no P V)
+            bf16x8_t kpre[kPipePF], vpre[kPipePF];
             sync();
-            pipe_step<D, false>(w, off, lds + TB, lds, sx, sy, py, pw, la, copies(0));
-            pipe_settle<D>(w, sx, pw, la);
+#pragma unroll
+            for (int i = 0; i < kPipePF; ++i) {
+                kpre[i] = wide_ld_k<D>(lds + TB, off, i);
+                vpre[i] = bf16x8_t{};
+            }
+            // each step takes the next one's barrier before its last slot
+            pipe_step<D, VG, false>(w, off, lds + TB, lds, sx, sy, py, pw, la, copies(0),
+                                    lds + 2 * TB, lds, kpre, vpre, sync);
+            pipe_settle<D, VG>(w, sx, pw, la);
             px[0] = __builtin_bit_cast(bf16x8_t, pw[0]);
             px[1] = __builtin_bit_cast(bf16x8_t, pw[1]);
             // step j >= 1: the register sets of block j (even: sx / px, odd:
@@ -3188,17 +3292,22 @@ fa_prefill_pipe_kernel(const Params p)
                 bf16x8_t(&pp)[2] = ODD ? px : py;
                 bf16x8_t(&pn)[2] = ODD ? py : px;
                 if (needs_mask(j)) BO::mask(s, j * 32, half, p.Sk, lim);
-                sync();
-                pipe_step<D, true>(w, off, Kn, Vp, s, sn, pp, pw, la, copies(j));
-                pipe_settle<D>(w, s, pw, la);
+                // the next step reads K(j + 2) and V(j)
+                pipe_step<D, VG, true>(w, off, Kn, Vp, s, sn, pp, pw, la, copies(j),
+                                       lds + ((ST + 2) % NSK) * TB, lds + ST * TB, kpre, vpre,
+                                       sync);
+                pipe_settle<D, VG>(w, s, pw, la);
                 pn[0] = __builtin_bit_cast(bf16x8_t, pw[0]);
                 pn[1] = __builtin_bit_cast(bf16x8_t, pw[1]);
             };
             using T = std::true_type;
             using F = std::false_type;
+            // the steps this wave computes: its live blocks, and the P V of
+            // the last (later steps only take the ring's barriers and copies)
+            const int NBw = min(NB, Lw + 2);
             int j = 1;
             // six steps per trip (j = 1 mod 6), then the rest
-            for (; j + 5 < NB; j += 6) {
+            for (; j + 5 < NBw; j += 6) {
                 step(T{}, std::integral_constant<int, 1>{}, j);
                 step(F{}, std::integral_constant<int, 2>{}, j + 1);
                 step(T{}, std::integral_constant<int, 0>{}, j + 2);
@@ -3207,24 +3316,44 @@ fa_prefill_pipe_kernel(const Params p)
                 step(F{}, std::integral_constant<int, 0>{}, j + 5);
             }
             // the rest: at most five steps, from j = 1 mod 6
-            if (j < NB) step(T{}, std::integral_constant<int, 1>{}, j);
-            if (j + 1 < NB) step(F{}, std::integral_constant<int, 2>{}, j + 1);
-            if (j + 2 < NB) step(T{}, std::integral_constant<int, 0>{}, j + 2);
-            if (j + 3 < NB) step(F{}, std::integral_constant<int, 1>{}, j + 3);
-            if (j + 4 < NB) step(T{}, std::integral_constant<int, 2>{}, j + 4);
-            // the last block's P V, once V(NB - 1) is in (the last step's
-            // copies may stay in flight)
-            sync();
-            const bf16x8_t(&pl)[2] = (NB & 1) ? px : py;
+            if (j < NBw) step(T{}, std::integral_constant<int, 1>{}, j);
+            if (j + 1 < NBw) step(F{}, std::integral_constant<int, 2>{}, j + 1);
+            if (j + 2 < NBw) step(T{}, std::integral_constant<int, 0>{}, j + 2);
+            if (j + 3 < NBw) step(F{}, std::integral_constant<int, 1>{}, j + 3);
+            if (j + 4 < NBw) step(T{}, std::integral_constant<int, 2>{}, j + 4);
+            for (int jd = max(1, NBw); jd < NB; ++jd) {
+                auto cp = copies(jd);
+#pragma unroll
+                for (int st = 0; st < LPS; ++st) cp(st);
+                sync();
+            }
+            // the last block's P V: V(NB - 1) is in (the last step took the
+            // barrier after it; that step's own copies may stay in flight)
+            if (NB - 1 <= Lw) {
+            bf16x8_t pl[2];
+#pragma unroll
+            for (int t2 = 0; t2 < 2; ++t2) {
+                pl[t2] = (NB & 1) ? px[t2] : py[t2];
+                // the select is a VALU write of an MFMA operand: two wait states
+                if constexpr (VG) asm volatile("s_nop 1" : "+v"(pl[t2]));
+            }
             const char *Vl = lds + ((NB - 1) % NSK) * TB;
 #pragma unroll
             for (int ps = 0; ps < QS; ++ps) {
                 const int t2 = ps / (D / 32), db = ps % (D / 32);
-                w.o[db] = mfma32(wide_ld_v<D>(Vl, off, ps), pl[t2], w.o[db]);
+                if constexpr (VG) pp_mfma_pv(w.o[db], wide_ld_v<D>(Vl, off, ps), pl[t2]);
+                else w.o[db] = mfma32(wide_ld_v<D>(Vl, off, ps), pl[t2], w.o[db]);
             }
-            w.l_acc = mfma16(w.sel, pl[0], w.l_acc);
-            w.l_acc = mfma16(w.sel, pl[1], w.l_acc);
+            if constexpr (VG) {
+                pipe_mfma_rowsum(w.l_acc, w.sel, pl[0]);
+                pipe_mfma_rowsum(w.l_acc, w.sel, pl[1]);
+            } else {
+                w.l_acc = mfma16(w.sel, pl[0], w.l_acc);
+                w.l_acc = mfma16(w.sel, pl[1], w.l_acc);
+            }
+            }
         }
+        if constexpr (VG) pipe_drain_o(w);
         __syncthreads();   // every wave is done with the rings before the next item
 
         finish_rows<D, OUT_F32>(w.o, w.m_ref, w.l_run, w.l_acc[0], c, half, p.o,
@@ -4879,6 +5008,22 @@ hipError_t launch_prefill(const Launch &L)
             if (L.prefill_pp == 5) launch_prefill_pp<64, 5>(L, p);
             else launch_prefill_pp<64, 4>(L, p);
         }
+        return hipGetLastError();
+    }
+    if (L.prefill_pipe) {
+        // the pipelined 32-key kernel at head dim 128: 8 waves x 32 rows
+        if (L.D != 128 || L.prefill_bn != 32 || L.prefill_nw != 8 || L.prefill_nr != 1)
+            return hipErrorInvalidValue;
+        Params p = make_params(L);
+        const int BH = L.B * L.Hq;
+        p.n_mblocks = (L.Sq + 255) / 256;
+        p.domains = (BH % 8 == 0 && L.grid % 8 == 0) ? 8 : 1;
+        p.head_major = L.head_major;
+        dim3 g(L.grid), blk(8 * 64);
+        if (L.o_f32)
+            hipLaunchKernelGGL((fa_prefill_pipe_kernel<128, 8, true>), g, blk, 0, L.stream, p);
+        else
+            hipLaunchKernelGGL((fa_prefill_pipe_kernel<128, 8, false>), g, blk, 0, L.stream, p);
         return hipGetLastError();
     }
     const PrefillCfg *cfg = find_prefill_cfg(L.D, L.prefill_bn, L.prefill_nw, L.prefill_nr);

@@ -63,6 +63,7 @@ struct Launch {
     int prefill_nr;      // prefill: 32-row column blocks per wave
     int head_major;      // prefill: item order (1: head by head, 0: rank by rank)
     int prefill_pp;      // prefill: 0, or the ring depth (4 or 5) of the ping-pong kernel
+    int prefill_pipe = 0;  // prefill: 1 = the pipelined 32-key kernel (head dim 128: 8 waves)
     int fp8_pipe = 0;    // FP8 prefill: 1 = the pipelined kernel (8 waves)
     hipStream_t stream;
 };

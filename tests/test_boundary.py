@@ -108,16 +108,23 @@ def test_workspace_size_and_plan_host_arithmetic(b):
     assert b.fa_workspace_size(32, 32, 8, 1, 8192, 128, 1) == 0
     assert b.fa_workspace_size(4, 16, 16, 4096, 4096, 128, 0) == 0   # prefill path
     assert b.fa_workspace_size(0, 16, 16, 4096, 4096, 128, 0) == 0   # invalid sizes
+    # head dim 128: the pipelined kernel, 8 waves x 32 rows, 32-key tiles
+    # (separate 3-stage K and V rings, 48 KiB), two waves per SIMD: one
+    # workgroup per CU
     p = b.fa_plan(16, 16, 16, 1024, 1024, 128, True, 0)
-    # short causal rows: 8 waves x 32 rows, 64-key tiles, 3 x 32 KiB of LDS:
-    # one workgroup per CU
-    assert p["path"] == 0 and p["block_m"] == 256 and p["block_n"] == 64
+    assert p["path"] == 0 and p["block_m"] == 256 and p["block_n"] == 32
     assert p["waves"] == 8 and p["rows_per_wave"] == 32
     assert p["work_items"] == 16 * 16 * 4 and p["grid"] == 256
-    # non-causal, and causal from 2048 rows: 4 waves x 64 rows, still
-    # 256-row blocks
     for causal, S in ((False, 4096), (True, 4096), (True, 16384)):
         p = b.fa_plan(1, 32, 8, S, S, 128, causal, 0)
+        assert p["block_m"] == 256 and p["block_n"] == 32 and p["grid"] == 256
+        assert p["waves"] == 8 and p["rows_per_wave"] == 32
+    # head dim 64, short causal rows: 8 waves x 32 rows, 64-key tiles
+    p = b.fa_plan(16, 16, 16, 1024, 1024, 64, True, 0)
+    assert p["block_m"] == 256 and p["block_n"] == 64 and p["waves"] == 8
+    # head dim 64, non-causal and causal from 2048 rows: 4 waves x 64 rows
+    for causal, S in ((False, 4096), (True, 4096)):
+        p = b.fa_plan(1, 32, 8, S, S, 64, causal, 0)
         assert p["block_m"] == 256 and p["block_n"] == 64 and p["grid"] == 256
         assert p["waves"] == 4 and p["rows_per_wave"] == 64
     # too few 256-row items to cover the CUs: 4-wave workgroups, 32-key tiles
@@ -148,10 +155,11 @@ def test_plan_tile_overrides(b, monkeypatch):
     p = b.fa_plan(1, 32, 8, 16384, 16384, 128, False, 0)
     assert p["block_m"] == 256 and p["block_n"] == 64 and p["work_items"] == 32 * 64
     assert p["grid"] == 256          # one wave per SIMD: one workgroup per CU
-    # the wide kernel needs two key blocks per tile: 32-key tiles are not compiled
+    # the wide kernel needs two key blocks per tile: 32-key tiles are not
+    # compiled, and the default (the pipelined 32-key kernel) applies again
     monkeypatch.setenv("FA_PREFILL_BN", "32")
     p = b.fa_plan(4, 16, 16, 4096, 4096, 128, True, 0)
-    assert p["block_m"] == 256 and p["block_n"] == 64      # the default again
+    assert p["block_m"] == 256 and p["block_n"] == 32 and p["waves"] == 8
     monkeypatch.setenv("FA_PREFILL_NR", "1")
     monkeypatch.setenv("FA_PREFILL_NW", "8")
     p = b.fa_plan(4, 16, 16, 4096, 4096, 128, True, 0)
