@@ -2917,6 +2917,18 @@ struct PipeRows {
     float c;
 };
 
+// Row block (32 rows) of wave `wave` within an item.  The waves of a
+// workgroup are spread over the CU's four SIMDs in turn, so waves w and w + 4
+// share one; in a causal item the diagonal work of a row block grows with
+// its index, so with 8 waves the second four take the blocks in reverse
+// order: SIMD s then holds blocks s and 7 - s, the same work on every SIMD.
+// (The mapping only balances the SIMDs; any assignment is correct.)
+template <int NW>
+__device__ __forceinline__ int pipe_row_block(int wave)
+{
+    return (NW == 8 && wave >= 4) ? 11 - wave : wave;
+}
+
 // With two waves per SIMD (8 waves, VG) a lane has 256 registers, which the
 // compiler splits evenly between VGPRs and AGPRs once a kernel uses any
 // AGPR; 128 VGPRs spill S, P and the operands.  There every MFMA is inline
@@ -3137,7 +3149,7 @@ fa_prefill_pipe_kernel(const Params p)
         const int hq = bh % p.Hq;
         const int g = hq / p.group;
         const int row0 = mb * BM;
-        const int wrow0 = row0 + wave * 32;
+        const int wrow0 = row0 + pipe_row_block<NW>(wave) * 32;
         const int qi = wrow0 + col;
         const int last_row = min(row0 + BM, p.Sq) - 1;
         int NB = (p.Sk + BN - 1) / BN;   // blocks (= tiles) the workgroup walks
@@ -3653,7 +3665,7 @@ fa_prefill_fp8_pipe_kernel(const Params p, const float v_descale)
         const int hq = bh % p.Hq;
         const int g = hq / p.group;
         const int row0 = mb * BM;
-        const int wrow0 = row0 + wave * 32;
+        const int wrow0 = row0 + pipe_row_block<NW>(wave) * 32;
         const int qi = wrow0 + col;
         const int last_row = min(row0 + BM, p.Sq) - 1;
         int NB = (p.Sk + BN - 1) / BN;   // blocks (= tiles) the workgroup walks
@@ -3772,6 +3784,17 @@ fa_prefill_fp8_pipe_kernel(const Params p, const float v_descale)
                 __builtin_amdgcn_s_waitcnt(0x0F70 | LPS);
                 pp_barrier();
             };
+            // the wave's last key block with an allowed key (-1: none).  Its
+            // later blocks are masked out entirely, so the steps past them
+            // are skipped: that gives the SIMD to the other wave on it
+            int Lw = NB - 1;
+            {
+                const int wlast = min(wrow0 + 31, p.Sq - 1);
+                if (wlast < wrow0)
+                    Lw = -1;
+                else if (p.causal)
+                    Lw = wlast + p.off < 0 ? -1 : min(NB - 1, (wlast + p.off) / BN);
+            }
             auto copies = [&](int j) __attribute__((always_inline)) {
                 return [&, j](int m) __attribute__((always_inline)) {
                     if (m < PER_WAVE) copy_k(j + 3, m);
@@ -3803,9 +3826,12 @@ fa_prefill_fp8_pipe_kernel(const Params p, const float v_descale)
             };
             using T = std::true_type;
             using F = std::false_type;
+            // the steps this wave computes: its live blocks, and the P V of
+            // the last (later steps only take the ring's barriers and copies)
+            const int NBw = min(NB, Lw + 2);
             int j = 1;
             // six steps per trip (j = 1 mod 6), then the rest
-            for (; j + 5 < NB; j += 6) {
+            for (; j + 5 < NBw; j += 6) {
                 step(T{}, std::integral_constant<int, 1>{}, j);
                 step(F{}, std::integral_constant<int, 2>{}, j + 1);
                 step(T{}, std::integral_constant<int, 0>{}, j + 2);
@@ -3814,21 +3840,30 @@ fa_prefill_fp8_pipe_kernel(const Params p, const float v_descale)
                 step(F{}, std::integral_constant<int, 0>{}, j + 5);
             }
             // the rest: at most five steps, from j = 1 mod 6
-            if (j < NB) step(T{}, std::integral_constant<int, 1>{}, j);
-            if (j + 1 < NB) step(F{}, std::integral_constant<int, 2>{}, j + 1);
-            if (j + 2 < NB) step(T{}, std::integral_constant<int, 0>{}, j + 2);
-            if (j + 3 < NB) step(F{}, std::integral_constant<int, 1>{}, j + 3);
-            if (j + 4 < NB) step(T{}, std::integral_constant<int, 2>{}, j + 4);
+            if (j < NBw) step(T{}, std::integral_constant<int, 1>{}, j);
+            if (j + 1 < NBw) step(F{}, std::integral_constant<int, 2>{}, j + 1);
+            if (j + 2 < NBw) step(T{}, std::integral_constant<int, 0>{}, j + 2);
+            if (j + 3 < NBw) step(F{}, std::integral_constant<int, 1>{}, j + 3);
+            if (j + 4 < NBw) step(T{}, std::integral_constant<int, 2>{}, j + 4);
+            for (int jd = max(1, NBw); jd < NB; ++jd) {
+                sync();
+                auto cp = copies(jd);
+#pragma unroll
+                for (int m = 0; m < LPS; ++m) cp(m);
+            }
             // the last block's P V, once V(NB - 1) is in (the last step's
             // copies may stay in flight)
             sync();
-            i32x8_t pl = (NB & 1) ? px : py;
-            // the select is a VALU write of an MFMA operand: two wait states
-            asm volatile("s_nop 1" : "+v"(pl));
-            const char *Vl = lds + ((NB - 1) % NSK) * TB;
+            if (NB - 1 <= Lw) {
+                i32x8_t pl = (NB & 1) ? px : py;
+                // the select is a VALU write of an MFMA operand: two wait states
+                asm volatile("s_nop 1" : "+v"(pl));
+                const char *Vl = lds + ((NB - 1) % NSK) * TB;
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db) mfma_o8(w.o[db], fp8_ld_v<D>(Vl, off, db), pl);
-            mfma_rowsum8(w.l_acc, w.ones, pl);
+                for (int db = 0; db < D / 32; ++db)
+                    mfma_o8(w.o[db], fp8_ld_v<D>(Vl, off, db), pl);
+                mfma_rowsum8(w.l_acc, w.ones, pl);
+            }
         }
         fp8_drain_o(w);
         __syncthreads();   // every wave is done with the rings before the next item
