@@ -3509,12 +3509,17 @@ __device__ __forceinline__ int fp8_word(const float *y)
 // turned into pw (P(j) as E4M3 bytes, byte 16 kb + r of the B operand) and la
 // (its exact sum over this lane half) against the reference max.  Slot m
 // issues S MFMA m and P V MFMA m with P(j)'s elements 8m .. 8m + 7 between
-// them, and copy(m); each slot's operands are read one slot ahead.
-template <int D, bool ACC, class CP>
+// them, and copy(m); each slot's operands are read one slot ahead.  kpre
+// holds the first slot's K operand on entry, and the next step's (K rows at
+// Kn2) on return: before its last slot the step waits for its own reads,
+// takes the next step's barrier (sync_next) and reads it.  (The V operand of
+// a step's first slot is read at its start: its P V MFMA comes second.)
+template <int D, bool ACC, class CP, class SY>
 __device__ __forceinline__ void fp8_pipe_step(Fp8PipeRows<D> &w, const Fp8Offsets<D> &off,
                                               const char *Kn, const char *Vp,
                                               const f32x16_t (&s)[2], f32x16_t (&sn)[2],
-                                              const i32x8_t &pp, i32x8_t &pw, float &la, CP &&copy)
+                                              const i32x8_t &pp, i32x8_t &pw, float &la, CP &&copy,
+                                              const char *Kn2, i32x8_t &kpre, SY &&sync_next)
 {
     constexpr int KS = D / 64, DB = D / 32, NM = 2 * KS;
     static_assert(NM == DB, "one S^T and one P V MFMA per slot");
@@ -3524,12 +3529,21 @@ __device__ __forceinline__ void fp8_pipe_step(Fp8PipeRows<D> &w, const Fp8Offset
         ka[i] = fp8_ld_k<D>(Kn, off, i);
         if (ACC) va[i] = fp8_ld_v<D>(Vp, off, i);
     };
-    rd(0);
-    __builtin_amdgcn_sched_barrier(0);
+    ka[0] = kpre;
+    if (ACC) va[0] = fp8_ld_v<D>(Vp, off, 0);
     la = -0.0f;   // -0 + x is x: the first add folds away
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
         const int kb = m / KS, st = m % KS;
+        if (m == NM - 1) {
+            // every read of this step has been issued: wait for them, take
+            // the next step's barrier and read its first operands
+            __builtin_amdgcn_sched_barrier(0);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            sync_next();
+            kpre = fp8_ld_k<D>(Kn2, off, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         if (st == 0) mfma_s8_first(sn[kb], ka[m], w.qf[st]);
         else mfma_s8_next(sn[kb], ka[m], w.qf[st]);
         __builtin_amdgcn_sched_barrier(0);
@@ -3776,9 +3790,12 @@ fa_prefill_fp8_pipe_kernel(const Params p, const float v_descale)
                 w.m_ref = mx;
                 w.mc = (mx == kNegInf) ? 0.0f : mx * c;
             }
-            // step j: wait for K(j + 1) and V(j - 1) (the copies of step
-            // j - 1 may stay in flight), barrier, then the step with the
-            // copies of K(j + 3) and V(j + 1) in its first slots
+            // the barrier before step j: wait for K(j + 1) and V(j - 1) (the
+            // copies of step j - 1 may stay in flight), then every wave's;
+            // step j copies K(j + 3) and V(j + 1) in its first slots.  Step
+            // j - 1 takes it before its last slot, once all its reads (of
+            // K(j) and V(j - 2), whose stages step j refills) are in
+            static_assert(LPS <= 2 * KS - 1, "a step's copies go out before its last slot");
             auto sync = [&]() __attribute__((always_inline)) {
                 __builtin_amdgcn_sched_barrier(0);
                 __builtin_amdgcn_s_waitcnt(0x0F70 | LPS);
@@ -3801,8 +3818,13 @@ fa_prefill_fp8_pipe_kernel(const Params p, const float v_descale)
                     else if (m < 2 * PER_WAVE) copy_v(j + 1, m - PER_WAVE);
                 };
             };
+            // the K operand of each step's first slot, read at the end of the
+            // step before (step 0's here: K(1))
             sync();
-            fp8_pipe_step<D, false>(w, off, lds + TB, lds, sx, sy, py, pw, la, copies(0));
+            i32x8_t kpre = fp8_ld_k<D>(lds + TB, off, 0);
+            // each step takes the next one's barrier before its last slot
+            fp8_pipe_step<D, false>(w, off, lds + TB, lds, sx, sy, py, pw, la, copies(0),
+                                    lds + 2 * TB, kpre, sync);
             fp8_pipe_settle<D>(w, sx, pw, la);
             px = pw;
             // step j >= 1: the register sets of block j (even: sx / px, odd:
@@ -3819,8 +3841,9 @@ fa_prefill_fp8_pipe_kernel(const Params p, const float v_descale)
                 i32x8_t &pp = ODD ? px : py;
                 i32x8_t &pn = ODD ? py : px;
                 if (needs_mask(j)) mask(s, j);
-                sync();
-                fp8_pipe_step<D, true>(w, off, Kn, Vp, s, sn, pp, pw, la, copies(j));
+                // the next step reads K(j + 2) first
+                fp8_pipe_step<D, true>(w, off, Kn, Vp, s, sn, pp, pw, la, copies(j),
+                                       lds + ((ST + 2) % NSK) * TB, kpre, sync);
                 fp8_pipe_settle<D>(w, s, pw, la);
                 pn = pw;
             };
@@ -3846,14 +3869,13 @@ fa_prefill_fp8_pipe_kernel(const Params p, const float v_descale)
             if (j + 3 < NBw) step(F{}, std::integral_constant<int, 1>{}, j + 3);
             if (j + 4 < NBw) step(T{}, std::integral_constant<int, 2>{}, j + 4);
             for (int jd = max(1, NBw); jd < NB; ++jd) {
-                sync();
                 auto cp = copies(jd);
 #pragma unroll
                 for (int m = 0; m < LPS; ++m) cp(m);
+                sync();
             }
-            // the last block's P V, once V(NB - 1) is in (the last step's
-            // copies may stay in flight)
-            sync();
+            // the last block's P V: V(NB - 1) is in (the last step took the
+            // barrier after it; that step's own copies may stay in flight)
             if (NB - 1 <= Lw) {
                 i32x8_t pl = (NB & 1) ? px : py;
                 // the select is a VALU write of an MFMA operand: two wait states
