@@ -209,19 +209,25 @@ fa_status make_plan(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal, i
         int bn = 64, nw = 8, nr = 1;
         int pipe = 0;
         const int64_t m8 = (Sq + 255) / 256;
+        // FA_PREFILL_PIPE: 0 = never the pipelined kernel at D = 128, 1 (the
+        // default) = when 256-row items cover the CUs, 2 = always (tests)
+        const int epipe = env_int("FA_PREFILL_PIPE", 1);
         if (D == 256) {
             // 32-key tiles (16 KiB per tile at D = 256: the three-stage ring
             // takes 96 KiB), 4 waves x 32 rows, one wave per SIMD (Q and O
             // alone take 192 registers per lane: two waves per SIMD spill)
             bn = 32;
             nw = 4;
+        } else if (D == 128 && epipe == 2) {
+            pipe = 1;
+            bn = 32;
         } else if ((int64_t)B * Hq * m8 < cus) {
             nw = 4;
             bn = 32;
             // still fewer 128-row items than CUs: 64-row items (two waves),
             // so that every CU's LDS and L1 serve the same waves
             if ((int64_t)B * Hq * ((Sq + 127) / 128) < cus) nw = 2;
-        } else if (D == 128 && env_int("FA_PREFILL_PIPE", 1) != 0) {
+        } else if (D == 128 && epipe != 0) {
             // head dim 128: the pipelined 32-key kernel, 8 waves x 32 rows
             // (two waves per SIMD).  Measured against the 64-row kernel
             // (median of 30 interleaved calls): causal S = 1024 -10 %, 2048

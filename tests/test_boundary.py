@@ -166,6 +166,25 @@ def test_plan_tile_overrides(b, monkeypatch):
     assert p["block_m"] == 256 and p["block_n"] == 32
 
 
+def test_plan_pipelined_kernel_switch(b, monkeypatch):
+    """FA_PREFILL_PIPE: 0 turns the pipelined head-dim-128 kernel off (the
+    64-row kernel takes long rows again), 2 forces it where the planner would
+    give the shape to the small-problem configurations."""
+    monkeypatch.setenv("FA_PREFILL_PIPE", "0")
+    p = b.fa_plan(4, 16, 16, 4096, 4096, 128, True, 0)
+    assert p["block_n"] == 64 and p["waves"] == 4 and p["rows_per_wave"] == 64
+    monkeypatch.setenv("FA_PREFILL_PIPE", "2")
+    p = b.fa_plan(2, 8, 8, 1024, 1024, 128, True, 0)
+    assert p["block_m"] == 256 and p["block_n"] == 32 and p["waves"] == 8
+    assert p["work_items"] == 2 * 8 * 4 and p["grid"] == 2 * 8 * 4
+    # head dim 64 has no pipelined kernel: the planner's own choice
+    p = b.fa_plan(2, 8, 8, 1024, 1024, 64, True, 0)
+    assert p["block_m"] == 64 and p["waves"] == 2
+    monkeypatch.delenv("FA_PREFILL_PIPE")
+    p = b.fa_plan(2, 8, 8, 1024, 1024, 128, True, 0)
+    assert p["block_n"] == 32 and p["waves"] == 2   # 64-row items: too few for the CUs
+
+
 def test_product_path_never_touches_the_oracle():
     pkg = os.path.join(ROOT, "attention_fwd_02_amd")
     for dirpath, _, files in os.walk(pkg):

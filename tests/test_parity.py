@@ -98,12 +98,16 @@ def test_prefill_shapes_elementwise(ops, oracle, shape):
 
 # The other compiled prefill configurations, forced through the planner's
 # override variables: 64 rows per wave (one wave per SIMD, software-pipelined
-# block loop), 32-key tiles with 8 waves, 64-key tiles with 4 waves.
+# block loop), 32-key tiles with 8 waves, 64-key tiles with 4 waves; and the
+# pipelined kernel forced at D = 128 on shapes the planner would give others.
 CONFIGS = {
     "rows64_bn64_w4": {"FA_PREFILL_BN": "64", "FA_PREFILL_NW": "4", "FA_PREFILL_NR": "2"},
     "bn32_w8": {"FA_PREFILL_BN": "32", "FA_PREFILL_NW": "8", "FA_PREFILL_NR": "1"},
     "bn64_w4": {"FA_PREFILL_BN": "64", "FA_PREFILL_NW": "4", "FA_PREFILL_NR": "1"},
     "bn32_w2": {"FA_PREFILL_BN": "32", "FA_PREFILL_NW": "2", "FA_PREFILL_NR": "1"},
+    # the pipelined 32-key kernel (the default at D = 128 when 256-row items
+    # cover the CUs) on every shape
+    "pipe_forced": {"FA_PREFILL_PIPE": "2"},
     # ping-pong kernel (8 waves, alternating MFMA and softmax phases), 4- and 5-tile rings
     "pingpong_ring4": {"FA_PREFILL_PP": "4"},
     "pingpong_ring5": {"FA_PREFILL_PP": "5"},

@@ -24,6 +24,9 @@ pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
 CONFIG_VARS = ("FA_PREFILL_BN", "FA_PREFILL_NW", "FA_PREFILL_NR")
+# even seeds without a forced configuration force the pipelined kernel at
+# D = 128 (the planner gives small shapes to the others)
+PIPE_VAR = "FA_PREFILL_PIPE"
 CONFIGS = [None, ("64", "4", "2"), ("32", "8", "1"), ("64", "4", "1")]
 
 
@@ -44,7 +47,7 @@ def oracle():
 
 @pytest.fixture
 def clean_env():
-    saved = {k: os.environ.get(k) for k in CONFIG_VARS}
+    saved = {k: os.environ.get(k) for k in CONFIG_VARS + (PIPE_VAR,)}
     yield
     for k, val in saved.items():
         if val is None:
@@ -103,11 +106,13 @@ def paged_case(seed):
 def test_random_dense(ops, oracle, clean_env, seed):
     c = dense_case(seed)
     say(f"[random] dense seed {seed}: {c}")
-    for k in CONFIG_VARS:
+    for k in CONFIG_VARS + (PIPE_VAR,):
         os.environ.pop(k, None)
     if c["cfg"] is not None:
         for k, val in zip(CONFIG_VARS, c["cfg"]):
             os.environ[k] = val
+    elif seed % 2 == 0:
+        os.environ[PIPE_VAR] = "2"
     q, k, v = random_qkv(c["B"], c["Hq"], c["Hkv"], c["Sq"], c["Sk"], c["D"], seed=seed)
     o = torch.empty((c["B"], c["Sq"], c["Hq"], c["D"]),
                     dtype=torch.float32 if c["out"] == "f32" else torch.bfloat16, device=DEV)
