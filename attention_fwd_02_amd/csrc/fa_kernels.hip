@@ -2904,6 +2904,11 @@ fa_prefill_wide_kernel(const Params p)
 // each two steps before it is read.  Every wave issues 2 PER_WAVE copies per
 // step; past the last block the copies read an empty range (zeros into a
 // free stage), which keeps that count fixed.
+// With 8 waves (head dim 128) the rings have six stages and the barrier
+// comes before every second step only: the one before step 2m waits for
+// K(2m + 1), K(2m + 2), V(2m - 1) and V(2m) and releases every stage read
+// in steps up to 2m - 1; steps 2m and 2m + 1 copy K(j + 5) and V(j + 3)
+// into stages read last in steps 2m - 2 and 2m - 1.
 // ---------------------------------------------------------------------------
 template <int D>
 struct PipeRows {
@@ -3095,11 +3100,15 @@ fa_prefill_pipe_kernel(const Params p)
     using TL = TileLoader<D, BN, NW>;
     using BO = BlockOps<D>;
     constexpr int TB = TL::TILE_BYTES;
-    constexpr int NSK = 3;                 // K ring stages, then as many V stages
+    constexpr int BP = VG ? 2 : 1;         // steps per barrier
+    constexpr int NSK = 3 * BP;            // K ring stages, then as many V stages
+    constexpr int KA = NSK - BP + 1;       // step j copies K(j + KA) ...
+    constexpr int VA = KA - 2;             // ... and V(j + VA)
     constexpr int VOFF = NSK * TB;         // V stage s sits at K stage s + VOFF
     constexpr int LPS = 2 * TL::PER_WAVE;  // copies per wave and step
-    static_assert(LPS <= 15, "vmcnt immediate");
+    static_assert(BP * LPS <= 15, "vmcnt immediate");
     __shared__ __attribute__((aligned(1024))) char lds[2 * NSK * TB];
+    static_assert(2 * NSK * TB <= 160 * 1024, "LDS");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -3208,18 +3217,23 @@ fa_prefill_pipe_kernel(const Params p)
         __syncthreads();   // K(0) is in LDS (every wave's copies)
 
         if (NB > 0) {
-            // the copies steps -2 and -1 would have issued: K(1) and V(-1)
-            // (nothing: an empty range into V(2)'s stage), then K(2) and V(0)
+            // the copies steps 1 - KA .. -1 would have issued: K(t + KA) and
+            // V(t + VA) for each of them, V of a block before 0 being
+            // nothing (an empty range into its free stage)
             const u32x4_t none = raw_desc(p.v, 0u);
 #pragma unroll
-            for (int i = 0; i < TL::PER_WAVE; ++i) copy_k(1, i);
+            for (int t = 1 - KA; t < 0; ++t) {
 #pragma unroll
-            for (int i = 0; i < TL::PER_WAVE; ++i)
-                lds_dma16(lds + VOFF + 2 * TB + (i * NW + wave) * 1024, loff[i], none);
+                for (int i = 0; i < TL::PER_WAVE; ++i) copy_k(t + KA, i);
 #pragma unroll
-            for (int i = 0; i < TL::PER_WAVE; ++i) copy_k(2, i);
-#pragma unroll
-            for (int i = 0; i < TL::PER_WAVE; ++i) copy_v(0, i);
+                for (int i = 0; i < TL::PER_WAVE; ++i) {
+                    if (t + VA >= 0)
+                        copy_v(t + VA, i);
+                    else
+                        lds_dma16(lds + VOFF + ((t + VA + NSK) % NSK) * TB + (i * NW + wave) * 1024,
+                                  loff[i], none);
+                }
+            }
 
             f32x16_t sx, sy;                 // S^T of the even / odd block
             bf16x8_t px[2], py[2];           // P of the even / odd block
@@ -3258,21 +3272,23 @@ fa_prefill_pipe_kernel(const Params p)
                 else if (p.causal)
                     Lw = wlast + p.off < 0 ? -1 : min(NB - 1, (wlast + p.off) / 32);
             }
-            // the barrier before step j: wait for K(j + 1) and V(j - 1) (the
-            // copies of step j - 1 may stay in flight), then every wave's;
-            // step j copies K(j + 3) and V(j + 1) in its first slots.  Step
-            // j - 1 takes it before its last slot, once all its reads (of
-            // K(j) and V(j - 2), whose stages step j refills) are in
+            // the barrier before step j (every BP-th step): wait for K(j + 1)
+            // and V(j - 1) (with BP = 2 also K(j + 2) and V(j); the copies of
+            // the BP steps before may stay in flight), then every wave's.
+            // Step j copies K(j + KA) and V(j + VA) in its first slots.  Step
+            // j - 1 takes the barrier before its last slot, once all its
+            // reads (of the stages the next BP steps refill) are in
             static_assert(LPS <= D / 16 - 1, "a step's copies go out before its last slot");
             auto sync = [&]() __attribute__((always_inline)) {
                 __builtin_amdgcn_sched_barrier(0);
-                __builtin_amdgcn_s_waitcnt(0x0F70 | LPS);
+                __builtin_amdgcn_s_waitcnt(0x0F70 | (BP * LPS));
                 pp_barrier();
             };
+            auto no_sync = [&]() __attribute__((always_inline)) {};
             auto copies = [&](int j) __attribute__((always_inline)) {
                 return [&, j](int st) __attribute__((always_inline)) {
-                    if (st < TL::PER_WAVE) copy_k(j + 3, st);
-                    else if (st < 2 * TL::PER_WAVE) copy_v(j + 1, st - TL::PER_WAVE);
+                    if (st < TL::PER_WAVE) copy_k(j + KA, st);
+                    else if (st < 2 * TL::PER_WAVE) copy_v(j + VA, st - TL::PER_WAVE);
                 };
             };
             // the operands of each step's first slots, read at the end of the
@@ -3284,15 +3300,19 @@ fa_prefill_pipe_kernel(const Params p)
                 kpre[i] = wide_ld_k<D>(lds + TB, off, i);
                 vpre[i] = bf16x8_t{};
             }
-            // each step takes the next one's barrier before its last slot
-            pipe_step<D, VG, false>(w, off, lds + TB, lds, sx, sy, py, pw, la, copies(0),
-                                    lds + 2 * TB, lds, kpre, vpre, sync);
+            // each step before a barrier takes it before its last slot
+            if constexpr (BP == 1)
+                pipe_step<D, VG, false>(w, off, lds + TB, lds, sx, sy, py, pw, la, copies(0),
+                                        lds + 2 * TB, lds, kpre, vpre, sync);
+            else
+                pipe_step<D, VG, false>(w, off, lds + TB, lds, sx, sy, py, pw, la, copies(0),
+                                        lds + 2 * TB, lds, kpre, vpre, no_sync);
             pipe_settle<D, VG>(w, sx, pw, la);
             px[0] = __builtin_bit_cast(bf16x8_t, pw[0]);
             px[1] = __builtin_bit_cast(bf16x8_t, pw[1]);
             // step j >= 1: the register sets of block j (even: sx / px, odd:
-            // sy / py) follow from its parity, and its ring stage j % 3 is a
-            // compile-time constant (STAGE), so that every LDS address of
+            // sy / py) follow from its parity, and its ring stage j % NSK is
+            // a compile-time constant (STAGE), so that every LDS address of
             // the step is a lane offset plus an immediate
             auto step = [&](auto odd, auto stage, int j) __attribute__((always_inline)) {
                 constexpr bool ODD = decltype(odd)::value;
@@ -3304,10 +3324,16 @@ fa_prefill_pipe_kernel(const Params p)
                 bf16x8_t(&pp)[2] = ODD ? px : py;
                 bf16x8_t(&pn)[2] = ODD ? py : px;
                 if (needs_mask(j)) BO::mask(s, j * 32, half, p.Sk, lim);
-                // the next step reads K(j + 2) and V(j)
-                pipe_step<D, VG, true>(w, off, Kn, Vp, s, sn, pp, pw, la, copies(j),
-                                       lds + ((ST + 2) % NSK) * TB, lds + ST * TB, kpre, vpre,
-                                       sync);
+                // the next step reads K(j + 2) and V(j); with BP = 2 only the
+                // odd steps take a barrier (the one before the even step)
+                if constexpr (BP == 1 || ODD)
+                    pipe_step<D, VG, true>(w, off, Kn, Vp, s, sn, pp, pw, la, copies(j),
+                                           lds + ((ST + 2) % NSK) * TB, lds + ST * TB, kpre,
+                                           vpre, sync);
+                else
+                    pipe_step<D, VG, true>(w, off, Kn, Vp, s, sn, pp, pw, la, copies(j),
+                                           lds + ((ST + 2) % NSK) * TB, lds + ST * TB, kpre,
+                                           vpre, no_sync);
                 pipe_settle<D, VG>(w, s, pw, la);
                 pn[0] = __builtin_bit_cast(bf16x8_t, pw[0]);
                 pn[1] = __builtin_bit_cast(bf16x8_t, pw[1]);
@@ -3319,25 +3345,33 @@ fa_prefill_pipe_kernel(const Params p)
             const int NBw = min(NB, Lw + 2);
             int j = 1;
             // six steps per trip (j = 1 mod 6), then the rest
+            using S1 = std::integral_constant<int, 1 % NSK>;
+            using S2 = std::integral_constant<int, 2 % NSK>;
+            using S3 = std::integral_constant<int, 3 % NSK>;
+            using S4 = std::integral_constant<int, 4 % NSK>;
+            using S5 = std::integral_constant<int, 5 % NSK>;
+            using S6 = std::integral_constant<int, 6 % NSK>;
             for (; j + 5 < NBw; j += 6) {
-                step(T{}, std::integral_constant<int, 1>{}, j);
-                step(F{}, std::integral_constant<int, 2>{}, j + 1);
-                step(T{}, std::integral_constant<int, 0>{}, j + 2);
-                step(F{}, std::integral_constant<int, 1>{}, j + 3);
-                step(T{}, std::integral_constant<int, 2>{}, j + 4);
-                step(F{}, std::integral_constant<int, 0>{}, j + 5);
+                step(T{}, S1{}, j);
+                step(F{}, S2{}, j + 1);
+                step(T{}, S3{}, j + 2);
+                step(F{}, S4{}, j + 3);
+                step(T{}, S5{}, j + 4);
+                step(F{}, S6{}, j + 5);
             }
             // the rest: at most five steps, from j = 1 mod 6
-            if (j < NBw) step(T{}, std::integral_constant<int, 1>{}, j);
-            if (j + 1 < NBw) step(F{}, std::integral_constant<int, 2>{}, j + 1);
-            if (j + 2 < NBw) step(T{}, std::integral_constant<int, 0>{}, j + 2);
-            if (j + 3 < NBw) step(F{}, std::integral_constant<int, 1>{}, j + 3);
-            if (j + 4 < NBw) step(T{}, std::integral_constant<int, 2>{}, j + 4);
+            if (j < NBw) step(T{}, S1{}, j);
+            if (j + 1 < NBw) step(F{}, S2{}, j + 1);
+            if (j + 2 < NBw) step(T{}, S3{}, j + 2);
+            if (j + 3 < NBw) step(F{}, S4{}, j + 3);
+            if (j + 4 < NBw) step(T{}, S5{}, j + 4);
+            // dead steps: their copies, and the barriers the other waves take
+            // (the one before step jd + 1 where BP divides jd + 1)
             for (int jd = max(1, NBw); jd < NB; ++jd) {
                 auto cp = copies(jd);
 #pragma unroll
                 for (int st = 0; st < LPS; ++st) cp(st);
-                sync();
+                if (BP == 1 || ((jd + 1) & 1) == 0) sync();
             }
             // the last block's P V: V(NB - 1) is in (the last step took the
             // barrier after it; that step's own copies may stay in flight)
