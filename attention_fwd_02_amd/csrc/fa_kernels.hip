@@ -2970,8 +2970,8 @@ __device__ __forceinline__ void pipe_drain_o(PipeRows<D> &w)
 // operands of the step's first kPipePF slots on entry, and those of the next
 // step (K rows at Kn2, V rows at Vn2) on return: before its last slot the
 // step waits for its own reads, then takes the next step's barrier
-// (sync_next) and reads them, so that the next step starts without waiting
-// for LDS.
+// (sync_next; nothing where the next step has none) and reads them, so that
+// the next step starts without waiting for LDS.
 template <int D, bool VG, bool ACC, class CP, class SY>
 __device__ __forceinline__ void pipe_step(PipeRows<D> &w, const OperandOffsets<D> &off,
                                           const char *Kn, const char *Vp, const f32x16_t &s,
