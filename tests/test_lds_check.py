@@ -103,6 +103,15 @@ CASES = {
     "prefill_pingpong_ring5": ({"FA_PREFILL_PP": "5"},
                                lambda: _dense(1, 8, 2, 1200, 1200, 128, False)),
     "prefill_d256": ({}, lambda: _dense(1, 4, 4, 600, 600, 256, True)),
+    # the 8-wave pipelined kernel (six-stage rings, a barrier every second
+    # step): forced on a causal ragged shape (waves past their last block,
+    # odd and even step counts) and a non-causal GQA one with an odd count,
+    # and chosen by the planner at a shape whose 256-row items fill the CUs
+    "prefill_pipe8_causal": ({"FA_PREFILL_PIPE": "2"},
+                             lambda: _dense(2, 4, 4, 700, 700, 128, True)),
+    "prefill_pipe8_gqa": ({"FA_PREFILL_PIPE": "2"},
+                          lambda: _dense(1, 8, 2, 1200, 1100, 128, False)),
+    "prefill_pipe8_default": ({}, lambda: _dense(4, 16, 16, 1024, 1024, 128, True)),
     "decode_split": ({}, lambda: _dense(4, 8, 2, 1, 3000, 128, False, splits=3)),
     "decode_split_d256": ({}, lambda: _dense(4, 8, 2, 1, 3000, 256, False, splits=2)),
     "decode_paged_ragged": ({}, _paged),
